@@ -1,0 +1,292 @@
+"""Plain float64 oracle: the teacher-forcing mask and masked attention + JVP.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Notation (Causal-rCM, arXiv 2606.25473): a side holds ``N_h = T_f * F``
+tokens (``T_f`` tokens per latent frame, ``F`` frames); a chunk holds
+``c`` frames, i.e. ``T = T_f * c`` tokens.  ``tf_layout = 0`` is the plain
+block-causal (DF) sequence of ``N = N_h`` tokens; ``tf_layout = 1`` is the
+teacher-forcing packed sequence [clean | noisy] of ``N = 2 N_h`` tokens
+(section 3.1.1, eq. 8).
+
+Readings of the pages taken here (the display formulas survive only as
+their numbers, so each is the plain reading of the surrounding text):
+
+* clean tokens see every clean token of the same or an earlier chunk
+  (block-causal, bidirectional inside a chunk) and never a noisy token;
+* a noisy token of chunk c sees the clean tokens of chunks strictly before
+  c and every noisy token of its own chunk c, nothing else (section 3.1.1:
+  each noisy chunk attends to its allowed clean history and its own noisy
+  tokens);
+* scores are scaled by 1/sqrt(d) unless a scale is given; the same scale
+  multiplies the score tangent (Appendix B, eqs. 42-43);
+* masked pairs carry probability exactly zero and no tangent: the tangent
+  is taken through the masked map with the mask held fixed (Appendix B,
+  text after eq. 43);
+* the log-sum-exp output is natural-log based (Algorithm 1 returns it
+  beside O and its tangent).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class MaskDesc:
+    tokens_per_frame: int
+    n_frames: int
+    frames_per_chunk: int
+    tf_layout: int
+
+    @property
+    def side_len(self) -> int:
+        return self.tokens_per_frame * self.n_frames
+
+    @property
+    def seq_len(self) -> int:
+        return self.side_len * (2 if self.tf_layout else 1)
+
+    @property
+    def chunk_len(self) -> int:
+        return self.tokens_per_frame * self.frames_per_chunk
+
+    @property
+    def n_chunks(self) -> int:
+        return self.n_frames // self.frames_per_chunk
+
+
+def _as_desc(desc) -> MaskDesc:
+    return desc if isinstance(desc, MaskDesc) else MaskDesc(*desc)
+
+
+# ----------------------------------------------------------------------------
+# Mask (section 2.3; section 3.1.1; section 4 chunking; Table 2 legend)
+# ----------------------------------------------------------------------------
+
+def _side_and_chunk(desc: MaskDesc, idx):
+    """Token index -> (is_noisy, chunk index); works on ints and int arrays."""
+    idx = np.asarray(idx, dtype=np.int64)
+    noisy = (idx >= desc.side_len) if desc.tf_layout else np.zeros(idx.shape, dtype=bool)
+    pos = idx % desc.side_len
+    return noisy, pos // desc.chunk_len
+
+
+def allowed(desc, i, j):
+    """allowed(i, j): may query token i attend to key token j?  (broadcasts)"""
+    desc = _as_desc(desc)
+    qi_noisy, qi_chunk = _side_and_chunk(desc, i)
+    kj_noisy, kj_chunk = _side_and_chunk(desc, j)
+    clean_row = (~qi_noisy) & (~kj_noisy) & (kj_chunk <= qi_chunk)
+    noisy_row = qi_noisy & (((~kj_noisy) & (kj_chunk < qi_chunk)) | (kj_noisy & (kj_chunk == qi_chunk)))
+    return clean_row | noisy_row
+
+
+def mask_dense(desc) -> np.ndarray:
+    """The [N, N] boolean mask, straight from ``allowed``.  Small N only."""
+    desc = _as_desc(desc)
+    n = desc.seq_len
+    return allowed(desc, np.arange(n)[:, None], np.arange(n)[None, :])
+
+
+def allowed_row(desc, i: int) -> np.ndarray:
+    """Boolean [N] vector of the keys query i may see, straight from ``allowed``."""
+    desc = _as_desc(desc)
+    return allowed(desc, np.int64(i), np.arange(desc.seq_len))
+
+
+def row_groups(desc):
+    """Rows that share one (side, chunk) pair, as (first row, stop row).
+
+    ``allowed(i, j)`` depends on i only through its side and chunk, so the
+    rows of one group share one key set; grouping them is vectorisation of
+    the definition, not a different algorithm.
+    """
+    desc = _as_desc(desc)
+    sides = 2 if desc.tf_layout else 1
+    out = []
+    for s in range(sides):
+        for c in range(desc.n_chunks):
+            lo = s * desc.side_len + c * desc.chunk_len
+            out.append((lo, lo + desc.chunk_len))
+    return out
+
+
+def pair_count(desc) -> int:
+    """Number of allowed (query, key) pairs per (b, h), by summing the mask."""
+    desc = _as_desc(desc)
+    total = 0
+    for lo, hi in row_groups(desc):
+        total += int(allowed_row(desc, lo).sum()) * (hi - lo)
+    return total
+
+
+# ----------------------------------------------------------------------------
+# Tile geometry and classification (Appendix B, "sparse custom mask
+# representation": tasks are query blocks; whole key/value blocks outside
+# every allowed range are skipped)
+# ----------------------------------------------------------------------------
+
+def query_blocks(desc, block_q: int):
+    """Query blocks as (start, stop): each side is cut from its own start."""
+    desc = _as_desc(desc)
+    sides = 2 if desc.tf_layout else 1
+    out = []
+    for s in range(sides):
+        base = s * desc.side_len
+        for lo in range(0, desc.side_len, block_q):
+            out.append((base + lo, base + min(lo + block_q, desc.side_len)))
+    return out
+
+
+def key_tiles(desc, block_k: int):
+    """Key tiles as (start, stop), cut from key 0 over the whole sequence."""
+    desc = _as_desc(desc)
+    n = desc.seq_len
+    return [(lo, min(lo + block_k, n)) for lo in range(0, n, block_k)]
+
+
+def tile_classes(desc, block_q: int, block_k: int) -> np.ndarray:
+    """uint8 [n_query_blocks, n_key_tiles]: 0 no allowed pair, 1 every pair
+    allowed, 2 otherwise -- counted from ``allowed`` row by row."""
+    desc = _as_desc(desc)
+    qb = query_blocks(desc, block_q)
+    kt = key_tiles(desc, block_k)
+    n = desc.seq_len
+    edges = np.array([lo for lo, _ in kt] + [n])
+    widths = np.diff(edges)
+    out = np.zeros((len(qb), len(kt)), dtype=np.uint8)
+    cache = {}
+    for bi, (lo, hi) in enumerate(qb):
+        counts = np.zeros(len(kt), dtype=np.int64)
+        for i in range(lo, hi):
+            key = tuple(int(x) for x in _side_and_chunk(desc, i))
+            if key not in cache:
+                row = allowed_row(desc, i).astype(np.int64)
+                cache[key] = np.add.reduceat(row, edges[:-1])
+            counts += cache[key]
+        rows = hi - lo
+        cls = np.where(counts == 0, 0, np.where(counts == rows * widths, 1, 2))
+        out[bi] = cls.astype(np.uint8)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Masked attention and its JVP (Appendix B, eqs. 42-44)
+# ----------------------------------------------------------------------------
+
+def _scale(d: int, scale):
+    return 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(scale)
+
+
+def _rows_forward(q, k, v, tq, tk, tv, keys, scale):
+    """Rows sharing one key set: two-pass softmax, then the analytic tangent.
+
+    s_ij   = scale * q_i . k_j                       (eq. 42)
+    ts_ij  = scale * (tq_i . k_j + q_i . tk_j)       (eq. 43)
+    p_ij   = exp(s_ij - m_i) / l_i over allowed j, 0 elsewhere
+    o_i    = sum_j p_ij v_j,      lse_i = m_i + ln l_i
+    tp_ij  = p_ij (ts_ij - sum_k p_ik ts_ik)         (softmax tangent)
+    to_i   = sum_j tp_ij v_j + sum_j p_ij tv_j       (eq. 44)
+    """
+    kk, vv, tkk, tvv = k[keys], v[keys], tk[keys], tv[keys]
+    s = scale * (q @ kk.T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    p = e / l
+    o = p @ vv
+    lse = (m + np.log(l))[:, 0]
+    ts = scale * (tq @ kk.T + q @ tkk.T)
+    rbar = (p * ts).sum(axis=1, keepdims=True)
+    tp = p * (ts - rbar)
+    to = tp @ vv + p @ tvv
+    return o, to, lse
+
+
+def masked_attention_jvp_slice(q, k, v, tq, tk, tv, desc, scale=None, rows=None):
+    """One (b, h) slice.  q, k, tq, tk are [N, d]; v, tv are [N, dv] (any float
+    type, widened to float64).
+
+    Returns float64 (o [R, dv], to [R, dv], lse [R]) for ``rows`` (default: all).
+    """
+    desc = _as_desc(desc)
+    arrs = [np.asarray(x, dtype=np.float64) for x in (q, k, v, tq, tk, tv)]
+    q, k, v, tq, tk, tv = arrs
+    n, d = q.shape
+    dv = v.shape[1]
+    if n != desc.seq_len:
+        raise ValueError(f"sequence length {n} does not match the mask ({desc.seq_len})")
+    sc = _scale(d, scale)
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((len(rows), dv))
+    to = np.zeros((len(rows), dv))
+    lse = np.full(len(rows), -np.inf)
+    noisy, chunk = _side_and_chunk(desc, rows)
+    groups = {}
+    for pos, key in enumerate(zip(noisy.tolist(), chunk.tolist())):
+        groups.setdefault(key, []).append(pos)
+    for _, positions in groups.items():
+        positions = np.asarray(positions)
+        sel = rows[positions]
+        keys = np.nonzero(allowed_row(desc, int(sel[0])))[0]
+        if keys.size == 0:  # unreachable for these masks; defined as zero output
+            continue
+        o_g, to_g, lse_g = _rows_forward(q[sel], k, v, tq[sel], tk, tv, keys, sc)
+        o[positions], to[positions], lse[positions] = o_g, to_g, lse_g
+    return o, to, lse
+
+
+def masked_attention_jvp(q, k, v, tq, tk, tv, desc, scale=None):
+    """Full [B, H, N, d] tensors -> float64 (o, to, lse [B, H, N])."""
+    q = np.asarray(q)
+    b_, h_, n, d = q.shape
+    o = np.empty((b_, h_, n, d))
+    to = np.empty((b_, h_, n, d))
+    lse = np.empty((b_, h_, n))
+    for b in range(b_):
+        for h in range(h_):
+            o[b, h], to[b, h], lse[b, h] = masked_attention_jvp_slice(
+                q[b, h], k[b, h], v[b, h], tq[b, h], tk[b, h], tv[b, h], desc, scale)
+    return o, to, lse
+
+
+def masked_attention_jvp_rows(slices, desc, rows, scale=None):
+    """Selected rows of one (b, h) slice; ``slices`` = (q, k, v, tq, tk, tv)."""
+    return masked_attention_jvp_slice(*slices, desc, scale=scale, rows=rows)
+
+
+def masked_attention_jvp_scalar(q, k, v, tq, tk, tv, desc, scale=None):
+    """Pure-Python scalar loops over one (b, h) slice; for N <= ~96 only.
+
+    Same definition as ``masked_attention_jvp_slice``, written without NumPy
+    so that the vectorised code is checked by an independent route.
+    """
+    desc = _as_desc(desc)
+    q, k, v, tq, tk, tv = [[[float(x) for x in row] for row in np.asarray(a)] for a in (q, k, v, tq, tk, tv)]
+    n, d = len(q), len(q[0])
+    sc = _scale(d, scale)
+
+    def dot(a, b):
+        return math.fsum(x * y for x, y in zip(a, b))
+
+    o = [[0.0] * d for _ in range(n)]
+    to = [[0.0] * d for _ in range(n)]
+    lse = [-math.inf] * n
+    for i in range(n):
+        keys = [j for j in range(n) if bool(allowed(desc, i, j))]
+        if not keys:
+            continue
+        s = {j: sc * dot(q[i], k[j]) for j in keys}
+        ts = {j: sc * (dot(tq[i], k[j]) + dot(q[i], tk[j])) for j in keys}
+        m = max(s.values())
+        l = math.fsum(math.exp(s[j] - m) for j in keys)
+        p = {j: math.exp(s[j] - m) / l for j in keys}
+        rbar = math.fsum(p[j] * ts[j] for j in keys)
+        for c in range(d):
+            o[i][c] = math.fsum(p[j] * v[j][c] for j in keys)
+            to[i][c] = math.fsum(p[j] * (ts[j] - rbar) * v[j][c] + p[j] * tv[j][c] for j in keys)
+        lse[i] = m + math.log(l)
+    return np.array(o), np.array(to), np.array(lse)
