@@ -1,0 +1,182 @@
+#!/usr/bin/env python3
+"""Benchmark: useful TFLOP/s of fused masked attention forward + JVP on one
+MI355X, and its fraction of the bf16 dense MFMA peak.
+
+One step = one call of the whole operation (attn_jvp_fwd: scores, score
+tangents, masked online softmax, both products with V and tV, epilogue) over
+one batch of seeded synthetic inputs already resident in HBM.  Default
+workload: frame-wise teacher forcing, B=1, H=12, d=128, 21 clean + 21 noisy
+frames of 1560 tokens (N = 65520), bf16.
+
+Useful FLOPs = 12 d x (allowed query-key pairs) x B x H: 2 flops per
+multiply-add over q.k, tq.k, q.tk, p.v, p.tv and (p ts).v, masked pairs not
+counted (partial tiles included), exp and other vector work not counted.
+
+Prints one JSON line.  --gpus above 1 is refused: this build measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4 SIMD x 1024 bf16 flop/clk x 2.4 GHz (dense)
+METRIC = "useful TFLOP/s of masked attn fwd+JVP and % of bf16 MFMA peak, 1 GPU"
+KERNEL_SRC = os.path.join(ROOT, "masked_attention_jvp_amd", "csrc", "attn_jvp_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_d128_tf_framewise_65520.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload id (2..5)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-heads", type=int, default=1)
+    return ap.parse_args()
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(workload_name):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256_16") != kernel_hash() or t.get("workload") != workload_name:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, heads):
+    """The oracle, untuned, on (b, h) slices of the same workload."""
+    import numpy as np
+    import oracle
+    import seeded_inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    flops = 0
+    elapsed = 0.0
+    for h in range(heads):
+        args = [si.slice_values(w, t, 0, h) for t in si.TENSORS]
+        t0 = time.perf_counter()
+        oracle.masked_attention_jvp_slice(*args, w.desc)
+        elapsed += time.perf_counter() - t0
+        flops += 12 * w.head_dim * oracle.pair_count(w.desc)
+    return {
+        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{heads} of {w.batch * w.heads} (b,h) slices of {w.name} (all rows), fp64 NumPy, "
+                  f"{elapsed:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import masked_attention_jvp_amd as aj
+    import seeded_inputs as si
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    w = si.WORKLOADS[args.config]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    x = {}
+    for t in si.TENSORS:
+        bits = si.full_tensor_bits(w, t)
+        x[t] = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        del bits
+    plan = aj.attn_jvp_create(w.desc, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16)
+    o = torch.empty_like(x["q"])
+    to = torch.empty_like(x["q"])
+    lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+    call = lambda: aj.attn_jvp_fwd(plan, *(x[t] for t in si.TENSORS), o, to, lse)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = float(np.mean(per_launch_ms))
+    total_ms = starts[0].elapsed_time(ends[-1])
+    ms_per_step = total_ms / args.steps
+
+    info = plan.info
+    useful = 12 * w.head_dim * info["allowed_pairs_per_head"] * w.batch * w.heads
+    value = useful / (ms_per_step * 1e-3) / 1e12
+    achieved = useful / (avg_ms * 1e-3) / 1e12
+    traffic = traffic_for(w.name)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k RMS-normalised N(0,1), v N(0,1), tangents N(0,%g^2))" % w.tangent_std,
+        "config": {
+            "workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
+            "head_dim": w.head_dim, "tokens_per_frame": w.tokens_per_frame, "n_frames": w.n_frames,
+            "frames_per_chunk": w.frames_per_chunk, "tf_layout": w.tf_layout,
+        },
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "useful_tflop_per_step": round(useful / 1e12, 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": f"fwd_bf16_kernel<{w.head_dim},{info['block_k']},{info['block_q'] // 32}>",
+            "avg_launch_ms": round(avg_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

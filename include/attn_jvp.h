@@ -1,0 +1,141 @@
+/*
+ * attn_jvp.h -- C ABI of the fused block-causal / teacher-forcing masked
+ * attention forward + forward-mode JVP for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Causal-rCM, arXiv 2606.25473, Appendix B, eqs. 42-45):
+ * for every batch b, head h and query row i,
+ *
+ *   s_ij  = scale * q_i . k_j,          ts_ij = scale * (tq_i . k_j + q_i . tk_j)
+ *   p_ij  = softmax over the keys j that the mask allows (0 for masked keys)
+ *   o_i   = sum_j p_ij v_j
+ *   to_i  = sum_j p_ij (ts_ij - sum_k p_ik ts_ik) v_j + sum_j p_ij tv_j
+ *   lse_i = log sum_j exp(s_ij)          (natural log, over allowed keys)
+ *
+ * i.e. o and its directional derivative along (tq, tk, tv) with the mask
+ * held fixed (Appendix B: the mask is a discrete routing object without a
+ * tangent).  The mask comes from four integers (section 2.3, section 3.1.1
+ * eq. 8, section 4 chunking):
+ *
+ *   T_f = tokens_per_frame, F = n_frames, c = frames_per_chunk,
+ *   T = T_f * c tokens per chunk, N_h = T_f * F tokens per side.
+ *   tf_layout = 0: plain block-causal sequence of N = N_h tokens; token i
+ *                  sees every token of its own chunk and of earlier chunks.
+ *   tf_layout = 1: teacher-forcing packed sequence [clean | noisy] of
+ *                  N = 2 N_h tokens.  Clean tokens are block-causal among
+ *                  themselves and never see noisy tokens; a noisy token of
+ *                  chunk k sees the clean tokens of chunks < k and the noisy
+ *                  tokens of chunk k.
+ *
+ * Layout: q, k, v, tq, tk, tv, o, to are contiguous [B, H, N, d] arrays
+ * (d innermost) in one element type: bf16 (ATTN_JVP_BF16, bf16 matrix-core
+ * products with fp32 accumulation, outputs rounded to nearest even) or fp32
+ * (ATTN_JVP_FP32, fp32 arithmetic throughout).  lse is [B, H, N] fp32.
+ * All device pointers must be 16-byte aligned (lse: 4-byte).
+ *
+ * Ownership: the caller owns every buffer.  A plan owns host memory only; the
+ * library never allocates device memory and never synchronises.  attn_jvp_fwd
+ * only enqueues work on the given stream; buffers must stay valid until the
+ * stream reaches that point.  Outputs must not overlap inputs.  A plan is
+ * immutable after creation and may be used from several threads and streams.
+ *
+ * Errors: every function returns ATTN_JVP_OK or an error code and never
+ * throws.  Argument errors are detected before any device work is enqueued.
+ * Faults inside the kernel surface at the caller's next synchronisation.
+ * attn_jvp_last_error_detail() returns a thread-local description of the
+ * last error raised on the calling thread.
+ */
+#ifndef ATTN_JVP_H
+#define ATTN_JVP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct attn_jvp_plan attn_jvp_plan;
+
+/* Mask descriptor (see above).  Every field >= 1 except tf_layout in {0, 1};
+ * n_frames must be a multiple of frames_per_chunk (all chunks equal). */
+typedef struct {
+  int32_t tokens_per_frame;
+  int32_t n_frames;
+  int32_t frames_per_chunk;
+  int32_t tf_layout;
+} attn_jvp_mask_desc;
+
+enum { ATTN_JVP_BF16 = 0, ATTN_JVP_FP32 = 1 };
+
+enum {
+  ATTN_JVP_OK = 0,
+  ATTN_JVP_E_INVALID = 1,            /* bad descriptor, size, dtype, head_dim or scale; aliasing */
+  ATTN_JVP_E_NULL = 2,               /* a required pointer is NULL */
+  ATTN_JVP_E_ALIGN = 3,              /* a pointer is not aligned as required */
+  ATTN_JVP_E_UNSUPPORTED_DEVICE = 4, /* the current HIP device is not gfx950 */
+  ATTN_JVP_E_HIP = 5,                /* a HIP runtime call failed (detail has the HIP error text) */
+  ATTN_JVP_E_NOMEM = 6,              /* host allocation failed */
+  ATTN_JVP_E_OVERFLOW = 7            /* N >= 2^31, N*d >= 2^31 or the grid does not fit */
+};
+
+/* Build a plan for one mask, shape and element type.
+ *   out           receives the plan (set to NULL on error)
+ *   mask          mask descriptor (read, not kept)
+ *   batch, heads  B and H (>= 1)
+ *   head_dim      d: 64 or 128
+ *   dtype         ATTN_JVP_BF16 or ATTN_JVP_FP32
+ *   softmax_scale scale applied to scores and score tangents;
+ *                 <= 0 selects 1/sqrt(d); must be finite
+ * Pure host work: touches no device. */
+int attn_jvp_create(attn_jvp_plan** out, const attn_jvp_mask_desc* mask, int32_t batch,
+                    int32_t heads, int32_t head_dim, int32_t dtype, float softmax_scale);
+
+/* Enqueue o, to (and lse when non-NULL) for the plan's shape on `hip_stream`
+ * (a hipStream_t; NULL is the null stream), on the current HIP device.
+ * Checks pointers, alignment, overlap and the device architecture first. */
+int attn_jvp_fwd(const attn_jvp_plan* plan, const void* q, const void* k, const void* v,
+                 const void* tq, const void* tk, const void* tv, void* o, void* t_o,
+                 float* lse, void* hip_stream);
+
+/* Free a plan.  NULL is accepted. */
+int attn_jvp_destroy(attn_jvp_plan* plan);
+
+/* Static text for an error code. */
+const char* attn_jvp_error_string(int code);
+
+/* Thread-local detail of the last error on this thread ("" if none). */
+const char* attn_jvp_last_error_detail(void);
+
+/* Geometry of the plan's schedule (Appendix B, "sparse custom mask
+ * representation": one task per query block; each task streams only the key
+ * tiles that meet its allowed key ranges).  Query blocks are cut per side
+ * (clean side from token 0, noisy side from token N_h); key tiles are cut
+ * from key 0 over the whole sequence.  Any output pointer may be NULL.
+ *   seq_len                N
+ *   block_q, block_k       query rows per block, keys per tile
+ *   n_query_blocks         query blocks per (b, h)
+ *   n_key_tiles            key tiles per (b, h)
+ *   allowed_pairs_per_head allowed (query, key) pairs per (b, h)
+ *   visited_tiles_per_head key tiles the kernel streams, summed over blocks */
+int attn_jvp_plan_info(const attn_jvp_plan* plan, int64_t* seq_len, int32_t* block_q,
+                       int32_t* block_k, int32_t* n_query_blocks, int32_t* n_key_tiles,
+                       int64_t* allowed_pairs_per_head, int64_t* visited_tiles_per_head);
+
+/* Per-row allowed key ranges, as the kernel uses them: host_out[4*i + 0..3]
+ * = lo1, hi1, lo2, hi2 (half-open, empty when lo >= hi) for rows
+ * i = 0..N-1.  n is the capacity of host_out in int32 elements (>= 4N). */
+int attn_jvp_row_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
+
+/* Tile map, row-major [n_query_blocks][n_key_tiles], query blocks in index
+ * order (clean side first): 0 = not streamed, 1 = streamed, every pair
+ * allowed (no masking), 2 = streamed, some pairs masked.  Two further codes
+ * flag schedule defects and never occur in a correct plan: 3 = streamed but
+ * no pair allowed, 4 = not streamed although a pair is allowed.
+ * n is the capacity of host_out in bytes. */
+int attn_jvp_tile_map(const attn_jvp_plan* plan, uint8_t* host_out, size_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_JVP_H */

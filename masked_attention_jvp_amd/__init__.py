@@ -1,0 +1,234 @@
+"""Python binding of libattn_jvp.so: fused teacher-forcing / block-causal
+masked attention forward + JVP on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the operation runs in the HIP
+library; PyTorch provides device memory and the stream.  The functions
+mirror the C ABI of ``include/attn_jvp.h`` one to one:
+
+    attn_jvp_create, attn_jvp_fwd, attn_jvp_destroy, attn_jvp_error_string,
+    attn_jvp_last_error_detail, attn_jvp_plan_info, attn_jvp_row_ranges,
+    attn_jvp_tile_map
+
+plus ``masked_attention_jvp(...)``, which allocates the outputs and calls
+``attn_jvp_fwd`` on the current stream.  If the library is not built the
+import of this module still works, but every call raises ``AttnJvpError``;
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+
+__all__ = [
+    "ATTN_JVP_BF16", "ATTN_JVP_FP32", "AttnJvpError", "Plan", "library_path",
+    "attn_jvp_create", "attn_jvp_fwd", "attn_jvp_destroy", "attn_jvp_error_string",
+    "attn_jvp_last_error_detail", "attn_jvp_plan_info", "attn_jvp_row_ranges",
+    "attn_jvp_tile_map", "masked_attention_jvp",
+]
+
+ATTN_JVP_BF16 = 0
+ATTN_JVP_FP32 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libattn_jvp.so")
+
+
+class AttnJvpError(RuntimeError):
+    def __init__(self, msg, code=None):
+        super().__init__(msg)
+        self.code = code
+
+
+class _MaskDesc(ctypes.Structure):
+    _fields_ = [("tokens_per_frame", ctypes.c_int32), ("n_frames", ctypes.c_int32),
+                ("frames_per_chunk", ctypes.c_int32), ("tf_layout", ctypes.c_int32)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(library_path):
+            raise AttnJvpError(f"{library_path} is not built; run `python -m masked_attention_jvp_amd.build`")
+        lib = ctypes.CDLL(library_path)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        P = ctypes.POINTER
+        lib.attn_jvp_create.argtypes = [P(vp), P(_MaskDesc), i32, i32, i32, i32, f32]
+        lib.attn_jvp_fwd.argtypes = [vp] * 9 + [vp, vp]
+        lib.attn_jvp_destroy.argtypes = [vp]
+        lib.attn_jvp_error_string.argtypes = [ctypes.c_int]
+        lib.attn_jvp_error_string.restype = ctypes.c_char_p
+        lib.attn_jvp_last_error_detail.argtypes = []
+        lib.attn_jvp_last_error_detail.restype = ctypes.c_char_p
+        lib.attn_jvp_plan_info.argtypes = [vp, P(i64), P(i32), P(i32), P(i32), P(i32), P(i64), P(i64)]
+        lib.attn_jvp_row_ranges.argtypes = [vp, P(i32), ctypes.c_size_t]
+        lib.attn_jvp_tile_map.argtypes = [vp, P(ctypes.c_uint8), ctypes.c_size_t]
+        for name in ("attn_jvp_create", "attn_jvp_fwd", "attn_jvp_destroy", "attn_jvp_plan_info",
+                     "attn_jvp_row_ranges", "attn_jvp_tile_map"):
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def attn_jvp_error_string(code: int) -> str:
+    return _load().attn_jvp_error_string(code).decode()
+
+
+def attn_jvp_last_error_detail() -> str:
+    return _load().attn_jvp_last_error_detail().decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise AttnJvpError(f"{what}: {attn_jvp_error_string(code)}: {attn_jvp_last_error_detail()}", code)
+
+
+class Plan:
+    """Owns one attn_jvp_plan*; immutable after creation."""
+
+    def __init__(self, handle, desc, batch, heads, head_dim, dtype, scale):
+        self._h = handle
+        self.desc = tuple(desc)
+        self.batch, self.heads, self.head_dim, self.dtype, self.scale = batch, heads, head_dim, dtype, scale
+        info = attn_jvp_plan_info(self)
+        self.seq_len = info["seq_len"]
+        self.info = info
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise AttnJvpError("plan already destroyed")
+        return self._h
+
+    @property
+    def shape(self):
+        return (self.batch, self.heads, self.seq_len, self.head_dim)
+
+    def __del__(self):
+        try:
+            attn_jvp_destroy(self)
+        except Exception:
+            pass
+
+
+def attn_jvp_create(desc, batch: int, heads: int, head_dim: int, dtype: int = ATTN_JVP_BF16,
+                    softmax_scale: float = 0.0) -> Plan:
+    """desc = (tokens_per_frame, n_frames, frames_per_chunk, tf_layout)."""
+    lib = _load()
+    h = ctypes.c_void_p()
+    d = _MaskDesc(*[int(x) for x in desc])
+    _check(lib.attn_jvp_create(ctypes.byref(h), ctypes.byref(d), int(batch), int(heads), int(head_dim),
+                               int(dtype), float(softmax_scale or 0.0)), "attn_jvp_create")
+    return Plan(h, desc, batch, heads, head_dim, dtype, softmax_scale)
+
+
+def attn_jvp_destroy(plan: Plan) -> None:
+    if plan is not None and plan._h is not None:
+        _check(_load().attn_jvp_destroy(plan._h), "attn_jvp_destroy")
+        plan._h = None
+
+
+def attn_jvp_plan_info(plan: Plan) -> dict:
+    i64, i32 = ctypes.c_int64, ctypes.c_int32
+    vals = [i64(), i32(), i32(), i32(), i32(), i64(), i64()]
+    _check(_load().attn_jvp_plan_info(plan.handle, *[ctypes.byref(v) for v in vals]), "attn_jvp_plan_info")
+    keys = ["seq_len", "block_q", "block_k", "n_query_blocks", "n_key_tiles", "allowed_pairs_per_head",
+            "visited_tiles_per_head"]
+    return {k: v.value for k, v in zip(keys, vals)}
+
+
+def attn_jvp_row_ranges(plan: Plan) -> np.ndarray:
+    n = plan.seq_len
+    out = np.empty((n, 4), dtype=np.int32)
+    _check(_load().attn_jvp_row_ranges(plan.handle, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), out.size),
+           "attn_jvp_row_ranges")
+    return out
+
+
+def attn_jvp_tile_map(plan: Plan) -> np.ndarray:
+    nq, nk = plan.info["n_query_blocks"], plan.info["n_key_tiles"]
+    out = np.empty((nq, nk), dtype=np.uint8)
+    _check(_load().attn_jvp_tile_map(plan.handle, out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), out.size),
+           "attn_jvp_tile_map")
+    return out
+
+
+def _torch_dtype(plan):
+    import torch
+    return torch.bfloat16 if plan.dtype == ATTN_JVP_BF16 else torch.float32
+
+
+def _check_tensor(name, t, plan, shape):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise AttnJvpError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise AttnJvpError(f"{name} must be on a GPU device (got {t.device})")
+    if t.dtype != _torch_dtype(plan):
+        raise AttnJvpError(f"{name} has dtype {t.dtype}, plan expects {_torch_dtype(plan)}")
+    if tuple(t.shape) != tuple(shape):
+        raise AttnJvpError(f"{name} has shape {tuple(t.shape)}, plan expects {tuple(shape)}")
+    if not t.is_contiguous():
+        raise AttnJvpError(f"{name} must be contiguous")
+
+
+def attn_jvp_fwd(plan: Plan, q, k, v, tq, tk, tv, o, t_o, lse=None, stream=None) -> None:
+    """Enqueue the operation on `stream` (default: torch's current stream)."""
+    import torch
+    ins = dict(q=q, k=k, v=v, tq=tq, tk=tk, tv=tv, o=o, t_o=t_o)
+    for name, t in ins.items():
+        _check_tensor(name, t, plan, plan.shape)
+    dev = q.device
+    for name, t in ins.items():
+        if t.device != dev:
+            raise AttnJvpError(f"{name} is on {t.device}, q is on {dev}")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != plan.shape[:3] or not lse.is_contiguous() \
+                or lse.device != dev:
+            raise AttnJvpError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        code = _load().attn_jvp_fwd(plan.handle, *[ctypes.c_void_p(t.data_ptr()) for t in ins.values()],
+                                    ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
+                                    ctypes.c_void_p(stream.cuda_stream))
+    _check(code, "attn_jvp_fwd")
+
+
+_plan_cache = {}
+_plan_lock = threading.Lock()
+
+
+def _cached_plan(desc, shape, dtype, scale):
+    key = (tuple(int(x) for x in desc), tuple(shape), dtype, float(scale or 0.0))
+    with _plan_lock:
+        p = _plan_cache.get(key)
+        if p is None:
+            b, h, _, d = shape
+            p = attn_jvp_create(desc, b, h, d, dtype, scale or 0.0)
+            if tuple(p.shape) != tuple(shape):
+                raise AttnJvpError(f"mask {tuple(desc)} gives N={p.seq_len}, tensors have N={shape[2]}")
+            _plan_cache[key] = p
+        return p
+
+
+def masked_attention_jvp(q, k, v, tq, tk, tv, desc, scale=None, return_lse=False):
+    """(o, t_o[, lse]) for [B, H, N, d] bf16 or fp32 CUDA tensors."""
+    import torch
+    dtype = ATTN_JVP_BF16 if q.dtype == torch.bfloat16 else ATTN_JVP_FP32
+    plan = _cached_plan(desc, q.shape, dtype, scale)
+    o = torch.empty_like(q)
+    t_o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    attn_jvp_fwd(plan, q, k, v, tq, tk, tv, o, t_o, lse)
+    return (o, t_o, lse) if return_lse else (o, t_o)

@@ -1,0 +1,134 @@
+// mask_index.h -- index arithmetic of the teacher-forcing / block-causal mask
+// and of the tile schedule, shared by the host planner and the device kernels.
+//
+// Mask (Causal-rCM, arXiv 2606.25473, section 2.3 and section 3.1.1 eq. 8;
+// chunking from section 4): with T tokens per chunk and N_h tokens per side,
+//   clean row of chunk c  -> keys [0, (c+1) T)
+//   noisy row of chunk c  -> keys [0, c T)  and  [N_h + c T, N_h + (c+1) T)
+// so every row's key set is at most two half-open intervals.
+//
+// Schedule (Appendix B, "sparse custom mask representation" and Algorithm 1:
+// one task per query block, streaming only the key blocks that intersect the
+// task's key ranges, with the same schedule for scores and score tangents):
+// query blocks are cut per side, key tiles from key 0 over the whole
+// sequence.  The rows of one block lie on one side and in consecutive
+// chunks, so the union of their key sets is again at most two intervals,
+// which the kernel walks tile by tile.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define AJ_HD __host__ __device__ __forceinline__
+#else
+#define AJ_HD inline
+#endif
+
+namespace attn_jvp {
+
+struct MaskGeom {
+  int32_t side_len;   // N_h
+  int32_t chunk_len;  // T
+  int32_t tf;         // 0 block-causal, 1 teacher-forcing [clean | noisy]
+  int32_t seq_len;    // N = N_h * (1 + tf)
+};
+
+// Half-open key intervals [lo1, hi1) and [lo2, hi2); empty when lo >= hi.
+struct Ranges {
+  int32_t lo1, hi1, lo2, hi2;
+};
+
+// Tile-index intervals [a0, a1) and [b0, b1), disjoint, in walking order.
+struct TileSpans {
+  int32_t a0, a1, b0, b1;
+};
+
+AJ_HD int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+AJ_HD bool is_noisy(const MaskGeom& g, int32_t i) { return g.tf != 0 && i >= g.side_len; }
+
+AJ_HD int32_t chunk_of(const MaskGeom& g, int32_t i) {
+  return (is_noisy(g, i) ? i - g.side_len : i) / g.chunk_len;
+}
+
+// Allowed keys of query row i.
+AJ_HD Ranges row_ranges(const MaskGeom& g, int32_t i) {
+  const int32_t c = chunk_of(g, i);
+  if (!is_noisy(g, i)) return Ranges{0, (c + 1) * g.chunk_len, 0, 0};
+  return Ranges{0, c * g.chunk_len, g.side_len + c * g.chunk_len, g.side_len + (c + 1) * g.chunk_len};
+}
+
+AJ_HD bool in_ranges(const Ranges& r, int32_t j) {
+  return (j >= r.lo1 && j < r.hi1) || (j >= r.lo2 && j < r.hi2);
+}
+
+// Does one interval of r contain all of [k0, k1)?
+AJ_HD bool covers(const Ranges& r, int32_t k0, int32_t k1) {
+  return (k0 >= r.lo1 && k1 <= r.hi1) || (k0 >= r.lo2 && k1 <= r.hi2);
+}
+
+AJ_HD bool meets(const Ranges& r, int32_t k0, int32_t k1) {
+  const bool a = r.lo1 < r.hi1 && k0 < r.hi1 && r.lo1 < k1;
+  const bool b = r.lo2 < r.hi2 && k0 < r.hi2 && r.lo2 < k1;
+  return a || b;
+}
+
+AJ_HD int32_t blocks_per_side(const MaskGeom& g, int32_t block_q) { return cdiv(g.side_len, block_q); }
+
+AJ_HD int32_t n_query_blocks(const MaskGeom& g, int32_t block_q) {
+  return blocks_per_side(g, block_q) * (g.tf ? 2 : 1);
+}
+
+AJ_HD int32_t n_key_tiles(const MaskGeom& g, int32_t block_k) { return cdiv(g.seq_len, block_k); }
+
+// Rows [*r0, *r1) of query block qb (clean-side blocks first).
+AJ_HD void qblock_rows(const MaskGeom& g, int32_t block_q, int32_t qb, int32_t* r0, int32_t* r1) {
+  const int32_t nbs = blocks_per_side(g, block_q);
+  const int32_t side = qb / nbs, k = qb - side * nbs;
+  const int32_t base = side * g.side_len;
+  const int32_t end = (k + 1) * block_q < g.side_len ? (k + 1) * block_q : g.side_len;
+  *r0 = base + k * block_q;
+  *r1 = base + end;
+}
+
+// Heavy-first launch order within one (b, h): a block's work grows with its
+// last chunk, and clean block k and noisy block k carry about the same work,
+// so walk k downwards, alternating sides.
+AJ_HD int32_t heavy_first_qblock(const MaskGeom& g, int32_t block_q, int32_t t) {
+  const int32_t nbs = blocks_per_side(g, block_q);
+  if (!g.tf) return nbs - 1 - t;
+  return (t & 1) * nbs + (nbs - 1 - (t >> 1));
+}
+
+// Union of the key sets of rows [r0, r1) (one side, consecutive chunks).
+AJ_HD Ranges block_ranges(const MaskGeom& g, int32_t r0, int32_t r1) {
+  const Ranges first = row_ranges(g, r0);
+  const Ranges last = row_ranges(g, r1 - 1);
+  if (!is_noisy(g, r0)) return Ranges{0, last.hi1, 0, 0};
+  return Ranges{0, last.hi1, first.lo2, last.hi2};
+}
+
+AJ_HD TileSpans block_tiles(const Ranges& u, int32_t block_k) {
+  TileSpans s{0, 0, 0, 0};
+  if (u.hi1 > u.lo1) {
+    s.a0 = u.lo1 / block_k;
+    s.a1 = cdiv(u.hi1, block_k);
+  }
+  if (u.hi2 > u.lo2) {
+    s.b0 = u.lo2 / block_k;
+    s.b1 = cdiv(u.hi2, block_k);
+    if (s.b0 < s.a1) s.b0 = s.a1;
+    if (s.b1 < s.b0) s.b1 = s.b0;
+  }
+  return s;
+}
+
+AJ_HD int32_t span_count(const TileSpans& s) { return (s.a1 - s.a0) + (s.b1 - s.b0); }
+
+// Tile index of the it-th streamed tile.
+AJ_HD int32_t span_tile(const TileSpans& s, int32_t it) {
+  const int32_t na = s.a1 - s.a0;
+  return it < na ? s.a0 + it : s.b0 + (it - na);
+}
+
+}  // namespace attn_jvp

@@ -1,0 +1,146 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no compute calls).
+
+* the library loads and exports every function include/attn_jvp.h declares;
+* plan creation validates its arguments and reports errors by code;
+* the plan's per-row key ranges equal the oracle's mask bit for bit;
+* the plan's tile map (what the kernel streams and masks) equals the
+  oracle's tile classification bit for bit, at small sizes with ragged tails
+  and at the full workload sizes;
+* pair and tile counts agree with the oracle and with closed forms.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import MaskDesc
+import masked_attention_jvp_amd as aj
+from seeded_inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_jvp.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(aj.library_path), reason="libattn_jvp.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_jvp_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) == 8
+    lib = ctypes.CDLL(aj.library_path)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_error_strings():
+    assert aj.attn_jvp_error_string(0) == "ok"
+    assert "null" in aj.attn_jvp_error_string(2)
+    assert aj.attn_jvp_error_string(99) == "unknown error code"
+
+
+@pytest.mark.parametrize("desc, b, h, d, dt, code", [
+    ((0, 3, 1, 1), 1, 1, 64, 0, 1),        # tokens_per_frame < 1
+    ((4, 3, 2, 1), 1, 1, 64, 0, 1),        # n_frames not a multiple of frames_per_chunk
+    ((4, 3, 1, 2), 1, 1, 64, 0, 1),        # tf_layout not in {0, 1}
+    ((4, 3, 1, 1), 0, 1, 64, 0, 1),        # batch < 1
+    ((4, 3, 1, 1), 1, 1, 96, 0, 1),        # unsupported head_dim
+    ((4, 3, 1, 1), 1, 1, 64, 7, 1),        # unknown dtype
+    ((1 << 20, 1 << 11, 1, 1), 1, 1, 64, 0, 7),  # sequence too long
+])
+def test_create_rejects_bad_arguments(desc, b, h, d, dt, code):
+    with pytest.raises(aj.AttnJvpError) as e:
+        aj.attn_jvp_create(desc, b, h, d, dt)
+    assert e.value.code == code
+    assert aj.attn_jvp_last_error_detail()
+
+
+def test_create_rejects_non_finite_scale():
+    with pytest.raises(aj.AttnJvpError) as e:
+        aj.attn_jvp_create((4, 3, 1, 1), 1, 1, 64, 0, float("nan"))
+    assert e.value.code == 1
+
+
+def test_fwd_argument_errors_before_any_device_call():
+    lib = aj._load()
+    p = aj.attn_jvp_create((4, 3, 1, 1), 1, 1, 64, aj.ATTN_JVP_BF16)
+    good = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(8)]
+    null = list(good)
+    null[2] = ctypes.c_void_p(0)
+    assert lib.attn_jvp_fwd(p.handle, *null, None, None) == 2
+    assert lib.attn_jvp_fwd(None, *good, None, None) == 2
+    mis = list(good)
+    mis[4] = ctypes.c_void_p(0x10008)
+    assert lib.attn_jvp_fwd(p.handle, *mis, None, None) == 3
+    alias = list(good)
+    alias[6] = alias[0]  # o aliases q
+    assert lib.attn_jvp_fwd(p.handle, *alias, None, None) == 1
+    assert "overlaps" in aj.attn_jvp_last_error_detail()
+
+
+def _ranges_to_mask(rr, n):
+    keys = np.arange(n)
+    lo1, hi1, lo2, hi2 = (rr[:, i:i + 1] for i in range(4))
+    return ((keys >= lo1) & (keys < hi1)) | ((keys >= lo2) & (keys < hi2))
+
+
+SMALL = [(16, 3, 1, 1), (50, 5, 1, 1), (40, 6, 3, 1), (37, 7, 1, 0), (100, 2, 2, 0), (1, 5, 1, 1),
+         (3, 9, 3, 1), (130, 3, 1, 1), (64, 4, 2, 1)]
+
+
+@pytest.mark.parametrize("desc", SMALL)
+@pytest.mark.parametrize("dtype", [aj.ATTN_JVP_BF16, aj.ATTN_JVP_FP32])
+def test_row_ranges_match_oracle_mask(desc, dtype):
+    p = aj.attn_jvp_create(desc, 1, 1, 64, dtype)
+    n = p.seq_len
+    assert n == MaskDesc(*desc).seq_len
+    assert np.array_equal(_ranges_to_mask(aj.attn_jvp_row_ranges(p), n), oracle.mask_dense(desc))
+
+
+@pytest.mark.parametrize("desc", SMALL)
+@pytest.mark.parametrize("dtype, d", [(aj.ATTN_JVP_BF16, 128), (aj.ATTN_JVP_BF16, 64), (aj.ATTN_JVP_FP32, 64)])
+def test_tile_map_matches_oracle(desc, dtype, d):
+    p = aj.attn_jvp_create(desc, 1, 1, d, dtype)
+    info = p.info
+    want = oracle.tile_classes(desc, info["block_q"], info["block_k"])
+    got = aj.attn_jvp_tile_map(p)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+    assert info["visited_tiles_per_head"] == int((got > 0).sum())
+    assert info["allowed_pairs_per_head"] == oracle.pair_count(desc)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_tile_map_matches_oracle_at_workload_size(cfg):
+    w = WORKLOADS[cfg]
+    p = aj.attn_jvp_create(w.desc, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16)
+    info = p.info
+    got = aj.attn_jvp_tile_map(p)
+    want = oracle.tile_classes(w.desc, info["block_q"], info["block_k"])
+    assert np.array_equal(got, want)
+    assert info["allowed_pairs_per_head"] == oracle.pair_count(w.desc)
+    assert info["visited_tiles_per_head"] == int((want > 0).sum())
+    # rows of every query block: the kernel's row ranges agree with the mask on sampled rows
+    rr = aj.attn_jvp_row_ranges(p)
+    rng = np.random.default_rng(cfg)
+    for i in rng.choice(p.seq_len, 64, replace=False):
+        keys = np.arange(p.seq_len)
+        mine = ((keys >= rr[i, 0]) & (keys < rr[i, 1])) | ((keys >= rr[i, 2]) & (keys < rr[i, 3]))
+        assert np.array_equal(mine, oracle.allowed_row(w.desc, int(i)))
+
+
+def test_plan_info_geometry():
+    p = aj.attn_jvp_create((1560, 21, 1, 1), 1, 12, 128, aj.ATTN_JVP_BF16)
+    info = p.info
+    assert info["seq_len"] == 65520
+    bq, bk = info["block_q"], info["block_k"]
+    assert info["n_query_blocks"] == 2 * -(-32760 // bq)
+    assert info["n_key_tiles"] == -(-65520 // bk)
+    assert info["allowed_pairs_per_head"] == 1_124_323_200
