@@ -11,17 +11,23 @@
 // both take the same rescale and the same 1/l, so their sum is carried
 // directly.
 //
-// bf16 kernel layout (one workgroup = one query block of 32*NW rows, one
-// wave = 32 query rows, 64-wide wavefronts on v_mfma_f32_32x32x16_bf16):
+// bf16 kernel (one workgroup = one query block of 32*NW rows, one wave = 32
+// query rows, 64-wide wavefronts, v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation):
 // * scores are formed transposed, S^T = K Q^T, so lane l owns query l%32 and
-//   16 of the 32 keys of a subtile; row max and row sums are in-lane plus one
+//   16 of the 32 keys of a tile; row max and row sums stay in-lane plus one
 //   permlane32 swap with the partner lane l^32;
-// * inside each 32-key subtile, MFMA row m stands for key perm32(m) (bits 2
-//   and 3 swapped).  With that order the S^T accumulator, converted to bf16,
-//   is already the B operand of O^T += V^T P^T, so no shuffle is needed;
-// * K and tK sit in LDS row-major, V and tV transposed ([d][key]), each with
-//   an XOR swizzle on 16-byte groups so the 16-byte fragment reads of a wave
-//   hit distinct banks;
+// * the S^T accumulator, rounded to bf16, is directly the B operand of
+//   O^T += V^T P^T: its 8 values per 16-key chunk are keys {4h..4h+3} and
+//   {8+4h..8+4h+3}, and V^T is fetched in exactly that key order with the
+//   gfx950 transposing LDS read (ds_read_b64_tr_b16), so V stays row-major;
+// * K, tK, V, tV tiles of 32 keys go HBM -> LDS by buffer_load ... lds (no
+//   registers, no VALU), into a ring of 4 stages, 3 tiles ahead of use; rows
+//   are XOR-swizzled in 16-byte groups so the fragment reads are
+//   bank-conflict free; loads past the end of the sequence return zeros;
+// * software pipelining: the score MFMAs of tile j+1 sit in the same basic
+//   block as the exp/convert VALU work and the P.V MFMAs of tile j, so the
+//   matrix cores and the vector ALUs of one wave overlap;
 // * rescaling is lazy: the stored row max only moves when a tile's max
 //   exceeds it by more than 2^8 (in exp2 units), which keeps every p~ <= 256
 //   and is exact in real arithmetic because l, r and the accumulators all
@@ -33,6 +39,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_jvp_launch.h"
 #include "mask_index.h"
 
@@ -42,6 +50,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLazyRescaleLog2 = 8.0f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -77,33 +87,78 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
+// 16 bytes per lane from global straight into LDS at lds + 16 * lane.
+__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds, 16, byte_off, 0, 0, 0);
+}
+__device__ __forceinline__ u32x2 read_tr16(const uint16_t* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)p));
+}
 
-// Key order inside a 32-key subtile: MFMA row m holds key perm32(m).
-__device__ __forceinline__ int perm32(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
+// 16-byte group swizzle of a tile row: group g of row `key` is stored at
+// g ^ row_swz(key).  Any 8 consecutive rows get 8 distinct values (for the
+// 16-byte fragment reads of 8 lanes), and any 4 rows 4k..4k+3 get values that
+// keep 32-byte pairs apart (for the transposing reads).
+__device__ __forceinline__ int row_swz(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
 
-// 16-byte group swizzles of the K rows and of the transposed V rows.
-__device__ __forceinline__ int k_swz(int key) { return (key & 3) | ((key >> 1) & 4); }
-template <int BC>
-__device__ __forceinline__ int v_swz(int d) { return ((d & 7) ^ ((d >> 3) & 7)) & (BC / 8 - 1); }
+// Workgroup barrier without a memory fence: the fence of __syncthreads()
+// would wait for every LDS DMA in flight.  Visibility of the tile about to be
+// read comes from the explicit vmcnt wait before it; the memory clobber keeps
+// the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int D, int BC, int NW>
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Instruction order for the pipelined block of one tile (masks: 0x008 MFMA,
+// 0x002 VALU, 0x100 LDS read): the 3*KS score MFMAs of the next tile are
+// spread over the softmax VALU work of the current one, two K-fragment
+// reads ahead; the transposing V reads of the first P.V group are issued
+// during that phase and every later group's reads one group ahead.
+template <int KS, int DC>
+__device__ __forceinline__ void schedule_hints() {
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (s == KS - 1) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 2 * DC; ++g) {
+    if (g + 1 < 2 * DC) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+  }
+}
+
+template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
-  static_assert(BC == 64, "the swizzles and subtile order assume 64-key tiles");
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-  constexpr int NT = NW * 64;
+  constexpr int BC = kBf16BlockK;            // keys per tile (= one MFMA subtile)
+  static_assert(BC == 32, "one 32-key subtile per tile");
+  constexpr int STAGES = 4;                  // LDS ring depth; tiles j+1..j+3 in flight
   constexpr int BR = NW * 32;
-  constexpr int DCH = D / 8;                 // 16-byte chunks per row
   constexpr int KS = D / 16;                 // k-steps of the score products
   constexpr int DC = D / 32;                 // 32-wide column blocks of the outputs
-  constexpr int NSUB = BC / 32;              // 32-key subtiles per tile
-  constexpr int KCH = BC * DCH / NT;         // K chunks staged per thread
-  constexpr int VIT = (BC / 2) * DCH / NT;   // V items (2 keys x 8 d) per thread
-  static_assert(KCH * NT == BC * DCH && VIT * NT == (BC / 2) * DCH, "staging split");
+  constexpr int CPR = D / 8;                 // 16-byte groups per row
+  constexpr int TILE = BC * D;               // elements per tensor per stage
+  constexpr int LOADS = TILE * 2 / 1024 / NW;  // 1 KB DMA loads per wave per tensor
+  constexpr int LPT = 4 * LOADS;             // DMA loads per wave per tile
+  static_assert(LOADS * NW * 1024 == TILE * 2, "DMA split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t stK[BC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * BC];
-  __shared__ __attribute__((aligned(16))) uint16_t stV[D * BC];
+  // The four ring stages are separate objects so that the compiler can tell
+  // a read of one stage from a DMA into another (one shared object would make
+  // it wait for every DMA in flight before each transposing read).
+  __shared__ __attribute__((aligned(1024))) uint16_t ring0[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring1[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring2[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring3[4 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -119,78 +174,68 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   const int ntiles = span_count(sp);
 
   const size_t base = (size_t)bh * (size_t)N * D;
-  const uint16_t* __restrict__ Qg = (const uint16_t*)p.q + base;
-  const uint16_t* __restrict__ Kg = (const uint16_t*)p.k + base;
-  const uint16_t* __restrict__ Vg = (const uint16_t*)p.v + base;
-  const uint16_t* __restrict__ tQg = (const uint16_t*)p.tq + base;
-  const uint16_t* __restrict__ tKg = (const uint16_t*)p.tk + base;
-  const uint16_t* __restrict__ tVg = (const uint16_t*)p.tv + base;
+  const int slice_bytes = N * D * 2;
+  const __amdgpu_buffer_rsrc_t rsrc[4] = {
+      make_rsrc((const uint16_t*)p.k + base, slice_bytes), make_rsrc((const uint16_t*)p.tk + base, slice_bytes),
+      make_rsrc((const uint16_t*)p.v + base, slice_bytes), make_rsrc((const uint16_t*)p.tv + base, slice_bytes)};
 
   const int row = r0 + wave * 32 + n;
   const bool row_ok = row < r1;
   const Ranges rr = row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0};
 
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  // Q and tQ fragments stay in registers for the whole task (B operands).
   u32x4 qf[KS], tqf[KS];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)p.q + base, slice_bytes);
+    const __amdgpu_buffer_rsrc_t rtq = make_rsrc((const uint16_t*)p.tq + base, slice_bytes);
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const size_t off = (size_t)row * D + 16 * s + 8 * h;
-    qf[s] = row_ok ? *(const u32x4*)(Qg + off) : zero4;
-    tqf[s] = row_ok ? *(const u32x4*)(tQg + off) : zero4;
+    for (int s = 0; s < KS; ++s) {
+      const int off = (row * D + 16 * s + 8 * h) * 2;
+      qf[s] = load16(rq, off);
+      tqf[s] = load16(rtq, off);
+    }
   }
 
-  // ---- global -> register prefetch of one tile -------------------------------
-  // Buffer loads: reads past the end of the (b, h) slice return zeros.
-  const int slice_bytes = N * D * 2;
-  const __amdgpu_buffer_rsrc_t rK = make_rsrc(Kg, slice_bytes);
-  const __amdgpu_buffer_rsrc_t rtK = make_rsrc(tKg, slice_bytes);
-  const __amdgpu_buffer_rsrc_t rV = make_rsrc(Vg, slice_bytes);
-  const __amdgpu_buffer_rsrc_t rtV = make_rsrc(tVg, slice_bytes);
-  u32x4 kr[KCH], tkr[KCH], vr[VIT][2], tvr[VIT][2];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BC;
+  auto stage = [&](auto st) -> uint16_t* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return ring0;
+    else if constexpr (S == 1) return ring1;
+    else if constexpr (S == 2) return ring2;
+    else return ring3;
+  };
+
+  // DMA of tile t into stage ST.  Lane L of 1 KB block `blk` fills LDS group
+  // (row, pc) and fetches global group pc ^ row_swz(row) of that row.
+  auto issue = [&](auto st, int t) {
+    if (t >= ntiles) return;
+    const int k0 = span_tile(sp, t) * BC;
+    uint16_t* dst = stage(st);
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * NT;
-      const int off = ((k0 + c / DCH) * D + (c % DCH) * 8) * 2;
-      kr[i] = load16(rK, off);
-      tkr[i] = load16(rtK, off);
-    }
+    for (int i = 0; i < LOADS; ++i) {
+      const int blk = wave * LOADS + i;
+      const int r = blk * (64 / CPR) + lane / CPR;
+      const int voff = ((k0 + r) * D + (((lane % CPR) ^ row_swz(r)) << 3)) * 2;
 #pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int it = tid + i * NT;
-      const int off = ((k0 + 2 * (it / DCH)) * D + (it % DCH) * 8) * 2;
-      vr[i][0] = load16(rV, off);
-      tvr[i][0] = load16(rtV, off);
-      vr[i][1] = load16(rV, off + 2 * D);
-      tvr[i][1] = load16(rtV, off + 2 * D);
+      for (int tt = 0; tt < 4; ++tt) load16_lds(rsrc[tt], dst + tt * TILE + blk * 512, voff);
     }
   };
-  // ---- register -> LDS, K row-major, V transposed ----------------------------
-  auto lstore = [&]() {
+
+  // S^T and tS^T of the tile held in stage ST.
+  auto scores = [&](auto st, f32x16& S, f32x16& TS) {
+    const uint16_t* src = stage(st);
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * NT;
-      const int key = c / DCH, ch = c % DCH;
-      const int off = key * D + ((ch ^ k_swz(key)) << 3);
-      *(u32x4*)(sK + off) = kr[i];
-      *(u32x4*)(stK + off) = tkr[i];
+    for (int i = 0; i < 16; ++i) {
+      S[i] = 0.f;
+      TS[i] = 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int it = tid + i * NT;
-      const int dc = it % DCH, kp = it / DCH;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int d = 8 * dc + j;
-        const int off = d * BC + (((kp >> 2) ^ v_swz<BC>(d)) << 3) + 2 * (kp & 3);
-        const uint32_t a0 = vr[i][0][j >> 1], a1 = vr[i][1][j >> 1];
-        const uint32_t b0 = tvr[i][0][j >> 1], b1 = tvr[i][1][j >> 1];
-        const uint32_t wv = (j & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
-        const uint32_t wt = (j & 1) ? ((b0 >> 16) | (b1 & 0xffff0000u)) : ((b0 & 0xffffu) | (b1 << 16));
-        *(uint32_t*)(sV + off) = wv;
-        *(uint32_t*)(stV + off) = wt;
-      }
+    for (int s = 0; s < KS; ++s) {
+      const int off = n * D + (((2 * s + h) ^ row_swz(n)) << 3);
+      const u32x4 kf = *(const u32x4*)(src + off);
+      const u32x4 tkf = *(const u32x4*)(src + TILE + off);
+      S = mfma_bf16(kf, qf[s], S);
+      TS = mfma_bf16(kf, tqf[s], TS);
+      TS = mfma_bf16(tkf, qf[s], TS);
     }
   };
 
@@ -207,99 +252,116 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   const float sl2 = p.score_log2;
   const float scale = p.scale;
 
-  if (ntiles > 0) gload(span_tile(sp, 0));
-  for (int it = 0; it < ntiles; ++it) {
-    const int k0 = span_tile(sp, it) * BC;
-    __syncthreads();
-    lstore();
-    __syncthreads();
-    if (it + 1 < ntiles) gload(span_tile(sp, it + 1));
+  // transposing-read addresses (element offsets inside a V tile): a lane
+  // group of 16 covers 16 columns; its lane L names key 4h + L/4 (and +8),
+  // columns 4 (L % 4) .. +3 of the group's 16.
+  const int tr_key = 4 * h + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    const bool masked = !__all(covers(rr, k0, k0 + BC));
-#pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) {
-      // S^T and tS^T of one 32-key subtile
-      f32x16 S, TS;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  // One streamed tile j held in stage ST: mask, online softmax, P.V, with the
+  // scores of tile j+1 (stage ST+1) formed in the same basic block.
+  auto step = [&](auto st, int j, f32x16& S, f32x16& TS, f32x16& S1, f32x16& TS1) {
+    constexpr int ST = decltype(st)::value;
+    using NX = std::integral_constant<int, (ST + 1) % STAGES>;
+    using AH = std::integral_constant<int, (ST + 3) % STAGES>;
+    // tile j+1 landed for this wave, then for all; stage (j-1) % 4 is free
+    if (j + 2 < ntiles) wait_vmcnt<LPT>();
+    else wait_vmcnt<0>();
+    barrier_nofence();
+    issue(AH{}, j + 3);
+
+    const int k0 = span_tile(sp, j) * BC;
+    if (!__all(covers(rr, k0, k0 + BC))) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        S[i] = 0.f;
-        TS[i] = 0.f;
-      }
-      const int skey = sub * 32 + perm32(n);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int off = skey * D + (((2 * s + h) ^ k_swz(skey)) << 3);
-        const u32x4 kf = *(const u32x4*)(sK + off);
-        const u32x4 tkf = *(const u32x4*)(stK + off);
-        S = mfma_bf16(kf, qf[s], S);
-        TS = mfma_bf16(kf, tqf[s], TS);
-        TS = mfma_bf16(tkf, qf[s], TS);
-      }
-
-      // element mask where some row of the wave does not cover the whole tile
-      if (masked) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + sub * 32 + perm32(8 * (i >> 2) + 4 * h + (i & 3));
-          if (!in_ranges(rr, key)) {
-            S[i] = -INFINITY;
-            TS[i] = 0.f;
-          }
-        }
-      }
-
-      // online softmax with lazy rescaling (exp2 units)
-      float tmax = S[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, S[i]);
-      const float tmax_x = pair_max(tmax) * sl2;
-      if (__any(tmax_x > m + kLazyRescaleLog2)) {
-        const float mn = fmaxf(m, tmax_x);
-        const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
-        m = mn;
-        l *= alpha;
-        r *= alpha;
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          accO[c] *= alpha;
-          accT[c] *= alpha;
-        }
-      }
-      const float mu = (m == -INFINITY) ? 0.f : m;
-
-      u32x4 P[2], W[2];
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const int i = 8 * c2 + j;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(S[i], sl2, -mu));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(S[i + 1], sl2, -mu));
-          const float w0 = p0 * (TS[i] * scale);
-          const float w1 = p1 * (TS[i + 1] * scale);
-          l += p0 + p1;
-          r += w0 + w1;
-          P[c2][j >> 1] = pack_bf16(p0, p1);
-          W[c2][j >> 1] = pack_bf16(w0, w1);
-        }
-      }
-
-      // O^T += V^T P^T ;  T^T += tV^T P^T + V^T W^T
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const int gk = 4 * sub + 2 * c2 + h;
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          const int d = 32 * c + n;
-          const int off = d * BC + ((gk ^ v_swz<BC>(d)) << 3);
-          const u32x4 vf = *(const u32x4*)(sV + off);
-          const u32x4 tvf = *(const u32x4*)(stV + off);
-          accO[c] = mfma_bf16(vf, P[c2], accO[c]);
-          accT[c] = mfma_bf16(tvf, P[c2], accT[c]);
-          accT[c] = mfma_bf16(vf, W[c2], accT[c]);
-        }
+        const bool ok = in_ranges(rr, k0 + 8 * (i >> 2) + 4 * h + (i & 3));
+        S[i] = ok ? S[i] : -INFINITY;
+        TS[i] = ok ? TS[i] : 0.f;
       }
     }
+
+    float tmax = S[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, S[i]);
+    const float tmax_x = pair_max(tmax) * sl2;
+    if (__any(tmax_x > m + kLazyRescaleLog2)) {
+      const float mn = fmaxf(m, tmax_x);
+      const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      l *= alpha;
+      r *= alpha;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        accO[c] *= alpha;
+        accT[c] *= alpha;
+      }
+    }
+    const float mu = (m == -INFINITY) ? 0.f : m;
+
+    scores(NX{}, S1, TS1);  // on the last tile this reads a stale stage; unused
+
+    u32x4 P[2], W[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+      for (int jj = 0; jj < 8; jj += 2) {
+        const int i = 8 * c2 + jj;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(S[i], sl2, -mu));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(S[i + 1], sl2, -mu));
+        const float w0 = p0 * (TS[i] * scale);
+        const float w1 = p1 * (TS[i + 1] * scale);
+        l += p0 + p1;
+        r += w0 + w1;
+        P[c2][jj >> 1] = pack_bf16(p0, p1);
+        W[c2][jj >> 1] = pack_bf16(w0, w1);
+      }
+    }
+
+    // O^T += V^T P^T ;  T^T += tV^T P^T + V^T W^T
+    const uint16_t* cur = stage(st);
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const int col = 32 * c + tr_col;
+        const int k1 = 16 * c2 + tr_key, k2 = k1 + 8;
+        const int o1 = k1 * D + (((col >> 3) ^ row_swz(k1)) << 3) + (col & 7);
+        const int o2 = k2 * D + (((col >> 3) ^ row_swz(k2)) << 3) + (col & 7);
+        const u32x2 va = read_tr16(cur + 2 * TILE + o1), vb = read_tr16(cur + 2 * TILE + o2);
+        const u32x2 ta = read_tr16(cur + 3 * TILE + o1), tb = read_tr16(cur + 3 * TILE + o2);
+        const u32x4 vf = {va[0], va[1], vb[0], vb[1]};
+        const u32x4 tvf = {ta[0], ta[1], tb[0], tb[1]};
+        accO[c] = mfma_bf16(vf, P[c2], accO[c]);
+        accT[c] = mfma_bf16(tvf, P[c2], accT[c]);
+        accT[c] = mfma_bf16(vf, W[c2], accT[c]);
+      }
+    }
+    schedule_hints<KS, DC>();
+  };
+
+  f32x16 Sa, TSa, Sb, TSb;
+  if (ntiles > 0) {
+    issue(I0{}, 0);
+    issue(I1{}, 1);
+    issue(I2{}, 2);
+    if (ntiles >= 3) wait_vmcnt<2 * LPT>();
+    else wait_vmcnt<0>();
+    barrier_nofence();
+    scores(I0{}, Sa, TSa);
+  }
+  for (int j = 0; j < ntiles; j += 4) {
+    step(I0{}, j, Sa, TSa, Sb, TSb);
+    if (j + 1 >= ntiles) break;
+    step(I1{}, j + 1, Sb, TSb, Sa, TSa);
+    if (j + 2 >= ntiles) break;
+    step(I2{}, j + 2, Sa, TSa, Sb, TSb);
+    if (j + 3 >= ntiles) break;
+    step(I3{}, j + 3, Sb, TSb, Sa, TSa);
   }
 
   // ---- epilogue: o = acc_o / l ; to = acc_t / l - (r / l) o ------------------
@@ -421,7 +483,7 @@ void block_sizes(int dtype, int head_dim, int* block_q, int* block_k) {
   (void)head_dim;
   if (dtype == kBf16) {
     *block_q = kBf16Waves * 32;
-    *block_k = 64;
+    *block_k = kBf16BlockK;
   } else {
     *block_q = 32;
     *block_k = 32;
@@ -431,9 +493,9 @@ void block_sizes(int dtype, int head_dim, int* block_q, int* block_k) {
 hipError_t launch_fwd(int dtype, int head_dim, int grid, const FwdParams& p, hipStream_t stream) {
   if (dtype == kBf16) {
     if (head_dim == 128)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, kBf16Waves>), dim3(grid), dim3(kBf16Waves * 64), 0, stream, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves>), dim3(grid), dim3(kBf16Waves * 64), 0, stream, p);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, kBf16Waves>), dim3(grid), dim3(kBf16Waves * 64), 0, stream, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves>), dim3(grid), dim3(kBf16Waves * 64), 0, stream, p);
   } else {
     if (head_dim == 128)
       hipLaunchKernelGGL((fwd_fp32_kernel<128>), dim3(grid), dim3(256), 0, stream, p);

@@ -10,7 +10,8 @@ namespace attn_jvp {
 
 constexpr int kBf16 = 0;
 constexpr int kFp32 = 1;
-constexpr int kBf16Waves = 4;  // waves per bf16 workgroup; 32 query rows per wave
+constexpr int kBf16Waves = 4;   // waves per bf16 workgroup; 32 query rows per wave
+constexpr int kBf16BlockK = 32;  // keys per bf16 tile
 
 struct FwdParams {
   const void* q;
