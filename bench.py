@@ -40,7 +40,26 @@ def parse():
     ap.add_argument("--config", type=int, default=3, help="workload id (2..5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=1)
+    ap.add_argument("--mode", choices=["attn", "copy"], default="attn",
+                    help="copy: a plain 1 GiB device copy, the reference for HBM byte counters")
     return ap.parse_args()
+
+
+def copy_reference(steps):
+    """A plain device-to-device copy of 1 GiB, timed, for calibrating the
+    FETCH_SIZE / WRITE_SIZE counters against bytes known to move."""
+    import torch
+    n = 1 << 29  # bf16 elements = 1 GiB
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"mode": "copy", "bytes_read_per_copy": 2 * n, "bytes_written_per_copy": 2 * n,
+                      "ms_per_copy": round(dt * 1e3, 4), "GB_per_s": round(4 * n / dt / 1e9, 1)}), flush=True)
 
 
 def kernel_hash():
@@ -91,6 +110,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
+    if args.mode == "copy":
+        copy_reference(args.steps)
+        return
 
     import numpy as np
     import torch

@@ -33,7 +33,9 @@ ATTN_JVP_BF16 = 0
 ATTN_JVP_FP32 = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libattn_jvp.so")
+# ATTN_JVP_LIBRARY selects another build of the same library (e.g. one made
+# with different compile-time options); default: the in-tree build.
+library_path = os.environ.get("ATTN_JVP_LIBRARY") or os.path.join(_HERE, "libattn_jvp.so")
 
 
 class AttnJvpError(RuntimeError):

@@ -113,30 +113,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Instruction order for the pipelined block of one tile (masks: 0x008 MFMA,
-// 0x002 VALU, 0x100 LDS read): the 3*KS score MFMAs of the next tile are
-// spread over the softmax VALU work of the current one, two K-fragment
-// reads ahead; the transposing V reads of the first P.V group are issued
-// during that phase and every later group's reads one group ahead.
-template <int KS, int DC>
-__device__ __forceinline__ void schedule_hints() {
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    if (s == KS - 1) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-    else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < 2 * DC; ++g) {
-    if (g + 1 < 2 * DC) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-  }
-}
-
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
@@ -203,13 +179,11 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     else if constexpr (S == 2) return ring2;
     else return ring3;
   };
-
-  // DMA of tile t into stage ST.  Lane L of 1 KB block `blk` fills LDS group
-  // (row, pc) and fetches global group pc ^ row_swz(row) of that row.
-  auto issue = [&](auto st, int t) {
+  // DMA of tile t into stage `dst`.  Lane L of 1 KB block `blk` fills LDS
+  // group (row, pc) and fetches global group pc ^ row_swz(row) of that row.
+  auto issue = [&](uint16_t* dst, int t) {
     if (t >= ntiles) return;
     const int k0 = span_tile(sp, t) * BC;
-    uint16_t* dst = stage(st);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int blk = wave * LOADS + i;
@@ -217,25 +191,6 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       const int voff = ((k0 + r) * D + (((lane % CPR) ^ row_swz(r)) << 3)) * 2;
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) load16_lds(rsrc[tt], dst + tt * TILE + blk * 512, voff);
-    }
-  };
-
-  // S^T and tS^T of the tile held in stage ST.
-  auto scores = [&](auto st, f32x16& S, f32x16& TS) {
-    const uint16_t* src = stage(st);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      S[i] = 0.f;
-      TS[i] = 0.f;
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int off = n * D + (((2 * s + h) ^ row_swz(n)) << 3);
-      const u32x4 kf = *(const u32x4*)(src + off);
-      const u32x4 tkf = *(const u32x4*)(src + TILE + off);
-      S = mfma_bf16(kf, qf[s], S);
-      TS = mfma_bf16(kf, tqf[s], TS);
-      TS = mfma_bf16(tkf, qf[s], TS);
     }
   };
 
@@ -263,9 +218,38 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
 
-  // One streamed tile j held in stage ST: mask, online softmax, P.V, with the
-  // scores of tile j+1 (stage ST+1) formed in the same basic block.
-  auto step = [&](auto st, int j, f32x16& S, f32x16& TS, f32x16& S1, f32x16& TS1) {
+  // Per-lane key window of this row: key k is allowed iff
+  // (unsigned)(k - lo1) < len1 or (unsigned)(k - lo2) < len2.
+  const int len1 = rr.hi1 - rr.lo1, len2 = rr.hi2 - rr.lo2;
+
+  // Mask tile t's scores where some row of the wave does not cover the whole
+  // tile (S -> -inf, TS -> 0 outside the row's ranges); returns the masked
+  // row max in exp2 units, or `tmx` unchanged for a fully covered tile.
+  auto mask_tile = [&](int t, f32x16& S, f32x16& TS, float tmx) -> float {
+    const int k0 = span_tile(sp, t) * BC;
+    if (__all(covers(rr, k0, k0 + BC))) return tmx;
+    const int b1 = k0 + 4 * h - rr.lo1, b2 = k0 + 4 * h - rr.lo2;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int off = 8 * (i >> 2) + (i & 3);
+      const bool ok = (unsigned)(b1 + off) < (unsigned)len1 || (unsigned)(b2 + off) < (unsigned)len2;
+      S[i] = ok ? S[i] : -INFINITY;
+      TS[i] = ok ? TS[i] : 0.f;
+      tmax = fmaxf(tmax, S[i]);
+    }
+    return pair_max(tmax) * sl2;
+  };
+
+  // One streamed tile j held in stage ST.
+  // Top (its own blocks): ring wait, barrier, DMA of tile j+3, the mask of
+  // tile j if it is partial (rare), lazy rescale.  Then one basic block, laid
+  // out slot by slot (sched_barrier fences keep the order): per k-step, the
+  // three score MFMAs of tile j+1 around one unit of tile j's softmax, with K
+  // reads two k-steps ahead; per P.V group of tile j, its three MFMAs around
+  // part of tile j+1's row max, with V reads one group ahead.  tmx carries
+  // the unmasked row max (exp2 units) of the tile about to be used.
+  auto step = [&](auto st, int j, f32x16& S, f32x16& TS, f32x16& S1, f32x16& TS1, float& tmx) {
     constexpr int ST = decltype(st)::value;
     using NX = std::integral_constant<int, (ST + 1) % STAGES>;
     using AH = std::integral_constant<int, (ST + 3) % STAGES>;
@@ -273,24 +257,11 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     if (j + 2 < ntiles) wait_vmcnt<LPT>();
     else wait_vmcnt<0>();
     barrier_nofence();
-    issue(AH{}, j + 3);
+    issue(stage(AH{}), j + 3);
 
-    const int k0 = span_tile(sp, j) * BC;
-    if (!__all(covers(rr, k0, k0 + BC))) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const bool ok = in_ranges(rr, k0 + 8 * (i >> 2) + 4 * h + (i & 3));
-        S[i] = ok ? S[i] : -INFINITY;
-        TS[i] = ok ? TS[i] : 0.f;
-      }
-    }
-
-    float tmax = S[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, S[i]);
-    const float tmax_x = pair_max(tmax) * sl2;
-    if (__any(tmax_x > m + kLazyRescaleLog2)) {
-      const float mn = fmaxf(m, tmax_x);
+    tmx = mask_tile(j, S, TS, tmx);
+    if (__any(tmx > m + kLazyRescaleLog2)) {
+      const float mn = fmaxf(m, tmx);
       const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
       m = mn;
       l *= alpha;
@@ -302,66 +273,115 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       }
     }
     const float mu = (m == -INFINITY) ? 0.f : m;
+    __builtin_amdgcn_sched_barrier(0);
 
-    scores(NX{}, S1, TS1);  // on the last tile this reads a stale stage; unused
-
-    u32x4 P[2], W[2];
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-#pragma unroll
-      for (int jj = 0; jj < 8; jj += 2) {
-        const int i = 8 * c2 + jj;
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(S[i], sl2, -mu));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(S[i + 1], sl2, -mu));
-        const float w0 = p0 * (TS[i] * scale);
-        const float w1 = p1 * (TS[i + 1] * scale);
-        l += p0 + p1;
-        r += w0 + w1;
-        P[c2][jj >> 1] = pack_bf16(p0, p1);
-        W[c2][jj >> 1] = pack_bf16(w0, w1);
-      }
-    }
-
-    // O^T += V^T P^T ;  T^T += tV^T P^T + V^T W^T
+    const uint16_t* nx = stage(NX{});  // on the last tile a stale stage; unused
     const uint16_t* cur = stage(st);
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        const int col = 32 * c + tr_col;
-        const int k1 = 16 * c2 + tr_key, k2 = k1 + 8;
-        const int o1 = k1 * D + (((col >> 3) ^ row_swz(k1)) << 3) + (col & 7);
-        const int o2 = k2 * D + (((col >> 3) ^ row_swz(k2)) << 3) + (col & 7);
-        const u32x2 va = read_tr16(cur + 2 * TILE + o1), vb = read_tr16(cur + 2 * TILE + o2);
-        const u32x2 ta = read_tr16(cur + 3 * TILE + o1), tb = read_tr16(cur + 3 * TILE + o2);
-        const u32x4 vf = {va[0], va[1], vb[0], vb[1]};
-        const u32x4 tvf = {ta[0], ta[1], tb[0], tb[1]};
-        accO[c] = mfma_bf16(vf, P[c2], accO[c]);
-        accT[c] = mfma_bf16(tvf, P[c2], accT[c]);
-        accT[c] = mfma_bf16(vf, W[c2], accT[c]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      S1[i] = 0.f;
+      TS1[i] = 0.f;
     }
-    schedule_hints<KS, DC>();
+    u32x4 kf[KS], tkf[KS];
+    auto kread = [&](int s) {
+      const int off = n * D + (((2 * s + h) ^ row_swz(n)) << 3);
+      kf[s] = *(const u32x4*)(nx + off);
+      tkf[s] = *(const u32x4*)(nx + TILE + off);
+    };
+    u32x4 P[2], W[2];
+    auto soft_pair = [&](int jj) {  // elements jj, jj+1 of tile j
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(S[jj], sl2, -mu));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(S[jj + 1], sl2, -mu));
+      const float w0 = p0 * (TS[jj] * scale);
+      const float w1 = p1 * (TS[jj + 1] * scale);
+      l += p0 + p1;
+      r += w0 + w1;
+      P[jj >> 3][(jj & 7) >> 1] = pack_bf16(p0, p1);
+      W[jj >> 3][(jj & 7) >> 1] = pack_bf16(w0, w1);
+    };
+    u32x4 vfr[2 * DC], tvfr[2 * DC];
+    auto vread = [&](int gidx) {
+      const int c2 = gidx / DC, c = gidx % DC;
+      const int col = 32 * c + tr_col;
+      const int k1 = 16 * c2 + tr_key, k2 = k1 + 8;
+      const int o1 = k1 * D + (((col >> 3) ^ row_swz(k1)) << 3) + (col & 7);
+      const int o2 = k2 * D + (((col >> 3) ^ row_swz(k2)) << 3) + (col & 7);
+      const u32x2 va = read_tr16(cur + 2 * TILE + o1), vb = read_tr16(cur + 2 * TILE + o2);
+      const u32x2 ta = read_tr16(cur + 3 * TILE + o1), tb = read_tr16(cur + 3 * TILE + o2);
+      vfr[gidx] = u32x4{va[0], va[1], vb[0], vb[1]};
+      tvfr[gidx] = u32x4{ta[0], ta[1], tb[0], tb[1]};
+    };
+
+    // phase 1: scores of tile j+1 under the softmax of tile j
+    constexpr int PAIRS_PER_STEP = 8 / KS;
+    kread(0);
+    if (KS > 1) kread(1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s + 2 < KS) kread(s + 2);
+      if (s == KS - 1) vread(0);
+      // the two TS1 products are kept one MFMA apart (dependent accumulation)
+      TS1 = mfma_bf16(kf[s], tqf[s], TS1);
+      S1 = mfma_bf16(kf[s], qf[s], S1);
+#pragma unroll
+      for (int u = 0; u < PAIRS_PER_STEP; ++u) soft_pair(2 * (s * PAIRS_PER_STEP + u));
+      TS1 = mfma_bf16(tkf[s], qf[s], TS1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // phase 2: P.V of tile j under the row max of tile j+1
+    constexpr int ELEMS_PER_GROUP = 16 / (2 * DC);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int gidx = 0; gidx < 2 * DC; ++gidx) {
+      if (gidx + 1 < 2 * DC) vread(gidx + 1);
+      const int c2 = gidx / DC, c = gidx % DC;
+      accT[c] = mfma_bf16(tvfr[gidx], P[c2], accT[c]);
+      accO[c] = mfma_bf16(vfr[gidx], P[c2], accO[c]);
+#pragma unroll
+      for (int e = 0; e < ELEMS_PER_GROUP; ++e) tmax = fmaxf(tmax, S1[gidx * ELEMS_PER_GROUP + e]);
+      accT[c] = mfma_bf16(vfr[gidx], W[c2], accT[c]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    tmx = pair_max(tmax) * sl2;
   };
 
   f32x16 Sa, TSa, Sb, TSb;
+  float tmx = -INFINITY;
   if (ntiles > 0) {
-    issue(I0{}, 0);
-    issue(I1{}, 1);
-    issue(I2{}, 2);
+    issue(ring0, 0);
+    issue(ring1, 1);
+    issue(ring2, 2);
     if (ntiles >= 3) wait_vmcnt<2 * LPT>();
     else wait_vmcnt<0>();
     barrier_nofence();
-    scores(I0{}, Sa, TSa);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      Sa[i] = 0.f;
+      TSa[i] = 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int off = n * D + (((2 * s + h) ^ row_swz(n)) << 3);
+      const u32x4 kf = *(const u32x4*)(ring0 + off);
+      const u32x4 tkf = *(const u32x4*)(ring0 + TILE + off);
+      Sa = mfma_bf16(kf, qf[s], Sa);
+      TSa = mfma_bf16(kf, tqf[s], TSa);
+      TSa = mfma_bf16(tkf, qf[s], TSa);
+    }
+    float tmax = Sa[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, Sa[i]);
+    tmx = pair_max(tmax) * sl2;
   }
   for (int j = 0; j < ntiles; j += 4) {
-    step(I0{}, j, Sa, TSa, Sb, TSb);
+    step(I0{}, j, Sa, TSa, Sb, TSb, tmx);
     if (j + 1 >= ntiles) break;
-    step(I1{}, j + 1, Sb, TSb, Sa, TSa);
+    step(I1{}, j + 1, Sb, TSb, Sa, TSa, tmx);
     if (j + 2 >= ntiles) break;
-    step(I2{}, j + 2, Sa, TSa, Sb, TSb);
+    step(I2{}, j + 2, Sa, TSa, Sb, TSb, tmx);
     if (j + 3 >= ntiles) break;
-    step(I3{}, j + 3, Sb, TSb, Sa, TSa);
+    step(I3{}, j + 3, Sb, TSb, Sa, TSa, tmx);
   }
 
   // ---- epilogue: o = acc_o / l ; to = acc_t / l - (r / l) o ------------------
