@@ -101,6 +101,24 @@ __device__ __forceinline__ u32x2 read_tr16(const uint16_t* p) {
 // keep 32-byte pairs apart (for the transposing reads).
 __device__ __forceinline__ int row_swz(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
 
+// Vector access to accumulation registers, written out so that the compiler
+// sees no vector-ALU reader of the loop-carried accumulators (it would
+// otherwise keep a second copy of all of them in vector registers and refresh
+// it on every tile).  Callers run acc_hazard_wait() first: an MFMA result may
+// be read by a vector instruction only after enough wait states (24 here,
+// above the requirement of the 32x32 bf16 MFMA).
+__device__ __forceinline__ void acc_hazard_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+__device__ __forceinline__ float acc_write(float v) {
+  float a;
+  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
+  return a;
+}
+
 // Workgroup barrier without a memory fence: the fence of __syncthreads()
 // would wait for every LDS DMA in flight.  Visibility of the tile about to be
 // read comes from the explicit vmcnt wait before it; the memory clobber keeps
@@ -227,7 +245,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   // row max in exp2 units, or `tmx` unchanged for a fully covered tile.
   auto mask_tile = [&](int t, f32x16& S, f32x16& TS, float tmx) -> float {
     const int k0 = span_tile(sp, t) * BC;
-    if (__all(covers(rr, k0, k0 + BC))) return tmx;
+    if (__builtin_expect(__all(covers(rr, k0, k0 + BC)), 1)) return tmx;
     const int b1 = k0 + 4 * h - rr.lo1, b2 = k0 + 4 * h - rr.lo2;
     float tmax = -INFINITY;
 #pragma unroll
@@ -260,16 +278,22 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     issue(stage(AH{}), j + 3);
 
     tmx = mask_tile(j, S, TS, tmx);
-    if (__any(tmx > m + kLazyRescaleLog2)) {
+    // Rare after the first tile; the hint keeps the register allocator from
+    // moving the accumulator copies this branch needs onto the common path.
+    if (__builtin_expect(__any(tmx > m + kLazyRescaleLog2), 0)) {
       const float mn = fmaxf(m, tmx);
       const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
       m = mn;
       l *= alpha;
       r *= alpha;
+      acc_hazard_wait();
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        accO[c] *= alpha;
-        accT[c] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          accO[c][i] = acc_write(acc_read(accO[c][i]) * alpha);
+          accT[c][i] = acc_write(acc_read(accT[c][i]) * alpha);
+        }
       }
     }
     const float mu = (m == -INFINITY) ? 0.f : m;
@@ -385,6 +409,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   }
 
   // ---- epilogue: o = acc_o / l ; to = acc_t / l - (r / l) o ------------------
+  acc_hazard_wait();
   const float lt = pair_sum(l);
   const float rt = pair_sum(r);
   if (row_ok) {
@@ -400,8 +425,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
         float o4[4], t4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          o4[e] = accO[c][4 * g4 + e] * inv;
-          t4[e] = accT[c][4 * g4 + e] * inv - rb * o4[e];
+          o4[e] = acc_read(accO[c][4 * g4 + e]) * inv;
+          t4[e] = acc_read(accT[c][4 * g4 + e]) * inv - rb * o4[e];
         }
         u32x2 ov = {pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])};
         u32x2 tv = {pack_bf16(t4[0], t4[1]), pack_bf16(t4[2], t4[3])};
