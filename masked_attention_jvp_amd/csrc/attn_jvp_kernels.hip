@@ -87,19 +87,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
-// 16 bytes per lane from global straight into LDS at lds + 16 * lane.
-__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int byte_off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds, 16, byte_off, 0, 0, 0);
+// 16 bytes per lane from global (byte offset voff + soff, soff wave-uniform)
+// straight into LDS at lds + 16 * lane.
+__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds, 16, voff, soff, 0, 0);
 }
 __device__ __forceinline__ u32x2 read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)p));
 }
 
 // 16-byte group swizzle of a tile row: group g of row `key` is stored at
-// g ^ row_swz(key).  Any 8 consecutive rows get 8 distinct values (for the
-// 16-byte fragment reads of 8 lanes), and any 4 rows 4k..4k+3 get values that
-// keep 32-byte pairs apart (for the transposing reads).
-__device__ __forceinline__ int row_swz(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
+// g ^ row_swz<D>(key).  gfx950 LDS has 64 banks (256 bytes per cycle).
+// * 16-byte fragment reads serve 16 lanes, i.e. 16 consecutive rows at one
+//   logical group: the swizzle maps them to 16 distinct bank groups.
+// * A transposing read serves a 16-lane group with 4 rows 4k..4k+3 and 16
+//   or 32 consecutive columns: the swizzle puts each of the 4 rows into its
+//   own aligned 64-byte bank group.
+// d = 128 rows are 256 bytes (all 64 banks); d = 64 rows are 128 bytes, so
+// rows of opposite parity already sit in opposite bank halves.
+template <int D>
+__device__ __forceinline__ int row_swz(int key) {
+  if constexpr (D == 128) return ((key & 3) << 2) | ((key >> 2) & 3);
+  else return (((key >> 1) & 1) << 2) | ((key >> 2) & 3);
+}
 
 // Vector access to accumulation registers, written out so that the compiler
 // sees no vector-ALU reader of the loop-carried accumulators (it would
@@ -155,7 +165,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t ring3[4 * TILE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int n = lane & 31, h = lane >> 5;
 
   const MaskGeom g = p.g;
@@ -199,16 +210,23 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   };
   // DMA of tile t into stage `dst`.  Lane L of 1 KB block `blk` fills LDS
   // group (row, pc) and fetches global group pc ^ row_swz(row) of that row.
+  // The per-lane part of the source offset is fixed; the tile's key offset
+  // rides in the scalar offset.
+  int dma_voff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int blk = wave * LOADS + i;
+    const int rw = blk * (64 / CPR) + lane / CPR;
+    dma_voff[i] = (rw * D + (((lane % CPR) ^ row_swz<D>(rw)) << 3)) * 2;
+  }
   auto issue = [&](uint16_t* dst, int t) {
     if (t >= ntiles) return;
-    const int k0 = span_tile(sp, t) * BC;
+    const int soff = span_tile(sp, t) * BC * D * 2;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int blk = wave * LOADS + i;
-      const int r = blk * (64 / CPR) + lane / CPR;
-      const int voff = ((k0 + r) * D + (((lane % CPR) ^ row_swz(r)) << 3)) * 2;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) load16_lds(rsrc[tt], dst + tt * TILE + blk * 512, voff);
+      for (int tt = 0; tt < 4; ++tt) load16_lds(rsrc[tt], dst + tt * TILE + blk * 512, dma_voff[i], soff);
     }
   };
 
@@ -243,7 +261,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   // Mask tile t's scores where some row of the wave does not cover the whole
   // tile (S -> -inf, TS -> 0 outside the row's ranges); returns the masked
   // row max in exp2 units, or `tmx` unchanged for a fully covered tile.
-  auto mask_tile = [&](int t, f32x16& S, f32x16& TS, float tmx) -> float {
+  auto mask_tile = [&](int t, float* S, float* TS, float tmx) -> float {
     const int k0 = span_tile(sp, t) * BC;
     if (__builtin_expect(__all(covers(rr, k0, k0 + BC)), 1)) return tmx;
     const int b1 = k0 + 4 * h - rr.lo1, b2 = k0 + 4 * h - rr.lo2;
@@ -259,15 +277,19 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     return pair_max(tmax) * sl2;
   };
 
-  // One streamed tile j held in stage ST.
+  // One streamed tile j held in stage ST; S, TS hold its scores in vector
+  // registers and receive those of tile j+1.
   // Top (its own blocks): ring wait, barrier, DMA of tile j+3, the mask of
-  // tile j if it is partial (rare), lazy rescale.  Then one basic block, laid
-  // out slot by slot (sched_barrier fences keep the order): per k-step, the
-  // three score MFMAs of tile j+1 around one unit of tile j's softmax, with K
-  // reads two k-steps ahead; per P.V group of tile j, its three MFMAs around
-  // part of tile j+1's row max, with V reads one group ahead.  tmx carries
-  // the unmasked row max (exp2 units) of the tile about to be used.
-  auto step = [&](auto st, int j, f32x16& S, f32x16& TS, f32x16& S1, f32x16& TS1, float& tmx) {
+  // tile j if it is partial (rare), lazy rescale (rare).  Then one basic
+  // block laid out slot by slot (sched_barrier fences keep the order):
+  // * per k-step: K reads two k-steps ahead, then the S, TS, TS MFMAs of tile
+  //   j+1 around one unit of tile j's softmax (the two TS products one MFMA
+  //   apart, as they accumulate into the same tile);
+  // * per P.V group of tile j: V reads two groups ahead, then its three MFMAs
+  //   around the copy of a quarter of tile j+1's scores into vector
+  //   registers and their row max.
+  // tmx carries the unmasked row max (exp2 units) of the tile about to be used.
+  auto step = [&](auto st, int j, float* S, float* TS, float& tmx) {
     constexpr int ST = decltype(st)::value;
     using NX = std::integral_constant<int, (ST + 1) % STAGES>;
     using AH = std::integral_constant<int, (ST + 3) % STAGES>;
@@ -278,8 +300,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     issue(stage(AH{}), j + 3);
 
     tmx = mask_tile(j, S, TS, tmx);
-    // Rare after the first tile; the hint keeps the register allocator from
-    // moving the accumulator copies this branch needs onto the common path.
+    // Rare after the first tile.
     if (__builtin_expect(__any(tmx > m + kLazyRescaleLog2), 0)) {
       const float mn = fmaxf(m, tmx);
       const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
@@ -301,6 +322,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 
     const uint16_t* nx = stage(NX{});  // on the last tile a stale stage; unused
     const uint16_t* cur = stage(st);
+    f32x16 S1, TS1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       S1[i] = 0.f;
@@ -308,7 +330,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     }
     u32x4 kf[KS], tkf[KS];
     auto kread = [&](int s) {
-      const int off = n * D + (((2 * s + h) ^ row_swz(n)) << 3);
+      const int off = n * D + (((2 * s + h) ^ row_swz<D>(n)) << 3);
       kf[s] = *(const u32x4*)(nx + off);
       tkf[s] = *(const u32x4*)(nx + TILE + off);
     };
@@ -328,8 +350,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       const int c2 = gidx / DC, c = gidx % DC;
       const int col = 32 * c + tr_col;
       const int k1 = 16 * c2 + tr_key, k2 = k1 + 8;
-      const int o1 = k1 * D + (((col >> 3) ^ row_swz(k1)) << 3) + (col & 7);
-      const int o2 = k2 * D + (((col >> 3) ^ row_swz(k2)) << 3) + (col & 7);
+      const int o1 = k1 * D + (((col >> 3) ^ row_swz<D>(k1)) << 3) + (col & 7);
+      const int o2 = k2 * D + (((col >> 3) ^ row_swz<D>(k2)) << 3) + (col & 7);
       const u32x2 va = read_tr16(cur + 2 * TILE + o1), vb = read_tr16(cur + 2 * TILE + o2);
       const u32x2 ta = read_tr16(cur + 3 * TILE + o1), tb = read_tr16(cur + 3 * TILE + o2);
       vfr[gidx] = u32x4{va[0], va[1], vb[0], vb[1]};
@@ -343,34 +365,48 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (s + 2 < KS) kread(s + 2);
-      if (s == KS - 1) vread(0);
-      // the two TS1 products are kept one MFMA apart (dependent accumulation)
-      TS1 = mfma_bf16(kf[s], tqf[s], TS1);
+      if (s == KS - 2) vread(0);
+      if (s == KS - 1) vread(1);
+      __builtin_amdgcn_sched_barrier(0);
       S1 = mfma_bf16(kf[s], qf[s], S1);
+      TS1 = mfma_bf16(kf[s], tqf[s], TS1);
 #pragma unroll
       for (int u = 0; u < PAIRS_PER_STEP; ++u) soft_pair(2 * (s * PAIRS_PER_STEP + u));
       TS1 = mfma_bf16(tkf[s], qf[s], TS1);
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // phase 2: P.V of tile j under the row max of tile j+1
-    constexpr int ELEMS_PER_GROUP = 16 / (2 * DC);
+    // phase 2: P.V of tile j under the copy-out and row max of tile j+1
+    constexpr int COPIES_PER_GROUP = 32 / (2 * DC);
+    static_assert(COPIES_PER_GROUP <= 16, "tangent-score reads must not start in group 0");
     float tmax = -INFINITY;
 #pragma unroll
     for (int gidx = 0; gidx < 2 * DC; ++gidx) {
-      if (gidx + 1 < 2 * DC) vread(gidx + 1);
+      if (gidx + 2 < 2 * DC) vread(gidx + 2);
+      __builtin_amdgcn_sched_barrier(0);
       const int c2 = gidx / DC, c = gidx % DC;
       accT[c] = mfma_bf16(tvfr[gidx], P[c2], accT[c]);
       accO[c] = mfma_bf16(vfr[gidx], P[c2], accO[c]);
+      // copy-out of tile j+1's 32 score values, COPIES_PER_GROUP per group,
+      // scores first: the tangent scores' last MFMA ends phase 1, so their
+      // reads start one group later, well past the result hazard.
 #pragma unroll
-      for (int e = 0; e < ELEMS_PER_GROUP; ++e) tmax = fmaxf(tmax, S1[gidx * ELEMS_PER_GROUP + e]);
+      for (int e = 0; e < COPIES_PER_GROUP; ++e) {
+        const int k = gidx * COPIES_PER_GROUP + e;
+        if (k < 16) {
+          S[k] = acc_read(S1[k]);
+          tmax = fmaxf(tmax, S[k]);
+        } else {
+          TS[k - 16] = acc_read(TS1[k - 16]);
+        }
+      }
       accT[c] = mfma_bf16(vfr[gidx], W[c2], accT[c]);
       __builtin_amdgcn_sched_barrier(0);
     }
     tmx = pair_max(tmax) * sl2;
   };
 
-  f32x16 Sa, TSa, Sb, TSb;
+  float S[16], TS[16];  // scores of the current tile, in vector registers
   float tmx = -INFINITY;
   if (ntiles > 0) {
     issue(ring0, 0);
@@ -379,6 +415,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     if (ntiles >= 3) wait_vmcnt<2 * LPT>();
     else wait_vmcnt<0>();
     barrier_nofence();
+    f32x16 Sa, TSa;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       Sa[i] = 0.f;
@@ -386,26 +423,30 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int off = n * D + (((2 * s + h) ^ row_swz(n)) << 3);
+      const int off = n * D + (((2 * s + h) ^ row_swz<D>(n)) << 3);
       const u32x4 kf = *(const u32x4*)(ring0 + off);
       const u32x4 tkf = *(const u32x4*)(ring0 + TILE + off);
       Sa = mfma_bf16(kf, qf[s], Sa);
       TSa = mfma_bf16(kf, tqf[s], TSa);
       TSa = mfma_bf16(tkf, qf[s], TSa);
     }
-    float tmax = Sa[0];
+    float tmax = -INFINITY;
 #pragma unroll
-    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, Sa[i]);
+    for (int i = 0; i < 16; ++i) {
+      S[i] = Sa[i];
+      TS[i] = TSa[i];
+      tmax = fmaxf(tmax, S[i]);
+    }
     tmx = pair_max(tmax) * sl2;
   }
   for (int j = 0; j < ntiles; j += 4) {
-    step(I0{}, j, Sa, TSa, Sb, TSb, tmx);
+    step(I0{}, j, S, TS, tmx);
     if (j + 1 >= ntiles) break;
-    step(I1{}, j + 1, Sb, TSb, Sa, TSa, tmx);
+    step(I1{}, j + 1, S, TS, tmx);
     if (j + 2 >= ntiles) break;
-    step(I2{}, j + 2, Sa, TSa, Sb, TSb, tmx);
+    step(I2{}, j + 2, S, TS, tmx);
     if (j + 3 >= ntiles) break;
-    step(I3{}, j + 3, Sb, TSb, Sa, TSa, tmx);
+    step(I3{}, j + 3, S, TS, tmx);
   }
 
   // ---- epilogue: o = acc_o / l ; to = acc_t / l - (r / l) o ------------------
