@@ -219,27 +219,34 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     const int rw = blk * (64 / CPR) + lane / CPR;
     dma_voff[i] = (rw * D + (((lane % CPR) ^ row_swz<D>(rw)) << 3)) * 2;
   }
+  // The q-th of the LPT DMA instructions of tile t.  Every step issues all
+  // of them, branch-free: past the last tile the last tile is loaded again
+  // into the stage that just became free, which nothing reads, so the ring
+  // always has the same number of loads in flight.
+  auto issue_part = [&](uint16_t* dst, int t, int q) {
+    const int soff = span_tile(sp, t < ntiles ? t : ntiles - 1) * BC * D * 2;
+    const int i = q >> 2, tt = q & 3;
+    load16_lds(rsrc[tt], dst + tt * TILE + (wave * LOADS + i) * 512, dma_voff[i], soff);
+  };
   auto issue = [&](uint16_t* dst, int t) {
-    if (t >= ntiles) return;
-    const int soff = span_tile(sp, t) * BC * D * 2;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int blk = wave * LOADS + i;
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) load16_lds(rsrc[tt], dst + tt * TILE + blk * 512, dma_voff[i], soff);
-    }
+    for (int q = 0; q < LPT; ++q) issue_part(dst, t, q);
   };
 
-  f32x16 accO[DC], accT[DC];
+  // accO = sum p~ v, accV = sum p~ tv, accS = sum (p~ ts') v with the
+  // unscaled score tangent ts' (the scale is applied once, in the epilogue).
+  // Three separate tiles keep each MFMA accumulation chain a few MFMAs apart.
+  f32x16 accO[DC], accV[DC], accS[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       accO[c][i] = 0.f;
-      accT[c][i] = 0.f;
+      accV[c][i] = 0.f;
+      accS[c][i] = 0.f;
     }
   }
-  float m = -INFINITY, l = 0.f, r = 0.f;
+  float m = -INFINITY, l = 0.f, r = 0.f;  // r = sum p~ ts' (unscaled)
   const float sl2 = p.score_log2;
   const float scale = p.scale;
 
@@ -258,12 +265,30 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   // (unsigned)(k - lo1) < len1 or (unsigned)(k - lo2) < len2.
   const int len1 = rr.hi1 - rr.lo1, len2 = rr.hi2 - rr.lo2;
 
+  // Tiles that every valid row of this wave sees whole: the wave's rows are
+  // consecutive and on one side, so (range 1 of each row starts at key 0 and
+  // grows with the row; range 2 slides with the row's chunk) a tile is whole
+  // for all of them iff it lies in [0, f1) or in [g0, g1): f1 and g1 from the
+  // wave's first valid row, g0 from its last.  Scalar values.
+  int f1 = 1 << 30, g0 = 0, g1 = 1 << 30;
+  {
+    const int wa = r0 + wave * 32;
+    const int wb = wa + 32 < r1 ? wa + 32 : r1;
+    if (wa < wb) {
+      const Ranges first = row_ranges(g, wa), last = row_ranges(g, wb - 1);
+      f1 = first.hi1;
+      g0 = last.lo2;
+      g1 = first.hi2;
+    }
+  }
+
   // Mask tile t's scores where some row of the wave does not cover the whole
   // tile (S -> -inf, TS -> 0 outside the row's ranges); returns the masked
   // row max in exp2 units, or `tmx` unchanged for a fully covered tile.
   auto mask_tile = [&](int t, float* S, float* TS, float tmx) -> float {
     const int k0 = span_tile(sp, t) * BC;
-    if (__builtin_expect(__all(covers(rr, k0, k0 + BC)), 1)) return tmx;
+    const bool whole = k0 + BC <= f1 || (k0 >= g0 && k0 + BC <= g1);
+    if (__builtin_expect(whole, 1)) return tmx;
     const int b1 = k0 + 4 * h - rr.lo1, b2 = k0 + 4 * h - rr.lo2;
     float tmax = -INFINITY;
 #pragma unroll
@@ -293,11 +318,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     constexpr int ST = decltype(st)::value;
     using NX = std::integral_constant<int, (ST + 1) % STAGES>;
     using AH = std::integral_constant<int, (ST + 3) % STAGES>;
-    // tile j+1 landed for this wave, then for all; stage (j-1) % 4 is free
-    if (j + 2 < ntiles) wait_vmcnt<LPT>();
-    else wait_vmcnt<0>();
+    // tile j+1 landed for this wave (only tile j+2's loads may remain), then
+    // for all; stage (j-1) % 4 is free
+    wait_vmcnt<LPT>();
     barrier_nofence();
-    issue(stage(AH{}), j + 3);
 
     tmx = mask_tile(j, S, TS, tmx);
     // Rare after the first tile.
@@ -313,7 +337,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           accO[c][i] = acc_write(acc_read(accO[c][i]) * alpha);
-          accT[c][i] = acc_write(acc_read(accT[c][i]) * alpha);
+          accV[c][i] = acc_write(acc_read(accV[c][i]) * alpha);
+          accS[c][i] = acc_write(acc_read(accS[c][i]) * alpha);
         }
       }
     }
@@ -322,11 +347,12 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 
     const uint16_t* nx = stage(NX{});  // on the last tile a stale stage; unused
     const uint16_t* cur = stage(st);
-    f32x16 S1, TS1;
+    f32x16 S1, TA1, TB1;  // tile j+1: q.k, tq.k, q.tk
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       S1[i] = 0.f;
-      TS1[i] = 0.f;
+      TA1[i] = 0.f;
+      TB1[i] = 0.f;
     }
     u32x4 kf[KS], tkf[KS];
     auto kread = [&](int s) {
@@ -338,8 +364,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     auto soft_pair = [&](int jj) {  // elements jj, jj+1 of tile j
       const float p0 = __builtin_amdgcn_exp2f(fmaf(S[jj], sl2, -mu));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(S[jj + 1], sl2, -mu));
-      const float w0 = p0 * (TS[jj] * scale);
-      const float w1 = p1 * (TS[jj + 1] * scale);
+      const float w0 = p0 * TS[jj];
+      const float w1 = p1 * TS[jj + 1];
       l += p0 + p1;
       r += w0 + w1;
       P[jj >> 3][(jj & 7) >> 1] = pack_bf16(p0, p1);
@@ -367,17 +393,20 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       if (s + 2 < KS) kread(s + 2);
       if (s == KS - 2) vread(0);
       if (s == KS - 1) vread(1);
+      // DMA of tile j+3 into the stage freed by the barrier, spread out
+#pragma unroll
+      for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q) issue_part(stage(AH{}), j + 3, q);
       __builtin_amdgcn_sched_barrier(0);
       S1 = mfma_bf16(kf[s], qf[s], S1);
-      TS1 = mfma_bf16(kf[s], tqf[s], TS1);
+      TA1 = mfma_bf16(kf[s], tqf[s], TA1);
 #pragma unroll
       for (int u = 0; u < PAIRS_PER_STEP; ++u) soft_pair(2 * (s * PAIRS_PER_STEP + u));
-      TS1 = mfma_bf16(tkf[s], qf[s], TS1);
+      TB1 = mfma_bf16(tkf[s], qf[s], TB1);
       __builtin_amdgcn_sched_barrier(0);
     }
 
     // phase 2: P.V of tile j under the copy-out and row max of tile j+1
-    constexpr int COPIES_PER_GROUP = 32 / (2 * DC);
+    constexpr int COPIES_PER_GROUP = 48 / (2 * DC);
     static_assert(COPIES_PER_GROUP <= 16, "tangent-score reads must not start in group 0");
     float tmax = -INFINITY;
 #pragma unroll
@@ -385,10 +414,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       if (gidx + 2 < 2 * DC) vread(gidx + 2);
       __builtin_amdgcn_sched_barrier(0);
       const int c2 = gidx / DC, c = gidx % DC;
-      accT[c] = mfma_bf16(tvfr[gidx], P[c2], accT[c]);
+      accV[c] = mfma_bf16(tvfr[gidx], P[c2], accV[c]);
       accO[c] = mfma_bf16(vfr[gidx], P[c2], accO[c]);
-      // copy-out of tile j+1's 32 score values, COPIES_PER_GROUP per group,
-      // scores first: the tangent scores' last MFMA ends phase 1, so their
+      // copy-out of tile j+1's 48 score values, COPIES_PER_GROUP per group,
+      // scores first: the tangent products' last MFMAs end phase 1, so their
       // reads start one group later, well past the result hazard.
 #pragma unroll
       for (int e = 0; e < COPIES_PER_GROUP; ++e) {
@@ -396,11 +425,13 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
         if (k < 16) {
           S[k] = acc_read(S1[k]);
           tmax = fmaxf(tmax, S[k]);
+        } else if (k < 32) {
+          TS[k - 16] = acc_read(TA1[k - 16]);
         } else {
-          TS[k - 16] = acc_read(TS1[k - 16]);
+          TS[k - 32] += acc_read(TB1[k - 32]);
         }
       }
-      accT[c] = mfma_bf16(vfr[gidx], W[c2], accT[c]);
+      accS[c] = mfma_bf16(vfr[gidx], W[c2], accS[c]);
       __builtin_amdgcn_sched_barrier(0);
     }
     tmx = pair_max(tmax) * sl2;
@@ -412,14 +443,14 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     issue(ring0, 0);
     issue(ring1, 1);
     issue(ring2, 2);
-    if (ntiles >= 3) wait_vmcnt<2 * LPT>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<2 * LPT>();
     barrier_nofence();
-    f32x16 Sa, TSa;
+    f32x16 Sa, TAa, TBa;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       Sa[i] = 0.f;
-      TSa[i] = 0.f;
+      TAa[i] = 0.f;
+      TBa[i] = 0.f;
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -427,14 +458,14 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       const u32x4 kf = *(const u32x4*)(ring0 + off);
       const u32x4 tkf = *(const u32x4*)(ring0 + TILE + off);
       Sa = mfma_bf16(kf, qf[s], Sa);
-      TSa = mfma_bf16(kf, tqf[s], TSa);
-      TSa = mfma_bf16(tkf, qf[s], TSa);
+      TAa = mfma_bf16(kf, tqf[s], TAa);
+      TBa = mfma_bf16(tkf, qf[s], TBa);
     }
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       S[i] = Sa[i];
-      TS[i] = TSa[i];
+      TS[i] = TAa[i] + TBa[i];
       tmax = fmaxf(tmax, S[i]);
     }
     tmx = pair_max(tmax) * sl2;
@@ -452,7 +483,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   // ---- epilogue: o = acc_o / l ; to = acc_t / l - (r / l) o ------------------
   acc_hazard_wait();
   const float lt = pair_sum(l);
-  const float rt = pair_sum(r);
+  const float rt = pair_sum(r) * scale;
   if (row_ok) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float rb = rt * inv;
@@ -466,8 +497,9 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
         float o4[4], t4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          o4[e] = acc_read(accO[c][4 * g4 + e]) * inv;
-          t4[e] = acc_read(accT[c][4 * g4 + e]) * inv - rb * o4[e];
+          const int i = 4 * g4 + e;
+          o4[e] = acc_read(accO[c][i]) * inv;
+          t4[e] = fmaf(acc_read(accS[c][i]), scale, acc_read(accV[c][i])) * inv - rb * o4[e];
         }
         u32x2 ov = {pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])};
         u32x2 tv = {pack_bf16(t4[0], t4[1]), pack_bf16(t4[2], t4[3])};
