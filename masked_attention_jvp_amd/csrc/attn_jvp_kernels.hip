@@ -347,12 +347,11 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 
     const uint16_t* nx = stage(NX{});  // on the last tile a stale stage; unused
     const uint16_t* cur = stage(st);
-    f32x16 S1, TA1, TB1;  // tile j+1: q.k, tq.k, q.tk
+    f32x16 S1, TS1;  // tile j+1: q.k and tq.k + q.tk
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       S1[i] = 0.f;
-      TA1[i] = 0.f;
-      TB1[i] = 0.f;
+      TS1[i] = 0.f;
     }
     u32x4 kf[KS], tkf[KS];
     auto kread = [&](int s) {
@@ -397,16 +396,16 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q) issue_part(stage(AH{}), j + 3, q);
       __builtin_amdgcn_sched_barrier(0);
+      TS1 = mfma_bf16(kf[s], tqf[s], TS1);
       S1 = mfma_bf16(kf[s], qf[s], S1);
-      TA1 = mfma_bf16(kf[s], tqf[s], TA1);
 #pragma unroll
       for (int u = 0; u < PAIRS_PER_STEP; ++u) soft_pair(2 * (s * PAIRS_PER_STEP + u));
-      TB1 = mfma_bf16(tkf[s], qf[s], TB1);
+      TS1 = mfma_bf16(tkf[s], qf[s], TS1);
       __builtin_amdgcn_sched_barrier(0);
     }
 
     // phase 2: P.V of tile j under the copy-out and row max of tile j+1
-    constexpr int COPIES_PER_GROUP = 48 / (2 * DC);
+    constexpr int COPIES_PER_GROUP = 32 / (2 * DC);
     static_assert(COPIES_PER_GROUP <= 16, "tangent-score reads must not start in group 0");
     float tmax = -INFINITY;
 #pragma unroll
@@ -416,8 +415,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       const int c2 = gidx / DC, c = gidx % DC;
       accV[c] = mfma_bf16(tvfr[gidx], P[c2], accV[c]);
       accO[c] = mfma_bf16(vfr[gidx], P[c2], accO[c]);
-      // copy-out of tile j+1's 48 score values, COPIES_PER_GROUP per group,
-      // scores first: the tangent products' last MFMAs end phase 1, so their
+      // copy-out of tile j+1's 32 score values, COPIES_PER_GROUP per group,
+      // scores first: the tangent product's last MFMA ends phase 1, so its
       // reads start one group later, well past the result hazard.
 #pragma unroll
       for (int e = 0; e < COPIES_PER_GROUP; ++e) {
@@ -425,10 +424,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
         if (k < 16) {
           S[k] = acc_read(S1[k]);
           tmax = fmaxf(tmax, S[k]);
-        } else if (k < 32) {
-          TS[k - 16] = acc_read(TA1[k - 16]);
         } else {
-          TS[k - 32] += acc_read(TB1[k - 32]);
+          TS[k - 16] = acc_read(TS1[k - 16]);
         }
       }
       accS[c] = mfma_bf16(vfr[gidx], W[c2], accS[c]);
