@@ -129,6 +129,22 @@ __device__ __forceinline__ float acc_write(float v) {
   return a;
 }
 
+// Score products in vector-register form: the scores go straight from the
+// matrix cores to the vector ALUs, with no accumulator-to-vector copies (on
+// gfx950 such a copy next to running MFMAs costs several times a plain vector
+// op).  Written out because the compiler gives all MFMAs of a kernel one
+// register form, and the output accumulators need the accumulation registers.
+// The compiler inserts the waits for the operands (LDS reads, loads) but does
+// not see the result hazard: vector instructions read these results only
+// after at least two further MFMAs have been issued, or after
+// acc_hazard_wait().
+__device__ __forceinline__ void mfma_v_first(f32x16& d, u32x4 a, u32x4 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_acc(f32x16& d, u32x4 a, u32x4 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+
 // Workgroup barrier without a memory fence: the fence of __syncthreads()
 // would wait for every LDS DMA in flight.  Visibility of the tile about to be
 // read comes from the explicit vmcnt wait before it; the memory clobber keeps
@@ -140,13 +156,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   constexpr int BC = kBf16BlockK;            // keys per tile (= one MFMA subtile)
   static_assert(BC == 32, "one 32-key subtile per tile");
-  constexpr int STAGES = 4;                  // LDS ring depth; tiles j+1..j+3 in flight
+  constexpr int STAGES = 4;                  // LDS ring depth; tiles j..j+3 resident or in flight
   constexpr int BR = NW * 32;
   constexpr int KS = D / 16;                 // k-steps of the score products
   constexpr int DC = D / 32;                 // 32-wide column blocks of the outputs
@@ -285,7 +306,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   // Mask tile t's scores where some row of the wave does not cover the whole
   // tile (S -> -inf, TS -> 0 outside the row's ranges); returns the masked
   // row max in exp2 units, or `tmx` unchanged for a fully covered tile.
-  auto mask_tile = [&](int t, float* S, float* TS, float tmx) -> float {
+  auto mask_tile = [&](int t, f32x16& S, f32x16& TS, float tmx) -> float {
     const int k0 = span_tile(sp, t) * BC;
     const bool whole = k0 + BC <= f1 || (k0 >= g0 && k0 + BC <= g1);
     if (__builtin_expect(whole, 1)) return tmx;
@@ -302,26 +323,33 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     return pair_max(tmax) * sl2;
   };
 
-  // One streamed tile j held in stage ST; S, TS hold its scores in vector
-  // registers and receive those of tile j+1.
-  // Top (its own blocks): ring wait, barrier, DMA of tile j+3, the mask of
-  // tile j if it is partial (rare), lazy rescale (rare).  Then one basic
-  // block laid out slot by slot (sched_barrier fences keep the order):
-  // * per k-step: K reads two k-steps ahead, then the S, TS, TS MFMAs of tile
-  //   j+1 around one unit of tile j's softmax (the two TS products one MFMA
-  //   apart, as they accumulate into the same tile);
-  // * per P.V group of tile j: V reads two groups ahead, then its three MFMAs
-  //   around the copy of a quarter of tile j+1's scores into vector
-  //   registers and their row max.
+  // K and tK fragments of the tile whose scores are formed next; the first
+  // two k-steps are read at the end of the previous step (loop-carried).
+  u32x4 kf[KS], tkf[KS];
+  auto kread = [&](const uint16_t* src, int s) {
+    const int off = n * D + (((2 * s + h) ^ row_swz<D>(n)) << 3);
+    kf[s] = *(const u32x4*)(src + off);
+    tkf[s] = *(const u32x4*)(src + TILE + off);
+  };
+
+  // Step j: tile j's scores S, TS (vector registers) are turned into p~ and
+  // p~ ts' and multiplied into the accumulators while tile j+1's scores are
+  // formed.  Ring use: tile t sits in stage t % 4; step j reads K of tile j+1
+  // and V of tile j, and issues the DMA of tile j+3 into the stage of tile
+  // j-1, freed by the previous step's barrier.  The barrier sits in phase 2,
+  // right after the last read of tile j's stage; before it each wave waits
+  // for its share of tile j+2, which the next step's first K reads (issued
+  // right after the barrier) need.  The last P.V MFMAs and the next step's
+  // top run while the waves meet.
+  // Scheduling unit: one MFMA plus a share of vector / LDS / DMA work, fenced
+  // by sched_barrier, so that no vector work piles up behind back-to-back
+  // MFMAs (with one wave per SIMD nothing else fills the matrix unit).
   // tmx carries the unmasked row max (exp2 units) of the tile about to be used.
-  auto step = [&](auto st, int j, float* S, float* TS, float& tmx) {
+  auto step = [&](auto st, int j, f32x16& S, f32x16& TS, f32x16& Sn, f32x16& TSn, float& tmx) {
     constexpr int ST = decltype(st)::value;
     using NX = std::integral_constant<int, (ST + 1) % STAGES>;
+    using N2 = std::integral_constant<int, (ST + 2) % STAGES>;
     using AH = std::integral_constant<int, (ST + 3) % STAGES>;
-    // tile j+1 landed for this wave (only tile j+2's loads may remain), then
-    // for all; stage (j-1) % 4 is free
-    wait_vmcnt<LPT>();
-    barrier_nofence();
 
     tmx = mask_tile(j, S, TS, tmx);
     // Rare after the first tile.
@@ -347,29 +375,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 
     const uint16_t* nx = stage(NX{});  // on the last tile a stale stage; unused
     const uint16_t* cur = stage(st);
-    f32x16 S1, TS1;  // tile j+1: q.k and tq.k + q.tk
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      S1[i] = 0.f;
-      TS1[i] = 0.f;
-    }
-    u32x4 kf[KS], tkf[KS];
-    auto kread = [&](int s) {
-      const int off = n * D + (((2 * s + h) ^ row_swz<D>(n)) << 3);
-      kf[s] = *(const u32x4*)(nx + off);
-      tkf[s] = *(const u32x4*)(nx + TILE + off);
-    };
+    float pv[16], wv[16];
     u32x4 P[2], W[2];
-    auto soft_pair = [&](int jj) {  // elements jj, jj+1 of tile j
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(S[jj], sl2, -mu));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(S[jj + 1], sl2, -mu));
-      const float w0 = p0 * TS[jj];
-      const float w1 = p1 * TS[jj + 1];
-      l += p0 + p1;
-      r += w0 + w1;
-      P[jj >> 3][(jj & 7) >> 1] = pack_bf16(p0, p1);
-      W[jj >> 3][(jj & 7) >> 1] = pack_bf16(w0, w1);
-    };
     u32x4 vfr[2 * DC], tvfr[2 * DC];
     auto vread = [&](int gidx) {
       const int c2 = gidx / DC, c = gidx % DC;
@@ -383,98 +390,125 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       tvfr[gidx] = u32x4{ta[0], ta[1], tb[0], tb[1]};
     };
 
-    // phase 1: scores of tile j+1 under the softmax of tile j
+    // phase 1: scores of tile j+1 under the softmax of tile j; per k-step
+    // three slots, the softmax of PAIRS_PER_STEP element pairs split as
+    // exp | p~ ts', pack p~, l | pack p~ ts', r; K reads two k-steps ahead.
     constexpr int PAIRS_PER_STEP = 8 / KS;
-    kread(0);
-    if (KS > 1) kread(1);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if (s + 2 < KS) kread(s + 2);
-      if (s == KS - 2) vread(0);
-      if (s == KS - 1) vread(1);
-      // DMA of tile j+3 into the stage freed by the barrier, spread out
+      if (s == 0) mfma_v_first(TSn, kf[s], tqf[s]);
+      else mfma_v_acc(TSn, kf[s], tqf[s]);
+#pragma unroll
+      for (int u = 0; u < PAIRS_PER_STEP; ++u) {
+        const int jj = 2 * (s * PAIRS_PER_STEP + u);
+        pv[jj] = __builtin_amdgcn_exp2f(fmaf(S[jj], sl2, -mu));
+        pv[jj + 1] = __builtin_amdgcn_exp2f(fmaf(S[jj + 1], sl2, -mu));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (s == 0) mfma_v_first(Sn, kf[s], qf[s]);
+      else mfma_v_acc(Sn, kf[s], qf[s]);
+      // (in this slot, so that the first MFMA of the k-step never waits for it)
+      if (s + 2 < KS) kread(nx, s + 2);
+      // DMA of tile j+3 into the stage freed by the previous barrier
 #pragma unroll
       for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q) issue_part(stage(AH{}), j + 3, q);
-      __builtin_amdgcn_sched_barrier(0);
-      TS1 = mfma_bf16(kf[s], tqf[s], TS1);
-      S1 = mfma_bf16(kf[s], qf[s], S1);
 #pragma unroll
-      for (int u = 0; u < PAIRS_PER_STEP; ++u) soft_pair(2 * (s * PAIRS_PER_STEP + u));
-      TS1 = mfma_bf16(tkf[s], qf[s], TS1);
+      for (int u = 0; u < PAIRS_PER_STEP; ++u) {
+        const int jj = 2 * (s * PAIRS_PER_STEP + u);
+        wv[jj] = pv[jj] * TS[jj];
+        wv[jj + 1] = pv[jj + 1] * TS[jj + 1];
+        P[jj >> 3][(jj & 7) >> 1] = pack_bf16(pv[jj], pv[jj + 1]);
+        l += pv[jj] + pv[jj + 1];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_v_acc(TSn, tkf[s], qf[s]);
+      if (s == KS - 2) vread(0);
+      if (s == KS - 1) vread(1);
+#pragma unroll
+      for (int u = 0; u < PAIRS_PER_STEP; ++u) {
+        const int jj = 2 * (s * PAIRS_PER_STEP + u);
+        W[jj >> 3][(jj & 7) >> 1] = pack_bf16(wv[jj], wv[jj + 1]);
+        r += wv[jj] + wv[jj + 1];
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // phase 2: P.V of tile j under the copy-out and row max of tile j+1
-    constexpr int COPIES_PER_GROUP = 32 / (2 * DC);
-    static_assert(COPIES_PER_GROUP <= 16, "tangent-score reads must not start in group 0");
+    // phase 2: P.V of tile j under the row max of tile j+1's scores, taken
+    // from group 1 on (two MFMAs after the last score product) in the
+    // groups' second and third slots.
+    constexpr int MAX_SLOTS = 2 * (2 * DC - 1);
+    constexpr int MAX_PER_SLOT = (16 + MAX_SLOTS - 1) / MAX_SLOTS;
     float tmax = -INFINITY;
+    auto row_max_part = [&](int slot) {
+#pragma unroll
+      for (int e = 0; e < MAX_PER_SLOT; ++e) {
+        const int k = slot * MAX_PER_SLOT + e;
+        if (k < 16) tmax = fmaxf(tmax, Sn[k]);
+        if (k == 15) tmx = pair_max(tmax) * sl2;
+      }
+    };
 #pragma unroll
     for (int gidx = 0; gidx < 2 * DC; ++gidx) {
-      if (gidx + 2 < 2 * DC) vread(gidx + 2);
-      __builtin_amdgcn_sched_barrier(0);
       const int c2 = gidx / DC, c = gidx % DC;
       accV[c] = mfma_bf16(tvfr[gidx], P[c2], accV[c]);
-      accO[c] = mfma_bf16(vfr[gidx], P[c2], accO[c]);
-      // copy-out of tile j+1's 32 score values, COPIES_PER_GROUP per group,
-      // scores first: the tangent product's last MFMA ends phase 1, so its
-      // reads start one group later, well past the result hazard.
-#pragma unroll
-      for (int e = 0; e < COPIES_PER_GROUP; ++e) {
-        const int k = gidx * COPIES_PER_GROUP + e;
-        if (k < 16) {
-          S[k] = acc_read(S1[k]);
-          tmax = fmaxf(tmax, S[k]);
-        } else {
-          TS[k - 16] = acc_read(TS1[k - 16]);
-        }
+      if (gidx + 2 < 2 * DC) vread(gidx + 2);
+      if (gidx == 2 * DC - 2) {
+        // every read of tile j's stage is done; tile j+2 has landed here
+        wait_lgkmcnt<0>();
+        wait_vmcnt<LPT>();
+        barrier_nofence();
       }
+      __builtin_amdgcn_sched_barrier(0);
+      accO[c] = mfma_bf16(vfr[gidx], P[c2], accO[c]);
+      if (gidx > 0) row_max_part(2 * (gidx - 1));
+      if (gidx == 2 * DC - 2) kread(stage(N2{}), 0);
+      __builtin_amdgcn_sched_barrier(0);
       accS[c] = mfma_bf16(vfr[gidx], W[c2], accS[c]);
+      if (gidx > 0) row_max_part(2 * (gidx - 1) + 1);
+      if (gidx == 2 * DC - 2) kread(stage(N2{}), 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    tmx = pair_max(tmax) * sl2;
   };
 
-  float S[16], TS[16];  // scores of the current tile, in vector registers
+  // Scores of two consecutive tiles in vector registers: the current tile's
+  // (read by the softmax) and the next one's (written by the MFMAs); the
+  // roles alternate from step to step.
+  f32x16 SA, TSA, SB, TSB;
   float tmx = -INFINITY;
   if (ntiles > 0) {
     issue(ring0, 0);
     issue(ring1, 1);
     issue(ring2, 2);
-    wait_vmcnt<2 * LPT>();
+    wait_vmcnt<LPT>();  // tiles 0 and 1
     barrier_nofence();
-    f32x16 Sa, TAa, TBa;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      Sa[i] = 0.f;
-      TAa[i] = 0.f;
-      TBa[i] = 0.f;
-    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int off = n * D + (((2 * s + h) ^ row_swz<D>(n)) << 3);
-      const u32x4 kf = *(const u32x4*)(ring0 + off);
-      const u32x4 tkf = *(const u32x4*)(ring0 + TILE + off);
-      Sa = mfma_bf16(kf, qf[s], Sa);
-      TAa = mfma_bf16(kf, tqf[s], TAa);
-      TBa = mfma_bf16(tkf, qf[s], TBa);
+      kread(ring0, s);
+      if (s == 0) {
+        mfma_v_first(SA, kf[s], qf[s]);
+        mfma_v_first(TSA, kf[s], tqf[s]);
+      } else {
+        mfma_v_acc(SA, kf[s], qf[s]);
+        mfma_v_acc(TSA, kf[s], tqf[s]);
+      }
+      mfma_v_acc(TSA, tkf[s], qf[s]);
     }
+    acc_hazard_wait();
     float tmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      S[i] = Sa[i];
-      TS[i] = TAa[i] + TBa[i];
-      tmax = fmaxf(tmax, S[i]);
-    }
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, SA[i]);
     tmx = pair_max(tmax) * sl2;
+    kread(ring1, 0);
+    kread(ring1, 1);
   }
   for (int j = 0; j < ntiles; j += 4) {
-    step(I0{}, j, S, TS, tmx);
+    step(I0{}, j, SA, TSA, SB, TSB, tmx);
     if (j + 1 >= ntiles) break;
-    step(I1{}, j + 1, S, TS, tmx);
+    step(I1{}, j + 1, SB, TSB, SA, TSA, tmx);
     if (j + 2 >= ntiles) break;
-    step(I2{}, j + 2, S, TS, tmx);
+    step(I2{}, j + 2, SA, TSA, SB, TSB, tmx);
     if (j + 3 >= ntiles) break;
-    step(I3{}, j + 3, S, TS, tmx);
+    step(I3{}, j + 3, SB, TSB, SA, TSA, tmx);
   }
 
   // ---- epilogue: o = acc_o / l ; to = acc_t / l - (r / l) o ------------------
@@ -507,6 +541,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     if (h == 0 && p.lse != nullptr)
       p.lse[(size_t)bh * N + row] = lt > 0.f ? m * kLn2 + logf(lt) : -INFINITY;
   }
+  // the last steps' DMAs (of tiles past the end) may still be in flight
+  wait_vmcnt<0>();
 }
 
 // fp32 kernel: 32 query rows per workgroup, 8 lanes per row, each lane owning
