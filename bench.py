@@ -191,7 +191,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": f"fwd_bf16_kernel<{w.head_dim},{info['block_k']},{info['block_q'] // 32}>",
+            "kernel": f"fwd_bf16_kernel<{w.head_dim},{info['block_q'] // 32}>",
             "avg_launch_ms": round(avg_ms, 4),
         },
     }

@@ -137,7 +137,8 @@ __device__ __forceinline__ float acc_write(float v) {
 // The compiler inserts the waits for the operands (LDS reads, loads) but does
 // not see the result hazard: vector instructions read these results only
 // after at least two further MFMAs have been issued, or after
-// acc_hazard_wait().
+// acc_hazard_wait() fenced by sched_barrier on both sides (plain vector code
+// may otherwise be scheduled across the asm).
 __device__ __forceinline__ void mfma_v_first(f32x16& d, u32x4 a, u32x4 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
@@ -493,7 +494,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       }
       mfma_v_acc(TSA, tkf[s], qf[s]);
     }
+    // fenced: the compiler would otherwise move the reads of SA above the wait
+    __builtin_amdgcn_sched_barrier(0);
     acc_hazard_wait();
+    __builtin_amdgcn_sched_barrier(0);
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, SA[i]);
