@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,7 +29,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4 SIMD x 1024 bf16 flop/clk x 2.4 GHz (dense)
 METRIC = "useful TFLOP/s of masked attn fwd+JVP and % of bf16 MFMA peak, 1 GPU"
-KERNEL_SRC = os.path.join(ROOT, "masked_attention_jvp_amd", "csrc", "attn_jvp_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "masked_attention_jvp_amd", "csrc", f)
+               for f in ("attn_jvp_kernels.hip", "attn_jvp_launch.h", "mask_index.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_d128_tf_framewise_65520.json")
 
 
@@ -63,8 +65,14 @@ def copy_reference(steps):
 
 
 def kernel_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the code the kernels are built from (comments and blank lines
+    removed), so that counters stay attached to an unchanged kernel."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path) as f:
+            code = re.sub(r"//[^\n]*", "", f.read())
+        h.update("\n".join(l.rstrip() for l in code.splitlines() if l.strip()).encode())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(workload_name):
@@ -75,7 +83,7 @@ def traffic_for(workload_name):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256_16") != kernel_hash() or t.get("workload") != workload_name:
+    if t.get("kernel_code_sha256_16") != kernel_hash() or t.get("workload") != workload_name:
         return None
     return t.get("hbm_bytes_per_launch")
 

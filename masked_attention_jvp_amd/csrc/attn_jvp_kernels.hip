@@ -7,9 +7,10 @@
 // accumulators sum p~ tv, sum p~ ts v and the row term r = sum p~ ts, all
 // rescaled by the same online factor; the epilogue forms
 //   o = acc_o / l,   to = (acc_tv + acc_tsv) / l - (r / l) o
-// with the normalised o.  Here acc_tv and acc_tsv share one register tile:
-// both take the same rescale and the same 1/l, so their sum is carried
-// directly.
+// with the normalised o.  All accumulators take the same rescale and the
+// same 1/l; the fp32 kernel carries acc_tv + acc_tsv as one sum, the bf16
+// kernel keeps them apart (acc_tsv with the unscaled score tangent, the
+// scale applied once in the epilogue).
 //
 // bf16 kernel (one workgroup = one query block of 32*NW rows, one wave = 32
 // query rows, 64-wide wavefronts, v_mfma_f32_32x32x16_bf16 with fp32
@@ -21,13 +22,16 @@
 //   O^T += V^T P^T: its 8 values per 16-key chunk are keys {4h..4h+3} and
 //   {8+4h..8+4h+3}, and V^T is fetched in exactly that key order with the
 //   gfx950 transposing LDS read (ds_read_b64_tr_b16), so V stays row-major;
+// * the score MFMAs write vector registers directly (VGPR form), so the
+//   softmax reads them with no accumulator-to-vector copies;
 // * K, tK, V, tV tiles of 32 keys go HBM -> LDS by buffer_load ... lds (no
-//   registers, no VALU), into a ring of 4 stages, 3 tiles ahead of use; rows
-//   are XOR-swizzled in 16-byte groups so the fragment reads are
-//   bank-conflict free; loads past the end of the sequence return zeros;
+//   registers, no VALU), into a ring of 4 stages; rows are XOR-swizzled in
+//   16-byte groups so the fragment reads are bank-conflict free; loads past
+//   the end of the sequence return zeros;
 // * software pipelining: the score MFMAs of tile j+1 sit in the same basic
-//   block as the exp/convert VALU work and the P.V MFMAs of tile j, so the
-//   matrix cores and the vector ALUs of one wave overlap;
+//   block as the softmax of tile j and the P.V MFMAs of tile j, one MFMA per
+//   scheduling slot with a share of the vector work, so the matrix cores and
+//   the vector ALUs of one wave overlap;
 // * rescaling is lazy: the stored row max only moves when a tile's max
 //   exceeds it by more than 2^8 (in exp2 units), which keeps every p~ <= 256
 //   and is exact in real arithmetic because l, r and the accumulators all
