@@ -21,7 +21,10 @@ import hashlib
 import json
 import os
 import re
+import statistics
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +45,9 @@ def parse():
     ap.add_argument("--config", type=int, default=3, help="workload id (2..5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=1)
+    ap.add_argument("--heads", type=int, default=0,
+                    help="override the workload's head count, e.g. 3 = one GPU's share of the 12-head "
+                         "workload under 4-way head (Ulysses) sharding")
     ap.add_argument("--mode", choices=["attn", "copy"], default="attn",
                     help="copy: a plain 1 GiB device copy, the reference for HBM byte counters")
     return ap.parse_args()
@@ -62,6 +68,42 @@ def copy_reference(steps):
     dt = (time.perf_counter() - t0) / steps
     print(json.dumps({"mode": "copy", "bytes_read_per_copy": 2 * n, "bytes_written_per_copy": 2 * n,
                       "ms_per_copy": round(dt * 1e3, 4), "GB_per_s": round(4 * n / dt / 1e9, 1)}), flush=True)
+
+
+def smi_sample():
+    """(socket power W, GFX clock MHz) from amd-smi, or None where unavailable."""
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True, timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    pw = re.search(r"SOCKET_POWER:\s*([\d.]+)\s*W", out)
+    ck = re.search(r"GFX_0:\s*CLK:\s*([\d.]+)\s*MHz", out)
+    if not pw or not ck:
+        return None
+    return float(pw.group(1)), float(ck.group(1))
+
+
+class SmiSampler(threading.Thread):
+    """Samples power and clock while the timed launches run."""
+
+    def __init__(self):
+        super().__init__(daemon=True)
+        self.samples, self.stop = [], threading.Event()
+
+    def run(self):
+        while not self.stop.is_set():
+            v = smi_sample()
+            if v is None:
+                return
+            self.samples.append(v)
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"samples": len(self.samples),
+                "power_w_median": statistics.median(v[0] for v in self.samples),
+                "sclk_mhz_median": statistics.median(v[1] for v in self.samples),
+                "sclk_mhz_min": min(v[1] for v in self.samples)}
 
 
 def kernel_hash():
@@ -131,6 +173,8 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     w = si.WORKLOADS[args.config]
+    if args.heads > 0 and args.heads != w.heads:
+        w = w.with_(heads=args.heads, name=f"{w.name}_h{args.heads}")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
@@ -152,7 +196,10 @@ def main():
     stream = torch.cuda.current_stream(dev)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    smi_before = smi_sample()
+    sampler = SmiSampler()
     torch.cuda.synchronize()
+    sampler.start()
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
@@ -160,6 +207,9 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sampler.stop.set()
+    sampler.join(timeout=15)
+    smi_after = smi_sample()
     per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_ms = float(np.mean(per_launch_ms))
     total_ms = starts[0].elapsed_time(ends[-1])
@@ -191,6 +241,12 @@ def main():
         },
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "useful_tflop_per_step": round(useful / 1e12, 4),
+        "launch_ms": {"mean": round(avg_ms, 4), "median": round(float(np.median(per_launch_ms)), 4),
+                      "min": round(float(np.min(per_launch_ms)), 4)},
+        # amd-smi's power and clock readings trail the load by about a second:
+        # samples during the timed launches are kept only for runs of 2 s or more.
+        "gpu_power_clock": {"before": smi_before, "after": smi_after,
+                            "during": sampler.summary() if wall >= 2.0 else None},
         "wall_s_timed": round(wall, 3),
         "roofline": {
             "bound": "mfma",
