@@ -150,6 +150,12 @@ __device__ __forceinline__ void mfma_v_acc(f32x16& d, u32x4 a, u32x4 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 
+// Pin a value to this point of the instruction stream: it must be computed
+// before the (volatile, hence ordered) empty asm, so the compiler cannot sink
+// it into a later block.  Emits no instruction.
+__device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void pin(uint32_t x) { asm volatile("" ::"v"(x)); }
+
 // Workgroup barrier without a memory fence: the fence of __syncthreads()
 // would wait for every LDS DMA in flight.  Visibility of the tile about to be
 // read comes from the explicit vmcnt wait before it; the memory clobber keeps
@@ -272,7 +278,9 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       accS[c][i] = 0.f;
     }
   }
-  float m = -INFINITY, l = 0.f, r = 0.f;  // r = sum p~ ts' (unscaled)
+  // m: reference max of l, r and the accumulators; mn: reference of the
+  // latest exponentiated tile (exp2 units).  r = sum p~ ts' (unscaled).
+  float m = -INFINITY, mn = -INFINITY, l = 0.f, r = 0.f;
   const float sl2 = p.score_log2;
   const float scale = p.scale;
 
@@ -309,24 +317,32 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   }
 
   // Mask tile t's scores where some row of the wave does not cover the whole
-  // tile (S -> -inf, TS -> 0 outside the row's ranges); returns the masked
-  // row max in exp2 units, or `tmx` unchanged for a fully covered tile.
-  auto mask_tile = [&](int t, f32x16& S, f32x16& TS, float tmx) -> float {
+  // tile (S -> -inf, TS -> 0 outside the row's ranges).  The test is scalar;
+  // the masking itself runs on partial tiles only.
+  auto tile_whole = [&](int t) {
     const int k0 = span_tile(sp, t) * BC;
-    const bool whole = k0 + BC <= f1 || (k0 >= g0 && k0 + BC <= g1);
-    if (__builtin_expect(whole, 1)) return tmx;
+    return k0 + BC <= f1 || (k0 >= g0 && k0 + BC <= g1);
+  };
+  auto mask_tile = [&](int t, f32x16& S, f32x16& TS) {
+    const int k0 = span_tile(sp, t) * BC;
     const int b1 = k0 + 4 * h - rr.lo1, b2 = k0 + 4 * h - rr.lo2;
-    float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int off = 8 * (i >> 2) + (i & 3);
       const bool ok = (unsigned)(b1 + off) < (unsigned)len1 || (unsigned)(b2 + off) < (unsigned)len2;
       S[i] = ok ? S[i] : -INFINITY;
       TS[i] = ok ? TS[i] : 0.f;
-      tmax = fmaxf(tmax, S[i]);
     }
-    return pair_max(tmax) * sl2;
   };
+  // New reference max of a row after a tile with row max tmx (exp2 units):
+  // it moves only when the tile exceeds it by more than 2^8.
+  auto next_ref = [&](float ref, float tmx) {
+    return tmx > ref + kLazyRescaleLog2 ? fmaxf(ref, tmx) : ref;
+  };
+  // p~ = exp2(s * sl2 - ref), in place, with nref = -ref (0 for ref = -inf:
+  // no allowed key yet, every score of the row is -inf).
+  auto neg_ref = [](float ref) { return ref == -INFINITY ? 0.f : -ref; };
+  auto exp_elem = [&](float x, float nref) { return __builtin_amdgcn_exp2f(fmaf(x, sl2, nref)); };
 
   // K and tK fragments of the tile whose scores are formed next; the first
   // two k-steps are read at the end of the previous step (loop-carried).
@@ -337,30 +353,39 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     tkf[s] = *(const u32x4*)(src + TILE + off);
   };
 
-  // Step j: tile j's scores S, TS (vector registers) are turned into p~ and
-  // p~ ts' and multiplied into the accumulators while tile j+1's scores are
-  // formed.  Ring use: tile t sits in stage t % 4; step j reads K of tile j+1
-  // and V of tile j, and issues the DMA of tile j+3 into the stage of tile
-  // j-1, freed by the previous step's barrier.  The barrier sits in phase 2,
-  // right after the last read of tile j's stage; before it each wave waits
-  // for its share of tile j+2, which the next step's first K reads (issued
-  // right after the barrier) need.  The last P.V MFMAs and the next step's
-  // top run while the waves meet.
-  // Scheduling unit: one MFMA plus a share of vector / LDS / DMA work, fenced
-  // by sched_barrier, so that no vector work piles up behind back-to-back
-  // MFMAs (with one wave per SIMD nothing else fills the matrix unit).
-  // tmx carries the unmasked row max (exp2 units) of the tile about to be used.
-  auto step = [&](auto st, int j, f32x16& S, f32x16& TS, f32x16& Sn, f32x16& TSn, float& tmx) {
+  // Step j.  On entry P holds tile j's p~ (already exponentiated against the
+  // reference mn) and TS its unscaled score tangents; Sn, TSn receive tile
+  // j+1's scores.
+  // * top: if some row's reference moved (mn != m), rescale l, r and the
+  //   accumulators to mn (rare after the first tile);
+  // * phase 1 (score MFMAs of tile j+1): p~ ts', the bf16 packs and the sums
+  //   l, r of tile j;
+  // * phase 2 (P.V MFMAs of tile j): tile j+1's element mask (partial tiles
+  //   only), row max, new reference and exponentials, in place in Sn.
+  // The exponentials thus run under the P.V MFMAs and the rest of the
+  // softmax under the score MFMAs, which balances the vector work of the
+  // two phases.
+  // Ring use: tile t sits in stage t % 4; step j reads K of tile j+1 and V of
+  // tile j, and issues the DMA of tile j+3 into the stage of tile j-1, freed
+  // by the previous step's barrier.  The barrier sits in phase 2, right after
+  // the last read of tile j's stage; before it each wave waits for its share
+  // of tile j+2, which the next step's first K reads (issued right after the
+  // barrier) need.  The last P.V MFMAs and the next step's top run while the
+  // waves meet.
+  // Scheduling unit: one MFMA followed by a share of vector / LDS / DMA work,
+  // fenced by sched_barrier on both sides of the MFMA, so that each MFMA's
+  // execution covers its own share and no vector work piles up behind
+  // back-to-back MFMAs (with one wave per SIMD nothing else fills the matrix
+  // unit).
+  auto step = [&](auto st, int j, f32x16& P, f32x16& TS, f32x16& Sn, f32x16& TSn) {
     constexpr int ST = decltype(st)::value;
     using NX = std::integral_constant<int, (ST + 1) % STAGES>;
     using N2 = std::integral_constant<int, (ST + 2) % STAGES>;
     using AH = std::integral_constant<int, (ST + 3) % STAGES>;
 
-    tmx = mask_tile(j, S, TS, tmx);
     // Rare after the first tile.
-    if (__builtin_expect(__any(tmx > m + kLazyRescaleLog2), 0)) {
-      const float mn = fmaxf(m, tmx);
-      const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+    if (__builtin_expect(__any(mn != m), 0)) {
+      const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
       m = mn;
       l *= alpha;
       r *= alpha;
@@ -375,13 +400,12 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
         }
       }
     }
-    const float mu = (m == -INFINITY) ? 0.f : m;
     __builtin_amdgcn_sched_barrier(0);
 
     const uint16_t* nx = stage(NX{});  // on the last tile a stale stage; unused
     const uint16_t* cur = stage(st);
-    float pv[16], wv[16];
-    u32x4 P[2], W[2];
+    float wv[16];
+    u32x4 PK[2], W[2];
     u32x4 vfr[2 * DC], tvfr[2 * DC];
     auto vread = [&](int gidx) {
       const int c2 = gidx / DC, c = gidx % DC;
@@ -395,23 +419,27 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       tvfr[gidx] = u32x4{ta[0], ta[1], tb[0], tb[1]};
     };
 
-    // phase 1: scores of tile j+1 under the softmax of tile j; per k-step
-    // three slots, the softmax of PAIRS_PER_STEP element pairs split as
-    // exp | p~ ts', pack p~, l | pack p~ ts', r; K reads two k-steps ahead.
+    // phase 1: scores of tile j+1 under the rest of tile j's softmax; per
+    // k-step three slots: p~ ts' | pack p~, l | pack p~ ts', r.  K reads two
+    // k-steps ahead.
     constexpr int PAIRS_PER_STEP = 8 / KS;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (s == 0) mfma_v_first(TSn, kf[s], tqf[s]);
       else mfma_v_acc(TSn, kf[s], tqf[s]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < PAIRS_PER_STEP; ++u) {
         const int jj = 2 * (s * PAIRS_PER_STEP + u);
-        pv[jj] = __builtin_amdgcn_exp2f(fmaf(S[jj], sl2, -mu));
-        pv[jj + 1] = __builtin_amdgcn_exp2f(fmaf(S[jj + 1], sl2, -mu));
+        wv[jj] = P[jj] * TS[jj];
+        wv[jj + 1] = P[jj + 1] * TS[jj + 1];
+        pin(wv[jj]);
+        pin(wv[jj + 1]);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (s == 0) mfma_v_first(Sn, kf[s], qf[s]);
       else mfma_v_acc(Sn, kf[s], qf[s]);
+      __builtin_amdgcn_sched_barrier(0);
       // (in this slot, so that the first MFMA of the k-step never waits for it)
       if (s + 2 < KS) kread(nx, s + 2);
       // DMA of tile j+3 into the stage freed by the previous barrier
@@ -420,13 +448,14 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int u = 0; u < PAIRS_PER_STEP; ++u) {
         const int jj = 2 * (s * PAIRS_PER_STEP + u);
-        wv[jj] = pv[jj] * TS[jj];
-        wv[jj + 1] = pv[jj + 1] * TS[jj + 1];
-        P[jj >> 3][(jj & 7) >> 1] = pack_bf16(pv[jj], pv[jj + 1]);
-        l += pv[jj] + pv[jj + 1];
+        PK[jj >> 3][(jj & 7) >> 1] = pack_bf16(P[jj], P[jj + 1]);
+        l += P[jj] + P[jj + 1];
+        pin(PK[jj >> 3][(jj & 7) >> 1]);
+        pin(l);
       }
       __builtin_amdgcn_sched_barrier(0);
       mfma_v_acc(TSn, tkf[s], qf[s]);
+      __builtin_amdgcn_sched_barrier(0);
       if (s == KS - 2) vread(0);
       if (s == KS - 1) vread(1);
 #pragma unroll
@@ -434,52 +463,81 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
         const int jj = 2 * (s * PAIRS_PER_STEP + u);
         W[jj >> 3][(jj & 7) >> 1] = pack_bf16(wv[jj], wv[jj + 1]);
         r += wv[jj] + wv[jj + 1];
+        pin(W[jj >> 3][(jj & 7) >> 1]);
+        pin(r);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // phase 2: P.V of tile j under the row max of tile j+1's scores, taken
-    // from group 1 on (two MFMAs after the last score product) in the
-    // groups' second and third slots.
-    constexpr int MAX_SLOTS = 2 * (2 * DC - 1);
-    constexpr int MAX_PER_SLOT = (16 + MAX_SLOTS - 1) / MAX_SLOTS;
-    float tmax = -INFINITY;
-    auto row_max_part = [&](int slot) {
+    // phase 2: P.V of tile j under tile j+1's softmax front half.  Group 0
+    // carries no vector work on Sn (two MFMAs must pass after its last score
+    // product); then the mask of a partial tile, the row max in the second
+    // and third slots of MAX_GROUPS groups, the new reference, and the
+    // exponentials spread over all slots of the remaining groups.
+    constexpr int NG = 2 * DC;
+    constexpr int MAX_GROUPS = NG >= 8 ? 2 : 1;
+    constexpr int MAX_SLOTS = 2 * MAX_GROUPS;
+    constexpr int MAX_PER_SLOT = 16 / MAX_SLOTS;
+    constexpr int EXP_SLOTS = 3 * (NG - 1 - MAX_GROUPS);
+    static_assert(MAX_PER_SLOT * MAX_SLOTS == 16 && EXP_SLOTS > 0, "phase-2 split");
+    float tmax = -INFINITY, ref = mn, nref = 0.f;
+    auto row_max = [&](int slot) {  // slot 0 .. MAX_SLOTS-1
 #pragma unroll
-      for (int e = 0; e < MAX_PER_SLOT; ++e) {
-        const int k = slot * MAX_PER_SLOT + e;
-        if (k < 16) tmax = fmaxf(tmax, Sn[k]);
-        if (k == 15) tmx = pair_max(tmax) * sl2;
+      for (int e = 0; e < MAX_PER_SLOT; ++e) tmax = fmaxf(tmax, Sn[slot * MAX_PER_SLOT + e]);
+      pin(tmax);
+      if (slot == MAX_SLOTS - 1) {
+        ref = next_ref(mn, pair_max(tmax) * sl2);
+        nref = neg_ref(ref);
+        pin(nref);
       }
     };
+    auto exps = [&](int slot) {  // slot 0 .. EXP_SLOTS-1: elements k with k * EXP_SLOTS / 16 == slot
 #pragma unroll
-    for (int gidx = 0; gidx < 2 * DC; ++gidx) {
+      for (int k = 0; k < 16; ++k) {
+        if (k * EXP_SLOTS / 16 == slot) {
+          Sn[k] = exp_elem(Sn[k], nref);
+          pin(Sn[k]);
+        }
+      }
+    };
+    // the vector work of slot `sl` (0..2) of group gidx
+    auto front_half = [&](int gidx, int sl) {
+      if (gidx >= 1 && gidx <= MAX_GROUPS && sl > 0) row_max(2 * (gidx - 1) + sl - 1);
+      if (gidx > MAX_GROUPS) exps(3 * (gidx - 1 - MAX_GROUPS) + sl);
+    };
+#pragma unroll
+    for (int gidx = 0; gidx < NG; ++gidx) {
       const int c2 = gidx / DC, c = gidx % DC;
-      accV[c] = mfma_bf16(tvfr[gidx], P[c2], accV[c]);
-      if (gidx + 2 < 2 * DC) vread(gidx + 2);
-      if (gidx == 2 * DC - 2) {
+      if (gidx == 1 && !tile_whole(j + 1)) mask_tile(j + 1, Sn, TSn);  // rare
+      accV[c] = mfma_bf16(tvfr[gidx], PK[c2], accV[c]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (gidx + 2 < NG) vread(gidx + 2);
+      front_half(gidx, 0);
+      if (gidx == NG - 2) {
         // every read of tile j's stage is done; tile j+2 has landed here
         wait_lgkmcnt<0>();
         wait_vmcnt<LPT>();
         barrier_nofence();
       }
       __builtin_amdgcn_sched_barrier(0);
-      accO[c] = mfma_bf16(vfr[gidx], P[c2], accO[c]);
-      if (gidx > 0) row_max_part(2 * (gidx - 1));
-      if (gidx == 2 * DC - 2) kread(stage(N2{}), 0);
+      accO[c] = mfma_bf16(vfr[gidx], PK[c2], accO[c]);
+      __builtin_amdgcn_sched_barrier(0);
+      front_half(gidx, 1);
+      if (gidx == NG - 2) kread(stage(N2{}), 0);
       __builtin_amdgcn_sched_barrier(0);
       accS[c] = mfma_bf16(vfr[gidx], W[c2], accS[c]);
-      if (gidx > 0) row_max_part(2 * (gidx - 1) + 1);
-      if (gidx == 2 * DC - 2) kread(stage(N2{}), 1);
+      __builtin_amdgcn_sched_barrier(0);
+      front_half(gidx, 2);
+      if (gidx == NG - 2) kread(stage(N2{}), 1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    mn = ref;
   };
 
   // Scores of two consecutive tiles in vector registers: the current tile's
-  // (read by the softmax) and the next one's (written by the MFMAs); the
-  // roles alternate from step to step.
+  // p~ (read by phase 1) and the next one's scores (written by the MFMAs,
+  // exponentiated in phase 2); the roles alternate from step to step.
   f32x16 SA, TSA, SB, TSB;
-  float tmx = -INFINITY;
   if (ntiles > 0) {
     issue(ring0, 0);
     issue(ring1, 1);
@@ -502,21 +560,25 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     acc_hazard_wait();
     __builtin_amdgcn_sched_barrier(0);
+    if (!tile_whole(0)) mask_tile(0, SA, TSA);
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, SA[i]);
-    tmx = pair_max(tmax) * sl2;
+    mn = next_ref(mn, pair_max(tmax) * sl2);
+    const float nref = neg_ref(mn);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) SA[i] = exp_elem(SA[i], nref);
     kread(ring1, 0);
     kread(ring1, 1);
   }
   for (int j = 0; j < ntiles; j += 4) {
-    step(I0{}, j, SA, TSA, SB, TSB, tmx);
+    step(I0{}, j, SA, TSA, SB, TSB);
     if (j + 1 >= ntiles) break;
-    step(I1{}, j + 1, SB, TSB, SA, TSA, tmx);
+    step(I1{}, j + 1, SB, TSB, SA, TSA);
     if (j + 2 >= ntiles) break;
-    step(I2{}, j + 2, SA, TSA, SB, TSB, tmx);
+    step(I2{}, j + 2, SA, TSA, SB, TSB);
     if (j + 3 >= ntiles) break;
-    step(I3{}, j + 3, SB, TSB, SA, TSA, tmx);
+    step(I3{}, j + 3, SB, TSB, SA, TSA);
   }
 
   // ---- epilogue: o = acc_o / l ; to = acc_t / l - (r / l) o ------------------
