@@ -16,7 +16,9 @@ Sources (Causal-rCM, arXiv 2606.25473):
 * section 4 "Experiments": frame-wise (c1-1) and chunk-wise (c3-3) chunking,
   with the same chunk pattern for every packed mask;
 * Appendix B, eqs. (42)-(45): masked attention, the score tangent, the
-  attention tangent with the mask held fixed, and its online form.
+  attention tangent with the mask held fixed, and its online form;
+* section 3.1.2 (teacher-forcing sCM, after eq. 17): the clean context
+  carries zero tangent, only the noisy tokens move.
 
 Parity pins (see ``tests/test_oracle_*.py``): hand-written golden masks,
 closed-form pair counts, finite differences, ``torch.func.jvp`` on dense
@@ -38,4 +40,8 @@ from .masked_attention import (  # noqa: F401
     masked_attention_jvp,
     masked_attention_jvp_rows,
     masked_attention_jvp_scalar,
+    zero_clean_tangents,
+    masked_attention_jvp_slice_ctz,
+    pair_counts_by_class,
+    useful_flops,
 )

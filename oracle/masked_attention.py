@@ -290,3 +290,60 @@ def masked_attention_jvp_scalar(q, k, v, tq, tk, tv, desc, scale=None):
             to[i][c] = math.fsum(p[j] * (ts[j] - rbar) * v[j][c] + p[j] * tv[j][c] for j in keys)
         lse[i] = m + math.log(l)
     return np.array(o), np.array(to), np.array(lse)
+
+
+# ----------------------------------------------------------------------------
+# Clean tangent zero (section 3.1.2, teacher-forcing sCM, the text after
+# eq. 17: the JVP runs through the same packed forward under the same
+# teacher-forcing mask; the clean context has zero tangent and only the noisy
+# tokens move)
+# ----------------------------------------------------------------------------
+
+def zero_clean_tangents(tq, tk, tv, desc):
+    """Float64 copies of the tangents with every clean token's row set to 0
+    (whatever the clean rows held before, NaN included)."""
+    desc = _as_desc(desc)
+    if not desc.tf_layout:
+        raise ValueError("the clean / noisy split needs tf_layout = 1")
+    out = []
+    for t in (tq, tk, tv):
+        t = np.array(t, dtype=np.float64, copy=True)
+        t[..., : desc.side_len, :] = 0.0
+        out.append(t)
+    return out
+
+
+def masked_attention_jvp_slice_ctz(q, k, v, tq, tk, tv, desc, scale=None, rows=None):
+    """One (b, h) slice with the clean tokens' tangents taken as zero."""
+    tq, tk, tv = zero_clean_tangents(tq, tk, tv, desc)
+    return masked_attention_jvp_slice(q, k, v, tq, tk, tv, desc, scale=scale, rows=rows)
+
+
+def pair_counts_by_class(desc):
+    """Allowed (query, key) pairs per (b, h), split as (clean rows, noisy rows
+    against clean keys, noisy rows against noisy keys), by summing the mask.
+    With tf_layout = 0 every pair is a clean-row pair."""
+    desc = _as_desc(desc)
+    cc = nc = nn = 0
+    for lo, hi in row_groups(desc):
+        keys = allowed_row(desc, lo)
+        clean_keys = int(keys[: desc.side_len].sum())
+        noisy_keys = int(keys[desc.side_len:].sum())
+        if desc.tf_layout and lo >= desc.side_len:
+            nc += clean_keys * (hi - lo)
+            nn += noisy_keys * (hi - lo)
+        else:
+            cc += (clean_keys + noisy_keys) * (hi - lo)
+    return cc, nc, nn
+
+
+def useful_flops(desc, head_dim, clean_tangent_zero=False):
+    """Useful FLOPs per (b, h): 2 per multiply-add of the products the result
+    needs over allowed pairs.  General: q.k, tq.k, q.tk, p.v, p.tv, (p ts).v,
+    i.e. 12 d per pair.  Clean tangent zero: clean rows need q.k and p.v
+    (4 d); noisy rows against clean keys need q.k, tq.k, p.v, (p ts).v (8 d);
+    noisy rows against noisy keys need all six (12 d)."""
+    cc, nc, nn = pair_counts_by_class(desc)
+    if clean_tangent_zero:
+        return head_dim * (4 * cc + 8 * nc + 12 * nn)
+    return head_dim * 12 * (cc + nc + nn)
