@@ -11,6 +11,8 @@ frames of 1560 tokens (N = 65520), bf16.
 Useful FLOPs = 12 d x (allowed query-key pairs) x B x H: 2 flops per
 multiply-add over q.k, tq.k, q.tk, p.v, p.tv and (p ts).v, masked pairs not
 counted (partial tiles included), exp and other vector work not counted.
+With --clean-tangent-zero: 4 d per clean-row pair, 8 d per noisy-row /
+clean-key pair, 12 d per noisy-row / noisy-key pair (attn_jvp_plan_flops).
 
 Prints one JSON line.  --gpus above 1 is refused: this build measures one GPU.
 """
@@ -48,6 +50,9 @@ def parse():
     ap.add_argument("--heads", type=int, default=0,
                     help="override the workload's head count, e.g. 3 = one GPU's share of the 12-head "
                          "workload under 4-way head (Ulysses) sharding")
+    ap.add_argument("--clean-tangent-zero", action="store_true",
+                    help="teacher-forcing plans whose clean tokens carry no tangent (useful FLOPs counted "
+                         "for that case: about half the general work)")
     ap.add_argument("--mode", choices=["attn", "copy"], default="attn",
                     help="copy: a plain 1 GiB device copy, the reference for HBM byte counters")
     return ap.parse_args()
@@ -130,7 +135,7 @@ def traffic_for(workload_name):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, heads):
+def cpu_baseline(w, heads, clean_tangent_zero=False):
     """The oracle, untuned, on (b, h) slices of the same workload."""
     import numpy as np
     import oracle
@@ -142,12 +147,13 @@ def cpu_baseline(w, heads):
         threads = 1
     flops = 0
     elapsed = 0.0
+    fn = oracle.masked_attention_jvp_slice_ctz if clean_tangent_zero else oracle.masked_attention_jvp_slice
     for h in range(heads):
         args = [si.slice_values(w, t, 0, h) for t in si.TENSORS]
         t0 = time.perf_counter()
-        oracle.masked_attention_jvp_slice(*args, w.desc)
+        fn(*args, w.desc)
         elapsed += time.perf_counter() - t0
-        flops += 12 * w.head_dim * oracle.pair_count(w.desc)
+        flops += oracle.useful_flops(w.desc, w.head_dim, clean_tangent_zero)
     return {
         "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"{heads} of {w.batch * w.heads} (b,h) slices of {w.name} (all rows), fp64 NumPy, "
@@ -175,6 +181,10 @@ def main():
     w = si.WORKLOADS[args.config]
     if args.heads > 0 and args.heads != w.heads:
         w = w.with_(heads=args.heads, name=f"{w.name}_h{args.heads}")
+    flags = 0
+    if args.clean_tangent_zero:
+        flags = aj.ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO
+        w = w.with_(name=f"{w.name}_ctz")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
@@ -183,7 +193,7 @@ def main():
         bits = si.full_tensor_bits(w, t)
         x[t] = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
         del bits
-    plan = aj.attn_jvp_create(w.desc, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16)
+    plan = aj.attn_jvp_create_ex(w.desc, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16, 0.0, flags)
     o = torch.empty_like(x["q"])
     to = torch.empty_like(x["q"])
     lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
@@ -216,7 +226,7 @@ def main():
     ms_per_step = total_ms / args.steps
 
     info = plan.info
-    useful = 12 * w.head_dim * info["allowed_pairs_per_head"] * w.batch * w.heads
+    useful = aj.attn_jvp_plan_flops(plan)
     value = useful / (ms_per_step * 1e-3) / 1e12
     achieved = useful / (avg_ms * 1e-3) / 1e12
     traffic = traffic_for(w.name)
@@ -238,6 +248,7 @@ def main():
             "workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
             "head_dim": w.head_dim, "tokens_per_frame": w.tokens_per_frame, "n_frames": w.n_frames,
             "frames_per_chunk": w.frames_per_chunk, "tf_layout": w.tf_layout,
+            "clean_tangent_zero": bool(flags),
         },
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "useful_tflop_per_step": round(useful / 1e12, 4),
@@ -260,7 +271,7 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads, bool(flags))
     print(json.dumps(out), flush=True)
 
 

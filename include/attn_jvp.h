@@ -75,8 +75,24 @@ enum {
   ATTN_JVP_E_UNSUPPORTED_DEVICE = 4, /* the current HIP device is not gfx950 */
   ATTN_JVP_E_HIP = 5,                /* a HIP runtime call failed (detail has the HIP error text) */
   ATTN_JVP_E_NOMEM = 6,              /* host allocation failed */
-  ATTN_JVP_E_OVERFLOW = 7            /* N >= 2^31, N*d >= 2^31 or the grid does not fit */
+  ATTN_JVP_E_OVERFLOW = 7            /* N >= 2^31, N*d >= 2^30 (bf16) or 2^31 (fp32), or the grid does not fit */
 };
+
+/* Plan flags (attn_jvp_create_ex).
+ *
+ * ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO (tf_layout = 1 only): the clean half of
+ * the sequence carries no tangent, as in teacher-forcing sCM, where the JVP
+ * runs through the same packed teacher-forcing mask and the clean context's
+ * tangent is zero while only the noisy tokens move (Causal-rCM, section
+ * 3.1.2, the text after eq. 17).  The result equals the general operation
+ * with tq, tk, tv set to 0 on tokens 0 .. N_h-1, and:
+ *   - the clean halves of tq, tk and tv are never read (any contents,
+ *     including NaN, are allowed there);
+ *   - t_o is exactly 0 on clean rows, which form only o and lse;
+ *   - noisy rows against clean keys form ts = scale * tq . k and no p tv
+ *     term; noisy rows against noisy keys do the general work.
+ * About half the general work on the 21-frame teacher-forcing sequences. */
+#define ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO 1u
 
 /* Build a plan for one mask, shape and element type.
  *   out           receives the plan (set to NULL on error)
@@ -89,6 +105,14 @@ enum {
  * Pure host work: touches no device. */
 int attn_jvp_create(attn_jvp_plan** out, const attn_jvp_mask_desc* mask, int32_t batch,
                     int32_t heads, int32_t head_dim, int32_t dtype, float softmax_scale);
+
+/* attn_jvp_create with plan flags (a bitwise OR of ATTN_JVP_FLAG_* values;
+ * 0 gives the same plan as attn_jvp_create).  Unknown bits, or
+ * ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO with tf_layout = 0, give
+ * ATTN_JVP_E_INVALID. */
+int attn_jvp_create_ex(attn_jvp_plan** out, const attn_jvp_mask_desc* mask, int32_t batch,
+                       int32_t heads, int32_t head_dim, int32_t dtype, float softmax_scale,
+                       uint32_t flags);
 
 /* Enqueue o, to (and lse when non-NULL) for the plan's shape on `hip_stream`
  * (a hipStream_t; NULL is the null stream), on the current HIP device.
@@ -120,6 +144,15 @@ const char* attn_jvp_last_error_detail(void);
 int attn_jvp_plan_info(const attn_jvp_plan* plan, int64_t* seq_len, int32_t* block_q,
                        int32_t* block_k, int32_t* n_query_blocks, int32_t* n_key_tiles,
                        int64_t* allowed_pairs_per_head, int64_t* visited_tiles_per_head);
+
+/* Useful floating-point operations of one attn_jvp_fwd call of the plan
+ * (all B * H heads): 2 per multiply-add of the products the operation needs
+ * over allowed (query, key) pairs, i.e. 12 d per pair for q.k, tq.k, q.tk,
+ * p.v, p.tv and (p ts).v.  With ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO: 4 d per
+ * clean-row pair (q.k, p.v), 8 d per noisy-row / clean-key pair (q.k, tq.k,
+ * p.v, (p ts).v) and 12 d per noisy-row / noisy-key pair.  Masked pairs
+ * inside partially allowed tiles and the exponentials are not counted. */
+int attn_jvp_plan_flops(const attn_jvp_plan* plan, int64_t* useful_flops);
 
 /* Per-row allowed key ranges, as the kernel uses them: host_out[4*i + 0..3]
  * = lo1, hi1, lo2, hi2 (half-open, empty when lo >= hi) for rows

@@ -5,9 +5,9 @@ Argument marshalling only.  Every step of the operation runs in the HIP
 library; PyTorch provides device memory and the stream.  The functions
 mirror the C ABI of ``include/attn_jvp.h`` one to one:
 
-    attn_jvp_create, attn_jvp_fwd, attn_jvp_destroy, attn_jvp_error_string,
-    attn_jvp_last_error_detail, attn_jvp_plan_info, attn_jvp_row_ranges,
-    attn_jvp_tile_map
+    attn_jvp_create, attn_jvp_create_ex, attn_jvp_fwd, attn_jvp_destroy,
+    attn_jvp_error_string, attn_jvp_last_error_detail, attn_jvp_plan_info,
+    attn_jvp_plan_flops, attn_jvp_row_ranges, attn_jvp_tile_map
 
 plus ``masked_attention_jvp(...)``, which allocates the outputs and calls
 ``attn_jvp_fwd`` on the current stream.  If the library is not built the
@@ -23,14 +23,15 @@ import threading
 import numpy as np
 
 __all__ = [
-    "ATTN_JVP_BF16", "ATTN_JVP_FP32", "AttnJvpError", "Plan", "library_path",
-    "attn_jvp_create", "attn_jvp_fwd", "attn_jvp_destroy", "attn_jvp_error_string",
-    "attn_jvp_last_error_detail", "attn_jvp_plan_info", "attn_jvp_row_ranges",
-    "attn_jvp_tile_map", "masked_attention_jvp",
+    "ATTN_JVP_BF16", "ATTN_JVP_FP32", "ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO", "AttnJvpError", "Plan",
+    "library_path", "attn_jvp_create", "attn_jvp_create_ex", "attn_jvp_fwd", "attn_jvp_destroy",
+    "attn_jvp_error_string", "attn_jvp_last_error_detail", "attn_jvp_plan_info", "attn_jvp_plan_flops",
+    "attn_jvp_row_ranges", "attn_jvp_tile_map", "masked_attention_jvp",
 ]
 
 ATTN_JVP_BF16 = 0
 ATTN_JVP_FP32 = 1
+ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # ATTN_JVP_LIBRARY selects another build of the same library (e.g. one made
@@ -66,6 +67,8 @@ def _load():
         vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         P = ctypes.POINTER
         lib.attn_jvp_create.argtypes = [P(vp), P(_MaskDesc), i32, i32, i32, i32, f32]
+        lib.attn_jvp_create_ex.argtypes = [P(vp), P(_MaskDesc), i32, i32, i32, i32, f32, ctypes.c_uint32]
+        lib.attn_jvp_plan_flops.argtypes = [vp, P(i64)]
         lib.attn_jvp_fwd.argtypes = [vp] * 9 + [vp, vp]
         lib.attn_jvp_destroy.argtypes = [vp]
         lib.attn_jvp_error_string.argtypes = [ctypes.c_int]
@@ -75,8 +78,8 @@ def _load():
         lib.attn_jvp_plan_info.argtypes = [vp, P(i64), P(i32), P(i32), P(i32), P(i32), P(i64), P(i64)]
         lib.attn_jvp_row_ranges.argtypes = [vp, P(i32), ctypes.c_size_t]
         lib.attn_jvp_tile_map.argtypes = [vp, P(ctypes.c_uint8), ctypes.c_size_t]
-        for name in ("attn_jvp_create", "attn_jvp_fwd", "attn_jvp_destroy", "attn_jvp_plan_info",
-                     "attn_jvp_row_ranges", "attn_jvp_tile_map"):
+        for name in ("attn_jvp_create", "attn_jvp_create_ex", "attn_jvp_fwd", "attn_jvp_destroy",
+                     "attn_jvp_plan_info", "attn_jvp_plan_flops", "attn_jvp_row_ranges", "attn_jvp_tile_map"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -98,10 +101,11 @@ def _check(code: int, what: str):
 class Plan:
     """Owns one attn_jvp_plan*; immutable after creation."""
 
-    def __init__(self, handle, desc, batch, heads, head_dim, dtype, scale):
+    def __init__(self, handle, desc, batch, heads, head_dim, dtype, scale, flags=0):
         self._h = handle
         self.desc = tuple(desc)
         self.batch, self.heads, self.head_dim, self.dtype, self.scale = batch, heads, head_dim, dtype, scale
+        self.flags = flags
         info = attn_jvp_plan_info(self)
         self.seq_len = info["seq_len"]
         self.info = info
@@ -132,6 +136,24 @@ def attn_jvp_create(desc, batch: int, heads: int, head_dim: int, dtype: int = AT
     _check(lib.attn_jvp_create(ctypes.byref(h), ctypes.byref(d), int(batch), int(heads), int(head_dim),
                                int(dtype), float(softmax_scale or 0.0)), "attn_jvp_create")
     return Plan(h, desc, batch, heads, head_dim, dtype, softmax_scale)
+
+
+def attn_jvp_create_ex(desc, batch: int, heads: int, head_dim: int, dtype: int = ATTN_JVP_BF16,
+                       softmax_scale: float = 0.0, flags: int = 0) -> Plan:
+    """attn_jvp_create with plan flags (ATTN_JVP_FLAG_*)."""
+    lib = _load()
+    h = ctypes.c_void_p()
+    d = _MaskDesc(*[int(x) for x in desc])
+    _check(lib.attn_jvp_create_ex(ctypes.byref(h), ctypes.byref(d), int(batch), int(heads), int(head_dim),
+                                  int(dtype), float(softmax_scale or 0.0), int(flags)), "attn_jvp_create_ex")
+    return Plan(h, desc, batch, heads, head_dim, dtype, softmax_scale, int(flags))
+
+
+def attn_jvp_plan_flops(plan: Plan) -> int:
+    """Useful FLOPs of one attn_jvp_fwd call of the plan (all heads)."""
+    v = ctypes.c_int64()
+    _check(_load().attn_jvp_plan_flops(plan.handle, ctypes.byref(v)), "attn_jvp_plan_flops")
+    return v.value
 
 
 def attn_jvp_destroy(plan: Plan) -> None:
@@ -211,24 +233,27 @@ _plan_cache = {}
 _plan_lock = threading.Lock()
 
 
-def _cached_plan(desc, shape, dtype, scale):
-    key = (tuple(int(x) for x in desc), tuple(shape), dtype, float(scale or 0.0))
+def _cached_plan(desc, shape, dtype, scale, flags=0):
+    key = (tuple(int(x) for x in desc), tuple(shape), dtype, float(scale or 0.0), int(flags))
     with _plan_lock:
         p = _plan_cache.get(key)
         if p is None:
             b, h, _, d = shape
-            p = attn_jvp_create(desc, b, h, d, dtype, scale or 0.0)
+            p = attn_jvp_create_ex(desc, b, h, d, dtype, scale or 0.0, flags)
             if tuple(p.shape) != tuple(shape):
                 raise AttnJvpError(f"mask {tuple(desc)} gives N={p.seq_len}, tensors have N={shape[2]}")
             _plan_cache[key] = p
         return p
 
 
-def masked_attention_jvp(q, k, v, tq, tk, tv, desc, scale=None, return_lse=False):
-    """(o, t_o[, lse]) for [B, H, N, d] bf16 or fp32 CUDA tensors."""
+def masked_attention_jvp(q, k, v, tq, tk, tv, desc, scale=None, return_lse=False, clean_tangent_zero=False):
+    """(o, t_o[, lse]) for [B, H, N, d] bf16 or fp32 CUDA tensors.  With
+    clean_tangent_zero (teacher-forcing masks only) the clean halves of tq,
+    tk, tv are taken as zero and never read."""
     import torch
     dtype = ATTN_JVP_BF16 if q.dtype == torch.bfloat16 else ATTN_JVP_FP32
-    plan = _cached_plan(desc, q.shape, dtype, scale)
+    flags = ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO if clean_tangent_zero else 0
+    plan = _cached_plan(desc, q.shape, dtype, scale, flags)
     o = torch.empty_like(q)
     t_o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None

@@ -23,10 +23,12 @@ struct attn_jvp_plan {
   MaskGeom g;
   int32_t batch, heads, head_dim, dtype;
   float scale;
+  uint32_t flags;
   int32_t block_q, block_k;
   int32_t n_qblocks, n_ktiles;
   int64_t allowed_pairs;
   int64_t visited_tiles;
+  int64_t useful_flops;
 };
 
 namespace {
@@ -60,6 +62,25 @@ int64_t count_pairs(const MaskGeom& g) {
       total += keys * g.chunk_len;
     }
   return total;
+}
+
+// Useful FLOPs per (b, h): 12 d per allowed pair; with clean-tangent-zero,
+// 4 d per clean-row pair, 8 d per noisy-row / clean-key pair, 12 d per
+// noisy-row / noisy-key pair.  Rows of one chunk share their key ranges.
+int64_t count_flops(const MaskGeom& g, int32_t head_dim, bool ctz) {
+  int64_t total = 0;
+  const int32_t nch = g.side_len / g.chunk_len;
+  for (int32_t side = 0; side < (g.tf ? 2 : 1); ++side)
+    for (int32_t c = 0; c < nch; ++c) {
+      const Ranges r = row_ranges(g, side * g.side_len + c * g.chunk_len);
+      const int64_t k1 = r.hi1 - r.lo1, k2 = r.hi2 > r.lo2 ? r.hi2 - r.lo2 : 0;  // clean, noisy keys
+      int64_t per_row;
+      if (!ctz) per_row = 12 * (k1 + k2);
+      else if (side == 0) per_row = 4 * k1;
+      else per_row = 8 * k1 + 12 * k2;
+      total += per_row * g.chunk_len;
+    }
+  return total * head_dim;
 }
 
 // Class of key tile [k0, k1) for rows [r0, r1): 0 none allowed, 1 all, 2 some.
@@ -110,6 +131,11 @@ extern "C" {
 
 int attn_jvp_create(attn_jvp_plan** out, const attn_jvp_mask_desc* mask, int32_t batch, int32_t heads,
                     int32_t head_dim, int32_t dtype, float softmax_scale) {
+  return attn_jvp_create_ex(out, mask, batch, heads, head_dim, dtype, softmax_scale, 0u);
+}
+
+int attn_jvp_create_ex(attn_jvp_plan** out, const attn_jvp_mask_desc* mask, int32_t batch, int32_t heads,
+                       int32_t head_dim, int32_t dtype, float softmax_scale, uint32_t flags) {
   if (out == nullptr || mask == nullptr) return fail(ATTN_JVP_E_NULL, "out and mask must be non-NULL");
   *out = nullptr;
   const attn_jvp_mask_desc& m = *mask;
@@ -125,12 +151,18 @@ int attn_jvp_create(attn_jvp_plan** out, const attn_jvp_mask_desc* mask, int32_t
   if (head_dim != 64 && head_dim != 128) return fail(ATTN_JVP_E_INVALID, "head_dim must be 64 or 128 (got %d)", head_dim);
   if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_FP32) return fail(ATTN_JVP_E_INVALID, "unknown dtype %d", dtype);
   if (!std::isfinite(softmax_scale)) return fail(ATTN_JVP_E_INVALID, "softmax_scale must be finite");
+  if (flags & ~ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO) return fail(ATTN_JVP_E_INVALID, "unknown flag bits 0x%x", flags);
+  if ((flags & ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO) && m.tf_layout != 1)
+    return fail(ATTN_JVP_E_INVALID, "ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO needs tf_layout = 1");
 
   const int64_t side = (int64_t)m.tokens_per_frame * m.n_frames;
   const int64_t n = side * (m.tf_layout ? 2 : 1);
-  if (n >= (int64_t(1) << 31) || n * head_dim >= (int64_t(1) << 31))
-    return fail(ATTN_JVP_E_OVERFLOW, "sequence of %lld tokens x d=%d exceeds 2^31 elements per head", (long long)n,
-                head_dim);
+  // The bf16 kernel forms per-head byte offsets in 32 bits (buffer offsets);
+  // the fp32 kernel indexes elements with 64-bit offsets.
+  const int64_t per_head = n * head_dim * (dtype == ATTN_JVP_BF16 ? 2 : 1);
+  if (n >= (int64_t(1) << 31) || per_head >= (int64_t(1) << 31))
+    return fail(ATTN_JVP_E_OVERFLOW, "sequence of %lld tokens x d=%d exceeds the per-head limit (2^31 %s)",
+                (long long)n, head_dim, dtype == ATTN_JVP_BF16 ? "bytes" : "elements");
 
   attn_jvp_plan* p = new (std::nothrow) attn_jvp_plan;
   if (p == nullptr) return fail(ATTN_JVP_E_NOMEM, "plan allocation failed");
@@ -139,6 +171,7 @@ int attn_jvp_create(attn_jvp_plan** out, const attn_jvp_mask_desc* mask, int32_t
   p->heads = heads;
   p->head_dim = head_dim;
   p->dtype = dtype;
+  p->flags = flags;
   p->scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   block_sizes(dtype, head_dim, &p->block_q, &p->block_k);
   p->n_qblocks = n_query_blocks(p->g, p->block_q);
@@ -156,6 +189,7 @@ int attn_jvp_create(attn_jvp_plan** out, const attn_jvp_mask_desc* mask, int32_t
     visited += span_count(block_tiles(block_ranges(p->g, r0, r1), p->block_k));
   }
   p->visited_tiles = visited;
+  p->useful_flops = count_flops(p->g, head_dim, (flags & ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO) != 0) * batch * heads;
   *out = p;
   return ok();
 }
@@ -213,6 +247,7 @@ int attn_jvp_fwd(const attn_jvp_plan* p, const void* q, const void* k, const voi
   fp.n_qblocks = p->n_qblocks;
   fp.scale = p->scale;
   fp.score_log2 = p->scale * 1.4426950408889634f;
+  fp.ctz = (p->flags & ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO) ? 1 : 0;
   const int grid = p->batch * p->heads * p->n_qblocks;
   hipError_t e = launch_fwd(p->dtype, p->head_dim, grid, fp, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(ATTN_JVP_E_HIP, "kernel launch: %s", hipGetErrorString(e));
@@ -245,6 +280,12 @@ int attn_jvp_plan_info(const attn_jvp_plan* p, int64_t* seq_len, int32_t* block_
   if (n_ktiles) *n_ktiles = p->n_ktiles;
   if (allowed_pairs) *allowed_pairs = p->allowed_pairs;
   if (visited_tiles) *visited_tiles = p->visited_tiles;
+  return ok();
+}
+
+int attn_jvp_plan_flops(const attn_jvp_plan* p, int64_t* useful_flops) {
+  if (p == nullptr || useful_flops == nullptr) return fail(ATTN_JVP_E_NULL, "plan and useful_flops must be non-NULL");
+  *useful_flops = p->useful_flops;
   return ok();
 }
 

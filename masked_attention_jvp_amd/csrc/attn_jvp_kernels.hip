@@ -173,7 +173,14 @@ __device__ __forceinline__ void wait_lgkmcnt() {
   asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, int NW>
+// Tile modes of the bf16 kernel.  kFull: the general operation.  With the
+// clean-tangent-zero option (teacher forcing, clean tokens carry no tangent):
+// kCleanKeys for noisy rows against clean keys (tk = tv = 0 there, so
+// ts' = tq.k and there is no p~ tv term), kPrimal for clean rows (tq = 0 and
+// every key they see is clean, so t_o = 0 and only o and lse are formed).
+enum : int { kFull = 0, kCleanKeys = 1, kPrimal = 2 };
+
+template <int D, int NW, bool CTZ>
 __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   constexpr int BC = kBf16BlockK;            // keys per tile (= one MFMA subtile)
@@ -182,10 +189,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   constexpr int BR = NW * 32;
   constexpr int KS = D / 16;                 // k-steps of the score products
   constexpr int DC = D / 32;                 // 32-wide column blocks of the outputs
+  constexpr int NG = 2 * DC;                 // P.V groups per tile (two 16-key halves x DC)
   constexpr int CPR = D / 8;                 // 16-byte groups per row
   constexpr int TILE = BC * D;               // elements per tensor per stage
   constexpr int LOADS = TILE * 2 / 1024 / NW;  // 1 KB DMA loads per wave per tensor
-  constexpr int LPT = 4 * LOADS;             // DMA loads per wave per tile
   static_assert(LOADS * NW * 1024 == TILE * 2, "DMA split");
 
   // The four ring stages are separate objects so that the compiler can tell
@@ -209,12 +216,28 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   qblock_rows(g, BR, qb, &r0, &r1);
   const TileSpans sp = block_tiles(block_ranges(g, r0, r1), BC);
   const int ntiles = span_count(sp);
+  const bool primal_only = CTZ && !is_noisy(g, r0);  // a clean-side block
+  // Clean-tangent-zero, noisy block: the leading tiles whose keys all lie on
+  // the clean side (below N_h) need no key tangents.  A tile that reaches N_h
+  // (for short sides the two key intervals can even share one) runs in the
+  // general mode, whose tk, tv loads give zeros on the clean side.
+  int n_clean_tiles = g.side_len / BC - sp.a0;
+  n_clean_tiles = n_clean_tiles < 0 ? 0 : (n_clean_tiles > sp.a1 - sp.a0 ? sp.a1 - sp.a0 : n_clean_tiles);
 
   const size_t base = (size_t)bh * (size_t)N * D;
   const int slice_bytes = N * D * 2;
   const __amdgpu_buffer_rsrc_t rsrc[4] = {
       make_rsrc((const uint16_t*)p.k + base, slice_bytes), make_rsrc((const uint16_t*)p.tk + base, slice_bytes),
       make_rsrc((const uint16_t*)p.v + base, slice_bytes), make_rsrc((const uint16_t*)p.tv + base, slice_bytes)};
+  // Clean-tangent-zero: tk and tv are read only through resources over the
+  // noisy half, with per-lane offsets relative to its start; a clean key's
+  // offset is negative, i.e. a huge unsigned offset, which the range check
+  // turns into zeros.  So no clean-side tangent is ever read, and the one
+  // tile that straddles the two halves gets zeros for its clean keys.
+  const size_t half = (size_t)g.side_len * D;
+  const int half_bytes = g.side_len * D * 2;
+  const __amdgpu_buffer_rsrc_t rsrc_tn[2] = {make_rsrc((const uint16_t*)p.tk + base + half, half_bytes),
+                                             make_rsrc((const uint16_t*)p.tv + base + half, half_bytes)};
 
   const int row = r0 + wave * 32 + n;
   const bool row_ok = row < r1;
@@ -227,9 +250,12 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     const __amdgpu_buffer_rsrc_t rtq = make_rsrc((const uint16_t*)p.tq + base, slice_bytes);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int off = (row * D + 16 * s + 8 * h) * 2;
-      qf[s] = load16(rq, off);
-      tqf[s] = load16(rtq, off);
+      qf[s] = load16(rq, (row * D + 16 * s + 8 * h) * 2);
+      tqf[s] = u32x4{0, 0, 0, 0};
+    }
+    if (!primal_only) {  // clean rows of a clean-tangent-zero plan: no tq read
+#pragma unroll
+      for (int s = 0; s < KS; ++s) tqf[s] = load16(rtq, (row * D + 16 * s + 8 * h) * 2);
     }
   }
 
@@ -251,18 +277,29 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     const int rw = blk * (64 / CPR) + lane / CPR;
     dma_voff[i] = (rw * D + (((lane % CPR) ^ row_swz<D>(rw)) << 3)) * 2;
   }
-  // The q-th of the LPT DMA instructions of tile t.  Every step issues all
-  // of them, branch-free: past the last tile the last tile is loaded again
-  // into the stage that just became free, which nothing reads, so the ring
-  // always has the same number of loads in flight.
-  auto issue_part = [&](uint16_t* dst, int t, int q) {
-    const int soff = span_tile(sp, t < ntiles ? t : ntiles - 1) * BC * D * 2;
-    const int i = q >> 2, tt = q & 3;
-    load16_lds(rsrc[tt], dst + tt * TILE + (wave * LOADS + i) * 512, dma_voff[i], soff);
+  // DMA instructions per wave and tile: all four tensors in kFull, K and V
+  // otherwise.
+  auto lpt = [](auto mode) { return decltype(mode)::value == kFull ? 4 * LOADS : 2 * LOADS; };
+  // The q-th DMA instruction of tile t.  Every step issues all of them,
+  // branch-free: past the run's last tile that tile is loaded again into the
+  // stage that just became free, which nothing reads, so the ring always has
+  // the same number of loads in flight.
+  auto issue_part = [&](auto mode, uint16_t* dst, int t, int q, int t_end) {
+    const int tile = span_tile(sp, t < t_end ? t : t_end - 1);
+    const int soff = tile * BC * D * 2;
+    if constexpr (decltype(mode)::value == kFull) {
+      const int i = q >> 2, tt = q & 3;
+      uint16_t* lds = dst + tt * TILE + (wave * LOADS + i) * 512;
+      if (CTZ && (tt & 1)) load16_lds(rsrc_tn[tt >> 1], lds, dma_voff[i] + (tile * BC - g.side_len) * D * 2, 0);
+      else load16_lds(rsrc[tt], lds, dma_voff[i], soff);
+    } else {
+      const int i = q >> 1, tt = 2 * (q & 1);
+      load16_lds(rsrc[tt], dst + tt * TILE + (wave * LOADS + i) * 512, dma_voff[i], soff);
+    }
   };
-  auto issue = [&](uint16_t* dst, int t) {
+  auto issue = [&](auto mode, uint16_t* dst, int t, int t_end) {
 #pragma unroll
-    for (int q = 0; q < LPT; ++q) issue_part(dst, t, q);
+    for (int q = 0; q < lpt(mode); ++q) issue_part(mode, dst, t, q, t_end);
   };
 
   // accO = sum p~ v, accV = sum p~ tv, accS = sum (p~ ts') v with the
@@ -294,6 +331,9 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
+  using MFull = std::integral_constant<int, kFull>;
+  using MCleanKeys = std::integral_constant<int, kCleanKeys>;
+  using MPrimal = std::integral_constant<int, kPrimal>;
 
   // Per-lane key window of this row: key k is allowed iff
   // (unsigned)(k - lo1) < len1 or (unsigned)(k - lo2) < len2.
@@ -339,23 +379,28 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   auto next_ref = [&](float ref, float tmx) {
     return tmx > ref + kLazyRescaleLog2 ? fmaxf(ref, tmx) : ref;
   };
-  // p~ = exp2(s * sl2 - ref), in place, with nref = -ref (0 for ref = -inf:
-  // no allowed key yet, every score of the row is -inf).
+  // p~ = exp2(s * sl2 - ref), with nref = -ref (0 for ref = -inf: no allowed
+  // key yet, every score of the row is -inf).
   auto neg_ref = [](float ref) { return ref == -INFINITY ? 0.f : -ref; };
   auto exp_elem = [&](float x, float nref) { return __builtin_amdgcn_exp2f(fmaf(x, sl2, nref)); };
 
   // K and tK fragments of the tile whose scores are formed next; the first
   // two k-steps are read at the end of the previous step (loop-carried).
   u32x4 kf[KS], tkf[KS];
-  auto kread = [&](const uint16_t* src, int s) {
+  auto kread = [&](auto mode, const uint16_t* src, int s) {
     const int off = n * D + (((2 * s + h) ^ row_swz<D>(n)) << 3);
     kf[s] = *(const u32x4*)(src + off);
-    tkf[s] = *(const u32x4*)(src + TILE + off);
+    if constexpr (decltype(mode)::value == kFull) tkf[s] = *(const u32x4*)(src + TILE + off);
   };
 
-  // Step j.  On entry P holds tile j's p~ (already exponentiated against the
-  // reference mn) and TS its unscaled score tangents; Sn, TSn receive tile
-  // j+1's scores.
+  // Scores of two consecutive tiles in vector registers: the current tile's
+  // p~ (read by phase 1) and the next one's scores (written by the MFMAs,
+  // exponentiated in phase 2); the roles alternate from step to step.
+  f32x16 SA, TSA, SB, TSB;
+
+  // Step j of a run over tiles [., t_end).  On entry P holds tile j's p~
+  // (already exponentiated against the reference mn) and TS its unscaled
+  // score tangents; Sn, TSn receive tile j+1's scores.
   // * top: if some row's reference moved (mn != m), rescale l, r and the
   //   accumulators to mn (rare after the first tile);
   // * phase 1 (score MFMAs of tile j+1): p~ ts', the bf16 packs and the sums
@@ -365,23 +410,27 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   // The exponentials thus run under the P.V MFMAs and the rest of the
   // softmax under the score MFMAs, which balances the vector work of the
   // two phases.
-  // Ring use: tile t sits in stage t % 4; step j reads K of tile j+1 and V of
-  // tile j, and issues the DMA of tile j+3 into the stage of tile j-1, freed
-  // by the previous step's barrier.  The barrier sits in phase 2, right after
-  // the last read of tile j's stage; before it each wave waits for its share
-  // of tile j+2, which the next step's first K reads (issued right after the
-  // barrier) need.  The last P.V MFMAs and the next step's top run while the
-  // waves meet.
+  // Ring use: tile t sits in stage (t - run start) % 4; step j reads K of
+  // tile j+1 and V of tile j, and issues the DMA of tile j+3 into the stage
+  // of tile j-1, freed by the previous step's barrier.  The barrier sits in
+  // phase 2, right after the last read of tile j's stage; before it each wave
+  // waits for its share of tile j+2, which the next step's first K reads
+  // (issued right after the barrier) need.  The last P.V MFMAs and the next
+  // step's top run while the waves meet.
   // Scheduling unit: one MFMA followed by a share of vector / LDS / DMA work,
   // fenced by sched_barrier on both sides of the MFMA, so that each MFMA's
   // execution covers its own share and no vector work piles up behind
   // back-to-back MFMAs (with one wave per SIMD nothing else fills the matrix
   // unit).
-  auto step = [&](auto st, int j, f32x16& P, f32x16& TS, f32x16& Sn, f32x16& TSn) {
+  auto step = [&](auto mode, auto st, int j, int t_end, f32x16& P, f32x16& TS, f32x16& Sn, f32x16& TSn) {
+    constexpr int MODE = decltype(mode)::value;
+    constexpr bool HAS_TS = MODE != kPrimal;  // score tangents (tq != 0)
+    constexpr bool HAS_TKV = MODE == kFull;   // key tangents (tk, tv != 0)
     constexpr int ST = decltype(st)::value;
     using NX = std::integral_constant<int, (ST + 1) % STAGES>;
     using N2 = std::integral_constant<int, (ST + 2) % STAGES>;
     using AH = std::integral_constant<int, (ST + 3) % STAGES>;
+    constexpr int LPTM = HAS_TKV ? 4 * LOADS : 2 * LOADS;
 
     // Rare after the first tile.
     if (__builtin_expect(__any(mn != m), 0)) {
@@ -395,8 +444,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           accO[c][i] = acc_write(acc_read(accO[c][i]) * alpha);
-          accV[c][i] = acc_write(acc_read(accV[c][i]) * alpha);
-          accS[c][i] = acc_write(acc_read(accS[c][i]) * alpha);
+          if constexpr (HAS_TKV) accV[c][i] = acc_write(acc_read(accV[c][i]) * alpha);
+          if constexpr (HAS_TS) accS[c][i] = acc_write(acc_read(accS[c][i]) * alpha);
         }
       }
     }
@@ -406,7 +455,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     const uint16_t* cur = stage(st);
     float wv[16];
     u32x4 PK[2], W[2];
-    u32x4 vfr[2 * DC], tvfr[2 * DC];
+    u32x4 vfr[NG], tvfr[NG];
     auto vread = [&](int gidx) {
       const int c2 = gidx / DC, c = gidx % DC;
       const int col = 32 * c + tr_col;
@@ -414,74 +463,95 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       const int o1 = k1 * D + (((col >> 3) ^ row_swz<D>(k1)) << 3) + (col & 7);
       const int o2 = k2 * D + (((col >> 3) ^ row_swz<D>(k2)) << 3) + (col & 7);
       const u32x2 va = read_tr16(cur + 2 * TILE + o1), vb = read_tr16(cur + 2 * TILE + o2);
-      const u32x2 ta = read_tr16(cur + 3 * TILE + o1), tb = read_tr16(cur + 3 * TILE + o2);
       vfr[gidx] = u32x4{va[0], va[1], vb[0], vb[1]};
-      tvfr[gidx] = u32x4{ta[0], ta[1], tb[0], tb[1]};
+      if constexpr (HAS_TKV) {
+        const u32x2 ta = read_tr16(cur + 3 * TILE + o1), tb = read_tr16(cur + 3 * TILE + o2);
+        tvfr[gidx] = u32x4{ta[0], ta[1], tb[0], tb[1]};
+      }
+    };
+    // pieces of tile j's softmax back half, per element pair jj, jj+1
+    auto w_mul = [&](int jj) {
+      wv[jj] = P[jj] * TS[jj];
+      wv[jj + 1] = P[jj + 1] * TS[jj + 1];
+      pin(wv[jj]);
+      pin(wv[jj + 1]);
+    };
+    auto pack_p = [&](int jj) {
+      PK[jj >> 3][(jj & 7) >> 1] = pack_bf16(P[jj], P[jj + 1]);
+      l += P[jj] + P[jj + 1];
+      pin(PK[jj >> 3][(jj & 7) >> 1]);
+      pin(l);
+    };
+    auto pack_w = [&](int jj) {
+      W[jj >> 3][(jj & 7) >> 1] = pack_bf16(wv[jj], wv[jj + 1]);
+      r += wv[jj] + wv[jj + 1];
+      pin(W[jj >> 3][(jj & 7) >> 1]);
+      pin(r);
+    };
+    auto dma = [&](int s) {  // this k-step's share of tile j+3's DMA
+#pragma unroll
+      for (int q = s * LPTM / KS; q < (s + 1) * LPTM / KS; ++q) issue_part(mode, stage(AH{}), j + 3, q, t_end);
     };
 
-    // phase 1: scores of tile j+1 under the rest of tile j's softmax; per
-    // k-step three slots: p~ ts' | pack p~, l | pack p~ ts', r.  K reads two
-    // k-steps ahead.
+    // phase 1: scores of tile j+1 under the back half of tile j's softmax.
+    // Per k-step, kFull: TS += k.tq | S += k.q | TS += tk.q with
+    // p~ ts' | K reads two k-steps ahead, DMA, pack p~, l | pack p~ ts', r;
+    // kCleanKeys: TS += k.tq | S += k.q; kPrimal: S += k.q.
     constexpr int PAIRS_PER_STEP = 8 / KS;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if (s == 0) mfma_v_first(TSn, kf[s], tqf[s]);
-      else mfma_v_acc(TSn, kf[s], tqf[s]);
-      __builtin_amdgcn_sched_barrier(0);
+      const int jj0 = 2 * s * PAIRS_PER_STEP;
+      if constexpr (HAS_TS) {
+        if (s == 0) mfma_v_first(TSn, kf[s], tqf[s]);
+        else mfma_v_acc(TSn, kf[s], tqf[s]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < PAIRS_PER_STEP; ++u) {
-        const int jj = 2 * (s * PAIRS_PER_STEP + u);
-        wv[jj] = P[jj] * TS[jj];
-        wv[jj + 1] = P[jj + 1] * TS[jj + 1];
-        pin(wv[jj]);
-        pin(wv[jj + 1]);
+        for (int u = 0; u < PAIRS_PER_STEP; ++u) w_mul(jj0 + 2 * u);
+        if constexpr (!HAS_TKV) {
+          if (s + 2 < KS) kread(mode, nx, s + 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
       if (s == 0) mfma_v_first(Sn, kf[s], qf[s]);
       else mfma_v_acc(Sn, kf[s], qf[s]);
       __builtin_amdgcn_sched_barrier(0);
-      // (in this slot, so that the first MFMA of the k-step never waits for it)
-      if (s + 2 < KS) kread(nx, s + 2);
-      // DMA of tile j+3 into the stage freed by the previous barrier
-#pragma unroll
-      for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q) issue_part(stage(AH{}), j + 3, q);
-#pragma unroll
-      for (int u = 0; u < PAIRS_PER_STEP; ++u) {
-        const int jj = 2 * (s * PAIRS_PER_STEP + u);
-        PK[jj >> 3][(jj & 7) >> 1] = pack_bf16(P[jj], P[jj + 1]);
-        l += P[jj] + P[jj + 1];
-        pin(PK[jj >> 3][(jj & 7) >> 1]);
-        pin(l);
+      // (not in the first slot, so that the first MFMA of the k-step never
+      // waits for it)
+      if constexpr (HAS_TKV || !HAS_TS) {
+        if (s + 2 < KS) kread(mode, nx, s + 2);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_v_acc(TSn, tkf[s], qf[s]);
-      __builtin_amdgcn_sched_barrier(0);
+      dma(s);
+#pragma unroll
+      for (int u = 0; u < PAIRS_PER_STEP; ++u) pack_p(jj0 + 2 * u);
+      if constexpr (HAS_TKV) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_v_acc(TSn, tkf[s], qf[s]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (s == KS - 2) vread(0);
       if (s == KS - 1) vread(1);
+      if constexpr (HAS_TS) {
 #pragma unroll
-      for (int u = 0; u < PAIRS_PER_STEP; ++u) {
-        const int jj = 2 * (s * PAIRS_PER_STEP + u);
-        W[jj >> 3][(jj & 7) >> 1] = pack_bf16(wv[jj], wv[jj + 1]);
-        r += wv[jj] + wv[jj + 1];
-        pin(W[jj >> 3][(jj & 7) >> 1]);
-        pin(r);
+        for (int u = 0; u < PAIRS_PER_STEP; ++u) pack_w(jj0 + 2 * u);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // phase 2: P.V of tile j under tile j+1's softmax front half.  Group 0
-    // carries no vector work on Sn (two MFMAs must pass after its last score
-    // product); then the mask of a partial tile, the row max in the second
-    // and third slots of MAX_GROUPS groups, the new reference, and the
+    // phase 2: P.V of tile j under tile j+1's softmax front half.  Per group
+    // NS2 MFMAs (kFull: p~.tv, p~.v, (p~ ts').v; kCleanKeys: the last two;
+    // kPrimal: p~.v).  Group 0 carries no vector work on Sn (two MFMAs must
+    // pass after its last score product); then the mask of a partial tile,
+    // the row max over MAX_GROUPS groups, the new reference, and the
     // exponentials spread over all slots of the remaining groups.
-    constexpr int NG = 2 * DC;
+    constexpr int NS2 = HAS_TKV ? 3 : HAS_TS ? 2 : 1;
     constexpr int MAX_GROUPS = NG >= 8 ? 2 : 1;
-    constexpr int MAX_SLOTS = 2 * MAX_GROUPS;
+    constexpr int RM_PER_GROUP = NS2 >= 2 ? NS2 - 1 : 1;  // row-max slots per group
+    constexpr int MAX_SLOTS = RM_PER_GROUP * MAX_GROUPS;
     constexpr int MAX_PER_SLOT = 16 / MAX_SLOTS;
-    constexpr int EXP_SLOTS = 3 * (NG - 1 - MAX_GROUPS);
+    constexpr int EXP_SLOTS = NS2 * (NG - 1 - MAX_GROUPS);
     static_assert(MAX_PER_SLOT * MAX_SLOTS == 16 && EXP_SLOTS > 0, "phase-2 split");
     float tmax = -INFINITY, ref = mn, nref = 0.f;
-    auto row_max = [&](int slot) {  // slot 0 .. MAX_SLOTS-1
+    auto row_max = [&](int slot) {
 #pragma unroll
       for (int e = 0; e < MAX_PER_SLOT; ++e) tmax = fmaxf(tmax, Sn[slot * MAX_PER_SLOT + e]);
       pin(tmax);
@@ -491,7 +561,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
         pin(nref);
       }
     };
-    auto exps = [&](int slot) {  // slot 0 .. EXP_SLOTS-1: elements k with k * EXP_SLOTS / 16 == slot
+    auto exps = [&](int slot) {  // elements k with k * EXP_SLOTS / 16 == slot
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         if (k * EXP_SLOTS / 16 == slot) {
@@ -500,67 +570,82 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
         }
       }
     };
-    // the vector work of slot `sl` (0..2) of group gidx
-    auto front_half = [&](int gidx, int sl) {
-      if (gidx >= 1 && gidx <= MAX_GROUPS && sl > 0) row_max(2 * (gidx - 1) + sl - 1);
-      if (gidx > MAX_GROUPS) exps(3 * (gidx - 1 - MAX_GROUPS) + sl);
+    // the vector / LDS work of slot sl (0 .. NS2-1) of group gidx
+    constexpr int UB = (NG - 2) * NS2;  // linear slot of the barrier
+    auto slot_work = [&](int gidx, int sl) {
+      const int u = gidx * NS2 + sl;
+      // (after group 1's first MFMA: two MFMAs past the last score product in every mode)
+      if (gidx == 1 && sl == 0 && !tile_whole(j + 1)) mask_tile(j + 1, Sn, TSn);  // rare
+      if (sl == 0 && gidx + 2 < NG) vread(gidx + 2);
+      if (u == UB) {
+        // every read of tile j's stage is done; tile j+2 has landed here
+        wait_lgkmcnt<0>();
+        wait_vmcnt<LPTM>();
+        barrier_nofence();
+      }
+      if (gidx >= 1 && gidx <= MAX_GROUPS) {
+        if (NS2 == 1) row_max(gidx - 1);
+        else if (sl >= 1) row_max((gidx - 1) * RM_PER_GROUP + sl - 1);
+      }
+      if (gidx > MAX_GROUPS) exps((gidx - 1 - MAX_GROUPS) * NS2 + sl);
+      // first K reads of tile j+2, behind the barrier
+      if (u == (UB + 1 < NG * NS2 ? UB + 1 : NG * NS2 - 1)) kread(mode, stage(N2{}), 0);
+      if (u == (UB + 2 < NG * NS2 ? UB + 2 : NG * NS2 - 1)) kread(mode, stage(N2{}), 1);
     };
 #pragma unroll
     for (int gidx = 0; gidx < NG; ++gidx) {
       const int c2 = gidx / DC, c = gidx % DC;
-      if (gidx == 1 && !tile_whole(j + 1)) mask_tile(j + 1, Sn, TSn);  // rare
-      accV[c] = mfma_bf16(tvfr[gidx], PK[c2], accV[c]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (gidx + 2 < NG) vread(gidx + 2);
-      front_half(gidx, 0);
-      if (gidx == NG - 2) {
-        // every read of tile j's stage is done; tile j+2 has landed here
-        wait_lgkmcnt<0>();
-        wait_vmcnt<LPT>();
-        barrier_nofence();
+      int sl = 0;
+      if constexpr (HAS_TKV) {
+        accV[c] = mfma_bf16(tvfr[gidx], PK[c2], accV[c]);
+        __builtin_amdgcn_sched_barrier(0);
+        slot_work(gidx, sl++);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
       accO[c] = mfma_bf16(vfr[gidx], PK[c2], accO[c]);
       __builtin_amdgcn_sched_barrier(0);
-      front_half(gidx, 1);
-      if (gidx == NG - 2) kread(stage(N2{}), 0);
+      slot_work(gidx, sl++);
       __builtin_amdgcn_sched_barrier(0);
-      accS[c] = mfma_bf16(vfr[gidx], W[c2], accS[c]);
-      __builtin_amdgcn_sched_barrier(0);
-      front_half(gidx, 2);
-      if (gidx == NG - 2) kread(stage(N2{}), 1);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (HAS_TS) {
+        accS[c] = mfma_bf16(vfr[gidx], W[c2], accS[c]);
+        __builtin_amdgcn_sched_barrier(0);
+        slot_work(gidx, sl++);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     mn = ref;
   };
 
-  // Scores of two consecutive tiles in vector registers: the current tile's
-  // p~ (read by phase 1) and the next one's scores (written by the MFMAs,
-  // exponentiated in phase 2); the roles alternate from step to step.
-  f32x16 SA, TSA, SB, TSB;
-  if (ntiles > 0) {
-    issue(ring0, 0);
-    issue(ring1, 1);
-    issue(ring2, 2);
-    wait_vmcnt<LPT>();  // tiles 0 and 1
+  // First tile of a run: DMA of its first three tiles, its scores, mask, row
+  // max, reference and exponentials, and the first K reads of the next tile.
+  auto first_tile = [&](auto mode, int t_begin, int t_end) {
+    constexpr int MODE = decltype(mode)::value;
+    issue(mode, ring0, t_begin, t_end);
+    issue(mode, ring1, t_begin + 1, t_end);
+    issue(mode, ring2, t_begin + 2, t_end);
+    if constexpr (MODE == kFull) wait_vmcnt<4 * LOADS>();  // first two tiles
+    else wait_vmcnt<2 * LOADS>();
     barrier_nofence();
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kread(ring0, s);
-      if (s == 0) {
-        mfma_v_first(SA, kf[s], qf[s]);
-        mfma_v_first(TSA, kf[s], tqf[s]);
-      } else {
-        mfma_v_acc(SA, kf[s], qf[s]);
-        mfma_v_acc(TSA, kf[s], tqf[s]);
+      kread(mode, ring0, s);
+      if (s == 0) mfma_v_first(SA, kf[s], qf[s]);
+      else mfma_v_acc(SA, kf[s], qf[s]);
+      if constexpr (MODE != kPrimal) {
+        if (s == 0) mfma_v_first(TSA, kf[s], tqf[s]);
+        else mfma_v_acc(TSA, kf[s], tqf[s]);
       }
-      mfma_v_acc(TSA, tkf[s], qf[s]);
+      if constexpr (MODE == kFull) mfma_v_acc(TSA, tkf[s], qf[s]);
     }
     // fenced: the compiler would otherwise move the reads of SA above the wait
     __builtin_amdgcn_sched_barrier(0);
     acc_hazard_wait();
     __builtin_amdgcn_sched_barrier(0);
-    if (!tile_whole(0)) mask_tile(0, SA, TSA);
+    if constexpr (MODE == kPrimal) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) TSA[i] = 0.f;
+    }
+    if (!tile_whole(t_begin)) mask_tile(t_begin, SA, TSA);
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, SA[i]);
@@ -568,20 +653,44 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     const float nref = neg_ref(mn);
 #pragma unroll
     for (int i = 0; i < 16; ++i) SA[i] = exp_elem(SA[i], nref);
-    kread(ring1, 0);
-    kread(ring1, 1);
-  }
-  for (int j = 0; j < ntiles; j += 4) {
-    step(I0{}, j, SA, TSA, SB, TSB);
-    if (j + 1 >= ntiles) break;
-    step(I1{}, j + 1, SB, TSB, SA, TSA);
-    if (j + 2 >= ntiles) break;
-    step(I2{}, j + 2, SA, TSA, SB, TSB);
-    if (j + 3 >= ntiles) break;
-    step(I3{}, j + 3, SB, TSB, SA, TSA);
+    kread(mode, ring1, 0);
+    kread(mode, ring1, 1);
+  };
+
+  // One pipelined pass over tiles [t_begin, t_end) in one mode; the ring is
+  // drained at the end, so runs in different modes can follow each other.
+  auto run = [&](auto mode, int t_begin, int t_end) {
+    if (t_begin >= t_end) return;
+    first_tile(mode, t_begin, t_end);
+    for (int j = t_begin; j < t_end; j += 4) {
+      step(mode, I0{}, j, t_end, SA, TSA, SB, TSB);
+      if (j + 1 >= t_end) break;
+      step(mode, I1{}, j + 1, t_end, SB, TSB, SA, TSA);
+      if (j + 2 >= t_end) break;
+      step(mode, I2{}, j + 2, t_end, SA, TSA, SB, TSB);
+      if (j + 3 >= t_end) break;
+      step(mode, I3{}, j + 3, t_end, SB, TSB, SA, TSA);
+    }
+    // the last step exponentiated scores of no tile: drop that reference
+    mn = m;
+    // DMAs of tiles past the end, and the last K reads, may be in flight
+    wait_vmcnt<0>();
+    wait_lgkmcnt<0>();
+    barrier_nofence();
+  };
+
+  if constexpr (CTZ) {
+    if (primal_only) {
+      run(MPrimal{}, 0, ntiles);
+    } else {
+      run(MCleanKeys{}, 0, n_clean_tiles);  // clean keys of earlier chunks
+      run(MFull{}, n_clean_tiles, ntiles);  // the block's own noisy chunks
+    }
+  } else {
+    run(MFull{}, 0, ntiles);
   }
 
-  // ---- epilogue: o = acc_o / l ; to = acc_t / l - (r / l) o ------------------
+  // ---- epilogue: o = acc_o / l ; to = (acc_tv + scale acc_tsv) / l - (r / l) o
   acc_hazard_wait();
   const float lt = pair_sum(l);
   const float rt = pair_sum(r) * scale;
@@ -600,7 +709,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g4 + e;
           o4[e] = acc_read(accO[c][i]) * inv;
-          t4[e] = fmaf(acc_read(accS[c][i]), scale, acc_read(accV[c][i])) * inv - rb * o4[e];
+          t4[e] = primal_only ? 0.f
+                              : fmaf(acc_read(accS[c][i]), scale, acc_read(accV[c][i])) * inv - rb * o4[e];
         }
         u32x2 ov = {pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])};
         u32x2 tv = {pack_bf16(t4[0], t4[1]), pack_bf16(t4[2], t4[3])};
@@ -608,11 +718,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
         *(u32x2*)(tOg + d0) = tv;
       }
     }
+    // one explicit fma: every instantiation rounds lse the same way
     if (h == 0 && p.lse != nullptr)
-      p.lse[(size_t)bh * N + row] = lt > 0.f ? m * kLn2 + logf(lt) : -INFINITY;
+      p.lse[(size_t)bh * N + row] = lt > 0.f ? fmaf(m, kLn2, logf(lt)) : -INFINITY;
   }
-  // the last steps' DMAs (of tiles past the end) may still be in flight
-  wait_vmcnt<0>();
 }
 
 // fp32 kernel: 32 query rows per workgroup, 8 lanes per row, each lane owning
@@ -640,14 +749,22 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(FwdParams p) {
   const float* __restrict__ V = (const float*)p.v + base + slice * E;
   const float* __restrict__ tK = (const float*)p.tk + base + slice * E;
   const float* __restrict__ tV = (const float*)p.tv + base + slice * E;
+  // clean-tangent-zero: clean rows and clean keys carry no tangent and their
+  // tangent rows are never read
+  const bool ctz = p.ctz != 0;
+  const bool row_tangent = !(ctz && !is_noisy(g, r0));  // the block's rows are on one side
   float q[E], tq[E], ao[E], at[E];
   const int qrow = row_ok ? row : r0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     q[e] = ((const float*)p.q)[base + (size_t)qrow * D + slice * E + e];
-    tq[e] = ((const float*)p.tq)[base + (size_t)qrow * D + slice * E + e];
+    tq[e] = 0.f;
     ao[e] = 0.f;
     at[e] = 0.f;
+  }
+  if (row_tangent) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) tq[e] = ((const float*)p.tq)[base + (size_t)qrow * D + slice * E + e];
   }
   float m = -INFINITY, l = 0.f, r = 0.f;
   for (int it = 0; it < ntiles; ++it) {
@@ -657,11 +774,20 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(FwdParams p) {
       if (!in_ranges(rr, j)) continue;  // uniform across the row's 8 lanes
       const float* kj = K + (size_t)j * D;
       const float* tkj = tK + (size_t)j * D;
+      const bool key_tangent = !(ctz && j < g.side_len);
       float s = 0.f, ts = 0.f;
+      if (key_tangent) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        s = fmaf(q[e], kj[e], s);
-        ts = fmaf(tq[e], kj[e], fmaf(q[e], tkj[e], ts));
+        for (int e = 0; e < E; ++e) {
+          s = fmaf(q[e], kj[e], s);
+          ts = fmaf(tq[e], kj[e], fmaf(q[e], tkj[e], ts));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          s = fmaf(q[e], kj[e], s);
+          ts = fmaf(tq[e], kj[e], ts);
+        }
       }
 #pragma unroll
       for (int o = 1; o < 8; o <<= 1) {
@@ -677,10 +803,18 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(FwdParams p) {
       r = r * alpha + pj * ts;
       const float* vj = V + (size_t)j * D;
       const float* tvj = tV + (size_t)j * D;
+      if (key_tangent) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        ao[e] = ao[e] * alpha + pj * vj[e];
-        at[e] = at[e] * alpha + pj * tvj[e] + (pj * ts) * vj[e];
+        for (int e = 0; e < E; ++e) {
+          ao[e] = ao[e] * alpha + pj * vj[e];
+          at[e] = at[e] * alpha + pj * tvj[e] + (pj * ts) * vj[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          ao[e] = ao[e] * alpha + pj * vj[e];
+          at[e] = at[e] * alpha + (pj * ts) * vj[e];
+        }
       }
       m = mn;
     }
@@ -694,7 +828,7 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(FwdParams p) {
   for (int e = 0; e < E; ++e) {
     const float o = ao[e] * inv;
     O[e] = o;
-    tO[e] = at[e] * inv - rb * o;
+    tO[e] = row_tangent ? at[e] * inv - rb * o : 0.f;
   }
   if (slice == 0 && p.lse != nullptr) p.lse[(size_t)bh * N + row] = l > 0.f ? m + logf(l) : -INFINITY;
 }
@@ -712,11 +846,15 @@ void block_sizes(int dtype, int head_dim, int* block_q, int* block_k) {
 }
 
 hipError_t launch_fwd(int dtype, int head_dim, int grid, const FwdParams& p, hipStream_t stream) {
+  const dim3 block(kBf16Waves * 64);
   if (dtype == kBf16) {
-    if (head_dim == 128)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves>), dim3(grid), dim3(kBf16Waves * 64), 0, stream, p);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves>), dim3(grid), dim3(kBf16Waves * 64), 0, stream, p);
+    if (head_dim == 128) {
+      if (p.ctz) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, true>), dim3(grid), block, 0, stream, p);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, false>), dim3(grid), block, 0, stream, p);
+    } else {
+      if (p.ctz) hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, true>), dim3(grid), block, 0, stream, p);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, false>), dim3(grid), block, 0, stream, p);
+    }
   } else {
     if (head_dim == 128)
       hipLaunchKernelGGL((fwd_fp32_kernel<128>), dim3(grid), dim3(256), 0, stream, p);

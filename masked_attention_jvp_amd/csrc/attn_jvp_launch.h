@@ -27,6 +27,7 @@ struct FwdParams {
   int32_t n_qblocks;  // query blocks per (b, h); the grid is (b, h) x blocks
   float score_log2;   // scale * log2(e)
   float scale;
+  int32_t ctz;        // clean-tangent-zero plan (teacher forcing only)
 };
 
 // Query rows per block and keys per tile of the kernel chosen for dtype/head_dim.

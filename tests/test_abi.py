@@ -34,7 +34,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert len(names) == 8
+    assert len(names) == 10
     lib = ctypes.CDLL(aj.library_path)
     for name in names:
         assert hasattr(lib, name), name
@@ -54,12 +54,47 @@ def test_error_strings():
     ((4, 3, 1, 1), 1, 1, 96, 0, 1),        # unsupported head_dim
     ((4, 3, 1, 1), 1, 1, 64, 7, 1),        # unknown dtype
     ((1 << 20, 1 << 11, 1, 1), 1, 1, 64, 0, 7),  # sequence too long
+    ((1 << 12, 1 << 11, 1, 0), 1, 1, 128, 0, 7),  # bf16: N d 2 = 2^31 bytes per head
+    ((1 << 13, 1 << 11, 1, 0), 1, 1, 128, 1, 7),  # fp32: N d = 2^31 elements per head
 ])
 def test_create_rejects_bad_arguments(desc, b, h, d, dt, code):
     with pytest.raises(aj.AttnJvpError) as e:
         aj.attn_jvp_create(desc, b, h, d, dt)
     assert e.value.code == code
     assert aj.attn_jvp_last_error_detail()
+
+
+def test_per_head_size_limits_by_dtype():
+    # bf16 byte offsets are 32-bit: N d 2 < 2^31; the fp32 kernel indexes elements with 64 bits: N d < 2^31
+    n = 1 << 23  # d = 128: bf16 needs exactly 2^31 bytes per head, fp32 2^30 elements
+    aj.attn_jvp_create((n, 1, 1, 0), 1, 1, 128, aj.ATTN_JVP_FP32)
+    with pytest.raises(aj.AttnJvpError) as e:
+        aj.attn_jvp_create((n, 1, 1, 0), 1, 1, 128, aj.ATTN_JVP_BF16)
+    assert e.value.code == 7
+    aj.attn_jvp_create((n - 1, 1, 1, 0), 1, 1, 128, aj.ATTN_JVP_BF16)
+    aj.attn_jvp_create((n, 1, 1, 0), 1, 1, 64, aj.ATTN_JVP_BF16)
+
+
+@pytest.mark.parametrize("desc, flags", [((4, 3, 1, 0), 1), ((4, 3, 1, 1), 2), ((4, 3, 1, 1), 0x80000000)])
+def test_create_ex_rejects_bad_flags(desc, flags):
+    with pytest.raises(aj.AttnJvpError) as e:
+        aj.attn_jvp_create_ex(desc, 1, 1, 64, aj.ATTN_JVP_BF16, 0.0, flags)
+    assert e.value.code == 1
+    assert aj.attn_jvp_last_error_detail()
+
+
+@pytest.mark.parametrize("desc", [(16, 3, 1, 1), (2, 6, 3, 1), (160, 9, 3, 1), (7, 5, 1, 0), (1560, 21, 1, 1),
+                                  (1560, 21, 3, 1), (1560, 21, 1, 0)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_plan_flops_match_oracle_counts(desc, d):
+    b, h = 2, 3
+    p = aj.attn_jvp_create(desc, b, h, d, aj.ATTN_JVP_BF16)
+    assert aj.attn_jvp_plan_flops(p) == b * h * oracle.useful_flops(MaskDesc(*desc), d)
+    p0 = aj.attn_jvp_create_ex(desc, b, h, d, aj.ATTN_JVP_BF16, 0.0, 0)
+    assert aj.attn_jvp_plan_flops(p0) == aj.attn_jvp_plan_flops(p)
+    if desc[3] == 1:
+        pz = aj.attn_jvp_create_ex(desc, b, h, d, aj.ATTN_JVP_FP32, 0.0, aj.ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO)
+        assert aj.attn_jvp_plan_flops(pz) == b * h * oracle.useful_flops(MaskDesc(*desc), d, True)
 
 
 def test_create_rejects_non_finite_scale():
