@@ -159,6 +159,15 @@ int attn_jvp_plan_flops(const attn_jvp_plan* plan, int64_t* useful_flops);
  * i = 0..N-1.  n is the capacity of host_out in int32 elements (>= 4N). */
 int attn_jvp_row_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
+/* Launch order: workgroup t (0 <= t < n_query_blocks) of every (b, h)
+ * handles query block host_out[t] (index order of attn_jvp_tile_map).
+ * Heaviest (latest) blocks first.  With tf_layout = 1 the sides alternate
+ * block by block; in clean-tangent-zero plans, whose clean blocks carry less
+ * work, clean and noisy blocks of the same chunks come in groups of 8 and 8,
+ * so that the round-robin hand-out of workgroups to the 8 XCDs gives each XCD
+ * both sides.  n is the capacity of host_out in int32 elements. */
+int attn_jvp_launch_order(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
+
 /* Tile map, row-major [n_query_blocks][n_key_tiles], query blocks in index
  * order (clean side first): 0 = not streamed, 1 = streamed, every pair
  * allowed (no masking), 2 = streamed, some pairs masked.  Two further codes

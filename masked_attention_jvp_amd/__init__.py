@@ -7,7 +7,7 @@ mirror the C ABI of ``include/attn_jvp.h`` one to one:
 
     attn_jvp_create, attn_jvp_create_ex, attn_jvp_fwd, attn_jvp_destroy,
     attn_jvp_error_string, attn_jvp_last_error_detail, attn_jvp_plan_info,
-    attn_jvp_plan_flops, attn_jvp_row_ranges, attn_jvp_tile_map
+    attn_jvp_plan_flops, attn_jvp_launch_order, attn_jvp_row_ranges, attn_jvp_tile_map
 
 plus ``masked_attention_jvp(...)``, which allocates the outputs and calls
 ``attn_jvp_fwd`` on the current stream.  If the library is not built the
@@ -26,7 +26,7 @@ __all__ = [
     "ATTN_JVP_BF16", "ATTN_JVP_FP32", "ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO", "AttnJvpError", "Plan",
     "library_path", "attn_jvp_create", "attn_jvp_create_ex", "attn_jvp_fwd", "attn_jvp_destroy",
     "attn_jvp_error_string", "attn_jvp_last_error_detail", "attn_jvp_plan_info", "attn_jvp_plan_flops",
-    "attn_jvp_row_ranges", "attn_jvp_tile_map", "masked_attention_jvp",
+    "attn_jvp_launch_order", "attn_jvp_row_ranges", "attn_jvp_tile_map", "masked_attention_jvp",
 ]
 
 ATTN_JVP_BF16 = 0
@@ -77,9 +77,11 @@ def _load():
         lib.attn_jvp_last_error_detail.restype = ctypes.c_char_p
         lib.attn_jvp_plan_info.argtypes = [vp, P(i64), P(i32), P(i32), P(i32), P(i32), P(i64), P(i64)]
         lib.attn_jvp_row_ranges.argtypes = [vp, P(i32), ctypes.c_size_t]
+        lib.attn_jvp_launch_order.argtypes = [vp, P(i32), ctypes.c_size_t]
         lib.attn_jvp_tile_map.argtypes = [vp, P(ctypes.c_uint8), ctypes.c_size_t]
         for name in ("attn_jvp_create", "attn_jvp_create_ex", "attn_jvp_fwd", "attn_jvp_destroy",
-                     "attn_jvp_plan_info", "attn_jvp_plan_flops", "attn_jvp_row_ranges", "attn_jvp_tile_map"):
+                     "attn_jvp_plan_info", "attn_jvp_plan_flops", "attn_jvp_launch_order", "attn_jvp_row_ranges",
+                     "attn_jvp_tile_map"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -176,6 +178,14 @@ def attn_jvp_row_ranges(plan: Plan) -> np.ndarray:
     out = np.empty((n, 4), dtype=np.int32)
     _check(_load().attn_jvp_row_ranges(plan.handle, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), out.size),
            "attn_jvp_row_ranges")
+    return out
+
+
+def attn_jvp_launch_order(plan: Plan) -> np.ndarray:
+    """Query block handled by workgroup t of each (b, h)."""
+    out = np.empty(plan.info["n_query_blocks"], dtype=np.int32)
+    _check(_load().attn_jvp_launch_order(plan.handle, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), out.size),
+           "attn_jvp_launch_order")
     return out
 
 

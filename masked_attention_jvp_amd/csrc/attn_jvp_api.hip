@@ -289,6 +289,15 @@ int attn_jvp_plan_flops(const attn_jvp_plan* p, int64_t* useful_flops) {
   return ok();
 }
 
+int attn_jvp_launch_order(const attn_jvp_plan* p, int32_t* out, size_t n) {
+  if (p == nullptr || out == nullptr) return fail(ATTN_JVP_E_NULL, "plan and host_out must be non-NULL");
+  if (n < (size_t)p->n_qblocks)
+    return fail(ATTN_JVP_E_INVALID, "host_out holds %zu int32, need %d", n, p->n_qblocks);
+  const bool balanced = (p->flags & ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO) != 0;
+  for (int32_t t = 0; t < p->n_qblocks; ++t) out[t] = heavy_first_qblock(p->g, p->block_q, t, balanced);
+  return ok();
+}
+
 int attn_jvp_row_ranges(const attn_jvp_plan* p, int32_t* out, size_t n) {
   if (p == nullptr || out == nullptr) return fail(ATTN_JVP_E_NULL, "plan and host_out must be non-NULL");
   if (n < (size_t)p->g.seq_len * 4)

@@ -92,9 +92,36 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 // 16 bytes per lane from global (byte offset voff + soff, soff wave-uniform)
-// straight into LDS at lds + 16 * lane.
+// straight into LDS at lds + 16 * lane, through the compiler builtin (kFull).
 __device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds, 16, voff, soff, 0, 0);
+}
+
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+// Buffer descriptor as four dwords (base, stride 0, byte size, the same
+// config word as make_rsrc): for the DMA below.  Loads at or past `bytes`
+// (vector + scalar offset, checked on the device) return zeros.
+__device__ __forceinline__ i32x4_t make_desc(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)base;
+  return i32x4_t{(int32_t)(uint32_t)a, (int32_t)(uint32_t)((a >> 32) & 0xffff), bytes, 0x00020000};
+}
+// The same DMA written out (the K and V streams of the modes with fewer
+// MFMAs per tile): there the compiler, tracking its own LDS DMA against later
+// LDS reads, waits for every DMA in flight (vmcnt(0)) before some V reads
+// although they read another ring stage, which exposes the whole DMA latency
+// once per tile.  The kernel orders the ring itself (explicit vmcnt waits and
+// barriers before a stage is read or refilled), so the DMA is hidden from the
+// compiler; the memory clobber keeps LDS accesses from moving across.
+// Vector-memory loads complete in order, so the compiler's own waits for its
+// loads stay correct (they only cover more).  One wait state between the M0
+// write and the DMA.
+__device__ __forceinline__ void load16_lds_asm(i32x4_t r, uint16_t* lds, int voff, int soff) {
+  // soff and the LDS address are wave-uniform; readfirstlane puts them in
+  // scalar registers where the compiler computed them in vector ones
+  const int m0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(LDS_AS void*)lds);
+  const int so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(r), "s"(so), "s"(m0) : "memory", "m0");
 }
 __device__ __forceinline__ u32x2 read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)p));
@@ -211,7 +238,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   const MaskGeom g = p.g;
   const int N = g.seq_len;
   const int bh = blockIdx.x / p.n_qblocks;
-  const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks);
+  const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks, CTZ);
   int r0, r1;
   qblock_rows(g, BR, qb, &r0, &r1);
   const TileSpans sp = block_tiles(block_ranges(g, r0, r1), BC);
@@ -229,6 +256,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   const __amdgpu_buffer_rsrc_t rsrc[4] = {
       make_rsrc((const uint16_t*)p.k + base, slice_bytes), make_rsrc((const uint16_t*)p.tk + base, slice_bytes),
       make_rsrc((const uint16_t*)p.v + base, slice_bytes), make_rsrc((const uint16_t*)p.tv + base, slice_bytes)};
+  const i32x4_t desc_k = make_desc((const uint16_t*)p.k + base, slice_bytes);
+  const i32x4_t desc_v = make_desc((const uint16_t*)p.v + base, slice_bytes);
   // Clean-tangent-zero: tk and tv are read only through resources over the
   // noisy half, with per-lane offsets relative to its start; a clean key's
   // offset is negative, i.e. a huge unsigned offset, which the range check
@@ -294,7 +323,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       else load16_lds(rsrc[tt], lds, dma_voff[i], soff);
     } else {
       const int i = q >> 1, tt = 2 * (q & 1);
-      load16_lds(rsrc[tt], dst + tt * TILE + (wave * LOADS + i) * 512, dma_voff[i], soff);
+      load16_lds_asm(tt ? desc_v : desc_k, dst + tt * TILE + (wave * LOADS + i) * 512, dma_voff[i], soff);
     }
   };
   auto issue = [&](auto mode, uint16_t* dst, int t, int t_end) {
@@ -735,7 +764,7 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(FwdParams p) {
   const int N = g.seq_len;
   const int slice = threadIdx.x & 7, lr = threadIdx.x >> 3;
   const int bh = blockIdx.x / p.n_qblocks;
-  const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks);
+  const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks, p.ctz != 0);
   int r0, r1;
   qblock_rows(g, BR, qb, &r0, &r1);
   const TileSpans sp = block_tiles(block_ranges(g, r0, r1), BC);

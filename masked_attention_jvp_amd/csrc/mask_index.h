@@ -91,13 +91,29 @@ AJ_HD void qblock_rows(const MaskGeom& g, int32_t block_q, int32_t qb, int32_t* 
   *r1 = base + end;
 }
 
-// Heavy-first launch order within one (b, h): a block's work grows with its
-// last chunk, and clean block k and noisy block k carry about the same work,
-// so walk k downwards, alternating sides.
-AJ_HD int32_t heavy_first_qblock(const MaskGeom& g, int32_t block_q, int32_t t) {
+// Heavy-first launch order within one (b, h): query block handled by
+// workgroup t.  A block's work grows with its last chunk, so k walks down.
+// Workgroups are handed to the 8 XCDs round robin.
+// * default: the sides alternate (clean block k, noisy block k, ...): clean
+//   and noisy block k carry the same work, and each XCD streams one side's
+//   key ranges;
+// * balanced (for plans whose sides carry different work, clean-tangent-
+//   zero): slots come in groups of 2 P, the P clean blocks k .. k-P+1 then
+//   the P noisy blocks of the same k, so every XCD gets one block of each
+//   side per group; the last nbs mod P blocks of each side alternate.
+AJ_HD int32_t heavy_first_qblock(const MaskGeom& g, int32_t block_q, int32_t t, bool balanced = false) {
   const int32_t nbs = blocks_per_side(g, block_q);
   if (!g.tf) return nbs - 1 - t;
-  return (t & 1) * nbs + (nbs - 1 - (t >> 1));
+  if (!balanced) return (t & 1) * nbs + (nbs - 1 - (t >> 1));
+  constexpr int32_t P = 8;
+  const int32_t full = nbs / P;
+  if (t < 2 * P * full) {
+    const int32_t grp = t / (2 * P), r = t - grp * 2 * P;
+    const int32_t side = r / P;
+    return side * nbs + (nbs - 1 - (grp * P + r - side * P));
+  }
+  const int32_t u = t - 2 * P * full, rem = nbs - P * full;
+  return (u & 1) * nbs + (rem - 1 - (u >> 1));
 }
 
 // Union of the key sets of rows [r0, r1) (one side, consecutive chunks).

@@ -34,7 +34,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     lib = ctypes.CDLL(aj.library_path)
     for name in names:
         assert hasattr(lib, name), name
@@ -95,6 +95,37 @@ def test_plan_flops_match_oracle_counts(desc, d):
     if desc[3] == 1:
         pz = aj.attn_jvp_create_ex(desc, b, h, d, aj.ATTN_JVP_FP32, 0.0, aj.ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO)
         assert aj.attn_jvp_plan_flops(pz) == b * h * oracle.useful_flops(MaskDesc(*desc), d, True)
+
+
+@pytest.mark.parametrize("desc", [(16, 3, 1, 1), (50, 5, 1, 1), (1, 5, 1, 1), (160, 9, 3, 1), (37, 7, 1, 0),
+                                  (1560, 21, 1, 1), (1560, 21, 3, 1), (1560, 21, 1, 0), (100, 40, 1, 1)])
+@pytest.mark.parametrize("ctz", [0, 1])
+def test_launch_order_is_a_heavy_first_permutation(desc, ctz):
+    if ctz and desc[3] == 0:
+        pytest.skip("clean-tangent-zero needs teacher forcing")
+    p = aj.attn_jvp_create_ex(desc, 1, 1, 128, aj.ATTN_JVP_BF16, 0.0, ctz)
+    order = aj.attn_jvp_launch_order(p)
+    nq = p.info["n_query_blocks"]
+    assert sorted(order.tolist()) == list(range(nq))  # every block exactly once
+    # a block's work grows with its last chunk: latest blocks of each side first
+    if desc[3] == 0:
+        assert np.all(np.diff(order) < 0)
+    else:
+        nbs = nq // 2
+        side = (order >= nbs).astype(int)
+        for sd in (0, 1):
+            assert np.all(np.diff(order[side == sd]) < 0)
+        if not ctz:  # sides alternate block by block
+            assert np.all(side == np.arange(nq) % 2)
+        else:
+            # each aligned group of 16 slots holds 8 clean and 8 noisy blocks:
+            # with round-robin hand-out every XCD gets both sides
+            full = (nbs // 8) * 16
+            for g0 in range(0, full, 16):
+                assert side[g0:g0 + 8].sum() == 0 and side[g0 + 8:g0 + 16].sum() == 8
+            for x in range(8):
+                sl = side[:full][x::8]
+                assert int(sl.sum()) * 2 == len(sl)
 
 
 def test_create_rejects_non_finite_scale():
