@@ -36,7 +36,7 @@ PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4 SIMD x 1024 bf16 flop/clk x 2.4 GHz (den
 METRIC = "useful TFLOP/s of masked attn fwd+JVP and % of bf16 MFMA peak, 1 GPU"
 KERNEL_SRCS = [os.path.join(ROOT, "masked_attention_jvp_amd", "csrc", f)
                for f in ("attn_jvp_kernels.hip", "attn_jvp_launch.h", "mask_index.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_d128_tf_framewise_65520.json")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -126,7 +126,7 @@ def traffic_for(workload_name):
     """HBM bytes per launch from committed rocprofv3 counters, if they were
     taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(PROFILES, f"traffic_{workload_name}.json")) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -266,7 +266,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": f"fwd_bf16_kernel<{w.head_dim},{info['block_q'] // 32}>",
+            "kernel": f"fwd_bf16_kernel<{w.head_dim},{info['block_q'] // 32},{'true' if flags else 'false'}>",
             "avg_launch_ms": round(avg_ms, 4),
         },
     }
