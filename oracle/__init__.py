@@ -18,7 +18,9 @@ Sources (Causal-rCM, arXiv 2606.25473):
 * Appendix B, eqs. (42)-(45): masked attention, the score tangent, the
   attention tangent with the mask held fixed, and its online form;
 * section 3.1.2 (teacher-forcing sCM, after eq. 17): the clean context
-  carries zero tangent, only the noisy tokens move.
+  carries zero tangent, only the noisy tokens move;
+* section 3.2.1 (FlashAttention-2 based kernel with custom masks): the
+  backward of the same masked attention, for training the student.
 
 Parity pins (see ``tests/test_oracle_*.py``): hand-written golden masks,
 closed-form pair counts, finite differences, ``torch.func.jvp`` on dense
@@ -44,4 +46,7 @@ from .masked_attention import (  # noqa: F401
     masked_attention_jvp_slice_ctz,
     pair_counts_by_class,
     useful_flops,
+    masked_attention_bwd_slice,
+    masked_attention_bwd,
+    backward_useful_flops,
 )

@@ -347,3 +347,63 @@ def useful_flops(desc, head_dim, clean_tangent_zero=False):
     if clean_tangent_zero:
         return head_dim * (4 * cc + 8 * nc + 12 * nn)
     return head_dim * 12 * (cc + nc + nn)
+
+
+# ----------------------------------------------------------------------------
+# Backward of the masked attention (section 3.2.1: the FlashAttention-2 based
+# kernel with custom masks; training the student needs the gradients of the
+# same masked attention).  The plain gradient of o = softmax(s) v with
+# s = scale q k^T under the mask, for an output cotangent do:
+#   dv_j = sum_i p_ij do_i
+#   dp_ij = do_i . v_j,   delta_i = sum_j p_ij dp_ij (= do_i . o_i)
+#   ds_ij = p_ij (dp_ij - delta_i)            (0 where masked)
+#   dq_i = scale sum_j ds_ij k_j,   dk_j = scale sum_i ds_ij q_i
+# ----------------------------------------------------------------------------
+
+def masked_attention_bwd_slice(q, k, v, do, desc, scale=None):
+    """One (b, h) slice: float64 (dq [N, d], dk [N, d], dv [N, dv], delta [N])."""
+    desc = _as_desc(desc)
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    n, d = q.shape
+    if n != desc.seq_len:
+        raise ValueError(f"sequence length {n} does not match the mask ({desc.seq_len})")
+    sc = _scale(d, scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    delta = np.zeros(n)
+    for lo, hi in row_groups(desc):
+        keys = np.nonzero(allowed_row(desc, lo))[0]
+        if keys.size == 0:
+            continue
+        kk, vv = k[keys], v[keys]
+        s = sc * (q[lo:hi] @ kk.T)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        dp = do[lo:hi] @ vv.T
+        dl = (p * dp).sum(axis=1)
+        ds = p * (dp - dl[:, None])
+        dq[lo:hi] = sc * (ds @ kk)
+        dk[keys] += sc * (ds.T @ q[lo:hi])
+        dv[keys] += p.T @ do[lo:hi]
+        delta[lo:hi] = dl
+    return dq, dk, dv, delta
+
+
+def masked_attention_bwd(q, k, v, do, desc, scale=None):
+    """Full [B, H, N, d] tensors -> float64 (dq, dk, dv, delta [B, H, N])."""
+    q = np.asarray(q)
+    b_, h_, n, d = q.shape
+    out = [np.empty((b_, h_, n, d)) for _ in range(3)] + [np.empty((b_, h_, n))]
+    for b in range(b_):
+        for h in range(h_):
+            r = masked_attention_bwd_slice(q[b, h], k[b, h], v[b, h], do[b, h], desc, scale)
+            for o_, x in zip(out, r):
+                o_[b, h] = x
+    return tuple(out)
+
+
+def backward_useful_flops(desc, head_dim):
+    """2 per multiply-add of the five products over allowed pairs (s, dp, dv,
+    dk, dq): 10 d per pair, per (b, h)."""
+    return 10 * head_dim * pair_count(desc)
