@@ -121,6 +121,45 @@ int attn_jvp_fwd(const attn_jvp_plan* plan, const void* q, const void* k, const 
                  const void* tq, const void* tk, const void* tv, void* o, void* t_o,
                  float* lse, void* hip_stream);
 
+/* Backward of the masked attention (without tangents) on the same plan:
+ * the gradients of a loss L with respect to q, k and v given dO = dL/do
+ * (Causal-rCM, section 3.2.1: the student's FlashAttention-2 based masked
+ * attention trains through it; the mask is held fixed as in the forward).
+ * With P the masked softmax of the scaled scores and lse from attn_jvp_fwd:
+ *
+ *   P_ij    = exp(scale q_i . k_j - lse_i)  on allowed pairs, 0 otherwise
+ *   delta_i = sum_d dO_id o_id
+ *   dS_ij   = P_ij (dO_i . v_j - delta_i)
+ *   dq_i    = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dO_i
+ *
+ *   q, k, v, o, d_o   [B, H, N, d] inputs in the plan's element type; o and
+ *                     lse are the outputs of attn_jvp_fwd for q, k, v (any
+ *                     tangents: they do not enter o and lse)
+ *   lse               [B, H, N] fp32 (natural log), 4-byte aligned
+ *   dq, dk, dv        [B, H, N, d] outputs in the plan's element type
+ *                     (bf16: fp32 accumulation, rounded to nearest even)
+ *   workspace         attn_jvp_bwd_workspace_size() bytes of device memory,
+ *                     4-byte aligned, owned by the caller; its contents on
+ *                     entry are ignored.  On completion it holds, per (b, h),
+ *                     N floats delta_i followed by N floats -lse_i log2(e),
+ *                     i.e. workspace[(b H + h) 2N + i] = delta_i.
+ * Enqueues two kernels on `hip_stream` (the dq kernel, which also fills the
+ * workspace, then the dk/dv kernel); no atomics, so results do not depend on
+ * scheduling.  No output may overlap an input or another output.  The plan's
+ * flags do not matter here.  Same checks and error codes as attn_jvp_fwd. */
+int attn_jvp_bwd(const attn_jvp_plan* plan, const void* q, const void* k, const void* v,
+                 const void* o, const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                 float* workspace, void* hip_stream);
+
+/* Workspace bytes attn_jvp_bwd needs for the plan: 8 B H N. */
+int attn_jvp_bwd_workspace_size(const attn_jvp_plan* plan, size_t* bytes);
+
+/* Useful floating-point operations of one attn_jvp_bwd call (all B * H
+ * heads): 10 d per allowed (query, key) pair, i.e. 2 per multiply-add of the
+ * five products q.k, dO.v, dS k, dS q and P dO (the dq kernel recomputes the
+ * scores and dO.v, which is not counted). */
+int attn_jvp_plan_bwd_flops(const attn_jvp_plan* plan, int64_t* useful_flops);
+
 /* Free a plan.  NULL is accepted. */
 int attn_jvp_destroy(attn_jvp_plan* plan);
 
@@ -158,6 +197,12 @@ int attn_jvp_plan_flops(const attn_jvp_plan* plan, int64_t* useful_flops);
  * = lo1, hi1, lo2, hi2 (half-open, empty when lo >= hi) for rows
  * i = 0..N-1.  n is the capacity of host_out in int32 elements (>= 4N). */
 int attn_jvp_row_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
+
+/* Per-key allowed query ranges (the columns of the mask), as the backward's
+ * dk/dv kernel uses them: host_out[4*j + 0..3] = lo1, hi1, lo2, hi2 for keys
+ * j = 0..N-1: row i attends to key j iff lo1 <= i < hi1 or lo2 <= i < hi2.
+ * n is the capacity of host_out in int32 elements (>= 4N). */
+int attn_jvp_key_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
 /* Launch order: workgroup t (0 <= t < n_query_blocks) of every (b, h)
  * handles query block host_out[t] (index order of attn_jvp_tile_map).

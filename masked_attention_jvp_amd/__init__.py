@@ -5,12 +5,15 @@ Argument marshalling only.  Every step of the operation runs in the HIP
 library; PyTorch provides device memory and the stream.  The functions
 mirror the C ABI of ``include/attn_jvp.h`` one to one:
 
-    attn_jvp_create, attn_jvp_create_ex, attn_jvp_fwd, attn_jvp_destroy,
-    attn_jvp_error_string, attn_jvp_last_error_detail, attn_jvp_plan_info,
-    attn_jvp_plan_flops, attn_jvp_launch_order, attn_jvp_row_ranges, attn_jvp_tile_map
+    attn_jvp_create, attn_jvp_create_ex, attn_jvp_fwd, attn_jvp_bwd,
+    attn_jvp_bwd_workspace_size, attn_jvp_destroy, attn_jvp_error_string,
+    attn_jvp_last_error_detail, attn_jvp_plan_info, attn_jvp_plan_flops,
+    attn_jvp_plan_bwd_flops, attn_jvp_launch_order, attn_jvp_row_ranges,
+    attn_jvp_key_ranges, attn_jvp_tile_map
 
-plus ``masked_attention_jvp(...)``, which allocates the outputs and calls
-``attn_jvp_fwd`` on the current stream.  If the library is not built the
+plus ``masked_attention_jvp(...)`` and ``masked_attention_bwd(...)``, which
+allocate the outputs (and the backward's workspace) and call ``attn_jvp_fwd``
+/ ``attn_jvp_bwd`` on the current stream.  If the library is not built the
 import of this module still works, but every call raises ``AttnJvpError``;
 there is no fallback implementation.
 """
@@ -27,6 +30,8 @@ __all__ = [
     "library_path", "attn_jvp_create", "attn_jvp_create_ex", "attn_jvp_fwd", "attn_jvp_destroy",
     "attn_jvp_error_string", "attn_jvp_last_error_detail", "attn_jvp_plan_info", "attn_jvp_plan_flops",
     "attn_jvp_launch_order", "attn_jvp_row_ranges", "attn_jvp_tile_map", "masked_attention_jvp",
+    "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops", "attn_jvp_key_ranges",
+    "masked_attention_bwd",
 ]
 
 ATTN_JVP_BF16 = 0
@@ -79,9 +84,14 @@ def _load():
         lib.attn_jvp_row_ranges.argtypes = [vp, P(i32), ctypes.c_size_t]
         lib.attn_jvp_launch_order.argtypes = [vp, P(i32), ctypes.c_size_t]
         lib.attn_jvp_tile_map.argtypes = [vp, P(ctypes.c_uint8), ctypes.c_size_t]
+        lib.attn_jvp_bwd.argtypes = [vp] * 12
+        lib.attn_jvp_bwd_workspace_size.argtypes = [vp, P(ctypes.c_size_t)]
+        lib.attn_jvp_plan_bwd_flops.argtypes = [vp, P(i64)]
+        lib.attn_jvp_key_ranges.argtypes = [vp, P(i32), ctypes.c_size_t]
         for name in ("attn_jvp_create", "attn_jvp_create_ex", "attn_jvp_fwd", "attn_jvp_destroy",
                      "attn_jvp_plan_info", "attn_jvp_plan_flops", "attn_jvp_launch_order", "attn_jvp_row_ranges",
-                     "attn_jvp_tile_map"):
+                     "attn_jvp_tile_map", "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops",
+                     "attn_jvp_key_ranges"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -181,6 +191,29 @@ def attn_jvp_row_ranges(plan: Plan) -> np.ndarray:
     return out
 
 
+def attn_jvp_key_ranges(plan: Plan) -> np.ndarray:
+    """[N, 4] int32: per key j, the query rows [lo1, hi1) and [lo2, hi2) that attend to it."""
+    n = plan.seq_len
+    out = np.empty((n, 4), dtype=np.int32)
+    _check(_load().attn_jvp_key_ranges(plan.handle, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), out.size),
+           "attn_jvp_key_ranges")
+    return out
+
+
+def attn_jvp_bwd_workspace_size(plan: Plan) -> int:
+    """Bytes of device workspace attn_jvp_bwd needs (8 B H N)."""
+    v = ctypes.c_size_t()
+    _check(_load().attn_jvp_bwd_workspace_size(plan.handle, ctypes.byref(v)), "attn_jvp_bwd_workspace_size")
+    return v.value
+
+
+def attn_jvp_plan_bwd_flops(plan: Plan) -> int:
+    """Useful FLOPs of one attn_jvp_bwd call of the plan (all heads): 10 d per allowed pair."""
+    v = ctypes.c_int64()
+    _check(_load().attn_jvp_plan_bwd_flops(plan.handle, ctypes.byref(v)), "attn_jvp_plan_bwd_flops")
+    return v.value
+
+
 def attn_jvp_launch_order(plan: Plan) -> np.ndarray:
     """Query block handled by workgroup t of each (b, h)."""
     out = np.empty(plan.info["n_query_blocks"], dtype=np.int32)
@@ -239,6 +272,34 @@ def attn_jvp_fwd(plan: Plan, q, k, v, tq, tk, tv, o, t_o, lse=None, stream=None)
     _check(code, "attn_jvp_fwd")
 
 
+def attn_jvp_bwd(plan: Plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace, stream=None) -> None:
+    """Enqueue the backward (dq, dk, dv) on `stream` (default: torch's current
+    stream).  `workspace` is a float32 CUDA tensor of at least
+    attn_jvp_bwd_workspace_size(plan) bytes; on return it holds delta and
+    -lse log2(e) per row, [B, H, 2, N]."""
+    import torch
+    ts = dict(q=q, k=k, v=v, o=o, d_o=d_o, dq=dq, dk=dk, dv=dv)
+    for name, t in ts.items():
+        _check_tensor(name, t, plan, plan.shape)
+    dev = q.device
+    for name, t in list(ts.items()) + [("lse", lse), ("workspace", workspace)]:
+        if not isinstance(t, torch.Tensor) or t.device != dev:
+            raise AttnJvpError(f"{name} must be a tensor on q's device ({dev})")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != plan.shape[:3] or not lse.is_contiguous():
+        raise AttnJvpError("lse must be a contiguous float32 [B, H, N] tensor")
+    if workspace.dtype != torch.float32 or not workspace.is_contiguous() \
+            or workspace.numel() * 4 < attn_jvp_bwd_workspace_size(plan):
+        raise AttnJvpError(f"workspace must be a contiguous float32 tensor of at least "
+                           f"{attn_jvp_bwd_workspace_size(plan)} bytes")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    ptrs = [q, k, v, o, lse, d_o, dq, dk, dv, workspace]
+    with torch.cuda.device(dev):
+        code = _load().attn_jvp_bwd(plan.handle, *[ctypes.c_void_p(t.data_ptr()) for t in ptrs],
+                                    ctypes.c_void_p(stream.cuda_stream))
+    _check(code, "attn_jvp_bwd")
+
+
 _plan_cache = {}
 _plan_lock = threading.Lock()
 
@@ -269,3 +330,16 @@ def masked_attention_jvp(q, k, v, tq, tk, tv, desc, scale=None, return_lse=False
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
     attn_jvp_fwd(plan, q, k, v, tq, tk, tv, o, t_o, lse)
     return (o, t_o, lse) if return_lse else (o, t_o)
+
+
+def masked_attention_bwd(q, k, v, o, lse, d_o, desc, scale=None, return_workspace=False):
+    """(dq, dk, dv[, workspace]) of masked attention for [B, H, N, d] bf16 or
+    fp32 CUDA tensors, from the forward's o and lse (masked_attention_jvp with
+    return_lse=True) and the output gradient d_o."""
+    import torch
+    dtype = ATTN_JVP_BF16 if q.dtype == torch.bfloat16 else ATTN_JVP_FP32
+    plan = _cached_plan(desc, q.shape, dtype, scale, 0)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(attn_jvp_bwd_workspace_size(plan) // 4, dtype=torch.float32, device=q.device)
+    attn_jvp_bwd(plan, q, k, v, o, lse, d_o, dq, dk, dv, ws)
+    return (dq, dk, dv, ws) if return_workspace else (dq, dk, dv)

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_jvp.so")
-SOURCES = ["attn_jvp_api.hip", "attn_jvp_kernels.hip"]
+SOURCES = ["attn_jvp_api.hip", "attn_jvp_kernels.hip", "attn_jvp_bwd_kernels.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
 HIP_FLAGS = [

@@ -29,6 +29,10 @@ struct attn_jvp_plan {
   int64_t allowed_pairs;
   int64_t visited_tiles;
   int64_t useful_flops;
+  // backward: rows per dq block, keys per dk/dv block, blocks per (b, h)
+  int32_t bwd_block_q, bwd_block_kv;
+  int32_t bwd_n_qblocks, bwd_n_kblocks;
+  int64_t bwd_useful_flops;
 };
 
 namespace {
@@ -190,6 +194,15 @@ int attn_jvp_create_ex(attn_jvp_plan** out, const attn_jvp_mask_desc* mask, int3
   }
   p->visited_tiles = visited;
   p->useful_flops = count_flops(p->g, head_dim, (flags & ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO) != 0) * batch * heads;
+  bwd_block_sizes(dtype, head_dim, &p->bwd_block_q, &p->bwd_block_kv);
+  p->bwd_n_qblocks = n_query_blocks(p->g, p->bwd_block_q);
+  p->bwd_n_kblocks = n_query_blocks(p->g, p->bwd_block_kv);  // key blocks are cut per side too
+  p->bwd_useful_flops = 10 * p->allowed_pairs * head_dim * batch * heads;
+  if ((int64_t)batch * heads * (p->bwd_n_qblocks > p->bwd_n_kblocks ? p->bwd_n_qblocks : p->bwd_n_kblocks) >=
+      (int64_t(1) << 31)) {
+    delete p;
+    return fail(ATTN_JVP_E_OVERFLOW, "backward grid does not fit");
+  }
   *out = p;
   return ok();
 }
@@ -251,6 +264,87 @@ int attn_jvp_fwd(const attn_jvp_plan* p, const void* q, const void* k, const voi
   const int grid = p->batch * p->heads * p->n_qblocks;
   hipError_t e = launch_fwd(p->dtype, p->head_dim, grid, fp, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(ATTN_JVP_E_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int attn_jvp_bwd_workspace_size(const attn_jvp_plan* p, size_t* bytes) {
+  if (p == nullptr || bytes == nullptr) return fail(ATTN_JVP_E_NULL, "plan and bytes must be non-NULL");
+  *bytes = (size_t)p->batch * p->heads * (size_t)p->g.seq_len * 2 * sizeof(float);
+  return ok();
+}
+
+int attn_jvp_bwd(const attn_jvp_plan* p, const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* d_o, void* dq, void* dk, void* dv, float* workspace,
+                 void* hip_stream) {
+  if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
+  static const char* names[10] = {"q", "k", "v", "o", "d_o", "lse", "dq", "dk", "dv", "workspace"};
+  const void* ins[6] = {q, k, v, o, d_o, lse};
+  void* outs[4] = {dq, dk, dv, workspace};
+  for (int i = 0; i < 6; ++i)
+    if (ins[i] == nullptr) return fail(ATTN_JVP_E_NULL, "%s is NULL", names[i]);
+  for (int i = 0; i < 4; ++i)
+    if (outs[i] == nullptr) return fail(ATTN_JVP_E_NULL, "%s is NULL", names[6 + i]);
+  const size_t elt = p->dtype == ATTN_JVP_BF16 ? 2 : 4;
+  const size_t rows = (size_t)p->batch * p->heads * (size_t)p->g.seq_len;
+  const size_t tbytes = rows * p->head_dim * elt;
+  const size_t in_bytes[6] = {tbytes, tbytes, tbytes, tbytes, tbytes, rows * 4};
+  const size_t out_bytes[4] = {tbytes, tbytes, tbytes, rows * 8};
+  for (int i = 0; i < 10; ++i) {
+    const uintptr_t a = (uintptr_t)(i < 6 ? ins[i] : outs[i - 6]);
+    const int need = (i == 5 || i == 9) ? 4 : 16;  // lse and workspace: fp32 rows
+    if (a % need) return fail(ATTN_JVP_E_ALIGN, "%s is not %d-byte aligned", names[i], need);
+  }
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j]))
+        return fail(ATTN_JVP_E_INVALID, "%s overlaps input %s", names[6 + i], names[j]);
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j]))
+        return fail(ATTN_JVP_E_INVALID, "%s overlaps %s", names[6 + i], names[6 + j]);
+  }
+
+  int dev;
+  int st = check_device(&dev);
+  if (st != ATTN_JVP_OK) return st;
+
+  BwdParams bp;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.o = o;
+  bp.dout = d_o;
+  bp.lse = lse;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.ws = workspace;
+  bp.g = p->g;
+  bp.n_qblocks = p->bwd_n_qblocks;
+  bp.n_kblocks = p->bwd_n_kblocks;
+  bp.scale = p->scale;
+  bp.score_log2 = p->scale * 1.4426950408889634f;
+  hipError_t e = launch_bwd(p->dtype, p->head_dim, p->batch * p->heads, bp, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(ATTN_JVP_E_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int attn_jvp_plan_bwd_flops(const attn_jvp_plan* p, int64_t* useful_flops) {
+  if (p == nullptr || useful_flops == nullptr) return fail(ATTN_JVP_E_NULL, "plan and useful_flops must be non-NULL");
+  *useful_flops = p->bwd_useful_flops;
+  return ok();
+}
+
+int attn_jvp_key_ranges(const attn_jvp_plan* p, int32_t* out, size_t n) {
+  if (p == nullptr || out == nullptr) return fail(ATTN_JVP_E_NULL, "plan and host_out must be non-NULL");
+  if (n < (size_t)p->g.seq_len * 4)
+    return fail(ATTN_JVP_E_INVALID, "host_out holds %zu int32, need %zu", n, (size_t)p->g.seq_len * 4);
+  for (int32_t j = 0; j < p->g.seq_len; ++j) {
+    const Ranges r = col_ranges(p->g, j);
+    out[4 * j + 0] = r.lo1;
+    out[4 * j + 1] = r.hi1;
+    out[4 * j + 2] = r.lo2;
+    out[4 * j + 3] = r.hi2;
+  }
   return ok();
 }
 

@@ -1,0 +1,875 @@
+// attn_jvp_bwd_kernels.hip -- gfx950 kernels for the backward of block-causal /
+// teacher-forcing masked attention: dq, dk, dv from q, k, v, o, lse and dO.
+//
+// What is computed (Causal-rCM, arXiv 2606.25473, section 3.2.1: the
+// FlashAttention-2 based masked attention of the student also runs its
+// backward; section 2.3 and section 3.1.1 eq. 8 for the mask): with P the
+// masked softmax of the scaled scores, recomputed from the forward's lse,
+//   dP = dO V^T,   delta_i = sum_d dO_id O_id  (= sum_j P_ij dP_ij),
+//   dS = P o (dP - delta),   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO,
+// where masked pairs have P = 0 and hence dS = 0.
+//
+// Two kernels per call, no atomics, so every result is a fixed function of
+// the inputs:
+// * dq kernel: one workgroup per query block with the forward's key-tile
+//   schedule; lane = query.  It also writes delta and -lse log2(e) of its rows
+//   to the workspace.  Per 32-key tile: S^T = K Q^T and dP^T = V dO^T (score
+//   products in vector-register form), P^T = exp2(S^T scale log2(e) -
+//   lse log2(e)), dS^T, then dQ^T += K^T dS^T with K^T from the transposing
+//   LDS read of the K tile.
+// * dk/dv kernel: one workgroup per block of 32 NW keys, cut per side like
+//   the query blocks, over the 32-row query tiles of the rows that attend to
+//   any of its keys (at most two intervals); lane = key.  Per query tile:
+//   X = Q K^T and dP = dO V^T, P, dS, then dV^T += dO^T P and dK^T += Q^T dS
+//   with dO^T and Q^T from the transposing LDS read; delta and lse of the
+//   tile's rows come from the workspace, staged in LDS with the tile.
+// Both follow the forward kernel's structure: 32-row tiles go HBM -> LDS by
+// DMA into a 4-stage ring (XOR-swizzled rows, zeros past the end), the score
+// products of tile j+1 run under the elementwise work of tile j and the
+// output products of tile j under the exponentials of tile j+1, one MFMA per
+// scheduling slot; whole tiles outside the key (query) ranges are never
+// visited and the element mask runs only on partial tiles.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "attn_jvp_launch.h"
+#include "kernel_common.h"
+#include "mask_index.h"
+
+namespace attn_jvp {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBwdStages = 4;  // LDS ring depth: tiles j .. j+3 resident or in flight
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Per-lane addressing shared by the two bf16 kernels.
+template <int D, int NW>
+struct TileGeom {
+  static constexpr int ROWS = 32;                     // rows per streamed tile
+  static constexpr int KS = D / 16;                   // k-steps of a score product
+  static constexpr int DC = D / 32;                   // 32-wide column blocks of an output
+  static constexpr int NG = 2 * DC;                   // output products per tile and accumulator
+  static constexpr int CPR = D / 8;                   // 16-byte groups per row
+  static constexpr int TILE = ROWS * D;               // elements per tensor per stage
+  static constexpr int LOADS = TILE * 2 / 1024 / NW;  // 1 KB DMA loads per wave per tensor
+  static_assert(LOADS * NW * 1024 == TILE * 2, "DMA split");
+
+  // DMA source offset of this lane for its i-th 1 KB block: lane L of block
+  // `blk` fills LDS group (row, pc) and fetches global group pc ^ swz(row).
+  __device__ static int dma_voff(int wave, int lane, int i) {
+    const int blk = wave * LOADS + i;
+    const int rw = blk * (64 / CPR) + lane / CPR;
+    return (rw * D + (((lane % CPR) ^ row_swz<D>(rw)) << 3)) * 2;
+  }
+  // Fragment of row n (16 bytes at k-step s, half h) of a swizzled tile: the
+  // A operand of a product contracting over d.
+  __device__ static u32x4 row_frag(const uint16_t* tile, int n, int h, int s) {
+    return *(const u32x4*)(tile + n * D + (((2 * s + h) ^ row_swz<D>(n)) << 3));
+  }
+  // Transposed fragment for output group gidx (16-row half c2, 32-column
+  // block c): the A operand of a product contracting over the tile's rows,
+  // rows {4h .. 4h+3, 8+4h .. 8+4h+3} of the half, matching the order in
+  // which a score accumulator holds them.
+  __device__ static u32x4 tr_frag(const uint16_t* tile, int lane, int gidx) {
+    const int h = lane >> 5;
+    const int tr_row = 4 * h + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int c2 = gidx / DC, c = gidx % DC;
+    const int col = 32 * c + tr_col;
+    const int k1 = 16 * c2 + tr_row, k2 = k1 + 8;
+    const int o1 = k1 * D + (((col >> 3) ^ row_swz<D>(k1)) << 3) + (col & 7);
+    const int o2 = k2 * D + (((col >> 3) ^ row_swz<D>(k2)) << 3) + (col & 7);
+    const u32x2 a = read_tr16(tile + o1), b = read_tr16(tile + o2);
+    return u32x4{a[0], a[1], b[0], b[1]};
+  }
+};
+
+// Element i of a score accumulator of lane (n, h) belongs to tile row
+// 8 (i / 4) + 4 h + i % 4; mask the elements whose row is outside the lane's
+// ranges r (scores -> -inf).
+__device__ __forceinline__ void mask_scores(f32x16& S, int x0, int h, const Ranges& r) {
+  const int len1 = r.hi1 - r.lo1, len2 = r.hi2 - r.lo2;
+  const int b1 = x0 + 4 * h - r.lo1, b2 = x0 + 4 * h - r.lo2;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int off = 8 * (i >> 2) + (i & 3);
+    const bool ok = (unsigned)(b1 + off) < (unsigned)len1 || (unsigned)(b2 + off) < (unsigned)len2;
+    S[i] = ok ? S[i] : -INFINITY;
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// dq kernel (bf16).  One wave = 32 query rows; the K and V tiles of 32 keys
+// stream through the LDS ring.
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  using TG = TileGeom<D, NW>;
+  constexpr int BC = TG::ROWS;  // keys per tile
+  constexpr int BR = NW * 32;   // query rows per block
+  constexpr int KS = TG::KS, DC = TG::DC, NG = TG::NG, TILE = TG::TILE, LOADS = TG::LOADS;
+  constexpr int LPT = 2 * LOADS;  // DMA instructions per wave and tile: K, V
+  constexpr int STAGES = kBwdStages;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t ring0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring2[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring3[2 * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+
+  const MaskGeom g = p.g;
+  const int N = g.seq_len;
+  const int bh = blockIdx.x / p.n_qblocks;
+  const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks);
+  int r0, r1;
+  qblock_rows(g, BR, qb, &r0, &r1);
+  const TileSpans sp = block_tiles(block_ranges(g, r0, r1), BC);
+  const int ntiles = span_count(sp);
+
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const int slice_bytes = N * D * 2;
+  const i32x4_t desc_k = make_desc((const uint16_t*)p.k + base, slice_bytes);
+  const i32x4_t desc_v = make_desc((const uint16_t*)p.v + base, slice_bytes);
+
+  const int row = r0 + wave * 32 + n;
+  const bool row_ok = row < r1;
+  const Ranges rr = row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0};
+
+  // Q and dO fragments (B operands) stay in registers; delta = dO . O and
+  // -lse log2(e) of the row go to the workspace for the dk/dv kernel.
+  u32x4 qf[KS], dof[KS];
+  float delta, nl;
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)p.q + base, slice_bytes);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const uint16_t*)p.dout + base, slice_bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const uint16_t*)p.o + base, slice_bytes);
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int off = (row * D + 16 * s + 8 * h) * 2;
+      qf[s] = load16(rq, off);
+      dof[s] = load16(rdo, off);
+      const u32x4 of = load16(ro, off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part = fmaf(bf16_lo(dof[s][e]), bf16_lo(of[e]), part);
+        part = fmaf(bf16_hi(dof[s][e]), bf16_hi(of[e]), part);
+      }
+    }
+    delta = pair_sum(part);
+    const float lse = row_ok ? p.lse[(size_t)bh * N + row] : 0.f;
+    nl = -lse * kLog2e;
+    if (row_ok) p.ws[(size_t)bh * 2 * N + (size_t)h * N + row] = h ? nl : delta;
+  }
+
+  auto stage = [&](auto st) -> uint16_t* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return ring0;
+    else if constexpr (S == 1) return ring1;
+    else if constexpr (S == 2) return ring2;
+    else return ring3;
+  };
+  int dma_voff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) dma_voff[i] = TG::dma_voff(wave, lane, i);
+  // The q-th DMA instruction of tile t (past the last tile: that tile again,
+  // into a stage nothing reads, so every step issues the same number).
+  auto issue_part = [&](uint16_t* dst, int t, int q, int t_end) {
+    const int tile = span_tile(sp, t < t_end ? t : t_end - 1);
+    const int soff = tile * BC * D * 2;
+    const int i = q >> 1, tt = q & 1;
+    load16_lds_asm(tt ? desc_v : desc_k, dst + tt * TILE + (wave * LOADS + i) * 512, dma_voff[i], soff);
+  };
+  auto issue = [&](uint16_t* dst, int t, int t_end) {
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) issue_part(dst, t, q, t_end);
+  };
+
+  f32x16 accQ[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) accQ[c][i] = 0.f;
+  }
+  const float sl2 = p.score_log2;
+
+  // Key tiles that every valid row of the wave sees whole (scalar test);
+  // a wave without valid rows masks every tile.
+  Ranges wfirst{0, 0, 0, 0}, wlast{0, 0, 0, 0};
+  {
+    const int wa = r0 + wave * 32;
+    const int wb = wa + 32 < r1 ? wa + 32 : r1;
+    if (wa < wb) {
+      wfirst = row_ranges(g, wa);
+      wlast = row_ranges(g, wb - 1);
+    }
+  }
+  auto tile_whole = [&](int t) {
+    const int k0 = span_tile(sp, t) * BC;
+    return run_covers(wfirst, wlast, k0, k0 + BC);
+  };
+  auto exp_elem = [&](float x) { return __builtin_amdgcn_exp2f(fmaf(x, sl2, nl)); };
+
+  u32x4 kf[KS], vf[KS];
+  auto kvread = [&](const uint16_t* src, int s) {
+    kf[s] = TG::row_frag(src, n, h, s);
+    vf[s] = TG::row_frag(src + TILE, n, h, s);
+  };
+
+  // S^T and dP^T of two consecutive tiles (vector registers): the current
+  // tile's P (exponentiated) and dP, the next tile's scores being formed.
+  f32x16 SA, DA, SB, DB;
+
+  // Step j.  Phase 1: S^T, dP^T of tile j+1 under dS of tile j and its
+  // packs.  Phase 2: dQ^T += K^T dS^T of tile j under the mask (partial tiles)
+  // and exponentials of tile j+1.  Ring: step j reads K, V of tile j+1 and
+  // K^T of tile j, and issues the DMA of tile j+3 into the stage of tile j-1;
+  // the barrier follows the last read of tile j's stage, after each wave's
+  // share of tile j+2 has landed; the first K, V reads of tile j+2 follow it.
+  auto step = [&](auto st, int j, int t_end, f32x16& P, f32x16& DP, f32x16& Sn, f32x16& DPn) {
+    constexpr int ST = decltype(st)::value;
+    using NX = IC<(ST + 1) % STAGES>;
+    using N2 = IC<(ST + 2) % STAGES>;
+    using AH = IC<(ST + 3) % STAGES>;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) keep_in_acc(accQ[c]);
+    const uint16_t* nx = stage(NX{});
+    const uint16_t* cur = stage(st);
+    u32x4 DS[2];
+    u32x4 ktf[NG];
+    auto ds_pair = [&](int jj) {
+      const float a = P[jj] * (DP[jj] - delta);
+      const float b = P[jj + 1] * (DP[jj + 1] - delta);
+      DS[jj >> 3][(jj & 7) >> 1] = pack_bf16(a, b);
+      pin(DS[jj >> 3][(jj & 7) >> 1]);
+    };
+    auto dma = [&](int s) {
+#pragma unroll
+      for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q) issue_part(stage(AH{}), j + 3, q, t_end);
+    };
+
+    constexpr int PAIRS = 8 / KS;  // dS element pairs per k-step
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s == 0) mfma_v_first(Sn, kf[s], qf[s]);
+      else mfma_v_acc(Sn, kf[s], qf[s]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 2 < KS) kvread(nx, s + 2);
+      dma(s);
+#pragma unroll
+      for (int u = 0; u < PAIRS; ++u) ds_pair(2 * (s * PAIRS + u));
+      __builtin_amdgcn_sched_barrier(0);
+      if (s == 0) mfma_v_first(DPn, vf[s], dof[s]);
+      else mfma_v_acc(DPn, vf[s], dof[s]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s == KS - 2) ktf[0] = TG::tr_frag(cur, lane, 0);
+      if (s == KS - 1) ktf[1] = TG::tr_frag(cur, lane, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // phase 2 (the last score product is two MFMAs back at the first slot)
+#pragma unroll
+    for (int gidx = 0; gidx < NG; ++gidx) {
+      const int c2 = gidx / DC, c = gidx % DC;
+      accQ[c] = mfma_bf16(ktf[gidx], DS[c2], accQ[c]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (gidx == 0 && !tile_whole(j + 1)) mask_scores(Sn, span_tile(sp, j + 1) * BC, h, rr);  // rare
+      if (gidx + 2 < NG) ktf[gidx + 2] = TG::tr_frag(cur, lane, gidx + 2);
+      if (gidx == NG - 2) {
+        // every read of tile j's stage is issued; tile j+2 has landed here
+        wait_lgkmcnt<0>();
+        wait_vmcnt<LPT>();
+        barrier_nofence();
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k * NG / 16 == gidx) {
+          Sn[k] = exp_elem(Sn[k]);
+          pin(Sn[k]);
+        }
+      }
+      if (gidx == NG - 1) {
+        kvread(stage(N2{}), 0);
+        kvread(stage(N2{}), 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  auto first_tile = [&](int t_begin, int t_end) {
+    issue(ring0, t_begin, t_end);
+    issue(ring1, t_begin + 1, t_end);
+    issue(ring2, t_begin + 2, t_end);
+    wait_vmcnt<LPT>();  // first two tiles
+    barrier_nofence();
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kvread(ring0, s);
+      if (s == 0) {
+        mfma_v_first(SA, kf[s], qf[s]);
+        mfma_v_first(DA, vf[s], dof[s]);
+      } else {
+        mfma_v_acc(SA, kf[s], qf[s]);
+        mfma_v_acc(DA, vf[s], dof[s]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    acc_hazard_wait();
+    __builtin_amdgcn_sched_barrier(0);
+    if (!tile_whole(t_begin)) mask_scores(SA, span_tile(sp, t_begin) * BC, h, rr);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) SA[i] = exp_elem(SA[i]);
+    kvread(ring1, 0);
+    kvread(ring1, 1);
+  };
+
+  if (ntiles > 0) {
+    first_tile(0, ntiles);
+    for (int j = 0; j < ntiles; j += 4) {
+      step(IC<0>{}, j, ntiles, SA, DA, SB, DB);
+      if (j + 1 >= ntiles) break;
+      step(IC<1>{}, j + 1, ntiles, SB, DB, SA, DA);
+      if (j + 2 >= ntiles) break;
+      step(IC<2>{}, j + 2, ntiles, SA, DA, SB, DB);
+      if (j + 3 >= ntiles) break;
+      step(IC<3>{}, j + 3, ntiles, SB, DB, SA, DA);
+    }
+    // DMAs past the last tile and the last K, V reads may be in flight
+    wait_vmcnt<0>();
+    wait_lgkmcnt<0>();
+    barrier_nofence();
+  }
+
+  // ---- epilogue: dq = scale acc
+  acc_hazard_wait();
+  if (row_ok) {
+    const float scale = p.scale;
+    uint16_t* Qg = (uint16_t*)p.dq + base + (size_t)row * D;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * c + 8 * g4 + 4 * h;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc_read(accQ[c][4 * g4 + e]) * scale;
+        *(u32x2*)(Qg + d0) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dk/dv kernel (bf16).  One wave = 32 keys; the Q and dO tiles of 32 rows
+// and the rows' delta and -lse log2(e) stream through the LDS ring.
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  using TG = TileGeom<D, NW>;
+  constexpr int BQ = TG::ROWS;  // query rows per tile
+  constexpr int BK = NW * 32;   // keys per block
+  constexpr int KS = TG::KS, DC = TG::DC, NG = TG::NG, TILE = TG::TILE, LOADS = TG::LOADS;
+  constexpr int LPT = 2 * LOADS + 1;  // DMA instructions per wave and tile: Q, dO, row terms
+  constexpr int STAGES = kBwdStages;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t ring0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring2[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring3[2 * TILE];
+  // per stage and wave: delta of the tile's 32 rows, then their -lse log2(e)
+  __shared__ __attribute__((aligned(256))) float rows0[NW * 64];
+  __shared__ __attribute__((aligned(256))) float rows1[NW * 64];
+  __shared__ __attribute__((aligned(256))) float rows2[NW * 64];
+  __shared__ __attribute__((aligned(256))) float rows3[NW * 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+
+  const MaskGeom g = p.g;
+  const int N = g.seq_len;
+  const int bh = blockIdx.x / p.n_kblocks;
+  // Key blocks are cut per side like query blocks; index order is heavy
+  // first (the earliest keys of a side are seen by the most rows).
+  const int kb = blockIdx.x - bh * p.n_kblocks;
+  int k0, k1;
+  qblock_rows(g, BK, kb, &k0, &k1);
+  const TileSpans sp = block_tiles(block_col_ranges(g, k0, k1), BQ);
+  const int ntiles = span_count(sp);
+
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const int slice_bytes = N * D * 2;
+  const i32x4_t desc_q = make_desc((const uint16_t*)p.q + base, slice_bytes);
+  const i32x4_t desc_do = make_desc((const uint16_t*)p.dout + base, slice_bytes);
+  // the row terms: lanes 0-31 fetch delta, lanes 32-63 -lse log2(e); past
+  // the end a delta lane reads the next plane (masked rows only) and an
+  // lse lane reads zeros
+  const i32x4_t desc_ws = make_desc(p.ws + (size_t)bh * 2 * N, N * 8);
+  const int ws_voff = (lane & 31) * 4 + (lane >> 5) * N * 4;
+
+  const int key = k0 + wave * 32 + n;
+  const bool key_ok = key < k1;
+  const Ranges cr = key_ok ? col_ranges(g, key) : Ranges{0, 0, 0, 0};
+
+  // K and V fragments (B operands) stay in accumulation registers for the
+  // whole task (zeros for keys past the block).
+  u32x4 kf[KS], vf[KS];
+  {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t*)p.k + base, slice_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t*)p.v + base, slice_bytes);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int off = (key * D + 16 * s + 8 * h) * 2;
+      kf[s] = load16(rk, off);
+      vf[s] = load16(rv, off);
+      if (!key_ok) {
+        kf[s] = u32x4{0, 0, 0, 0};
+        vf[s] = u32x4{0, 0, 0, 0};
+      }
+      keep_in_acc(kf[s]);
+      keep_in_acc(vf[s]);
+    }
+  }
+
+  auto stage = [&](auto st) -> uint16_t* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return ring0;
+    else if constexpr (S == 1) return ring1;
+    else if constexpr (S == 2) return ring2;
+    else return ring3;
+  };
+  auto rstage = [&](auto st) -> float* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return rows0 + wave * 64;
+    else if constexpr (S == 1) return rows1 + wave * 64;
+    else if constexpr (S == 2) return rows2 + wave * 64;
+    else return rows3 + wave * 64;
+  };
+  int dma_voff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) dma_voff[i] = TG::dma_voff(wave, lane, i);
+  auto issue_part = [&](uint16_t* dst, float* rdst, int t, int q, int t_end) {
+    const int tile = span_tile(sp, t < t_end ? t : t_end - 1);
+    if (q < 2 * LOADS) {
+      const int i = q >> 1, tt = q & 1;
+      load16_lds_asm(tt ? desc_do : desc_q, dst + tt * TILE + (wave * LOADS + i) * 512, dma_voff[i],
+                     tile * BQ * D * 2);
+    } else {
+      load4_lds_asm(desc_ws, rdst, ws_voff, tile * BQ * 4);
+    }
+  };
+  auto issue = [&](auto st, int t, int t_end) {
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) issue_part(stage(st), rstage(st), t, q, t_end);
+  };
+
+  f32x16 accV[DC], accK[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      accV[c][i] = 0.f;
+      accK[c][i] = 0.f;
+    }
+  }
+  const float sl2 = p.score_log2;
+
+  // Query tiles that every valid key of the wave sees whole.
+  Ranges wfirst{0, 0, 0, 0}, wlast{0, 0, 0, 0};
+  {
+    const int wa = k0 + wave * 32;
+    const int wb = wa + 32 < k1 ? wa + 32 : k1;
+    if (wa < wb) {
+      wfirst = col_ranges(g, wa);
+      wlast = col_ranges(g, wb - 1);
+    }
+  }
+  auto tile_whole = [&](int t) {
+    const int q0 = span_tile(sp, t) * BQ;
+    return run_covers(wfirst, wlast, q0, q0 + BQ);
+  };
+  // Row terms of the lane's elements 4 q4 .. 4 q4 + 3 (rows 8 q4 + 4h + 0..3):
+  // plane 0 delta, plane 1 -lse log2(e).  Read a quad at a time, shortly
+  // before use, to keep few of them live.
+  auto rows_read = [&](const float* src, int plane, int q4, float* dst) {
+    const float4 v = *(const float4*)(src + 32 * plane + 8 * q4 + 4 * h);
+    dst[4 * q4 + 0] = v.x;
+    dst[4 * q4 + 1] = v.y;
+    dst[4 * q4 + 2] = v.z;
+    dst[4 * q4 + 3] = v.w;
+  };
+
+  u32x4 qf[KS], dof[KS];
+  auto qdread = [&](const uint16_t* src, int s) {
+    qf[s] = TG::row_frag(src, n, h, s);
+    dof[s] = TG::row_frag(src + TILE, n, h, s);
+  };
+
+  f32x16 XA, DA, XB, DB;
+  float nlv[16];  // -lse log2(e) of the rows of the tile being exponentiated
+
+  // Step j.  Phase 1: X, dP of tile j+1 under dS of tile j and the packs of
+  // P and dS.  Phase 2: dV^T += dO^T P and dK^T += Q^T dS of tile j under
+  // the mask (partial tiles) and exponentials of tile j+1.  Ring use as in
+  // the dq kernel, with the rows' terms in the same stage.
+  auto step = [&](auto st, int j, int t_end, f32x16& P, f32x16& DP, f32x16& Xn, f32x16& DPn) {
+    constexpr int ST = decltype(st)::value;
+    using NX = IC<(ST + 1) % STAGES>;
+    using N2 = IC<(ST + 2) % STAGES>;
+    using AH = IC<(ST + 3) % STAGES>;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      keep_in_acc(accV[c]);
+      keep_in_acc(accK[c]);
+    }
+    const uint16_t* nx = stage(NX{});
+    const uint16_t* cur = stage(st);
+    u32x4 PK[2], DSK[2];
+    u32x4 doT[NG], qT[NG];
+    float dl[16];
+    auto ds_pair = [&](int jj) {
+      const float a = P[jj] * (DP[jj] - dl[jj]);
+      const float b = P[jj + 1] * (DP[jj + 1] - dl[jj + 1]);
+      DSK[jj >> 3][(jj & 7) >> 1] = pack_bf16(a, b);
+      PK[jj >> 3][(jj & 7) >> 1] = pack_bf16(P[jj], P[jj + 1]);
+      pin(DSK[jj >> 3][(jj & 7) >> 1]);
+      pin(PK[jj >> 3][(jj & 7) >> 1]);
+    };
+    auto trread = [&](int gidx) {
+      doT[gidx] = TG::tr_frag(cur + TILE, lane, gidx);
+      qT[gidx] = TG::tr_frag(cur, lane, gidx);
+    };
+    auto dma = [&](int s) {
+#pragma unroll
+      for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q)
+        issue_part(stage(AH{}), rstage(AH{}), j + 3, q, t_end);
+    };
+
+    // dS pairs of k-step s (none at s = 0, while the first deltas are read)
+    auto pair_lo = [](int s) { return s == 0 ? 0 : (8 * (s - 1)) / (KS - 1); };
+    auto pair_hi = [&](int s) { return s + 1 < KS ? pair_lo(s + 1) : 8; };
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s == 0) mfma_v_first_ba(Xn, qf[s], kf[s]);
+      else mfma_v_acc_ba(Xn, qf[s], kf[s]);
+      __builtin_amdgcn_sched_barrier(0);
+      // delta quads needed by the pairs of k-steps s+1 (s = 0: also s+1's)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int first_pair = 2 * q4;  // pairs 2 q4, 2 q4 + 1 use quad q4
+        const int need = [&] {
+          for (int t = 1; t < KS; ++t)
+            if (first_pair < pair_hi(t)) return t;
+          return KS - 1;
+        }();
+        if (need - 1 == s || (s == 0 && need == 1)) rows_read(rstage(st), 0, q4, dl);
+      }
+      if (s + 2 < KS) qdread(nx, s + 2);
+      dma(s);
+      if (s > 0) {
+#pragma unroll
+        for (int u = pair_lo(s); u < pair_hi(s); ++u) ds_pair(2 * u);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (s == 0) mfma_v_first_ba(DPn, dof[s], vf[s]);
+      else mfma_v_acc_ba(DPn, dof[s], vf[s]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s == KS - 2) trread(0);
+      if (s == KS - 1) {
+        trread(1);
+        rows_read(rstage(NX{}), 1, 0, nlv);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // phase 2: 2 NG slots; the last score product is two MFMAs back at the
+    // first one
+    constexpr int UB = 2 * (NG - 2);  // slot of the barrier
+#pragma unroll
+    for (int gidx = 0; gidx < NG; ++gidx) {
+      const int c2 = gidx / DC, c = gidx % DC;
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        if (sl == 0) accV[c] = mfma_bf16(doT[gidx], PK[c2], accV[c]);
+        else accK[c] = mfma_bf16(qT[gidx], DSK[c2], accK[c]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int u = 2 * gidx + sl;
+        if (u == 0 && !tile_whole(j + 1)) mask_scores(Xn, span_tile(sp, j + 1) * BQ, h, cr);  // rare
+        if (sl == 0 && gidx + 2 < NG) trread(gidx + 2);
+        if (u == UB) {
+          wait_lgkmcnt<0>();
+          wait_vmcnt<LPT>();
+          barrier_nofence();
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          if (k * 2 * NG / 16 == u) {
+            Xn[k] = __builtin_amdgcn_exp2f(fmaf(Xn[k], sl2, nlv[k]));
+            pin(Xn[k]);
+          }
+        }
+        // -lse log2(e) quads of tile j+1, three slots before their first use
+#pragma unroll
+        for (int q4 = 1; q4 < 4; ++q4) {
+          const int first = (4 * q4) * 2 * NG / 16;
+          if (u == (first >= 3 ? first - 3 : 0)) rows_read(rstage(NX{}), 1, q4, nlv);
+        }
+        if (u == UB + 1) qdread(stage(N2{}), 0);
+        if (u == UB + 2) qdread(stage(N2{}), 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  auto first_tile = [&](int t_begin, int t_end) {
+    issue(IC<0>{}, t_begin, t_end);
+    issue(IC<1>{}, t_begin + 1, t_end);
+    issue(IC<2>{}, t_begin + 2, t_end);
+    wait_vmcnt<LPT>();  // first two tiles
+    barrier_nofence();
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) rows_read(rstage(IC<0>{}), 1, q4, nlv);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qdread(ring0, s);
+      if (s == 0) {
+        mfma_v_first_ba(XA, qf[s], kf[s]);
+        mfma_v_first_ba(DA, dof[s], vf[s]);
+      } else {
+        mfma_v_acc_ba(XA, qf[s], kf[s]);
+        mfma_v_acc_ba(DA, dof[s], vf[s]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    acc_hazard_wait();
+    __builtin_amdgcn_sched_barrier(0);
+    if (!tile_whole(t_begin)) mask_scores(XA, span_tile(sp, t_begin) * BQ, h, cr);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) XA[i] = __builtin_amdgcn_exp2f(fmaf(XA[i], sl2, nlv[i]));
+    qdread(ring1, 0);
+    qdread(ring1, 1);
+  };
+
+  if (ntiles > 0) {
+    first_tile(0, ntiles);
+    for (int j = 0; j < ntiles; j += 4) {
+      step(IC<0>{}, j, ntiles, XA, DA, XB, DB);
+      if (j + 1 >= ntiles) break;
+      step(IC<1>{}, j + 1, ntiles, XB, DB, XA, DA);
+      if (j + 2 >= ntiles) break;
+      step(IC<2>{}, j + 2, ntiles, XA, DA, XB, DB);
+      if (j + 3 >= ntiles) break;
+      step(IC<3>{}, j + 3, ntiles, XB, DB, XA, DA);
+    }
+    wait_vmcnt<0>();
+    wait_lgkmcnt<0>();
+    barrier_nofence();
+  }
+
+  // ---- epilogue: dv = acc_v, dk = scale acc_k
+  acc_hazard_wait();
+  if (key_ok) {
+    const float scale = p.scale;
+    uint16_t* Kg = (uint16_t*)p.dk + base + (size_t)key * D;
+    uint16_t* Vg = (uint16_t*)p.dv + base + (size_t)key * D;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * c + 8 * g4 + 4 * h;
+        float xk[4], xv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xk[e] = acc_read(accK[c][4 * g4 + e]) * scale;
+          xv[e] = acc_read(accV[c][4 * g4 + e]);
+        }
+        *(u32x2*)(Kg + d0) = u32x2{pack_bf16(xk[0], xk[1]), pack_bf16(xk[2], xk[3])};
+        *(u32x2*)(Vg + d0) = u32x2{pack_bf16(xv[0], xv[1]), pack_bf16(xv[2], xv[3])};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernels: 32 rows (keys) per workgroup, 8 lanes per row (key), each
+// lane owning D/8 consecutive columns; pairs are taken one at a time from
+// the same schedules with the exact mask, in fp32 throughout.
+__device__ __forceinline__ float sum8(float x) {
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) x += __shfl_xor(x, o, 8);
+  return x;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dq_fp32_kernel(BwdParams p) {
+  constexpr int BR = 32, BC = 32, E = D / 8;
+  const MaskGeom g = p.g;
+  const int N = g.seq_len;
+  const int slice = threadIdx.x & 7, lr = threadIdx.x >> 3;
+  const int bh = blockIdx.x / p.n_qblocks;
+  const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks);
+  int r0, r1;
+  qblock_rows(g, BR, qb, &r0, &r1);
+  const TileSpans sp = block_tiles(block_ranges(g, r0, r1), BC);
+  const int ntiles = span_count(sp);
+  const int row = r0 + lr;
+  const bool row_ok = row < r1;
+  const Ranges rr = row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0};
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const float* __restrict__ K = (const float*)p.k + base + slice * E;
+  const float* __restrict__ V = (const float*)p.v + base + slice * E;
+  const int qrow = row_ok ? row : r0;
+  const size_t roff = base + (size_t)qrow * D + slice * E;
+  float q[E], dob[E], acc[E];
+  float part = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    q[e] = ((const float*)p.q)[roff + e];
+    dob[e] = ((const float*)p.dout)[roff + e];
+    part = fmaf(dob[e], ((const float*)p.o)[roff + e], part);
+    acc[e] = 0.f;
+  }
+  const float delta = sum8(part);
+  const float nl = -p.lse[(size_t)bh * N + qrow] * kLog2e;
+  if (row_ok && slice < 2) p.ws[(size_t)bh * 2 * N + (size_t)slice * N + row] = slice ? nl : delta;
+  const float sl2 = p.score_log2;
+  for (int it = 0; it < ntiles; ++it) {
+    const int k0 = span_tile(sp, it) * BC;
+    const int k1 = k0 + BC < N ? k0 + BC : N;
+    for (int j = k0; j < k1; ++j) {
+      if (!in_ranges(rr, j)) continue;  // uniform across the row's 8 lanes
+      const float* kj = K + (size_t)j * D;
+      const float* vj = V + (size_t)j * D;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        s = fmaf(q[e], kj[e], s);
+        dp = fmaf(dob[e], vj[e], dp);
+      }
+      s = sum8(s);
+      dp = sum8(dp);
+      const float pj = exp2f(fmaf(s, sl2, nl));
+      const float ds = pj * (dp - delta);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(ds, kj[e], acc[e]);
+    }
+  }
+  if (!row_ok) return;
+  float* dQ = (float*)p.dq + base + (size_t)row * D + slice * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) dQ[e] = acc[e] * p.scale;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dkdv_fp32_kernel(BwdParams p) {
+  constexpr int BK = 32, BQ = 32, E = D / 8;
+  const MaskGeom g = p.g;
+  const int N = g.seq_len;
+  const int slice = threadIdx.x & 7, lk = threadIdx.x >> 3;
+  const int bh = blockIdx.x / p.n_kblocks;
+  int k0, k1;
+  qblock_rows(g, BK, blockIdx.x - bh * p.n_kblocks, &k0, &k1);
+  const TileSpans sp = block_tiles(block_col_ranges(g, k0, k1), BQ);
+  const int ntiles = span_count(sp);
+  const int key = k0 + lk;
+  const bool key_ok = key < k1;
+  const Ranges cr = key_ok ? col_ranges(g, key) : Ranges{0, 0, 0, 0};
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const float* __restrict__ Q = (const float*)p.q + base + slice * E;
+  const float* __restrict__ dO = (const float*)p.dout + base + slice * E;
+  const float* __restrict__ dl = p.ws + (size_t)bh * 2 * N;
+  const float* __restrict__ nlr = dl + N;
+  const int krow = key_ok ? key : k0;
+  float kk[E], vv[E], ak[E], av[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    kk[e] = ((const float*)p.k)[base + (size_t)krow * D + slice * E + e];
+    vv[e] = ((const float*)p.v)[base + (size_t)krow * D + slice * E + e];
+    ak[e] = 0.f;
+    av[e] = 0.f;
+  }
+  const float sl2 = p.score_log2;
+  for (int it = 0; it < ntiles; ++it) {
+    const int q0 = span_tile(sp, it) * BQ;
+    const int q1 = q0 + BQ < N ? q0 + BQ : N;
+    for (int i = q0; i < q1; ++i) {
+      if (!in_ranges(cr, i)) continue;  // uniform across the key's 8 lanes
+      const float* qi = Q + (size_t)i * D;
+      const float* doi = dO + (size_t)i * D;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        s = fmaf(qi[e], kk[e], s);
+        dp = fmaf(doi[e], vv[e], dp);
+      }
+      s = sum8(s);
+      dp = sum8(dp);
+      const float pij = exp2f(fmaf(s, sl2, nlr[i]));
+      const float ds = pij * (dp - dl[i]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        av[e] = fmaf(pij, doi[e], av[e]);
+        ak[e] = fmaf(ds, qi[e], ak[e]);
+      }
+    }
+  }
+  if (!key_ok) return;
+  float* dK = (float*)p.dk + base + (size_t)key * D + slice * E;
+  float* dV = (float*)p.dv + base + (size_t)key * D + slice * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    dK[e] = ak[e] * p.scale;
+    dV[e] = av[e];
+  }
+}
+
+// ---------------------------------------------------------------------------
+void bwd_block_sizes(int dtype, int head_dim, int* block_q, int* block_kv) {
+  (void)head_dim;
+  if (dtype == kBf16) {
+    *block_q = kBf16Waves * 32;
+    *block_kv = kBf16Waves * 32;
+  } else {
+    *block_q = 32;
+    *block_kv = 32;
+  }
+}
+
+hipError_t launch_bwd(int dtype, int head_dim, int bh, const BwdParams& p, hipStream_t stream) {
+  const dim3 gq((unsigned)bh * (unsigned)p.n_qblocks), gk((unsigned)bh * (unsigned)p.n_kblocks);
+  if (dtype == kBf16) {
+    const dim3 block(kBf16Waves * 64);
+    if (head_dim == 128) {
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<128, kBf16Waves>), gq, block, 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<128, kBf16Waves>), gk, block, 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<64, kBf16Waves>), gq, block, 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<64, kBf16Waves>), gk, block, 0, stream, p);
+    }
+  } else {
+    if (head_dim == 128) {
+      hipLaunchKernelGGL((bwd_dq_fp32_kernel<128>), gq, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_fp32_kernel<128>), gk, dim3(256), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((bwd_dq_fp32_kernel<64>), gq, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_fp32_kernel<64>), gk, dim3(256), 0, stream, p);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn_jvp

@@ -46,159 +46,13 @@
 #include <type_traits>
 
 #include "attn_jvp_launch.h"
+#include "kernel_common.h"
 #include "mask_index.h"
 
 namespace attn_jvp {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-#define LDS_AS __attribute__((address_space(3)))
-
 constexpr float kLazyRescaleLog2 = 8.0f;
 constexpr float kLn2 = 0.6931471805599453f;
-
-__device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// Combine a value with the one held by lane l^32 (symmetric ops only: the
-// swap returns own and partner values, one in each result).
-__device__ __forceinline__ float pair_max(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v;
-  v[0] = (__bf16)a;
-  v[1] = (__bf16)b;
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// Raw buffer resource over [base, base + bytes): out-of-range loads return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
-// 16 bytes per lane from global (byte offset voff + soff, soff wave-uniform)
-// straight into LDS at lds + 16 * lane, through the compiler builtin (kFull).
-__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds, 16, voff, soff, 0, 0);
-}
-
-typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
-// Buffer descriptor as four dwords (base, stride 0, byte size, the same
-// config word as make_rsrc): for the DMA below.  Loads at or past `bytes`
-// (vector + scalar offset, checked on the device) return zeros.
-__device__ __forceinline__ i32x4_t make_desc(const void* base, int bytes) {
-  const uint64_t a = (uint64_t)base;
-  return i32x4_t{(int32_t)(uint32_t)a, (int32_t)(uint32_t)((a >> 32) & 0xffff), bytes, 0x00020000};
-}
-// The same DMA written out (the K and V streams of the modes with fewer
-// MFMAs per tile): there the compiler, tracking its own LDS DMA against later
-// LDS reads, waits for every DMA in flight (vmcnt(0)) before some V reads
-// although they read another ring stage, which exposes the whole DMA latency
-// once per tile.  The kernel orders the ring itself (explicit vmcnt waits and
-// barriers before a stage is read or refilled), so the DMA is hidden from the
-// compiler; the memory clobber keeps LDS accesses from moving across.
-// Vector-memory loads complete in order, so the compiler's own waits for its
-// loads stay correct (they only cover more).  One wait state between the M0
-// write and the DMA.
-__device__ __forceinline__ void load16_lds_asm(i32x4_t r, uint16_t* lds, int voff, int soff) {
-  // soff and the LDS address are wave-uniform; readfirstlane puts them in
-  // scalar registers where the compiler computed them in vector ones
-  const int m0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(LDS_AS void*)lds);
-  const int so = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(r), "s"(so), "s"(m0) : "memory", "m0");
-}
-__device__ __forceinline__ u32x2 read_tr16(const uint16_t* p) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)p));
-}
-
-// 16-byte group swizzle of a tile row: group g of row `key` is stored at
-// g ^ row_swz<D>(key).  gfx950 LDS has 64 banks (256 bytes per cycle).
-// * 16-byte fragment reads serve 16 lanes, i.e. 16 consecutive rows at one
-//   logical group: the swizzle maps them to 16 distinct bank groups.
-// * A transposing read serves a 16-lane group with 4 rows 4k..4k+3 and 16
-//   or 32 consecutive columns: the swizzle puts each of the 4 rows into its
-//   own aligned 64-byte bank group.
-// d = 128 rows are 256 bytes (all 64 banks); d = 64 rows are 128 bytes, so
-// rows of opposite parity already sit in opposite bank halves.
-template <int D>
-__device__ __forceinline__ int row_swz(int key) {
-  if constexpr (D == 128) return ((key & 3) << 2) | ((key >> 2) & 3);
-  else return (((key >> 1) & 1) << 2) | ((key >> 2) & 3);
-}
-
-// Vector access to accumulation registers, written out so that the compiler
-// sees no vector-ALU reader of the loop-carried accumulators (it would
-// otherwise keep a second copy of all of them in vector registers and refresh
-// it on every tile).  Callers run acc_hazard_wait() first: an MFMA result may
-// be read by a vector instruction only after enough wait states (24 here,
-// above the requirement of the 32x32 bf16 MFMA).
-__device__ __forceinline__ void acc_hazard_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
-__device__ __forceinline__ float acc_read(float a) {
-  float v;
-  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
-  return v;
-}
-__device__ __forceinline__ float acc_write(float v) {
-  float a;
-  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
-  return a;
-}
-
-// Score products in vector-register form: the scores go straight from the
-// matrix cores to the vector ALUs, with no accumulator-to-vector copies (on
-// gfx950 such a copy next to running MFMAs costs several times a plain vector
-// op).  Written out because the compiler gives all MFMAs of a kernel one
-// register form, and the output accumulators need the accumulation registers.
-// The compiler inserts the waits for the operands (LDS reads, loads) but does
-// not see the result hazard: vector instructions read these results only
-// after at least two further MFMAs have been issued, or after
-// acc_hazard_wait() fenced by sched_barrier on both sides (plain vector code
-// may otherwise be scheduled across the asm).
-__device__ __forceinline__ void mfma_v_first(f32x16& d, u32x4 a, u32x4 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_v_acc(f32x16& d, u32x4 a, u32x4 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
-
-// Pin a value to this point of the instruction stream: it must be computed
-// before the (volatile, hence ordered) empty asm, so the compiler cannot sink
-// it into a later block.  Emits no instruction.
-__device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
-__device__ __forceinline__ void pin(uint32_t x) { asm volatile("" ::"v"(x)); }
-
-// Workgroup barrier without a memory fence: the fence of __syncthreads()
-// would wait for every LDS DMA in flight.  Visibility of the tile about to be
-// read comes from the explicit vmcnt wait before it; the memory clobber keeps
-// the compiler from moving LDS accesses across the barrier.
-__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_lgkmcnt() {
-  static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // Tile modes of the bf16 kernel.  kFull: the general operation.  With the
 // clean-tangent-zero option (teacher forcing, clean tokens carry no tangent):

@@ -30,10 +30,34 @@ struct FwdParams {
   int32_t ctz;        // clean-tangent-zero plan (teacher forcing only)
 };
 
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* ws;          // per (b, h): [2][N] floats, delta then -lse * log2(e)
+  MaskGeom g;
+  int32_t n_qblocks;  // dq kernel: query blocks per (b, h)
+  int32_t n_kblocks;  // dk/dv kernel: key blocks per (b, h)
+  float score_log2;   // scale * log2(e)
+  float scale;
+};
+
 // Query rows per block and keys per tile of the kernel chosen for dtype/head_dim.
 void block_sizes(int dtype, int head_dim, int* block_q, int* block_k);
 
 // Launch one forward + JVP over `grid` workgroups; returns hipGetLastError().
 hipError_t launch_fwd(int dtype, int head_dim, int grid, const FwdParams& p, hipStream_t stream);
+
+// Rows per dq-kernel block and keys per dk/dv-kernel block of the backward.
+void bwd_block_sizes(int dtype, int head_dim, int* block_q, int* block_kv);
+
+// Launch the backward (dq kernel, then dk/dv kernel) for bh = B * H slices.
+hipError_t launch_bwd(int dtype, int head_dim, int bh, const BwdParams& p, hipStream_t stream);
 
 }  // namespace attn_jvp

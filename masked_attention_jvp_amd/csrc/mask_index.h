@@ -58,6 +58,17 @@ AJ_HD Ranges row_ranges(const MaskGeom& g, int32_t i) {
   return Ranges{0, c * g.chunk_len, g.side_len + c * g.chunk_len, g.side_len + (c + 1) * g.chunk_len};
 }
 
+// Query rows that attend to key j (the transpose of row_ranges):
+//   clean key of chunk c -> clean rows [c T, N_h) and noisy rows [N_h + (c+1) T, N)
+//   noisy key of chunk c -> noisy rows [N_h + c T, N_h + (c+1) T)
+//   block-causal key of chunk c -> rows [c T, N)
+AJ_HD Ranges col_ranges(const MaskGeom& g, int32_t j) {
+  const int32_t c = chunk_of(g, j);
+  if (!g.tf) return Ranges{c * g.chunk_len, g.seq_len, 0, 0};
+  if (is_noisy(g, j)) return Ranges{g.side_len + c * g.chunk_len, g.side_len + (c + 1) * g.chunk_len, 0, 0};
+  return Ranges{c * g.chunk_len, g.side_len, g.side_len + (c + 1) * g.chunk_len, g.seq_len};
+}
+
 AJ_HD bool in_ranges(const Ranges& r, int32_t j) {
   return (j >= r.lo1 && j < r.hi1) || (j >= r.lo2 && j < r.hi2);
 }
@@ -122,6 +133,24 @@ AJ_HD Ranges block_ranges(const MaskGeom& g, int32_t r0, int32_t r1) {
   const Ranges last = row_ranges(g, r1 - 1);
   if (!is_noisy(g, r0)) return Ranges{0, last.hi1, 0, 0};
   return Ranges{0, last.hi1, first.lo2, last.hi2};
+}
+
+// Union of the query sets of keys [k0, k1) (one side, consecutive chunks):
+// along one side both ends of each interval are non-decreasing in the key,
+// so the first key's lower ends and the last key's upper ends bound it.
+AJ_HD Ranges block_col_ranges(const MaskGeom& g, int32_t k0, int32_t k1) {
+  const Ranges first = col_ranges(g, k0);
+  const Ranges last = col_ranges(g, k1 - 1);
+  return Ranges{first.lo1, last.hi1, first.lo2, last.hi2};
+}
+
+// Is [x0, x1) inside one interval of the ranges of every position of a run
+// of consecutive positions on one side (row ranges or column ranges), given
+// the run's first and last ranges?  Both ends of each interval are
+// non-decreasing along the run, so the intersection of the first intervals
+// over the run is [last.lo1, first.hi1), and likewise for the second.
+AJ_HD bool run_covers(const Ranges& first, const Ranges& last, int32_t x0, int32_t x1) {
+  return (x0 >= last.lo1 && x1 <= first.hi1) || (x0 >= last.lo2 && x1 <= first.hi2);
 }
 
 AJ_HD TileSpans block_tiles(const Ranges& u, int32_t block_k) {

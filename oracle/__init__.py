@@ -48,5 +48,6 @@ from .masked_attention import (  # noqa: F401
     useful_flops,
     masked_attention_bwd_slice,
     masked_attention_bwd,
+    masked_attention_bwd_rows,
     backward_useful_flops,
 )

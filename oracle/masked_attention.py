@@ -403,6 +403,49 @@ def masked_attention_bwd(q, k, v, do, desc, scale=None):
     return tuple(out)
 
 
+def masked_attention_bwd_rows(q, k, v, do, desc, rows, scale=None, batch_rows=256):
+    """The same backward restricted to the query rows ``rows`` of one (b, h)
+    slice: float64 (dq [len(rows), d], dk_part [N, d], dv_part [N, dv],
+    delta [len(rows)]), where dk_part and dv_part hold the contributions of
+    these rows only (sum over i in rows of the per-pair terms).  For a key
+    whose attending rows all lie in ``rows`` they are that key's full dk and
+    dv; dq and delta of a row need only that row.  Consecutive rows (in
+    sorted order) with the same allowed keys are taken together, at most
+    ``batch_rows`` at a time."""
+    desc = _as_desc(desc)
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    n, d = q.shape
+    sc = _scale(d, scale)
+    rows = np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((rows.size, d))
+    delta = np.zeros(rows.size)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    order = np.argsort(rows, kind="stable")
+    i = 0
+    while i < order.size:
+        mask = allowed_row(desc, int(rows[order[i]]))
+        j = i + 1
+        while j < order.size and j - i < batch_rows and np.array_equal(allowed_row(desc, int(rows[order[j]])), mask):
+            j += 1
+        sel = order[i:j]
+        rr = rows[sel]
+        keys = np.nonzero(mask)[0]
+        kk, vv = k[keys], v[keys]
+        s = sc * (q[rr] @ kk.T)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        dp = do[rr] @ vv.T
+        dl = (p * dp).sum(axis=1)
+        ds = p * (dp - dl[:, None])
+        dq[sel] = sc * (ds @ kk)
+        dk[keys] += sc * (ds.T @ q[rr])
+        dv[keys] += p.T @ do[rr]
+        delta[sel] = dl
+        i = j
+    return dq, dk, dv, delta
+
+
 def backward_useful_flops(desc, head_dim):
     """2 per multiply-add of the five products over allowed pairs (s, dp, dv,
     dk, dq): 10 d per pair, per (b, h)."""

@@ -10,8 +10,9 @@ Recipe (stand-in for Wan2.1 DiT self-attention activations at 480p with
 
 * one PCG64 stream per (workload seed, config id, tensor, b, h), from
   ``np.random.SeedSequence([20261203, cfg_id, tensor_id, b, h])`` with
-  tensor ids q=0, k=1, v=2, tq=3, tk=4, tv=5, so that any (b, h) slice can
-  be regenerated on its own;
+  tensor ids q=0, k=1, v=2, tq=3, tk=4, tv=5 and, for the backward, the
+  output gradient do=6, so that any (b, h) slice can be regenerated on its
+  own;
 * every slice is ``standard_normal((N, d), float32)``;
 * q and k are RMS-normalised per token over the head dimension when the
   workload asks for it: x / sqrt(mean(x^2) + 1e-6), computed in float32;
@@ -29,6 +30,9 @@ import os
 import numpy as np
 
 TENSORS = ("q", "k", "v", "tq", "tk", "tv")
+# The output gradient of the backward (dL/do): its own stream, id 6.
+GRAD_TENSORS = ("do",)
+_TENSOR_IDS = {t: i for i, t in enumerate(TENSORS + GRAD_TENSORS)}
 ROOT_SEED = 20261203
 
 
@@ -104,7 +108,7 @@ def _stream(w: Workload, tensor_id: int, b: int, h: int) -> np.random.Generator:
 
 def slice_f32(w: Workload, tensor: str, b: int, h: int) -> np.ndarray:
     """One (b, h) slice [N, d] as float32, before any bf16 rounding."""
-    tid = TENSORS.index(tensor)
+    tid = _TENSOR_IDS[tensor]
     x = _stream(w, tid, b, h).standard_normal((w.seq_len, w.head_dim), dtype=np.float32)
     if tensor in ("q", "k") and w.rms_norm_qk:
         ms = np.mean(x * x, axis=1, keepdims=True, dtype=np.float32)

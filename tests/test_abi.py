@@ -6,7 +6,10 @@
 * the plan's tile map (what the kernel streams and masks) equals the
   oracle's tile classification bit for bit, at small sizes with ragged tails
   and at the full workload sizes;
-* pair and tile counts agree with the oracle and with closed forms.
+* pair and tile counts agree with the oracle and with closed forms;
+* the backward's per-key query ranges are the mask's columns bit for bit,
+  its workspace size and useful FLOPs follow their definitions, and its
+  argument errors come before any device call.
 """
 import ctypes
 import os
@@ -34,7 +37,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert len(names) == 11
+    assert len(names) == 15
     lib = ctypes.CDLL(aj.library_path)
     for name in names:
         assert hasattr(lib, name), name
@@ -210,3 +213,52 @@ def test_plan_info_geometry():
     assert info["n_query_blocks"] == 2 * -(-32760 // bq)
     assert info["n_key_tiles"] == -(-65520 // bk)
     assert info["allowed_pairs_per_head"] == 1_124_323_200
+
+
+@pytest.mark.parametrize("desc", SMALL)
+def test_key_ranges_match_oracle_mask_columns(desc):
+    p = aj.attn_jvp_create(desc, 1, 1, 64, aj.ATTN_JVP_BF16)
+    n = p.seq_len
+    assert np.array_equal(_ranges_to_mask(aj.attn_jvp_key_ranges(p), n), oracle.mask_dense(desc).T)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_key_ranges_match_oracle_at_workload_size(cfg):
+    # for sampled rows i: the keys whose query ranges hold i are the row's allowed keys
+    w = WORKLOADS[cfg]
+    p = aj.attn_jvp_create(w.desc, 1, 1, w.head_dim, aj.ATTN_JVP_BF16)
+    kr = aj.attn_jvp_key_ranges(p)
+    rng = np.random.default_rng(100 + cfg)
+    for i in rng.choice(p.seq_len, 48, replace=False):
+        sees = ((i >= kr[:, 0]) & (i < kr[:, 1])) | ((i >= kr[:, 2]) & (i < kr[:, 3]))
+        assert np.array_equal(sees, oracle.allowed_row(w.desc, int(i)))
+
+
+@pytest.mark.parametrize("desc", [(16, 3, 1, 1), (160, 9, 3, 1), (7, 5, 1, 0), (1560, 21, 1, 1), (1560, 21, 3, 1)])
+@pytest.mark.parametrize("dtype, d", [(aj.ATTN_JVP_BF16, 128), (aj.ATTN_JVP_FP32, 64)])
+def test_bwd_workspace_and_flops(desc, dtype, d):
+    b, h = 2, 3
+    p = aj.attn_jvp_create(desc, b, h, d, dtype)
+    assert aj.attn_jvp_bwd_workspace_size(p) == 8 * b * h * p.seq_len
+    assert aj.attn_jvp_plan_bwd_flops(p) == b * h * oracle.backward_useful_flops(MaskDesc(*desc), d)
+
+
+def test_bwd_argument_errors_before_any_device_call():
+    lib = aj._load()
+    p = aj.attn_jvp_create((4, 3, 1, 1), 1, 1, 64, aj.ATTN_JVP_BF16)
+    # q k v o lse d_o dq dk dv workspace: disjoint, aligned fake addresses
+    good = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(10)]
+    assert lib.attn_jvp_bwd(None, *good, None) == 2
+    for i in range(10):
+        bad = list(good)
+        bad[i] = ctypes.c_void_p(0)
+        assert lib.attn_jvp_bwd(p.handle, *bad, None) == 2
+    for i, off in ((0, 8), (5, 2), (9, 2), (7, 4)):
+        bad = list(good)
+        bad[i] = ctypes.c_void_p(good[i].value + off)
+        assert lib.attn_jvp_bwd(p.handle, *bad, None) == 3, i
+    for out, inp in ((6, 0), (8, 5), (9, 4), (7, 8), (9, 6)):
+        bad = list(good)
+        bad[out] = bad[inp]
+        assert lib.attn_jvp_bwd(p.handle, *bad, None) == 1, (out, inp)
+        assert "overlaps" in aj.attn_jvp_last_error_detail()

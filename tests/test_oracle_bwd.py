@@ -82,3 +82,39 @@ def test_backward_invariants(desc):
 def test_backward_useful_flops():
     desc = MaskDesc(1560, 21, 1, 1)
     assert oracle.backward_useful_flops(desc, 128) == 10 * 128 * 1_124_323_200
+
+
+@pytest.mark.parametrize("desc", DESCS + [MaskDesc(5, 6, 2, 1), MaskDesc(7, 4, 1, 0)])
+def test_rows_variant_matches_torch_autograd(desc):
+    # the row-restricted backward against autograd through the dense masked
+    # attention with the gradient confined to the chosen rows (dO = 0 on the
+    # other rows): dq on those rows, dk and dv in full, delta on those rows
+    q, k, v, do = _rand(desc, 8, 31)
+    n = desc.seq_len
+    rng = np.random.default_rng(32)
+    rows = np.sort(rng.choice(n, max(1, n // 3), replace=False))
+    do_r = np.zeros_like(do)
+    do_r[rows] = do[rows]
+    t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v)]
+    sc = 1 / np.sqrt(8)
+    s = (sc * (t[0] @ t[1].T)).masked_fill(~torch.tensor(mask_dense(desc)), float("-inf"))
+    o = torch.softmax(s, dim=-1) @ t[2]
+    o.backward(torch.tensor(do_r))
+    dq, dk, dv, delta = oracle.masked_attention_bwd_rows(q, k, v, do, desc, rows, batch_rows=3)
+    assert _rel(dq, t[0].grad.numpy()[rows]) < 1e-12
+    assert _rel(dk, t[1].grad.numpy()) < 1e-12
+    assert _rel(dv, t[2].grad.numpy()) < 1e-12
+    assert np.max(np.abs(delta - (do[rows] * o.detach().numpy()[rows]).sum(axis=1))) < 1e-12
+
+
+def test_rows_variant_gives_full_gradients_of_keys_seen_only_by_those_rows():
+    # noisy keys of chunk c are seen only by the noisy rows of chunk c
+    desc = MaskDesc(6, 4, 1, 1)
+    q, k, v, do = _rand(desc, 8, 33)
+    full = masked_attention_bwd_slice(q, k, v, do, desc)
+    T, nh = desc.chunk_len, desc.side_len
+    c = 2
+    rows = np.arange(nh + c * T, nh + (c + 1) * T)
+    _, dk, dv, _ = oracle.masked_attention_bwd_rows(q, k, v, do, desc, rows)
+    assert _rel(dk[rows], full[1][rows]) < 1e-12
+    assert _rel(dv[rows], full[2][rows]) < 1e-12
