@@ -14,6 +14,10 @@ counted (partial tiles included), exp and other vector work not counted.
 With --clean-tangent-zero: 4 d per clean-row pair, 8 d per noisy-row /
 clean-key pair, 12 d per noisy-row / noisy-key pair (attn_jvp_plan_flops).
 
+--backward measures the backward instead (attn_jvp_bwd: the dq kernel, then
+the dk/dv kernel, from q, k, v, o, lse and dO on the same plan); useful
+FLOPs = 10 d x (allowed pairs) x B x H (q.k, dO.v, dS k, dS q, P dO).
+
 Prints one JSON line.  --gpus above 1 is refused: this build measures one GPU.
 """
 from __future__ import annotations
@@ -34,8 +38,14 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4 SIMD x 1024 bf16 flop/clk x 2.4 GHz (dense)
 METRIC = "useful TFLOP/s of masked attn fwd+JVP and % of bf16 MFMA peak, 1 GPU"
-KERNEL_SRCS = [os.path.join(ROOT, "masked_attention_jvp_amd", "csrc", f)
-               for f in ("attn_jvp_kernels.hip", "attn_jvp_launch.h", "mask_index.h")]
+METRIC_BWD = "useful TFLOP/s of masked attn backward (dq, dk, dv) and % of bf16 MFMA peak, 1 GPU"
+_CSRC = os.path.join(ROOT, "masked_attention_jvp_amd", "csrc")
+KERNEL_SRCS = {
+    "fwd": [os.path.join(_CSRC, f) for f in ("attn_jvp_kernels.hip", "kernel_common.h", "attn_jvp_launch.h",
+                                               "mask_index.h")],
+    "bwd": [os.path.join(_CSRC, f) for f in ("attn_jvp_bwd_kernels.hip", "kernel_common.h", "attn_jvp_launch.h",
+                                               "mask_index.h")],
+}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -53,6 +63,8 @@ def parse():
     ap.add_argument("--clean-tangent-zero", action="store_true",
                     help="teacher-forcing plans whose clean tokens carry no tangent (useful FLOPs counted "
                          "for that case: about half the general work)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (dq, dk, dv) on the same plan instead of the forward + JVP")
     ap.add_argument("--mode", choices=["attn", "copy"], default="attn",
                     help="copy: a plain 1 GiB device copy, the reference for HBM byte counters")
     return ap.parse_args()
@@ -111,18 +123,19 @@ class SmiSampler(threading.Thread):
                 "sclk_mhz_min": min(v[1] for v in self.samples)}
 
 
-def kernel_hash():
-    """Hash of the code the kernels are built from (comments and blank lines
-    removed), so that counters stay attached to an unchanged kernel."""
+def kernel_hash(part="fwd"):
+    """Hash of the code the kernels of one part (fwd, bwd) are built from
+    (comments and blank lines removed), so that counters stay attached to an
+    unchanged kernel."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for path in KERNEL_SRCS[part]:
         with open(path) as f:
             code = re.sub(r"//[^\n]*", "", f.read())
         h.update("\n".join(l.rstrip() for l in code.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload_name):
+def traffic_for(workload_name, part="fwd"):
     """HBM bytes per launch from committed rocprofv3 counters, if they were
     taken on the current kernel source; else None."""
     try:
@@ -130,9 +143,33 @@ def traffic_for(workload_name):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_code_sha256_16") != kernel_hash() or t.get("workload") != workload_name:
+    if t.get("kernel_code_sha256_16") != kernel_hash(part) or t.get("workload") != workload_name:
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline_bwd(w, heads):
+    """The oracle's backward, untuned, on (b, h) slices of the same workload."""
+    import oracle
+    import seeded_inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    flops = 0
+    elapsed = 0.0
+    for h in range(heads):
+        args = [si.slice_values(w, t, 0, h) for t in ("q", "k", "v", "do")]
+        t0 = time.perf_counter()
+        oracle.masked_attention_bwd_slice(*args, w.desc)
+        elapsed += time.perf_counter() - t0
+        flops += oracle.backward_useful_flops(w.desc, w.head_dim)
+    return {
+        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{heads} of {w.batch * w.heads} (b,h) slices of {w.name} (all rows, backward), fp64 NumPy, "
+                  f"{elapsed:.1f} s",
+    }
 
 
 def cpu_baseline(w, heads, clean_tangent_zero=False):
@@ -182,14 +219,19 @@ def main():
     if args.heads > 0 and args.heads != w.heads:
         w = w.with_(heads=args.heads, name=f"{w.name}_h{args.heads}")
     flags = 0
+    if args.clean_tangent_zero and args.backward:
+        print(json.dumps({"error": "--clean-tangent-zero concerns the forward + JVP only"}))
+        sys.exit(2)
     if args.clean_tangent_zero:
         flags = aj.ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO
         w = w.with_(name=f"{w.name}_ctz")
+    if args.backward:
+        w = w.with_(name=f"{w.name}_bwd")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
     x = {}
-    for t in si.TENSORS:
+    for t in si.TENSORS + (si.GRAD_TENSORS if args.backward else ()):
         bits = si.full_tensor_bits(w, t)
         x[t] = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
         del bits
@@ -197,7 +239,15 @@ def main():
     o = torch.empty_like(x["q"])
     to = torch.empty_like(x["q"])
     lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
-    call = lambda: aj.attn_jvp_fwd(plan, *(x[t] for t in si.TENSORS), o, to, lse)
+    if not args.backward:
+        call = lambda: aj.attn_jvp_fwd(plan, *(x[t] for t in si.TENSORS), o, to, lse)
+    else:
+        # o and lse of these inputs, once, outside the timed region
+        aj.attn_jvp_fwd(plan, *(x[t] for t in si.TENSORS), o, to, lse)
+        del to, x["tq"], x["tk"], x["tv"]
+        dq, dk, dv = (torch.empty_like(x["q"]) for _ in range(3))
+        ws = torch.empty(aj.attn_jvp_bwd_workspace_size(plan) // 4, dtype=torch.float32, device=dev)
+        call = lambda: aj.attn_jvp_bwd(plan, x["q"], x["k"], x["v"], o, lse, x["do"], dq, dk, dv, ws)
 
     for _ in range(args.warmup):
         call()
@@ -226,13 +276,17 @@ def main():
     ms_per_step = total_ms / args.steps
 
     info = plan.info
-    useful = aj.attn_jvp_plan_flops(plan)
+    useful = aj.attn_jvp_plan_bwd_flops(plan) if args.backward else aj.attn_jvp_plan_flops(plan)
     value = useful / (ms_per_step * 1e-3) / 1e12
     achieved = useful / (avg_ms * 1e-3) / 1e12
-    traffic = traffic_for(w.name)
+    part = "bwd" if args.backward else "fwd"
+    traffic = traffic_for(w.name, part)
+    nw = info["block_q"] // 32
+    kernel = (f"bwd_dq_bf16_kernel<{w.head_dim},{nw}> + bwd_dkdv_bf16_kernel<{w.head_dim},{nw}>" if args.backward
+              else f"fwd_bf16_kernel<{w.head_dim},{nw},{'true' if flags else 'false'}>")
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if args.backward else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -243,12 +297,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; q,k RMS-normalised N(0,1), v N(0,1), tangents N(0,%g^2))" % w.tangent_std,
+        "data": ("synthetic (seeded; q,k RMS-normalised N(0,1), v N(0,1), dO N(0,1); o, lse from the forward)"
+                 if args.backward else
+                 "synthetic (seeded; q,k RMS-normalised N(0,1), v N(0,1), tangents N(0,%g^2))" % w.tangent_std),
         "config": {
             "workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
             "head_dim": w.head_dim, "tokens_per_frame": w.tokens_per_frame, "n_frames": w.n_frames,
             "frames_per_chunk": w.frames_per_chunk, "tf_layout": w.tf_layout,
-            "clean_tangent_zero": bool(flags),
+            "clean_tangent_zero": bool(flags), "pass": "backward" if args.backward else "forward+jvp",
         },
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "useful_tflop_per_step": round(useful / 1e12, 4),
@@ -266,12 +322,13 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": f"fwd_bf16_kernel<{w.head_dim},{info['block_q'] // 32},{'true' if flags else 'false'}>",
+            "kernel": kernel,
             "avg_launch_ms": round(avg_ms, 4),
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads, bool(flags))
+        out["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_sample_heads) if args.backward
+                               else cpu_baseline(w, args.cpu_sample_heads, bool(flags)))
     print(json.dumps(out), flush=True)
 
 

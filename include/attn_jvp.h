@@ -141,8 +141,8 @@ int attn_jvp_fwd(const attn_jvp_plan* plan, const void* q, const void* k, const 
  *   workspace         attn_jvp_bwd_workspace_size() bytes of device memory,
  *                     4-byte aligned, owned by the caller; its contents on
  *                     entry are ignored.  On completion it holds, per (b, h),
- *                     N floats delta_i followed by N floats -lse_i log2(e),
- *                     i.e. workspace[(b H + h) 2N + i] = delta_i.
+ *                     N floats -delta_i followed by N floats -lse_i log2(e),
+ *                     i.e. workspace[(b H + h) 2N + i] = -delta_i.
  * Enqueues two kernels on `hip_stream` (the dq kernel, which also fills the
  * workspace, then the dk/dv kernel); no atomics, so results do not depend on
  * scheduling.  No output may overlap an input or another output.  The plan's

@@ -275,7 +275,7 @@ def attn_jvp_fwd(plan: Plan, q, k, v, tq, tk, tv, o, t_o, lse=None, stream=None)
 def attn_jvp_bwd(plan: Plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace, stream=None) -> None:
     """Enqueue the backward (dq, dk, dv) on `stream` (default: torch's current
     stream).  `workspace` is a float32 CUDA tensor of at least
-    attn_jvp_bwd_workspace_size(plan) bytes; on return it holds delta and
+    attn_jvp_bwd_workspace_size(plan) bytes; on return it holds -delta and
     -lse log2(e) per row, [B, H, 2, N]."""
     import torch
     ts = dict(q=q, k=k, v=v, o=o, d_o=d_o, dq=dq, dk=dk, dv=dv)

@@ -12,17 +12,19 @@
 // Two kernels per call, no atomics, so every result is a fixed function of
 // the inputs:
 // * dq kernel: one workgroup per query block with the forward's key-tile
-//   schedule; lane = query.  It also writes delta and -lse log2(e) of its rows
-//   to the workspace.  Per 32-key tile: S^T = K Q^T and dP^T = V dO^T (score
-//   products in vector-register form), P^T = exp2(S^T scale log2(e) -
-//   lse log2(e)), dS^T, then dQ^T += K^T dS^T with K^T from the transposing
-//   LDS read of the K tile.
+//   schedule; lane = query.  It also writes -delta and -lse log2(e) of its
+//   rows to the workspace.  Per 32-key tile: S^T = K Q^T and dP^T - delta =
+//   V dO^T - delta (score products in vector-register form, the second one
+//   started from -delta instead of 0), P^T = exp2(S^T scale log2(e) -
+//   lse log2(e)), dS^T = P^T o (dP^T - delta), then dQ^T += K^T dS^T with K^T
+//   from the transposing LDS read of the K tile.
 // * dk/dv kernel: one workgroup per block of 32 NW keys, cut per side like
 //   the query blocks, over the 32-row query tiles of the rows that attend to
 //   any of its keys (at most two intervals); lane = key.  Per query tile:
 //   X = Q K^T and dP = dO V^T, P, dS, then dV^T += dO^T P and dK^T += Q^T dS
-//   with dO^T and Q^T from the transposing LDS read; delta and lse of the
-//   tile's rows come from the workspace, staged in LDS with the tile.
+//   with dO^T and Q^T from the transposing LDS read; -delta (the start of
+//   the dP product) and -lse log2(e) of the tile's rows come from the
+//   workspace, staged in LDS with the tile.
 // Both follow the forward kernel's structure: 32-row tiles go HBM -> LDS by
 // DMA into a 4-stage ring (XOR-swizzled rows, zeros past the end), the score
 // products of tile j+1 run under the elementwise work of tile j and the
@@ -148,10 +150,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   const bool row_ok = row < r1;
   const Ranges rr = row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0};
 
-  // Q and dO fragments (B operands) stay in registers; delta = dO . O and
-  // -lse log2(e) of the row go to the workspace for the dk/dv kernel.
+  // Q and dO fragments (B operands) stay in accumulation registers; -delta
+  // = -dO . O and -lse log2(e) of the row go to the workspace for the dk/dv
+  // kernel.
   u32x4 qf[KS], dof[KS];
-  float delta, nl;
+  float ndelta, nl;
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)p.q + base, slice_bytes);
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const uint16_t*)p.dout + base, slice_bytes);
@@ -169,11 +172,19 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
         part = fmaf(bf16_hi(dof[s][e]), bf16_hi(of[e]), part);
       }
     }
-    delta = pair_sum(part);
+    ndelta = -pair_sum(part);
     const float lse = row_ok ? p.lse[(size_t)bh * N + row] : 0.f;
     nl = -lse * kLog2e;
-    if (row_ok) p.ws[(size_t)bh * 2 * N + (size_t)h * N + row] = h ? nl : delta;
+    if (row_ok) p.ws[(size_t)bh * 2 * N + (size_t)h * N + row] = h ? nl : ndelta;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      keep_in_acc(qf[s]);
+      keep_in_acc(dof[s]);
+    }
   }
+  f32x16 negd;  // start of the dP^T product: every element of the lane is its row's
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negd[i] = ndelta;
 
   auto stage = [&](auto st) -> uint16_t* {
     constexpr int S = decltype(st)::value;
@@ -250,10 +261,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
     const uint16_t* cur = stage(st);
     u32x4 DS[2];
     u32x4 ktf[NG];
-    auto ds_pair = [&](int jj) {
-      const float a = P[jj] * (DP[jj] - delta);
-      const float b = P[jj + 1] * (DP[jj + 1] - delta);
-      DS[jj >> 3][(jj & 7) >> 1] = pack_bf16(a, b);
+    auto ds_pair = [&](int jj) {  // DP holds dP - delta
+      DS[jj >> 3][(jj & 7) >> 1] = pack_bf16(P[jj] * DP[jj], P[jj + 1] * DP[jj + 1]);
       pin(DS[jj >> 3][(jj & 7) >> 1]);
     };
     auto dma = [&](int s) {
@@ -264,16 +273,16 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
     constexpr int PAIRS = 8 / KS;  // dS element pairs per k-step
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if (s == 0) mfma_v_first(Sn, kf[s], qf[s]);
-      else mfma_v_acc(Sn, kf[s], qf[s]);
+      if (s == 0) mfma_v_first_ba(Sn, kf[s], qf[s]);
+      else mfma_v_acc_ba(Sn, kf[s], qf[s]);
       __builtin_amdgcn_sched_barrier(0);
       if (s + 2 < KS) kvread(nx, s + 2);
       dma(s);
 #pragma unroll
       for (int u = 0; u < PAIRS; ++u) ds_pair(2 * (s * PAIRS + u));
       __builtin_amdgcn_sched_barrier(0);
-      if (s == 0) mfma_v_first(DPn, vf[s], dof[s]);
-      else mfma_v_acc(DPn, vf[s], dof[s]);
+      if (s == 0) mfma_v_init_ba(DPn, vf[s], dof[s], negd);
+      else mfma_v_acc_ba(DPn, vf[s], dof[s]);
       __builtin_amdgcn_sched_barrier(0);
       if (s == KS - 2) ktf[0] = TG::tr_frag(cur, lane, 0);
       if (s == KS - 1) ktf[1] = TG::tr_frag(cur, lane, 1);
@@ -319,11 +328,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
     for (int s = 0; s < KS; ++s) {
       kvread(ring0, s);
       if (s == 0) {
-        mfma_v_first(SA, kf[s], qf[s]);
-        mfma_v_first(DA, vf[s], dof[s]);
+        mfma_v_first_ba(SA, kf[s], qf[s]);
+        mfma_v_init_ba(DA, vf[s], dof[s], negd);
       } else {
-        mfma_v_acc(SA, kf[s], qf[s]);
-        mfma_v_acc(DA, vf[s], dof[s]);
+        mfma_v_acc_ba(SA, kf[s], qf[s]);
+        mfma_v_acc_ba(DA, vf[s], dof[s]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -389,7 +398,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
   __shared__ __attribute__((aligned(1024))) uint16_t ring1[2 * TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t ring2[2 * TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t ring3[2 * TILE];
-  // per stage and wave: delta of the tile's 32 rows, then their -lse log2(e)
+  // per stage and wave: -delta of the tile's 32 rows, then their -lse log2(e)
   __shared__ __attribute__((aligned(256))) float rows0[NW * 64];
   __shared__ __attribute__((aligned(256))) float rows1[NW * 64];
   __shared__ __attribute__((aligned(256))) float rows2[NW * 64];
@@ -415,7 +424,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
   const int slice_bytes = N * D * 2;
   const i32x4_t desc_q = make_desc((const uint16_t*)p.q + base, slice_bytes);
   const i32x4_t desc_do = make_desc((const uint16_t*)p.dout + base, slice_bytes);
-  // the row terms: lanes 0-31 fetch delta, lanes 32-63 -lse log2(e); past
+  // the row terms: lanes 0-31 fetch -delta, lanes 32-63 -lse log2(e); past
   // the end a delta lane reads the next plane (masked rows only) and an
   // lse lane reads zeros
   const i32x4_t desc_ws = make_desc(p.ws + (size_t)bh * 2 * N, N * 8);
@@ -503,7 +512,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
     return run_covers(wfirst, wlast, q0, q0 + BQ);
   };
   // Row terms of the lane's elements 4 q4 .. 4 q4 + 3 (rows 8 q4 + 4h + 0..3):
-  // plane 0 delta, plane 1 -lse log2(e).  Read a quad at a time, shortly
+  // plane 0 -delta, plane 1 -lse log2(e).  Read a quad at a time, shortly
   // before use, to keep few of them live.
   auto rows_read = [&](const float* src, int plane, int q4, float* dst) {
     const float4 v = *(const float4*)(src + 32 * plane + 8 * q4 + 4 * h);
@@ -521,6 +530,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
 
   f32x16 XA, DA, XB, DB;
   float nlv[16];  // -lse log2(e) of the rows of the tile being exponentiated
+  float ndl[16];  // -delta of the rows of the tile whose dP is formed next: its start
 
   // Step j.  Phase 1: X, dP of tile j+1 under dS of tile j and the packs of
   // P and dS.  Phase 2: dV^T += dO^T P and dK^T += Q^T dS of tile j under
@@ -540,11 +550,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
     const uint16_t* cur = stage(st);
     u32x4 PK[2], DSK[2];
     u32x4 doT[NG], qT[NG];
-    float dl[16];
-    auto ds_pair = [&](int jj) {
-      const float a = P[jj] * (DP[jj] - dl[jj]);
-      const float b = P[jj + 1] * (DP[jj + 1] - dl[jj + 1]);
-      DSK[jj >> 3][(jj & 7) >> 1] = pack_bf16(a, b);
+    auto ds_pair = [&](int jj) {  // DP holds dP - delta
+      DSK[jj >> 3][(jj & 7) >> 1] = pack_bf16(P[jj] * DP[jj], P[jj + 1] * DP[jj + 1]);
       PK[jj >> 3][(jj & 7) >> 1] = pack_bf16(P[jj], P[jj + 1]);
       pin(DSK[jj >> 3][(jj & 7) >> 1]);
       pin(PK[jj >> 3][(jj & 7) >> 1]);
@@ -559,35 +566,21 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
         issue_part(stage(AH{}), rstage(AH{}), j + 3, q, t_end);
     };
 
-    // dS pairs of k-step s (none at s = 0, while the first deltas are read)
-    auto pair_lo = [](int s) { return s == 0 ? 0 : (8 * (s - 1)) / (KS - 1); };
-    auto pair_hi = [&](int s) { return s + 1 < KS ? pair_lo(s + 1) : 8; };
+    constexpr int PAIRS = 8 / KS;  // dS element pairs per k-step
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (s == 0) mfma_v_first_ba(Xn, qf[s], kf[s]);
       else mfma_v_acc_ba(Xn, qf[s], kf[s]);
       __builtin_amdgcn_sched_barrier(0);
-      // delta quads needed by the pairs of k-steps s+1 (s = 0: also s+1's)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int first_pair = 2 * q4;  // pairs 2 q4, 2 q4 + 1 use quad q4
-        const int need = [&] {
-          for (int t = 1; t < KS; ++t)
-            if (first_pair < pair_hi(t)) return t;
-          return KS - 1;
-        }();
-        if (need - 1 == s || (s == 0 && need == 1)) rows_read(rstage(st), 0, q4, dl);
-      }
       if (s + 2 < KS) qdread(nx, s + 2);
       dma(s);
-      if (s > 0) {
 #pragma unroll
-        for (int u = pair_lo(s); u < pair_hi(s); ++u) ds_pair(2 * u);
-      }
+      for (int u = 0; u < PAIRS; ++u) ds_pair(2 * (s * PAIRS + u));
       __builtin_amdgcn_sched_barrier(0);
-      if (s == 0) mfma_v_first_ba(DPn, dof[s], vf[s]);
+      if (s == 0) mfma_v_init_ba(DPn, dof[s], vf[s], *(const f32x16*)ndl);
       else mfma_v_acc_ba(DPn, dof[s], vf[s]);
       __builtin_amdgcn_sched_barrier(0);
+      if (s == 1) hold(*(const f32x16*)ndl);  // two MFMAs past its read as the start of dP
       if (s == KS - 2) trread(0);
       if (s == KS - 1) {
         trread(1);
@@ -628,7 +621,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
           const int first = (4 * q4) * 2 * NG / 16;
           if (u == (first >= 3 ? first - 3 : 0)) rows_read(rstage(NX{}), 1, q4, nlv);
         }
-        if (u == UB + 1) qdread(stage(N2{}), 0);
+        if (u == UB + 1) {
+          qdread(stage(N2{}), 0);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) rows_read(rstage(N2{}), 0, q4, ndl);  // for the next step's dP
+        }
         if (u == UB + 2) qdread(stage(N2{}), 1);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -642,17 +639,21 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
     wait_vmcnt<LPT>();  // first two tiles
     barrier_nofence();
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) rows_read(rstage(IC<0>{}), 1, q4, nlv);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      rows_read(rstage(IC<0>{}), 1, q4, nlv);
+      rows_read(rstage(IC<0>{}), 0, q4, ndl);
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       qdread(ring0, s);
       if (s == 0) {
         mfma_v_first_ba(XA, qf[s], kf[s]);
-        mfma_v_first_ba(DA, dof[s], vf[s]);
+        mfma_v_init_ba(DA, dof[s], vf[s], *(const f32x16*)ndl);
       } else {
         mfma_v_acc_ba(XA, qf[s], kf[s]);
         mfma_v_acc_ba(DA, dof[s], vf[s]);
       }
+      if (s == 1) hold(*(const f32x16*)ndl);
     }
     __builtin_amdgcn_sched_barrier(0);
     acc_hazard_wait();
@@ -662,6 +663,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
     for (int i = 0; i < 16; ++i) XA[i] = __builtin_amdgcn_exp2f(fmaf(XA[i], sl2, nlv[i]));
     qdread(ring1, 0);
     qdread(ring1, 1);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) rows_read(rstage(IC<1>{}), 0, q4, ndl);
   };
 
   if (ntiles > 0) {
@@ -745,7 +748,7 @@ __global__ void __launch_bounds__(256) bwd_dq_fp32_kernel(BwdParams p) {
   }
   const float delta = sum8(part);
   const float nl = -p.lse[(size_t)bh * N + qrow] * kLog2e;
-  if (row_ok && slice < 2) p.ws[(size_t)bh * 2 * N + (size_t)slice * N + row] = slice ? nl : delta;
+  if (row_ok && slice < 2) p.ws[(size_t)bh * 2 * N + (size_t)slice * N + row] = slice ? nl : -delta;
   const float sl2 = p.score_log2;
   for (int it = 0; it < ntiles; ++it) {
     const int k0 = span_tile(sp, it) * BC;
@@ -791,8 +794,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_fp32_kernel(BwdParams p) {
   const size_t base = (size_t)bh * (size_t)N * D;
   const float* __restrict__ Q = (const float*)p.q + base + slice * E;
   const float* __restrict__ dO = (const float*)p.dout + base + slice * E;
-  const float* __restrict__ dl = p.ws + (size_t)bh * 2 * N;
-  const float* __restrict__ nlr = dl + N;
+  const float* __restrict__ ndl = p.ws + (size_t)bh * 2 * N;  // -delta
+  const float* __restrict__ nlr = ndl + N;
   const int krow = key_ok ? key : k0;
   float kk[E], vv[E], ak[E], av[E];
 #pragma unroll
@@ -819,7 +822,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_fp32_kernel(BwdParams p) {
       s = sum8(s);
       dp = sum8(dp);
       const float pij = exp2f(fmaf(s, sl2, nlr[i]));
-      const float ds = pij * (dp - dl[i]);
+      const float ds = pij * (dp + ndl[i]);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         av[e] = fmaf(pij, doi[e], av[e]);

@@ -160,12 +160,21 @@ __device__ __forceinline__ void mfma_v_first_ba(f32x16& d, u32x4 a, u32x4 b) {
 __device__ __forceinline__ void mfma_v_acc_ba(f32x16& d, u32x4 a, u32x4 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
+// First product of a chain started from c instead of 0 (d = a b + c; c kept).
+__device__ __forceinline__ void mfma_v_init_ba(f32x16& d, u32x4 a, u32x4 b, const f32x16& c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+}
 
 // Pin a value to this point of the instruction stream: it must be computed
 // before the (volatile, hence ordered) empty asm, so the compiler cannot sink
 // it into a later block.  Emits no instruction.
 __device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void pin(uint32_t x) { asm volatile("" ::"v"(x)); }
+// Keep the start value c of an MFMA chain (mfma_v_init_ba) allocated until
+// this point: the compiler does not know that the matrix core reads it over
+// several passes after issue, and would reuse its registers at once.  Place
+// it after two further MFMAs.
+__device__ __forceinline__ void hold(const f32x16& c) { asm volatile("" ::"v"(c)); }
 
 // Workgroup barrier without a memory fence: the fence of __syncthreads()
 // would wait for every LDS DMA in flight.  Visibility of the tile about to be

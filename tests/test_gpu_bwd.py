@@ -6,9 +6,9 @@ forward is checked against the oracle elsewhere); the oracle computes the
 backward from q, k, v and dO alone.  Tolerances (normwise relative error
 over a slice): bf16 1e-2 -- inputs, P and dS enter the matrix cores rounded
 to bf16 (relative 2^-9 each) and o is the forward's bf16 output, which
-enters delta; fp32 1e-4.  The workspace's delta is compared with the
-oracle's delta (bf16: 1e-2 normwise; fp32: 1e-5) and its second plane with
--lse log2(e) of the library's own lse (exact up to one rounding).
+enters delta; fp32 1e-4.  The workspace's first plane (-delta) is compared
+with the oracle's delta (bf16: 1e-2 normwise; fp32: 1e-5) and its second
+plane with -lse log2(e) of the library's own lse (exact up to one rounding).
 """
 import numpy as np
 import pytest
@@ -62,7 +62,7 @@ def _full_parity(w):
     for b in range(w.batch):
         for h in range(w.heads):
             rq, rk, rv, rd = oracle.masked_attention_bwd_slice(*_slices(w, b, h), w.desc)
-            e = [rel_err(dq[b, h], rq), rel_err(dk[b, h], rk), rel_err(dv[b, h], rv), rel_err(ws[b, h, 0], rd)]
+            e = [rel_err(dq[b, h], rq), rel_err(dk[b, h], rk), rel_err(dv[b, h], rv), rel_err(-ws[b, h, 0], rd)]
             worst = np.maximum(worst, e)
             assert np.isfinite(dq[b, h]).all() and np.isfinite(dk[b, h]).all() and np.isfinite(dv[b, h]).all()
             nl = -lse[b, h].astype(np.float32) * np.float32(LOG2E)
@@ -125,7 +125,7 @@ def test_bwd_workload_sampled(cfg):
         sl = _slices(w, b, h)
         rq, _, _, rd = oracle.masked_attention_bwd_rows(*sl, w.desc, rows)
         e_q = rel_err(to_f64(dq[b, h, rows]), rq)
-        e_d = rel_err(to_f64(ws[b, h, 0, rows]), rd)
+        e_d = rel_err(-to_f64(ws[b, h, 0, rows]), rd)
         log(f"    ({b},{h}) {len(rows)} rows: dq {e_q:.3e} delta {e_d:.3e}")
         assert e_q < TOL["bf16"] and e_d < DELTA_TOL["bf16"]
         for side in range(2 if w.tf_layout else 1):
