@@ -154,6 +154,25 @@ int attn_jvp_bwd(const attn_jvp_plan* plan, const void* q, const void* k, const 
 /* Workspace bytes attn_jvp_bwd needs for the plan: 8 B H N. */
 int attn_jvp_bwd_workspace_size(const attn_jvp_plan* plan, size_t* bytes);
 
+/* Geometry of the backward: rows per dq-kernel block and query blocks per
+ * (b, h) (the dq kernel walks the forward's key tiles for each), keys per
+ * dk/dv-kernel block and key blocks per (b, h).  Key blocks are cut per side
+ * like query blocks (clean side from key 0, noisy side from key N_h); a key
+ * block streams the 32-row query tiles of the rows that attend to any of its
+ * keys (attn_jvp_key_ranges).  Any output pointer may be NULL. */
+int attn_jvp_plan_bwd_info(const attn_jvp_plan* plan, int32_t* block_q, int32_t* block_kv,
+                           int32_t* n_query_blocks, int32_t* n_key_blocks);
+
+/* Launch order of the dk/dv kernel: workgroup b (0 <= b < B H n_key_blocks)
+ * processes task host_out[b], i.e. (b, h) slice task / n_key_blocks and key
+ * block task mod n_key_blocks.  Tasks are heavy first (the earliest keys of a
+ * side are seen by the most rows); workgroups are handed to the 8 XCDs round
+ * robin, and each round of 128 workgroups gives each XCD a group of 16
+ * neighbouring key blocks, which stream nearly the same query tiles through
+ * that XCD's L2, the group-to-XCD direction alternating from round to round.
+ * n is the capacity of host_out in int32 elements. */
+int attn_jvp_bwd_launch_order(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
+
 /* Useful floating-point operations of one attn_jvp_bwd call (all B * H
  * heads): 10 d per allowed (query, key) pair, i.e. 2 per multiply-add of the
  * five products q.k, dO.v, dS k, dS q and P dO (the dq kernel recomputes the

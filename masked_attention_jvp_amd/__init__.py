@@ -8,8 +8,9 @@ mirror the C ABI of ``include/attn_jvp.h`` one to one:
     attn_jvp_create, attn_jvp_create_ex, attn_jvp_fwd, attn_jvp_bwd,
     attn_jvp_bwd_workspace_size, attn_jvp_destroy, attn_jvp_error_string,
     attn_jvp_last_error_detail, attn_jvp_plan_info, attn_jvp_plan_flops,
-    attn_jvp_plan_bwd_flops, attn_jvp_launch_order, attn_jvp_row_ranges,
-    attn_jvp_key_ranges, attn_jvp_tile_map
+    attn_jvp_plan_bwd_flops, attn_jvp_plan_bwd_info, attn_jvp_launch_order,
+    attn_jvp_bwd_launch_order, attn_jvp_row_ranges, attn_jvp_key_ranges,
+    attn_jvp_tile_map
 
 plus ``masked_attention_jvp(...)`` and ``masked_attention_bwd(...)``, which
 allocate the outputs (and the backward's workspace) and call ``attn_jvp_fwd``
@@ -31,6 +32,7 @@ __all__ = [
     "attn_jvp_error_string", "attn_jvp_last_error_detail", "attn_jvp_plan_info", "attn_jvp_plan_flops",
     "attn_jvp_launch_order", "attn_jvp_row_ranges", "attn_jvp_tile_map", "masked_attention_jvp",
     "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops", "attn_jvp_key_ranges",
+    "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order",
     "masked_attention_bwd",
 ]
 
@@ -88,10 +90,12 @@ def _load():
         lib.attn_jvp_bwd_workspace_size.argtypes = [vp, P(ctypes.c_size_t)]
         lib.attn_jvp_plan_bwd_flops.argtypes = [vp, P(i64)]
         lib.attn_jvp_key_ranges.argtypes = [vp, P(i32), ctypes.c_size_t]
+        lib.attn_jvp_plan_bwd_info.argtypes = [vp, P(i32), P(i32), P(i32), P(i32)]
+        lib.attn_jvp_bwd_launch_order.argtypes = [vp, P(i32), ctypes.c_size_t]
         for name in ("attn_jvp_create", "attn_jvp_create_ex", "attn_jvp_fwd", "attn_jvp_destroy",
                      "attn_jvp_plan_info", "attn_jvp_plan_flops", "attn_jvp_launch_order", "attn_jvp_row_ranges",
                      "attn_jvp_tile_map", "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops",
-                     "attn_jvp_key_ranges"):
+                     "attn_jvp_key_ranges", "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -197,6 +201,22 @@ def attn_jvp_key_ranges(plan: Plan) -> np.ndarray:
     out = np.empty((n, 4), dtype=np.int32)
     _check(_load().attn_jvp_key_ranges(plan.handle, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), out.size),
            "attn_jvp_key_ranges")
+    return out
+
+
+def attn_jvp_plan_bwd_info(plan: Plan) -> dict:
+    """Backward geometry: dq block rows, dk/dv block keys, blocks per (b, h)."""
+    vals = [ctypes.c_int32() for _ in range(4)]
+    _check(_load().attn_jvp_plan_bwd_info(plan.handle, *[ctypes.byref(v) for v in vals]), "attn_jvp_plan_bwd_info")
+    return dict(zip(["block_q", "block_kv", "n_query_blocks", "n_key_blocks"], [v.value for v in vals]))
+
+
+def attn_jvp_bwd_launch_order(plan: Plan) -> np.ndarray:
+    """Task (b*H + h) * n_key_blocks + key block of each dk/dv workgroup."""
+    n = plan.batch * plan.heads * attn_jvp_plan_bwd_info(plan)["n_key_blocks"]
+    out = np.empty(n, dtype=np.int32)
+    _check(_load().attn_jvp_bwd_launch_order(plan.handle, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n),
+           "attn_jvp_bwd_launch_order")
     return out
 
 

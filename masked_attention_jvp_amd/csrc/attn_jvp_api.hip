@@ -328,6 +328,16 @@ int attn_jvp_bwd(const attn_jvp_plan* p, const void* q, const void* k, const voi
   return ok();
 }
 
+int attn_jvp_plan_bwd_info(const attn_jvp_plan* p, int32_t* block_q, int32_t* block_kv, int32_t* n_query_blocks,
+                           int32_t* n_key_blocks) {
+  if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
+  if (block_q) *block_q = p->bwd_block_q;
+  if (block_kv) *block_kv = p->bwd_block_kv;
+  if (n_query_blocks) *n_query_blocks = p->bwd_n_qblocks;
+  if (n_key_blocks) *n_key_blocks = p->bwd_n_kblocks;
+  return ok();
+}
+
 int attn_jvp_plan_bwd_flops(const attn_jvp_plan* p, int64_t* useful_flops) {
   if (p == nullptr || useful_flops == nullptr) return fail(ATTN_JVP_E_NULL, "plan and useful_flops must be non-NULL");
   *useful_flops = p->bwd_useful_flops;
@@ -389,6 +399,14 @@ int attn_jvp_launch_order(const attn_jvp_plan* p, int32_t* out, size_t n) {
     return fail(ATTN_JVP_E_INVALID, "host_out holds %zu int32, need %d", n, p->n_qblocks);
   const bool balanced = (p->flags & ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO) != 0;
   for (int32_t t = 0; t < p->n_qblocks; ++t) out[t] = heavy_first_qblock(p->g, p->block_q, t, balanced);
+  return ok();
+}
+
+int attn_jvp_bwd_launch_order(const attn_jvp_plan* p, int32_t* out, size_t n) {
+  if (p == nullptr || out == nullptr) return fail(ATTN_JVP_E_NULL, "plan and host_out must be non-NULL");
+  const int64_t total = (int64_t)p->batch * p->heads * p->bwd_n_kblocks;
+  if (n < (size_t)total) return fail(ATTN_JVP_E_INVALID, "host_out holds %zu int32, need %lld", n, (long long)total);
+  for (int32_t b = 0; b < (int32_t)total; ++b) out[b] = xcd_grouped(b, (int32_t)total, kDkdvXcdGroup);
   return ok();
 }
 

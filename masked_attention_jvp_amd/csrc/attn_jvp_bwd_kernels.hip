@@ -245,11 +245,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   f32x16 SA, DA, SB, DB;
 
   // Step j.  Phase 1: S^T, dP^T of tile j+1 under dS of tile j and its
-  // packs.  Phase 2: dQ^T += K^T dS^T of tile j under the mask (partial tiles)
-  // and exponentials of tile j+1.  Ring: step j reads K, V of tile j+1 and
-  // K^T of tile j, and issues the DMA of tile j+3 into the stage of tile j-1;
-  // the barrier follows the last read of tile j's stage, after each wave's
-  // share of tile j+2 has landed; the first K, V reads of tile j+2 follow it.
+  // packs, and all transposed K reads of tile j.  Phase 2: dQ^T += K^T dS^T
+  // of tile j under the mask (partial tiles) and exponentials of tile j+1.
+  // Ring: step j reads K, V of tile j+1 and K^T of tile j, and issues the DMA
+  // of tile j+3 into the stage of tile j-1; the barrier opens phase 2 (every
+  // read of tile j's stage is then issued), after each wave's share of tile
+  // j+2 has landed; the first K, V reads of tile j+2 follow it, seven MFMAs
+  // ahead of their use.
   auto step = [&](auto st, int j, int t_end, f32x16& P, f32x16& DP, f32x16& Sn, f32x16& DPn) {
     constexpr int ST = decltype(st)::value;
     using NX = IC<(ST + 1) % STAGES>;
@@ -284,8 +286,9 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
       if (s == 0) mfma_v_init_ba(DPn, vf[s], dof[s], negd);
       else mfma_v_acc_ba(DPn, vf[s], dof[s]);
       __builtin_amdgcn_sched_barrier(0);
-      if (s == KS - 2) ktf[0] = TG::tr_frag(cur, lane, 0);
-      if (s == KS - 1) ktf[1] = TG::tr_frag(cur, lane, 1);
+#pragma unroll
+      for (int gq = 0; gq < NG; ++gq)
+        if (gq * KS / NG == s) ktf[gq] = TG::tr_frag(cur, lane, gq);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -296,8 +299,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
       accQ[c] = mfma_bf16(ktf[gidx], DS[c2], accQ[c]);
       __builtin_amdgcn_sched_barrier(0);
       if (gidx == 0 && !tile_whole(j + 1)) mask_scores(Sn, span_tile(sp, j + 1) * BC, h, rr);  // rare
-      if (gidx + 2 < NG) ktf[gidx + 2] = TG::tr_frag(cur, lane, gidx + 2);
-      if (gidx == NG - 2) {
+      if (gidx == 0) {
         // every read of tile j's stage is issued; tile j+2 has landed here
         wait_lgkmcnt<0>();
         wait_vmcnt<LPT>();
@@ -310,10 +312,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
           pin(Sn[k]);
         }
       }
-      if (gidx == NG - 1) {
-        kvread(stage(N2{}), 0);
-        kvread(stage(N2{}), 1);
-      }
+      if (gidx == 1) kvread(stage(N2{}), 0);
+      if (gidx == 2) kvread(stage(N2{}), 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -411,10 +411,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
 
   const MaskGeom g = p.g;
   const int N = g.seq_len;
-  const int bh = blockIdx.x / p.n_kblocks;
   // Key blocks are cut per side like query blocks; index order is heavy
-  // first (the earliest keys of a side are seen by the most rows).
-  const int kb = blockIdx.x - bh * p.n_kblocks;
+  // first (the earliest keys of a side are seen by the most rows).  Groups of
+  // 16 neighbouring key blocks, which stream nearly the same query tiles, run
+  // on one XCD (a quarter of the fetches past L2 of plain round robin).
+  const int task = xcd_grouped((int)blockIdx.x, (int)gridDim.x, kDkdvXcdGroup);
+  const int bh = task / p.n_kblocks;
+  const int kb = task - bh * p.n_kblocks;
   int k0, k1;
   qblock_rows(g, BK, kb, &k0, &k1);
   const TileSpans sp = block_tiles(block_col_ranges(g, k0, k1), BQ);
@@ -581,17 +584,19 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
       else mfma_v_acc_ba(DPn, dof[s], vf[s]);
       __builtin_amdgcn_sched_barrier(0);
       if (s == 1) hold(*(const f32x16*)ndl);  // two MFMAs past its read as the start of dP
-      if (s == KS - 2) trread(0);
+      if (s == KS - 3) trread(0);
+      if (s == KS - 2) trread(1);
       if (s == KS - 1) {
-        trread(1);
+        trread(2);
         rows_read(rstage(NX{}), 1, 0, nlv);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
 
     // phase 2: 2 NG slots; the last score product is two MFMAs back at the
-    // first one
-    constexpr int UB = 2 * (NG - 2);  // slot of the barrier
+    // first one.  Transposed reads run three groups ahead, so the barrier
+    // comes four slots before the end and the first reads of tile j+2 three.
+    constexpr int UB = 2 * (NG - 3);  // slot of the barrier
 #pragma unroll
     for (int gidx = 0; gidx < NG; ++gidx) {
       const int c2 = gidx / DC, c = gidx % DC;
@@ -602,7 +607,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
         __builtin_amdgcn_sched_barrier(0);
         const int u = 2 * gidx + sl;
         if (u == 0 && !tile_whole(j + 1)) mask_scores(Xn, span_tile(sp, j + 1) * BQ, h, cr);  // rare
-        if (sl == 0 && gidx + 2 < NG) trread(gidx + 2);
+        if (sl == 0 && gidx + 3 < NG) trread(gidx + 3);
         if (u == UB) {
           wait_lgkmcnt<0>();
           wait_vmcnt<LPT>();

@@ -57,6 +57,9 @@ hipError_t launch_fwd(int dtype, int head_dim, int grid, const FwdParams& p, hip
 // Rows per dq-kernel block and keys per dk/dv-kernel block of the backward.
 void bwd_block_sizes(int dtype, int head_dim, int* block_q, int* block_kv);
 
+// Key blocks per XCD group of the dk/dv kernel's launch order (xcd_grouped).
+constexpr int kDkdvXcdGroup = 16;
+
 // Launch the backward (dq kernel, then dk/dv kernel) for bh = B * H slices.
 hipError_t launch_bwd(int dtype, int head_dim, int bh, const BwdParams& p, hipStream_t stream);
 

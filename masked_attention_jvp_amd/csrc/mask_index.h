@@ -127,6 +127,24 @@ AJ_HD int32_t heavy_first_qblock(const MaskGeom& g, int32_t block_q, int32_t t, 
   return (u & 1) * nbs + (rem - 1 - (u >> 1));
 }
 
+// XCD-aware launch order: workgroup b of a grid of `total` runs logical task
+// xcd_grouped(b).  Workgroups are handed to the 8 XCDs round robin (b mod 8),
+// and each XCD has its own L2.  Within every round of 8 G workgroups the
+// XCDs take groups of G consecutive logical tasks, so tasks that stream the
+// same tiles (neighbouring blocks of one chunk) share an L2.  The rounds keep
+// the logical (heavy-first) order, and the group-to-XCD direction alternates
+// from round to round (XCD x takes group x, then group 7 - x), so that work
+// that falls along the logical order is spread evenly over the XCDs.  The
+// last total mod 8 G workgroups keep their index.
+AJ_HD int32_t xcd_grouped(int32_t b, int32_t total, int32_t G) {
+  const int32_t round = 8 * G;
+  const int32_t r = b / round;
+  if ((r + 1) * round > total) return b;
+  const int32_t u = b - r * round;
+  const int32_t x = (r & 1) ? 7 - (u & 7) : (u & 7);  // snake: the direction alternates by round
+  return r * round + x * G + (u >> 3);
+}
+
 // Union of the key sets of rows [r0, r1) (one side, consecutive chunks).
 AJ_HD Ranges block_ranges(const MaskGeom& g, int32_t r0, int32_t r1) {
   const Ranges first = row_ranges(g, r0);
