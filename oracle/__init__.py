@@ -20,7 +20,12 @@ Sources (Causal-rCM, arXiv 2606.25473):
 * section 3.1.2 (teacher-forcing sCM, after eq. 17): the clean context
   carries zero tangent, only the noisy tokens move;
 * section 3.2.1 (FlashAttention-2 based kernel with custom masks): the
-  backward of the same masked attention, for training the student.
+  backward of the same masked attention, for training the student;
+* Appendix B, "sparse custom mask representation": masks as query groups
+  (contiguous query intervals) with lists of allowed key intervals
+  (``RangeMask``); section 4 (cA-B chunk patterns with an initial chunk of
+  another size, ``ChunkListDesc``) and section 4.2.2 / Figure 9 (an
+  understanding / generation layout) give the range masks exercised.
 
 Parity pins (see ``tests/test_oracle_*.py``): hand-written golden masks,
 closed-form pair counts, finite differences, ``torch.func.jvp`` on dense
@@ -30,6 +35,8 @@ has at least one pin.
 """
 from .masked_attention import (  # noqa: F401
     MaskDesc,
+    ChunkListDesc,
+    RangeMask,
     allowed,
     allowed_row,
     mask_dense,

@@ -58,8 +58,40 @@ class MaskDesc:
         return self.n_frames // self.frames_per_chunk
 
 
-def _as_desc(desc) -> MaskDesc:
-    return desc if isinstance(desc, MaskDesc) else MaskDesc(*desc)
+@dataclass(frozen=True)
+class ChunkListDesc:
+    """Teacher-forcing / block-causal mask whose chunks have arbitrary sizes
+    (section 4: a cA-B pattern is an initial chunk of A latent frames, then
+    chunks of B frames).  ``chunk_lens`` are the chunk lengths in tokens of
+    one side, in order; the rule is that of ``MaskDesc`` with chunk index
+    taken from these boundaries."""
+    chunk_lens: tuple
+    tf_layout: int
+
+    @property
+    def side_len(self) -> int:
+        return int(sum(self.chunk_lens))
+
+    @property
+    def seq_len(self) -> int:
+        return self.side_len * (2 if self.tf_layout else 1)
+
+
+@dataclass(frozen=True)
+class RangeMask:
+    """Query groups x key intervals (Appendix B, sparse custom mask
+    representation): each group is a contiguous query interval with a list
+    of allowed key intervals; query i may see key j iff i lies in a group one
+    of whose intervals holds j.  Rows in no group see no key.
+    ``groups`` = ((row_lo, row_hi, ((key_lo, key_hi), ...)), ...), half-open."""
+    seq_len: int
+    groups: tuple
+
+
+def _as_desc(desc):
+    if isinstance(desc, (MaskDesc, ChunkListDesc, RangeMask)):
+        return desc
+    return MaskDesc(*desc)
 
 
 # ----------------------------------------------------------------------------
@@ -74,11 +106,41 @@ def _side_and_chunk(desc: MaskDesc, idx):
     return noisy, pos // desc.chunk_len
 
 
+def _chunklist_side_and_chunk(desc: ChunkListDesc, idx):
+    idx = np.asarray(idx, dtype=np.int64)
+    noisy = (idx >= desc.side_len) if desc.tf_layout else np.zeros(idx.shape, dtype=bool)
+    pos = idx % desc.side_len
+    starts = np.cumsum((0,) + tuple(desc.chunk_lens))[:-1]
+    return noisy, np.searchsorted(starts, pos, side="right") - 1
+
+
+def _range_group(desc: RangeMask, idx):
+    """Group index of each query row (-1: in no group)."""
+    idx = np.asarray(idx, dtype=np.int64)
+    out = np.full(idx.shape, -1, dtype=np.int64)
+    for g, (lo, hi, _) in enumerate(desc.groups):
+        out[(idx >= lo) & (idx < hi)] = g
+    return out
+
+
 def allowed(desc, i, j):
     """allowed(i, j): may query token i attend to key token j?  (broadcasts)"""
     desc = _as_desc(desc)
-    qi_noisy, qi_chunk = _side_and_chunk(desc, i)
-    kj_noisy, kj_chunk = _side_and_chunk(desc, j)
+    if isinstance(desc, RangeMask):
+        i, j = np.broadcast_arrays(np.asarray(i, dtype=np.int64), np.asarray(j, dtype=np.int64))
+        g = _range_group(desc, i)
+        out = np.zeros(i.shape, dtype=bool)
+        for gi, (_, _, ivs) in enumerate(desc.groups):
+            sel = g == gi
+            for lo, hi in ivs:
+                out |= sel & (j >= lo) & (j < hi)
+        return out
+    if isinstance(desc, ChunkListDesc):
+        qi_noisy, qi_chunk = _chunklist_side_and_chunk(desc, i)
+        kj_noisy, kj_chunk = _chunklist_side_and_chunk(desc, j)
+    else:
+        qi_noisy, qi_chunk = _side_and_chunk(desc, i)
+        kj_noisy, kj_chunk = _side_and_chunk(desc, j)
     clean_row = (~qi_noisy) & (~kj_noisy) & (kj_chunk <= qi_chunk)
     noisy_row = qi_noisy & (((~kj_noisy) & (kj_chunk < qi_chunk)) | (kj_noisy & (kj_chunk == qi_chunk)))
     return clean_row | noisy_row
@@ -98,20 +160,45 @@ def allowed_row(desc, i: int) -> np.ndarray:
 
 
 def row_groups(desc):
-    """Rows that share one (side, chunk) pair, as (first row, stop row).
+    """Rows that share one key set, as (first row, stop row), covering all
+    rows: one (side, chunk) pair of a chunked mask; one query group of a
+    range mask, and the runs of rows in no group.
 
-    ``allowed(i, j)`` depends on i only through its side and chunk, so the
-    rows of one group share one key set; grouping them is vectorisation of
-    the definition, not a different algorithm.
+    ``allowed(i, j)`` depends on i only through its side and chunk (or its
+    group), so the rows of one group share one key set; grouping them is
+    vectorisation of the definition, not a different algorithm.
     """
     desc = _as_desc(desc)
+    if isinstance(desc, RangeMask):
+        out, at = [], 0
+        for lo, hi, _ in sorted(desc.groups):
+            if lo > at:
+                out.append((at, lo))
+            out.append((lo, hi))
+            at = hi
+        if at < desc.seq_len:
+            out.append((at, desc.seq_len))
+        return out
     sides = 2 if desc.tf_layout else 1
+    lens = desc.chunk_lens if isinstance(desc, ChunkListDesc) else (desc.chunk_len,) * desc.n_chunks
     out = []
     for s in range(sides):
-        for c in range(desc.n_chunks):
-            lo = s * desc.side_len + c * desc.chunk_len
-            out.append((lo, lo + desc.chunk_len))
+        lo = s * desc.side_len
+        for t in lens:
+            out.append((lo, lo + t))
+            lo += t
     return out
+
+
+def _row_key(desc, rows):
+    """A hashable label per row; rows with one label share one key set."""
+    if isinstance(desc, RangeMask):
+        return [(int(g),) for g in np.atleast_1d(_range_group(desc, rows))]
+    if isinstance(desc, ChunkListDesc):
+        noisy, chunk = _chunklist_side_and_chunk(desc, rows)
+    else:
+        noisy, chunk = _side_and_chunk(desc, rows)
+    return list(zip(np.atleast_1d(noisy).tolist(), np.atleast_1d(chunk).tolist()))
 
 
 def pair_count(desc) -> int:
@@ -130,8 +217,12 @@ def pair_count(desc) -> int:
 # ----------------------------------------------------------------------------
 
 def query_blocks(desc, block_q: int):
-    """Query blocks as (start, stop): each side is cut from its own start."""
+    """Query blocks as (start, stop): each side is cut from its own start; a
+    range mask is cut from row 0 over the whole sequence."""
     desc = _as_desc(desc)
+    if isinstance(desc, RangeMask):
+        n = desc.seq_len
+        return [(lo, min(lo + block_q, n)) for lo in range(0, n, block_q)]
     sides = 2 if desc.tf_layout else 1
     out = []
     for s in range(sides):
@@ -162,7 +253,7 @@ def tile_classes(desc, block_q: int, block_k: int) -> np.ndarray:
     for bi, (lo, hi) in enumerate(qb):
         counts = np.zeros(len(kt), dtype=np.int64)
         for i in range(lo, hi):
-            key = tuple(int(x) for x in _side_and_chunk(desc, i))
+            key = _row_key(desc, np.int64(i))[0]
             if key not in cache:
                 row = allowed_row(desc, i).astype(np.int64)
                 cache[key] = np.add.reduceat(row, edges[:-1])
@@ -224,15 +315,14 @@ def masked_attention_jvp_slice(q, k, v, tq, tk, tv, desc, scale=None, rows=None)
     o = np.zeros((len(rows), dv))
     to = np.zeros((len(rows), dv))
     lse = np.full(len(rows), -np.inf)
-    noisy, chunk = _side_and_chunk(desc, rows)
     groups = {}
-    for pos, key in enumerate(zip(noisy.tolist(), chunk.tolist())):
+    for pos, key in enumerate(_row_key(desc, rows)):
         groups.setdefault(key, []).append(pos)
     for _, positions in groups.items():
         positions = np.asarray(positions)
         sel = rows[positions]
         keys = np.nonzero(allowed_row(desc, int(sel[0])))[0]
-        if keys.size == 0:  # unreachable for these masks; defined as zero output
+        if keys.size == 0:  # rows that see no key (e.g. in no group): zero output, lse = -inf
             continue
         o_g, to_g, lse_g = _rows_forward(q[sel], k, v, tq[sel], tk, tv, keys, sc)
         o[positions], to[positions], lse[positions] = o_g, to_g, lse_g

@@ -52,6 +52,9 @@ class Workload:
     dtype: str  # "bf16" or "fp32"
     tangent_std: float
     rms_norm_qk: bool
+    # chunk sizes in frames, first to last, when the chunks are not all equal
+    # (a cA-B pattern); empty: n_frames / frames_per_chunk chunks of equal size
+    chunk_frames: tuple = ()
 
     @property
     def tokens_per_side(self) -> int:
@@ -69,6 +72,17 @@ class Workload:
     def desc(self):
         return (self.tokens_per_frame, self.n_frames, self.frames_per_chunk, self.tf_layout)
 
+    @property
+    def chunks(self) -> tuple:
+        """Chunk sizes in frames."""
+        if self.chunk_frames:
+            return tuple(self.chunk_frames)
+        return (self.frames_per_chunk,) * (self.n_frames // self.frames_per_chunk)
+
+    def mask_ranges(self):
+        """The workload's mask as (seq_len, query groups x key intervals)."""
+        return chunked_mask_ranges(self.tokens_per_frame, self.chunks, self.tf_layout)
+
     def with_(self, **kw) -> "Workload":
         d = dict(self.__dict__)
         d.update(kw)
@@ -85,6 +99,49 @@ WORKLOADS = {
     4: Workload("tf_chunkwise_65520_b2", 4, 2, 12, 128, 1560, 21, 3, 1, "bf16", 0.1, True),
     5: Workload("tf_framewise_65520_h40", 5, 1, 40, 128, 1560, 21, 1, 1, "bf16", 0.05, True),
 }
+
+
+# Workloads whose mask is given as a range list: frame-wise teacher forcing
+# with a one-frame first chunk followed by four-frame chunks (c1-4, 21 frames).
+RANGE_WORKLOADS = {
+    6: Workload("tf_c1_4_65520", 6, 1, 12, 128, 1560, 21, 1, 1, "bf16", 0.1, True, (1, 4, 4, 4, 4, 4)),
+}
+
+
+def chunked_mask_ranges(tokens_per_frame: int, chunk_frames, tf_layout: int):
+    """Structure of a chunked teacher-forcing / block-causal mask as query
+    groups x key intervals: one group per chunk and side.  Clean chunk c sees
+    the clean tokens of chunks 0..c; noisy chunk c sees the clean tokens of
+    chunks 0..c-1 and its own noisy tokens (section 3.1.1); a block-causal
+    mask is the clean side alone.  Returns (seq_len, groups) with groups =
+    ((row_lo, row_hi, ((key_lo, key_hi), ...)), ...), half-open."""
+    lens = [tokens_per_frame * int(c) for c in chunk_frames]
+    nh = sum(lens)
+    groups = []
+    start = 0
+    for t in lens:
+        groups.append((start, start + t, ((0, start + t),)))
+        start += t
+    if tf_layout:
+        start = 0
+        for t in lens:
+            own = (nh + start, nh + start + t)
+            groups.append((own[0], own[1], (((0, start), own) if start > 0 else (own,))))
+            start += t
+    return nh * (2 if tf_layout else 1), tuple(groups)
+
+
+def und_gen_ranges(n_und: int, n_frames: int, tokens_per_frame: int):
+    """Structure of an understanding / generation layout [UND | GEN] as query
+    groups x key intervals (section 4.2.2, Figure 9): UND tokens attend
+    causally (one group per UND token); a GEN token of frame f attends to
+    every UND token and to the GEN tokens of frames 0..f (one group per
+    frame).  Returns (seq_len, groups)."""
+    groups = [(i, i + 1, ((0, i + 1),)) for i in range(n_und)]
+    for f in range(n_frames):
+        lo = n_und + f * tokens_per_frame
+        groups.append((lo, lo + tokens_per_frame, ((0, lo + tokens_per_frame),)))
+    return n_und + n_frames * tokens_per_frame, tuple(groups)
 
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
