@@ -114,6 +114,55 @@ int attn_jvp_create_ex(attn_jvp_plan** out, const attn_jvp_mask_desc* mask, int3
                        int32_t heads, int32_t head_dim, int32_t dtype, float softmax_scale,
                        uint32_t flags);
 
+/* Range-list masks (Causal-rCM, Appendix B, "sparse custom mask
+ * representation"): the mask is a set of query groups, each a contiguous
+ * interval of query rows with a list of allowed key intervals; a row in no
+ * group sees no key (its o and t_o are 0 and its lse is -inf).  This covers
+ * dense attention (one group, one key interval), block-causal and
+ * teacher-forcing masks with chunks of any size (e.g. an initial chunk of
+ * another size, the cA-B patterns of section 4) and understanding /
+ * generation layouts (section 4.2.2, Figure 9).
+ *
+ * Groups are given sorted by row_lo and disjoint; every interval lies in
+ * [0, n_tokens).  A group's intervals may come in any order and may overlap
+ * or touch: the plan sorts and merges them (at most 255 after merging).
+ * Query blocks are cut from row 0 over the whole sequence; each block
+ * streams the key tiles that meet the intervals of its rows' groups. */
+typedef struct {
+  int32_t row_lo, row_hi;      /* query rows [row_lo, row_hi) */
+  int32_t key_begin, key_end;  /* the group's key intervals: intervals[2k], intervals[2k+1] (half-open) for
+                                  key_begin <= k < key_end */
+} attn_jvp_query_group;
+
+/* Build a plan from a range list of n_tokens tokens (arguments as in
+ * attn_jvp_create otherwise; no plan flags).  Pure host work: the plan
+ * holds, besides its host copy, a schedule table (attn_jvp_plan_table) that
+ * the caller places in device memory and passes to attn_jvp_fwd_table.
+ * ATTN_JVP_E_OVERFLOW if, in a bf16 plan, one query block streams more than
+ * 7680 key tiles (the kernel stages a block's tile list in LDS). */
+int attn_jvp_create_ranges(attn_jvp_plan** out, int32_t n_tokens, int32_t n_groups,
+                           const attn_jvp_query_group* groups, int32_t n_intervals,
+                           const int32_t* intervals, int32_t batch, int32_t heads, int32_t head_dim,
+                           int32_t dtype, float softmax_scale);
+
+/* Bytes of a range-list plan's schedule table (0 for descriptor plans). */
+int attn_jvp_plan_table_size(const attn_jvp_plan* plan, size_t* bytes);
+
+/* Copy a range-list plan's schedule table (int32 words, independent of the
+ * device) to host memory of at least attn_jvp_plan_table_size() bytes.  The
+ * caller copies it to device memory it owns, 4-byte aligned, and keeps it
+ * there while kernels that use it may run. */
+int attn_jvp_plan_table(const attn_jvp_plan* plan, void* host_out, size_t bytes);
+
+/* attn_jvp_fwd for range-list plans: the same operation and arguments, with
+ * the plan's schedule table in device memory (bytes from attn_jvp_plan_table
+ * of this plan; its contents are not checked).  attn_jvp_fwd refuses range-
+ * list plans and this call refuses descriptor plans (ATTN_JVP_E_INVALID).
+ * Range-list plans have no backward and no clean-tangent-zero option. */
+int attn_jvp_fwd_table(const attn_jvp_plan* plan, const void* device_table, const void* q,
+                       const void* k, const void* v, const void* tq, const void* tk, const void* tv,
+                       void* o, void* t_o, float* lse, void* hip_stream);
+
 /* Enqueue o, to (and lse when non-NULL) for the plan's shape on `hip_stream`
  * (a hipStream_t; NULL is the null stream), on the current HIP device.
  * Checks pointers, alignment, overlap and the device architecture first. */
@@ -214,7 +263,9 @@ int attn_jvp_plan_flops(const attn_jvp_plan* plan, int64_t* useful_flops);
 
 /* Per-row allowed key ranges, as the kernel uses them: host_out[4*i + 0..3]
  * = lo1, hi1, lo2, hi2 (half-open, empty when lo >= hi) for rows
- * i = 0..N-1.  n is the capacity of host_out in int32 elements (>= 4N). */
+ * i = 0..N-1.  n is the capacity of host_out in int32 elements (>= 4N).
+ * Range-list plans: the first two intervals of the row's group (zeros for
+ * rows in no group); ATTN_JVP_E_INVALID if some group has more than two. */
 int attn_jvp_row_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
 /* Per-key allowed query ranges (the columns of the mask), as the backward's

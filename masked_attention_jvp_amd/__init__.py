@@ -10,11 +10,13 @@ mirror the C ABI of ``include/attn_jvp.h`` one to one:
     attn_jvp_last_error_detail, attn_jvp_plan_info, attn_jvp_plan_flops,
     attn_jvp_plan_bwd_flops, attn_jvp_plan_bwd_info, attn_jvp_launch_order,
     attn_jvp_bwd_launch_order, attn_jvp_row_ranges, attn_jvp_key_ranges,
-    attn_jvp_tile_map
+    attn_jvp_tile_map, attn_jvp_create_ranges, attn_jvp_plan_table_size,
+    attn_jvp_plan_table, attn_jvp_fwd_table
 
-plus ``masked_attention_jvp(...)`` and ``masked_attention_bwd(...)``, which
-allocate the outputs (and the backward's workspace) and call ``attn_jvp_fwd``
-/ ``attn_jvp_bwd`` on the current stream.  If the library is not built the
+plus ``masked_attention_jvp(...)``, ``masked_attention_jvp_ranges(...)`` and
+``masked_attention_bwd(...)``, which allocate the outputs (and the backward's
+workspace, or a range-list plan's device table) and call ``attn_jvp_fwd`` /
+``attn_jvp_fwd_table`` / ``attn_jvp_bwd`` on the current stream.  If the library is not built the
 import of this module still works, but every call raises ``AttnJvpError``;
 there is no fallback implementation.
 """
@@ -32,7 +34,8 @@ __all__ = [
     "attn_jvp_error_string", "attn_jvp_last_error_detail", "attn_jvp_plan_info", "attn_jvp_plan_flops",
     "attn_jvp_launch_order", "attn_jvp_row_ranges", "attn_jvp_tile_map", "masked_attention_jvp",
     "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops", "attn_jvp_key_ranges",
-    "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order",
+    "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order", "attn_jvp_create_ranges", "attn_jvp_plan_table_size",
+    "attn_jvp_plan_table", "attn_jvp_fwd_table", "masked_attention_jvp_ranges",
     "masked_attention_bwd",
 ]
 
@@ -50,6 +53,11 @@ class AttnJvpError(RuntimeError):
     def __init__(self, msg, code=None):
         super().__init__(msg)
         self.code = code
+
+
+class _QueryGroup(ctypes.Structure):
+    _fields_ = [("row_lo", ctypes.c_int32), ("row_hi", ctypes.c_int32),
+                ("key_begin", ctypes.c_int32), ("key_end", ctypes.c_int32)]
 
 
 class _MaskDesc(ctypes.Structure):
@@ -92,10 +100,15 @@ def _load():
         lib.attn_jvp_key_ranges.argtypes = [vp, P(i32), ctypes.c_size_t]
         lib.attn_jvp_plan_bwd_info.argtypes = [vp, P(i32), P(i32), P(i32), P(i32)]
         lib.attn_jvp_bwd_launch_order.argtypes = [vp, P(i32), ctypes.c_size_t]
+        lib.attn_jvp_create_ranges.argtypes = [P(vp), i32, i32, P(_QueryGroup), i32, P(i32), i32, i32, i32, i32, f32]
+        lib.attn_jvp_plan_table_size.argtypes = [vp, P(ctypes.c_size_t)]
+        lib.attn_jvp_plan_table.argtypes = [vp, vp, ctypes.c_size_t]
+        lib.attn_jvp_fwd_table.argtypes = [vp] * 10 + [vp, vp]
         for name in ("attn_jvp_create", "attn_jvp_create_ex", "attn_jvp_fwd", "attn_jvp_destroy",
                      "attn_jvp_plan_info", "attn_jvp_plan_flops", "attn_jvp_launch_order", "attn_jvp_row_ranges",
                      "attn_jvp_tile_map", "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops",
-                     "attn_jvp_key_ranges", "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order"):
+                     "attn_jvp_key_ranges", "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order",
+                     "attn_jvp_create_ranges", "attn_jvp_plan_table_size", "attn_jvp_plan_table", "attn_jvp_fwd_table"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -163,6 +176,43 @@ def attn_jvp_create_ex(desc, batch: int, heads: int, head_dim: int, dtype: int =
     _check(lib.attn_jvp_create_ex(ctypes.byref(h), ctypes.byref(d), int(batch), int(heads), int(head_dim),
                                   int(dtype), float(softmax_scale or 0.0), int(flags)), "attn_jvp_create_ex")
     return Plan(h, desc, batch, heads, head_dim, dtype, softmax_scale, int(flags))
+
+
+def attn_jvp_create_ranges(n_tokens: int, groups, batch: int, heads: int, head_dim: int,
+                           dtype: int = ATTN_JVP_BF16, softmax_scale: float = 0.0) -> Plan:
+    """Plan for a range-list mask: groups = [(row_lo, row_hi, [(key_lo, key_hi), ...]), ...]
+    (half-open, sorted by row_lo, disjoint)."""
+    lib = _load()
+    groups = list(groups)
+    qg = (_QueryGroup * max(1, len(groups)))()
+    flat = []
+    for i, (lo, hi, ivs) in enumerate(groups):
+        b = len(flat) // 2
+        for a, z in ivs:
+            flat += [int(a), int(z)]
+        qg[i] = _QueryGroup(int(lo), int(hi), b, len(flat) // 2)
+    iv = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    h = ctypes.c_void_p()
+    _check(lib.attn_jvp_create_ranges(ctypes.byref(h), int(n_tokens), len(groups), qg, len(flat) // 2, iv, int(batch),
+                                      int(heads), int(head_dim), int(dtype), float(softmax_scale or 0.0)),
+           "attn_jvp_create_ranges")
+    plan = Plan(h, (int(n_tokens), len(groups)), batch, heads, head_dim, dtype, softmax_scale)
+    plan.ranges = tuple((int(lo), int(hi), tuple((int(a), int(z)) for a, z in ivs)) for lo, hi, ivs in groups)
+    return plan
+
+
+def attn_jvp_plan_table_size(plan: Plan) -> int:
+    v = ctypes.c_size_t()
+    _check(_load().attn_jvp_plan_table_size(plan.handle, ctypes.byref(v)), "attn_jvp_plan_table_size")
+    return v.value
+
+
+def attn_jvp_plan_table(plan: Plan) -> np.ndarray:
+    """A range-list plan's schedule table as int32 host words (to be copied to the device)."""
+    n = attn_jvp_plan_table_size(plan)
+    out = np.empty(n // 4, dtype=np.int32)
+    _check(_load().attn_jvp_plan_table(plan.handle, out.ctypes.data_as(ctypes.c_void_p), n), "attn_jvp_plan_table")
+    return out
 
 
 def attn_jvp_plan_flops(plan: Plan) -> int:
@@ -320,6 +370,31 @@ def attn_jvp_bwd(plan: Plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace, stream
     _check(code, "attn_jvp_bwd")
 
 
+def attn_jvp_fwd_table(plan: Plan, table, q, k, v, tq, tk, tv, o, t_o, lse=None, stream=None) -> None:
+    """attn_jvp_fwd for a range-list plan; `table` is the plan's table as an
+    int32 CUDA tensor (attn_jvp_plan_table copied to the device)."""
+    import torch
+    ins = dict(q=q, k=k, v=v, tq=tq, tk=tk, tv=tv, o=o, t_o=t_o)
+    for name, t in ins.items():
+        _check_tensor(name, t, plan, plan.shape)
+    dev = q.device
+    if not isinstance(table, torch.Tensor) or table.device != dev or table.dtype != torch.int32 \
+            or not table.is_contiguous() or table.numel() * 4 < attn_jvp_plan_table_size(plan):
+        raise AttnJvpError("table must be the plan's int32 table as a contiguous tensor on q's device")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != plan.shape[:3] or not lse.is_contiguous() \
+                or lse.device != dev:
+            raise AttnJvpError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        code = _load().attn_jvp_fwd_table(plan.handle, ctypes.c_void_p(table.data_ptr()),
+                                          *[ctypes.c_void_p(t.data_ptr()) for t in ins.values()],
+                                          ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
+                                          ctypes.c_void_p(stream.cuda_stream))
+    _check(code, "attn_jvp_fwd_table")
+
+
 _plan_cache = {}
 _plan_lock = threading.Lock()
 
@@ -363,3 +438,29 @@ def masked_attention_bwd(q, k, v, o, lse, d_o, desc, scale=None, return_workspac
     ws = torch.empty(attn_jvp_bwd_workspace_size(plan) // 4, dtype=torch.float32, device=q.device)
     attn_jvp_bwd(plan, q, k, v, o, lse, d_o, dq, dk, dv, ws)
     return (dq, dk, dv, ws) if return_workspace else (dq, dk, dv)
+
+
+_range_cache = {}
+
+
+def masked_attention_jvp_ranges(q, k, v, tq, tk, tv, groups, scale=None, return_lse=False):
+    """(o, t_o[, lse]) for a range-list mask: groups = [(row_lo, row_hi,
+    [(key_lo, key_hi), ...]), ...].  The plan and its device table are
+    cached per (mask, shape, dtype, scale, device)."""
+    import torch
+    dtype = ATTN_JVP_BF16 if q.dtype == torch.bfloat16 else ATTN_JVP_FP32
+    b, h, n, d = q.shape
+    key = (tuple((int(lo), int(hi), tuple((int(a), int(z)) for a, z in ivs)) for lo, hi, ivs in groups),
+           tuple(q.shape), dtype, float(scale or 0.0), str(q.device))
+    with _plan_lock:
+        hit = _range_cache.get(key)
+        if hit is None:
+            plan = attn_jvp_create_ranges(n, groups, b, h, d, dtype, scale or 0.0)
+            table = torch.from_numpy(attn_jvp_plan_table(plan)).to(q.device)
+            hit = _range_cache[key] = (plan, table)
+    plan, table = hit
+    o = torch.empty_like(q)
+    t_o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    attn_jvp_fwd_table(plan, table, q, k, v, tq, tk, tv, o, t_o, lse)
+    return (o, t_o, lse) if return_lse else (o, t_o)

@@ -10,8 +10,11 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <new>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "attn_jvp.h"
 #include "attn_jvp_launch.h"
@@ -19,7 +22,24 @@
 
 using namespace attn_jvp;
 
+// Schedule of a range-list plan (query groups x key intervals), serialised
+// into one int32 table that the caller places in device memory:
+//   [0..7]     header: magic, n_qblocks, n_entries, n_intervals, max entries per block
+//   blk        [n_qblocks + 1]  first entry of each query block
+//   order      [n_qblocks]      launch order (workgroup t -> query block)
+//   entries    one per streamed key tile: tile | (whole bit of wave w) << (24 + w)
+//   rows       [N]              per query row: (first interval << 8) | interval count
+//   intervals  [2 n_intervals]  key intervals (lo, hi), merged and sorted per group
+struct RangeSchedule {
+  std::vector<int32_t> table;
+  int64_t off_blk = 0, off_order = 0, off_ent = 0, off_rows = 0, off_iv = 0;
+  int32_t n_entries = 0, max_entries = 0;
+  std::vector<uint8_t> ent_class;  // per entry: 1 every row of the block sees the whole tile, 2 otherwise
+  bool rows_over_two = false;      // some row has more than two key intervals
+};
+
 struct attn_jvp_plan {
+  RangeSchedule* rs = nullptr;  // range-list plans only
   MaskGeom g;
   int32_t batch, heads, head_dim, dtype;
   float scale;
@@ -207,14 +227,221 @@ int attn_jvp_create_ex(attn_jvp_plan** out, const attn_jvp_mask_desc* mask, int3
   return ok();
 }
 
+int attn_jvp_create_ranges(attn_jvp_plan** out, int32_t n_tokens, int32_t n_groups,
+                           const attn_jvp_query_group* groups, int32_t n_intervals, const int32_t* intervals,
+                           int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype, float softmax_scale) {
+  if (out == nullptr) return fail(ATTN_JVP_E_NULL, "out must be non-NULL");
+  *out = nullptr;
+  if (n_groups > 0 && groups == nullptr) return fail(ATTN_JVP_E_NULL, "groups is NULL");
+  if (n_intervals > 0 && intervals == nullptr) return fail(ATTN_JVP_E_NULL, "intervals is NULL");
+  if (n_tokens < 1) return fail(ATTN_JVP_E_INVALID, "n_tokens must be >= 1 (got %d)", n_tokens);
+  if (n_groups < 0 || n_intervals < 0) return fail(ATTN_JVP_E_INVALID, "n_groups and n_intervals must be >= 0");
+  if (batch < 1 || heads < 1) return fail(ATTN_JVP_E_INVALID, "batch and heads must be >= 1 (got %d, %d)", batch, heads);
+  if (head_dim != 64 && head_dim != 128) return fail(ATTN_JVP_E_INVALID, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_FP32) return fail(ATTN_JVP_E_INVALID, "unknown dtype %d", dtype);
+  if (!std::isfinite(softmax_scale)) return fail(ATTN_JVP_E_INVALID, "softmax_scale must be finite");
+  const int64_t n = n_tokens;
+  const int64_t per_head = n * head_dim * (dtype == ATTN_JVP_BF16 ? 2 : 1);
+  if (per_head >= (int64_t(1) << 31))
+    return fail(ATTN_JVP_E_OVERFLOW, "sequence of %lld tokens x d=%d exceeds the per-head limit (2^31 %s)",
+                (long long)n, head_dim, dtype == ATTN_JVP_BF16 ? "bytes" : "elements");
+
+  // Validate and normalise the groups: sorted, disjoint query intervals;
+  // each group's key intervals sorted and merged (empty ones dropped).
+  std::vector<int32_t> g_lo(n_groups), g_hi(n_groups), g_iv(n_groups + 1, 0), ivs;
+  for (int32_t g = 0; g < n_groups; ++g) {
+    const attn_jvp_query_group& q = groups[g];
+    if (q.row_lo < 0 || q.row_lo >= q.row_hi || q.row_hi > n_tokens)
+      return fail(ATTN_JVP_E_INVALID, "group %d: rows [%d, %d) not a non-empty part of [0, %d)", g, q.row_lo,
+                  q.row_hi, n_tokens);
+    if (g > 0 && q.row_lo < g_hi[g - 1])
+      return fail(ATTN_JVP_E_INVALID, "group %d: rows start at %d, before the end of group %d (%d); groups must be "
+                  "sorted and disjoint", g, q.row_lo, g - 1, g_hi[g - 1]);
+    if (q.key_begin < 0 || q.key_begin > q.key_end || q.key_end > n_intervals)
+      return fail(ATTN_JVP_E_INVALID, "group %d: intervals [%d, %d) outside [0, %d)", g, q.key_begin, q.key_end,
+                  n_intervals);
+    std::vector<std::pair<int32_t, int32_t>> kv;
+    for (int32_t k = q.key_begin; k < q.key_end; ++k) {
+      const int32_t lo = intervals[2 * k], hi = intervals[2 * k + 1];
+      if (lo < 0 || hi < lo || hi > n_tokens)
+        return fail(ATTN_JVP_E_INVALID, "group %d: key interval [%d, %d) not inside [0, %d)", g, lo, hi, n_tokens);
+      if (lo < hi) kv.emplace_back(lo, hi);
+    }
+    std::sort(kv.begin(), kv.end());
+    std::vector<std::pair<int32_t, int32_t>> merged;
+    for (const auto& iv : kv) {
+      if (!merged.empty() && iv.first <= merged.back().second) merged.back().second = std::max(merged.back().second, iv.second);
+      else merged.push_back(iv);
+    }
+    if (merged.size() > 255)
+      return fail(ATTN_JVP_E_INVALID, "group %d has %zu key intervals after merging; at most 255", g, merged.size());
+    g_lo[g] = q.row_lo;
+    g_hi[g] = q.row_hi;
+    for (const auto& iv : merged) {
+      ivs.push_back(iv.first);
+      ivs.push_back(iv.second);
+    }
+    g_iv[g + 1] = (int32_t)(ivs.size() / 2);
+    if (g_iv[g + 1] >= (1 << 23)) return fail(ATTN_JVP_E_OVERFLOW, "more than 2^23 key intervals");
+  }
+
+  attn_jvp_plan* p = new (std::nothrow) attn_jvp_plan;
+  RangeSchedule* rs = p ? new (std::nothrow) RangeSchedule : nullptr;
+  if (rs == nullptr) {
+    delete p;
+    return fail(ATTN_JVP_E_NOMEM, "plan allocation failed");
+  }
+  p->rs = rs;
+  p->g = MaskGeom{n_tokens, n_tokens, 0, n_tokens};  // only seq_len is used by range plans
+  p->batch = batch;
+  p->heads = heads;
+  p->head_dim = head_dim;
+  p->dtype = dtype;
+  p->flags = 0;
+  p->scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  block_sizes(dtype, head_dim, &p->block_q, &p->block_k);
+  const int32_t bq = p->block_q, bk = p->block_k, nw = bq / 32;
+  p->n_qblocks = cdiv(n_tokens, bq);
+  p->n_ktiles = cdiv(n_tokens, bk);
+  if ((int64_t)batch * heads * p->n_qblocks >= (int64_t(1) << 31)) {
+    delete rs;
+    delete p;
+    return fail(ATTN_JVP_E_OVERFLOW, "grid does not fit");
+  }
+
+  try {
+    std::vector<int32_t> row_group(n_tokens, -1);
+    int64_t pairs = 0;
+    for (int32_t g = 0; g < n_groups; ++g) {
+      int64_t keys = 0;
+      for (int32_t k = g_iv[g]; k < g_iv[g + 1]; ++k) keys += ivs[2 * k + 1] - ivs[2 * k];
+      pairs += keys * (g_hi[g] - g_lo[g]);
+      for (int32_t r = g_lo[g]; r < g_hi[g]; ++r) row_group[r] = g;
+    }
+    // Does group g (or "no group", g < 0) see all of keys [k0, k1)?
+    auto covers_g = [&](int32_t g, int32_t k0, int32_t k1) {
+      if (g < 0) return false;
+      for (int32_t k = g_iv[g]; k < g_iv[g + 1]; ++k)
+        if (ivs[2 * k] <= k0 && k1 <= ivs[2 * k + 1]) return true;
+      return false;
+    };
+    std::vector<int32_t> blk(p->n_qblocks + 1, 0), ent;
+    std::vector<uint8_t> cls;
+    std::vector<std::pair<int32_t, int32_t>> runs;
+    std::vector<int32_t> bgroups;
+    for (int32_t b = 0; b < p->n_qblocks; ++b) {
+      const int32_t r0 = b * bq, r1 = std::min(r0 + bq, n_tokens);
+      // distinct groups of the block's rows (-1: rows in no group)
+      bgroups.clear();
+      for (int32_t r = r0; r < r1; ++r)
+        if (bgroups.empty() || bgroups.back() != row_group[r]) bgroups.push_back(row_group[r]);
+      runs.clear();
+      for (int32_t g : bgroups) {
+        if (g < 0) continue;
+        for (int32_t k = g_iv[g]; k < g_iv[g + 1]; ++k) runs.emplace_back(ivs[2 * k] / bk, cdiv(ivs[2 * k + 1], bk));
+      }
+      std::sort(runs.begin(), runs.end());
+      int32_t at = -1;
+      for (const auto& run : runs) {
+        for (int32_t t = std::max(run.first, at); t < run.second; ++t) {
+          const int32_t k0 = t * bk, k1c = std::min(k0 + bk, n_tokens);
+          int32_t e = t;
+          for (int32_t w = 0; w < nw; ++w) {
+            const int32_t wa = r0 + 32 * w, wb = std::min(wa + 32, r1);
+            bool whole = true;  // waves without valid rows never mask
+            // every row of the wave sees all 32 keys of the tile (keys past N are zeros: not whole)
+            for (int32_t r = wa; r < wb && whole; ++r) {
+              if (r > wa && row_group[r] == row_group[r - 1]) continue;
+              whole = k0 + bk <= n_tokens && covers_g(row_group[r], k0, k0 + bk);
+            }
+            if (whole) e |= 1 << (24 + w);
+          }
+          bool all = true;
+          for (int32_t g : bgroups) all = all && covers_g(g, k0, k1c);
+          ent.push_back(e);
+          cls.push_back(all ? 1 : 2);
+        }
+        at = std::max(at, run.second);
+      }
+      blk[b + 1] = (int32_t)ent.size();
+      rs->max_entries = std::max(rs->max_entries, blk[b + 1] - blk[b]);
+    }
+    if (dtype == ATTN_JVP_BF16 && rs->max_entries > kMaxTableEntries) {
+      const int32_t me = rs->max_entries;
+      delete rs;
+      delete p;
+      return fail(ATTN_JVP_E_OVERFLOW, "a query block streams %d key tiles; range-list plans allow at most %d", me,
+                  kMaxTableEntries);
+    }
+    // heavy first: blocks with more tiles first (stable)
+    std::vector<int32_t> order(p->n_qblocks);
+    for (int32_t b = 0; b < p->n_qblocks; ++b) order[b] = b;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t a, int32_t b2) { return blk[a + 1] - blk[a] > blk[b2 + 1] - blk[b2]; });
+    rs->n_entries = (int32_t)ent.size();
+    const int32_t n_iv = (int32_t)(ivs.size() / 2);
+    std::vector<int32_t>& tb = rs->table;
+    tb.assign(8, 0);
+    tb[0] = kTableMagic;
+    tb[1] = p->n_qblocks;
+    tb[2] = rs->n_entries;
+    tb[3] = n_iv;
+    tb[4] = rs->max_entries;
+    rs->off_blk = (int64_t)tb.size();
+    tb.insert(tb.end(), blk.begin(), blk.end());
+    rs->off_order = (int64_t)tb.size();
+    tb.insert(tb.end(), order.begin(), order.end());
+    rs->off_ent = (int64_t)tb.size();
+    tb.insert(tb.end(), ent.begin(), ent.end());
+    rs->off_rows = (int64_t)tb.size();
+    for (int32_t r = 0; r < n_tokens; ++r) {
+      const int32_t g = row_group[r];
+      const int32_t cnt = g < 0 ? 0 : g_iv[g + 1] - g_iv[g];
+      tb.push_back(g < 0 ? 0 : (g_iv[g] << 8) | cnt);
+      rs->rows_over_two = rs->rows_over_two || cnt > 2;
+    }
+    rs->off_iv = (int64_t)tb.size();
+    tb.insert(tb.end(), ivs.begin(), ivs.end());
+    rs->ent_class = std::move(cls);
+    p->allowed_pairs = pairs;
+    p->visited_tiles = rs->n_entries;
+    p->useful_flops = 12 * pairs * head_dim * batch * heads;
+    p->bwd_block_q = p->bwd_block_kv = p->bwd_n_qblocks = p->bwd_n_kblocks = 0;
+    p->bwd_useful_flops = 10 * pairs * head_dim * batch * heads;
+  } catch (const std::bad_alloc&) {
+    delete rs;
+    delete p;
+    return fail(ATTN_JVP_E_NOMEM, "plan tables do not fit in host memory");
+  }
+  *out = p;
+  return ok();
+}
+
+int attn_jvp_plan_table_size(const attn_jvp_plan* p, size_t* bytes) {
+  if (p == nullptr || bytes == nullptr) return fail(ATTN_JVP_E_NULL, "plan and bytes must be non-NULL");
+  *bytes = p->rs ? p->rs->table.size() * sizeof(int32_t) : 0;
+  return ok();
+}
+
+int attn_jvp_plan_table(const attn_jvp_plan* p, void* host_out, size_t bytes) {
+  if (p == nullptr || host_out == nullptr) return fail(ATTN_JVP_E_NULL, "plan and host_out must be non-NULL");
+  if (p->rs == nullptr) return fail(ATTN_JVP_E_INVALID, "descriptor plans have no table");
+  const size_t need = p->rs->table.size() * sizeof(int32_t);
+  if (bytes < need) return fail(ATTN_JVP_E_INVALID, "host_out holds %zu bytes, need %zu", bytes, need);
+  std::memcpy(host_out, p->rs->table.data(), need);
+  return ok();
+}
+
 int attn_jvp_destroy(attn_jvp_plan* p) {
+  if (p) delete p->rs;
   delete p;
   return ok();
 }
 
-int attn_jvp_fwd(const attn_jvp_plan* p, const void* q, const void* k, const void* v, const void* tq,
-                 const void* tk, const void* tv, void* o, void* t_o, float* lse, void* hip_stream) {
-  if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
+namespace {
+
+int fwd_common(const attn_jvp_plan* p, const void* table, const void* q, const void* k, const void* v,
+               const void* tq, const void* tk, const void* tv, void* o, void* t_o, float* lse, void* hip_stream) {
   const void* ins[6] = {q, k, v, tq, tk, tv};
   static const char* names[8] = {"q", "k", "v", "tq", "tk", "tv", "o", "t_o"};
   void* outs[2] = {o, t_o};
@@ -241,6 +468,12 @@ int attn_jvp_fwd(const attn_jvp_plan* p, const void* q, const void* k, const voi
   if (lse)
     for (int j = 0; j < 6; ++j)
       if (overlaps(lse, rows * 4, ins[j], bytes)) return fail(ATTN_JVP_E_INVALID, "lse overlaps input %s", names[j]);
+  if (table) {
+    const size_t tbytes = p->rs->table.size() * sizeof(int32_t);
+    for (int i = 0; i < 2; ++i)
+      if (overlaps(outs[i], bytes, table, tbytes)) return fail(ATTN_JVP_E_INVALID, "%s overlaps the table", names[6 + i]);
+    if (lse && overlaps(lse, rows * 4, table, tbytes)) return fail(ATTN_JVP_E_INVALID, "lse overlaps the table");
+  }
 
   int dev;
   int st = check_device(&dev);
@@ -261,10 +494,38 @@ int attn_jvp_fwd(const attn_jvp_plan* p, const void* q, const void* k, const voi
   fp.scale = p->scale;
   fp.score_log2 = p->scale * 1.4426950408889634f;
   fp.ctz = (p->flags & ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO) ? 1 : 0;
+  fp.tb_blk = fp.tb_order = fp.tb_ent = fp.tb_rows = fp.tb_iv = nullptr;
+  if (table) {
+    const int32_t* t = (const int32_t*)table;
+    fp.tb_blk = t + p->rs->off_blk;
+    fp.tb_order = t + p->rs->off_order;
+    fp.tb_ent = t + p->rs->off_ent;
+    fp.tb_rows = t + p->rs->off_rows;
+    fp.tb_iv = t + p->rs->off_iv;
+  }
   const int grid = p->batch * p->heads * p->n_qblocks;
   hipError_t e = launch_fwd(p->dtype, p->head_dim, grid, fp, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(ATTN_JVP_E_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+int attn_jvp_fwd(const attn_jvp_plan* p, const void* q, const void* k, const void* v, const void* tq,
+                 const void* tk, const void* tv, void* o, void* t_o, float* lse, void* hip_stream) {
+  if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
+  if (p->rs) return fail(ATTN_JVP_E_INVALID, "range-list plans run through attn_jvp_fwd_table");
+  return fwd_common(p, nullptr, q, k, v, tq, tk, tv, o, t_o, lse, hip_stream);
+}
+
+int attn_jvp_fwd_table(const attn_jvp_plan* p, const void* device_table, const void* q, const void* k,
+                       const void* v, const void* tq, const void* tk, const void* tv, void* o, void* t_o,
+                       float* lse, void* hip_stream) {
+  if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
+  if (p->rs == nullptr) return fail(ATTN_JVP_E_INVALID, "descriptor plans have no table: use attn_jvp_fwd");
+  if (device_table == nullptr) return fail(ATTN_JVP_E_NULL, "device_table is NULL");
+  if ((uintptr_t)device_table % 4) return fail(ATTN_JVP_E_ALIGN, "device_table is not 4-byte aligned");
+  return fwd_common(p, device_table, q, k, v, tq, tk, tv, o, t_o, lse, hip_stream);
 }
 
 int attn_jvp_bwd_workspace_size(const attn_jvp_plan* p, size_t* bytes) {
@@ -277,6 +538,7 @@ int attn_jvp_bwd(const attn_jvp_plan* p, const void* q, const void* k, const voi
                  const float* lse, const void* d_o, void* dq, void* dk, void* dv, float* workspace,
                  void* hip_stream) {
   if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
+  if (p->rs) return fail(ATTN_JVP_E_INVALID, "the backward takes descriptor plans; range-list plans are forward only");
   static const char* names[10] = {"q", "k", "v", "o", "d_o", "lse", "dq", "dk", "dv", "workspace"};
   const void* ins[6] = {q, k, v, o, d_o, lse};
   void* outs[4] = {dq, dk, dv, workspace};
@@ -346,6 +608,7 @@ int attn_jvp_plan_bwd_flops(const attn_jvp_plan* p, int64_t* useful_flops) {
 
 int attn_jvp_key_ranges(const attn_jvp_plan* p, int32_t* out, size_t n) {
   if (p == nullptr || out == nullptr) return fail(ATTN_JVP_E_NULL, "plan and host_out must be non-NULL");
+  if (p->rs) return fail(ATTN_JVP_E_INVALID, "range-list plans have no backward key ranges");
   if (n < (size_t)p->g.seq_len * 4)
     return fail(ATTN_JVP_E_INVALID, "host_out holds %zu int32, need %zu", n, (size_t)p->g.seq_len * 4);
   for (int32_t j = 0; j < p->g.seq_len; ++j) {
@@ -397,6 +660,10 @@ int attn_jvp_launch_order(const attn_jvp_plan* p, int32_t* out, size_t n) {
   if (p == nullptr || out == nullptr) return fail(ATTN_JVP_E_NULL, "plan and host_out must be non-NULL");
   if (n < (size_t)p->n_qblocks)
     return fail(ATTN_JVP_E_INVALID, "host_out holds %zu int32, need %d", n, p->n_qblocks);
+  if (p->rs) {
+    std::memcpy(out, p->rs->table.data() + p->rs->off_order, sizeof(int32_t) * p->n_qblocks);
+    return ok();
+  }
   const bool balanced = (p->flags & ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO) != 0;
   for (int32_t t = 0; t < p->n_qblocks; ++t) out[t] = heavy_first_qblock(p->g, p->block_q, t, balanced);
   return ok();
@@ -404,6 +671,7 @@ int attn_jvp_launch_order(const attn_jvp_plan* p, int32_t* out, size_t n) {
 
 int attn_jvp_bwd_launch_order(const attn_jvp_plan* p, int32_t* out, size_t n) {
   if (p == nullptr || out == nullptr) return fail(ATTN_JVP_E_NULL, "plan and host_out must be non-NULL");
+  if (p->rs) return fail(ATTN_JVP_E_INVALID, "range-list plans have no backward");
   const int64_t total = (int64_t)p->batch * p->heads * p->bwd_n_kblocks;
   if (n < (size_t)total) return fail(ATTN_JVP_E_INVALID, "host_out holds %zu int32, need %lld", n, (long long)total);
   for (int32_t b = 0; b < (int32_t)total; ++b) out[b] = xcd_grouped(b, (int32_t)total, kDkdvXcdGroup);
@@ -414,6 +682,19 @@ int attn_jvp_row_ranges(const attn_jvp_plan* p, int32_t* out, size_t n) {
   if (p == nullptr || out == nullptr) return fail(ATTN_JVP_E_NULL, "plan and host_out must be non-NULL");
   if (n < (size_t)p->g.seq_len * 4)
     return fail(ATTN_JVP_E_INVALID, "host_out holds %zu int32, need %zu", n, (size_t)p->g.seq_len * 4);
+  if (p->rs) {
+    if (p->rs->rows_over_two) return fail(ATTN_JVP_E_INVALID, "some row has more than two key intervals");
+    const int32_t* rows = p->rs->table.data() + p->rs->off_rows;
+    const int32_t* iv = p->rs->table.data() + p->rs->off_iv;
+    for (int32_t i = 0; i < p->g.seq_len; ++i) {
+      const int32_t off = rows[i] >> 8, cnt = rows[i] & 255;
+      out[4 * i + 0] = cnt >= 1 ? iv[2 * off] : 0;
+      out[4 * i + 1] = cnt >= 1 ? iv[2 * off + 1] : 0;
+      out[4 * i + 2] = cnt >= 2 ? iv[2 * off + 2] : 0;
+      out[4 * i + 3] = cnt >= 2 ? iv[2 * off + 3] : 0;
+    }
+    return ok();
+  }
   for (int32_t i = 0; i < p->g.seq_len; ++i) {
     const Ranges r = row_ranges(p->g, i);
     out[4 * i + 0] = r.lo1;
@@ -429,6 +710,13 @@ int attn_jvp_tile_map(const attn_jvp_plan* p, uint8_t* out, size_t n) {
   const size_t need = (size_t)p->n_qblocks * p->n_ktiles;
   if (n < need) return fail(ATTN_JVP_E_INVALID, "host_out holds %zu bytes, need %zu", n, need);
   std::memset(out, 0, need);
+  if (p->rs) {
+    const int32_t* blk = p->rs->table.data() + p->rs->off_blk;
+    const int32_t* ent = p->rs->table.data() + p->rs->off_ent;
+    for (int32_t qb = 0; qb < p->n_qblocks; ++qb)
+      for (int32_t e = blk[qb]; e < blk[qb + 1]; ++e) out[(size_t)qb * p->n_ktiles + (ent[e] & 0xffffff)] = p->rs->ent_class[e];
+    return ok();
+  }
   for (int32_t qb = 0; qb < p->n_qblocks; ++qb) {
     int32_t r0, r1;
     qblock_rows(p->g, p->block_q, qb, &r0, &r1);

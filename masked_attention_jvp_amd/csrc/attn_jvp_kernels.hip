@@ -61,9 +61,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 // every key they see is clean, so t_o = 0 and only o and lse are formed).
 enum : int { kFull = 0, kCleanKeys = 1, kPrimal = 2 };
 
-template <int D, int NW, bool CTZ>
+template <int D, int NW, bool CTZ, bool TABLE>
 __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  static_assert(!(CTZ && TABLE), "range-list plans have no clean-tangent-zero mode");
   constexpr int BC = kBf16BlockK;            // keys per tile (= one MFMA subtile)
   static_assert(BC == 32, "one 32-key subtile per tile");
   constexpr int STAGES = 4;                  // LDS ring depth; tiles j..j+3 resident or in flight
@@ -92,11 +93,35 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   const MaskGeom g = p.g;
   const int N = g.seq_len;
   const int bh = blockIdx.x / p.n_qblocks;
-  const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks, CTZ);
-  int r0, r1;
-  qblock_rows(g, BR, qb, &r0, &r1);
-  const TileSpans sp = block_tiles(block_ranges(g, r0, r1), BC);
-  const int ntiles = span_count(sp);
+  int qb, r0, r1, ntiles, e0 = 0;
+  TileSpans sp{0, 0, 0, 0};
+  if constexpr (TABLE) {
+    // range-list plan: block, rows and tile list from the schedule table
+    qb = p.tb_order[blockIdx.x - bh * p.n_qblocks];
+    r0 = qb * BR;
+    r1 = r0 + BR < N ? r0 + BR : N;
+    e0 = p.tb_blk[qb];
+    ntiles = p.tb_blk[qb + 1] - e0;
+  } else {
+    qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks, CTZ);
+    qblock_rows(g, BR, qb, &r0, &r1);
+    sp = block_tiles(block_ranges(g, r0, r1), BC);
+    ntiles = span_count(sp);
+  }
+  // Range-list plans: the block's tile entries (tile | whole bit of wave w
+  // << (24 + w)) staged in LDS for the whole task.
+  int32_t* ent = nullptr;
+  if constexpr (TABLE) {
+    __shared__ int32_t ent_buf[kMaxTableEntries];
+    for (int i = tid; i < ntiles; i += NW * 64) ent_buf[i] = p.tb_ent[e0 + i];
+    __syncthreads();
+    ent = ent_buf;
+  }
+  // tile index of the t-th streamed tile (t < ntiles)
+  auto tile_at = [&](int t) -> int {
+    if constexpr (TABLE) return __builtin_amdgcn_readfirstlane(ent[t] & 0xffffff);
+    else return span_tile(sp, t);
+  };
   const bool primal_only = CTZ && !is_noisy(g, r0);  // a clean-side block
   // Clean-tangent-zero, noisy block: the leading tiles whose keys all lie on
   // the clean side (below N_h) need no key tangents.  A tile that reaches N_h
@@ -124,7 +149,37 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 
   const int row = r0 + wave * 32 + n;
   const bool row_ok = row < r1;
-  const Ranges rr = row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0};
+  // Range-list plans: the row's first two intervals here, any further ones
+  // read in the (rare) mask branch; n_iv = 0 for rows in no group.
+  int n_iv = 0, iv_off = 0;
+  const Ranges rr = [&]() -> Ranges {
+    if constexpr (TABLE) {
+      Ranges r{0, 0, 0, 0};
+      if (row_ok) {
+        const int info = p.tb_rows[row];
+        n_iv = info & 255;
+        iv_off = info >> 8;
+        if (n_iv >= 1) {
+          r.lo1 = p.tb_iv[2 * iv_off];
+          r.hi1 = p.tb_iv[2 * iv_off + 1];
+        }
+        if (n_iv >= 2) {
+          r.lo2 = p.tb_iv[2 * iv_off + 2];
+          r.hi2 = p.tb_iv[2 * iv_off + 3];
+        }
+      }
+      return r;
+    } else {
+      return row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0};
+    }
+  }();
+  int max_iv = 0;  // wave-uniform: the most intervals any row of the wave has
+  if constexpr (TABLE) {
+    int m = n_iv;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o));
+    max_iv = __builtin_amdgcn_readfirstlane(m);
+  }
 
   // Q and tQ fragments stay in registers for the whole task (B operands).
   u32x4 qf[KS], tqf[KS];
@@ -168,7 +223,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   // stage that just became free, which nothing reads, so the ring always has
   // the same number of loads in flight.
   auto issue_part = [&](auto mode, uint16_t* dst, int t, int q, int t_end) {
-    const int tile = span_tile(sp, t < t_end ? t : t_end - 1);
+    const int tile = tile_at(t < t_end ? t : t_end - 1);
     const int soff = tile * BC * D * 2;
     if constexpr (decltype(mode)::value == kFull) {
       const int i = q >> 2, tt = q & 3;
@@ -228,7 +283,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   // for all of them iff it lies in [0, f1) or in [g0, g1): f1 and g1 from the
   // wave's first valid row, g0 from its last.  Scalar values.
   int f1 = 1 << 30, g0 = 0, g1 = 1 << 30;
-  {
+  if constexpr (!TABLE) {
     const int wa = r0 + wave * 32;
     const int wb = wa + 32 < r1 ? wa + 32 : r1;
     if (wa < wb) {
@@ -242,19 +297,54 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   // Mask tile t's scores where some row of the wave does not cover the whole
   // tile (S -> -inf, TS -> 0 outside the row's ranges).  The test is scalar;
   // the masking itself runs on partial tiles only.
+  // (t may run one past the last tile on a run's last step; range-list
+  // plans clamp it, its result is not used)
   auto tile_whole = [&](int t) {
-    const int k0 = span_tile(sp, t) * BC;
-    return k0 + BC <= f1 || (k0 >= g0 && k0 + BC <= g1);
+    if constexpr (TABLE) {
+      const int e = __builtin_amdgcn_readfirstlane(ent[t < ntiles ? t : ntiles - 1]);
+      return ((e >> (24 + wave)) & 1) != 0;
+    } else {
+      const int k0 = span_tile(sp, t) * BC;
+      return k0 + BC <= f1 || (k0 >= g0 && k0 + BC <= g1);
+    }
   };
   auto mask_tile = [&](int t, f32x16& S, f32x16& TS) {
-    const int k0 = span_tile(sp, t) * BC;
-    const int b1 = k0 + 4 * h - rr.lo1, b2 = k0 + 4 * h - rr.lo2;
+    if constexpr (TABLE) {
+      const int k0 = tile_at(t < ntiles ? t : ntiles - 1) * BC;
+      const int b1 = k0 + 4 * h - rr.lo1, b2 = k0 + 4 * h - rr.lo2;
+      uint32_t okm = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int off = 8 * (i >> 2) + (i & 3);
-      const bool ok = (unsigned)(b1 + off) < (unsigned)len1 || (unsigned)(b2 + off) < (unsigned)len2;
-      S[i] = ok ? S[i] : -INFINITY;
-      TS[i] = ok ? TS[i] : 0.f;
+      for (int i = 0; i < 16; ++i) {
+        const int off = 8 * (i >> 2) + (i & 3);
+        if ((unsigned)(b1 + off) < (unsigned)len1 || (unsigned)(b2 + off) < (unsigned)len2) okm |= 1u << i;
+      }
+      for (int k = 2; k < max_iv; ++k) {  // rows with more than two intervals (rare)
+        int lo = 0, len = 0;
+        if (k < n_iv) {
+          lo = p.tb_iv[2 * (iv_off + k)];
+          len = p.tb_iv[2 * (iv_off + k) + 1] - lo;
+        }
+        const int b3 = k0 + 4 * h - lo;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if ((unsigned)(b3 + 8 * (i >> 2) + (i & 3)) < (unsigned)len) okm |= 1u << i;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool ok = (okm >> i) & 1u;
+        S[i] = ok ? S[i] : -INFINITY;
+        TS[i] = ok ? TS[i] : 0.f;
+      }
+    } else {
+      const int k0 = span_tile(sp, t) * BC;
+      const int b1 = k0 + 4 * h - rr.lo1, b2 = k0 + 4 * h - rr.lo2;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int off = 8 * (i >> 2) + (i & 3);
+        const bool ok = (unsigned)(b1 + off) < (unsigned)len1 || (unsigned)(b2 + off) < (unsigned)len2;
+        S[i] = ok ? S[i] : -INFINITY;
+        TS[i] = ok ? TS[i] : 0.f;
+      }
     }
   };
   // New reference max of a row after a tile with row max tmx (exp2 units):
@@ -611,21 +701,30 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 // D/8 consecutive columns.  Keys are taken one at a time from the same tile
 // schedule as the bf16 kernel, with the exact per-row mask; the online
 // softmax is the plain FlashAttention-2 recurrence in fp32 (no lazy scaling).
-template <int D>
+// Range-list plans (TABLE) take each row's key intervals from the table, in
+// ascending order.
+template <int D, bool TABLE>
 __global__ void __launch_bounds__(256) fwd_fp32_kernel(FwdParams p) {
   constexpr int BR = 32, BC = 32, E = D / 8;
   const MaskGeom g = p.g;
   const int N = g.seq_len;
   const int slice = threadIdx.x & 7, lr = threadIdx.x >> 3;
   const int bh = blockIdx.x / p.n_qblocks;
-  const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks, p.ctz != 0);
-  int r0, r1;
-  qblock_rows(g, BR, qb, &r0, &r1);
-  const TileSpans sp = block_tiles(block_ranges(g, r0, r1), BC);
-  const int ntiles = span_count(sp);
+  int qb, r0, r1, ntiles = 0;
+  TileSpans sp{0, 0, 0, 0};
+  if constexpr (TABLE) {
+    qb = p.tb_order[blockIdx.x - bh * p.n_qblocks];
+    r0 = qb * BR;
+    r1 = r0 + BR < N ? r0 + BR : N;
+  } else {
+    qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks, p.ctz != 0);
+    qblock_rows(g, BR, qb, &r0, &r1);
+    sp = block_tiles(block_ranges(g, r0, r1), BC);
+    ntiles = span_count(sp);
+  }
   const int row = r0 + lr;
   const bool row_ok = row < r1;
-  const Ranges rr = row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0};
+  const Ranges rr = TABLE ? Ranges{0, 0, 0, 0} : (row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0});
 
   const size_t base = (size_t)bh * (size_t)N * D;
   const float* __restrict__ K = (const float*)p.k + base + slice * E;
@@ -650,11 +749,7 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(FwdParams p) {
     for (int e = 0; e < E; ++e) tq[e] = ((const float*)p.tq)[base + (size_t)qrow * D + slice * E + e];
   }
   float m = -INFINITY, l = 0.f, r = 0.f;
-  for (int it = 0; it < ntiles; ++it) {
-    const int k0 = span_tile(sp, it) * BC;
-    const int k1 = k0 + BC < N ? k0 + BC : N;
-    for (int j = k0; j < k1; ++j) {
-      if (!in_ranges(rr, j)) continue;  // uniform across the row's 8 lanes
+  auto key_step = [&](int j) {
       const float* kj = K + (size_t)j * D;
       const float* tkj = tK + (size_t)j * D;
       const bool key_tangent = !(ctz && j < g.side_len);
@@ -700,6 +795,22 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(FwdParams p) {
         }
       }
       m = mn;
+  };
+  if constexpr (TABLE) {
+    if (row_ok) {  // uniform across the row's 8 lanes
+      const int info = p.tb_rows[row];
+      const int n_iv = info & 255, iv_off = info >> 8;
+      for (int k = 0; k < n_iv; ++k)
+        for (int j = p.tb_iv[2 * (iv_off + k)], j1 = p.tb_iv[2 * (iv_off + k) + 1]; j < j1; ++j) key_step(j);
+    }
+  } else {
+    for (int it = 0; it < ntiles; ++it) {
+      const int k0 = span_tile(sp, it) * BC;
+      const int k1 = k0 + BC < N ? k0 + BC : N;
+      for (int j = k0; j < k1; ++j) {
+        if (!in_ranges(rr, j)) continue;  // uniform across the row's 8 lanes
+        key_step(j);
+      }
     }
   }
   if (!row_ok) return;
@@ -730,19 +841,25 @@ void block_sizes(int dtype, int head_dim, int* block_q, int* block_k) {
 
 hipError_t launch_fwd(int dtype, int head_dim, int grid, const FwdParams& p, hipStream_t stream) {
   const dim3 block(kBf16Waves * 64);
+  const bool table = p.tb_ent != nullptr;
   if (dtype == kBf16) {
     if (head_dim == 128) {
-      if (p.ctz) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, true>), dim3(grid), block, 0, stream, p);
-      else hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, false>), dim3(grid), block, 0, stream, p);
+      if (table) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, false, true>), dim3(grid), block, 0, stream, p);
+      else if (p.ctz) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, true, false>), dim3(grid), block, 0, stream, p);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, false, false>), dim3(grid), block, 0, stream, p);
     } else {
-      if (p.ctz) hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, true>), dim3(grid), block, 0, stream, p);
-      else hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, false>), dim3(grid), block, 0, stream, p);
+      if (table) hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, false, true>), dim3(grid), block, 0, stream, p);
+      else if (p.ctz) hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, true, false>), dim3(grid), block, 0, stream, p);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, false, false>), dim3(grid), block, 0, stream, p);
     }
   } else {
-    if (head_dim == 128)
-      hipLaunchKernelGGL((fwd_fp32_kernel<128>), dim3(grid), dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((fwd_fp32_kernel<64>), dim3(grid), dim3(256), 0, stream, p);
+    if (head_dim == 128) {
+      if (table) hipLaunchKernelGGL((fwd_fp32_kernel<128, true>), dim3(grid), dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((fwd_fp32_kernel<128, false>), dim3(grid), dim3(256), 0, stream, p);
+    } else {
+      if (table) hipLaunchKernelGGL((fwd_fp32_kernel<64, true>), dim3(grid), dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((fwd_fp32_kernel<64, false>), dim3(grid), dim3(256), 0, stream, p);
+    }
   }
   return hipGetLastError();
 }

@@ -13,6 +13,11 @@ constexpr int kFp32 = 1;
 constexpr int kBf16Waves = 4;   // waves per bf16 workgroup; 32 query rows per wave
 constexpr int kBf16BlockK = 32;  // keys per bf16 tile
 
+// Range-list plans: the bf16 kernel stages a query block's tile entries in
+// LDS next to the 128 KB ring, so a block may stream at most this many tiles.
+constexpr int kMaxTableEntries = 7680;
+constexpr int32_t kTableMagic = 0x314a5441;  // "ATJ1"
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -28,6 +33,12 @@ struct FwdParams {
   float score_log2;   // scale * log2(e)
   float scale;
   int32_t ctz;        // clean-tangent-zero plan (teacher forcing only)
+  // range-list plans (all null otherwise): sections of the device table
+  const int32_t* tb_blk;    // [n_qblocks + 1] first entry of each query block
+  const int32_t* tb_order;  // [n_qblocks] launch order
+  const int32_t* tb_ent;    // tile | (whole bit of wave w) << (24 + w)
+  const int32_t* tb_rows;   // [N] (first interval << 8) | interval count
+  const int32_t* tb_iv;     // (lo, hi) pairs
 };
 
 struct BwdParams {

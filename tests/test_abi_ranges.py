@@ -1,0 +1,163 @@
+"""Host-side checks of range-list plans (query groups x key intervals), no GPU.
+
+* argument validation before anything is built;
+* the plan's tile map (which key tiles each query block streams, and whether
+  every pair of a tile is allowed) equals the oracle's tile classification of
+  the same RangeMask bit for bit, for bf16 and fp32 block sizes, at small
+  ragged sizes and at the full c1-4 workload;
+* per-row key intervals equal the oracle mask; pair counts and useful FLOPs;
+* the serialised table: header, heavy-first launch order, per-wave whole bits
+  against the oracle mask.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from oracle import RangeMask
+import masked_attention_jvp_amd as aj
+
+pytestmark = pytest.mark.skipif(not os.path.exists(aj.library_path), reason="libattn_jvp.so not built")
+
+GAPS = (40, ((0, 6, ((0, 3), (10, 14))), (9, 15, ((0, 40),)), (15, 33, ((5, 6), (20, 33))), (35, 40, ((1, 2),))))
+MULTI = (70, ((0, 30, ((0, 3), (7, 9), (12, 20), (33, 40))), (30, 70, ((0, 70),))))  # rows with four intervals
+
+MASKS = {
+    "tf_c1_2": si.chunked_mask_ranges(16, (1, 2, 2), 1),
+    "tf_c1_4_t50": si.chunked_mask_ranges(50, (1, 4, 4), 1),
+    "bc_c2_1_t37": si.chunked_mask_ranges(37, (2, 1, 1, 3), 0),
+    "und_gen": si.und_gen_ranges(20, 5, 30),
+    "dense": (150, ((0, 150, ((0, 150),)),)),
+    "gaps": GAPS,
+    "multi": MULTI,
+    "tf_eq_as_ranges": si.chunked_mask_ranges(50, (1,) * 5, 1),
+}
+
+
+def _plan(name, dtype=aj.ATTN_JVP_BF16, d=128, b=1, h=1):
+    n, groups = MASKS[name]
+    return aj.attn_jvp_create_ranges(n, groups, b, h, d, dtype), RangeMask(n, groups)
+
+
+@pytest.mark.parametrize("name", sorted(MASKS))
+@pytest.mark.parametrize("dtype, d", [(aj.ATTN_JVP_BF16, 128), (aj.ATTN_JVP_BF16, 64), (aj.ATTN_JVP_FP32, 64)])
+def test_range_tile_map_matches_oracle(name, dtype, d):
+    p, rm = _plan(name, dtype, d)
+    info = p.info
+    want = oracle.tile_classes(rm, info["block_q"], info["block_k"])
+    got = aj.attn_jvp_tile_map(p)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+    assert info["visited_tiles_per_head"] == int((want > 0).sum())
+    assert info["allowed_pairs_per_head"] == oracle.pair_count(rm)
+
+
+@pytest.mark.parametrize("name", sorted(set(MASKS) - {"multi"}))
+def test_range_row_ranges_match_oracle(name):
+    p, rm = _plan(name)
+    rr = aj.attn_jvp_row_ranges(p)
+    keys = np.arange(p.seq_len)
+    lo1, hi1, lo2, hi2 = (rr[:, i:i + 1] for i in range(4))
+    got = ((keys >= lo1) & (keys < hi1)) | ((keys >= lo2) & (keys < hi2))
+    assert np.array_equal(got, oracle.mask_dense(rm))
+
+
+def test_row_ranges_refuse_rows_with_more_than_two_intervals():
+    p, _ = _plan("multi")
+    with pytest.raises(aj.AttnJvpError) as e:
+        aj.attn_jvp_row_ranges(p)
+    assert e.value.code == 1
+
+
+@pytest.mark.parametrize("name", sorted(MASKS))
+def test_range_table_order_and_whole_bits(name):
+    p, rm = _plan(name)
+    t = aj.attn_jvp_plan_table(p)
+    nq = p.info["n_query_blocks"]
+    assert t[0] == 0x314a5441 and t[1] == nq
+    blk = t[8:8 + nq + 1]
+    order = t[8 + nq + 1:8 + 2 * nq + 1]
+    ent = t[8 + 2 * nq + 1:8 + 2 * nq + 1 + t[2]]
+    assert blk[0] == 0 and blk[-1] == t[2] == len(ent) and np.all(np.diff(blk) >= 0)
+    assert sorted(order.tolist()) == list(range(nq))
+    assert np.array_equal(order, aj.attn_jvp_launch_order(p))
+    counts = np.diff(blk)[order]
+    assert np.all(np.diff(counts) <= 0)  # heavy (more tiles) first
+    m = oracle.mask_dense(rm)
+    n = p.seq_len
+    for qb in range(nq):
+        tiles = ent[blk[qb]:blk[qb + 1]] & 0xffffff
+        assert np.all(np.diff(tiles) > 0)  # ascending key order
+        for e in ent[blk[qb]:blk[qb + 1]]:
+            tile = int(e) & 0xffffff
+            k0 = 32 * tile
+            for w in range(4):
+                r0, r1 = 128 * qb + 32 * w, min(128 * qb + 32 * w + 32, 128 * qb + 128, n)
+                whole = bool((int(e) >> (24 + w)) & 1)
+                if r0 >= r1:
+                    assert whole  # no valid rows in this wave
+                else:
+                    assert whole == bool(k0 + 32 <= n and m[r0:r1, k0:k0 + 32].all())
+
+
+def test_c1_4_workload_tile_map_matches_oracle():
+    w = si.RANGE_WORKLOADS[6]
+    n, groups = w.mask_ranges()
+    p = aj.attn_jvp_create_ranges(n, groups, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16)
+    rm = RangeMask(n, groups)
+    info = p.info
+    assert np.array_equal(aj.attn_jvp_tile_map(p), oracle.tile_classes(rm, info["block_q"], info["block_k"]))
+    assert info["allowed_pairs_per_head"] == oracle.pair_count(rm)
+    assert aj.attn_jvp_plan_flops(p) == 12 * 128 * 12 * oracle.pair_count(rm)
+
+
+def test_equal_chunks_as_ranges_count_like_the_descriptor():
+    for desc in [(1560, 21, 1, 1), (1560, 21, 3, 1), (1560, 21, 1, 0)]:
+        tpf, f, c, tf = desc
+        n, groups = si.chunked_mask_ranges(tpf, (c,) * (f // c), tf)
+        pr = aj.attn_jvp_create_ranges(n, groups, 1, 12, 128)
+        pd = aj.attn_jvp_create(desc, 1, 12, 128)
+        assert pr.info["allowed_pairs_per_head"] == pd.info["allowed_pairs_per_head"]
+        assert aj.attn_jvp_plan_flops(pr) == aj.attn_jvp_plan_flops(pd)
+
+
+def test_overlapping_and_unsorted_intervals_are_merged():
+    p = aj.attn_jvp_create_ranges(64, [(0, 64, [(40, 50), (0, 10), (5, 20), (20, 25), (30, 30)])], 1, 1, 128)
+    rr = aj.attn_jvp_row_ranges(p)
+    assert rr[0].tolist() == [0, 25, 40, 50]
+    assert p.info["allowed_pairs_per_head"] == 64 * 35
+
+
+@pytest.mark.parametrize("n, groups", [
+    (0, [(0, 1, [(0, 1)])]),                       # no tokens
+    (10, [(0, 5, [(0, 5)]), (3, 8, [(0, 5)])]),     # overlapping groups
+    (10, [(5, 8, [(0, 5)]), (0, 3, [(0, 5)])]),     # unsorted groups
+    (10, [(0, 11, [(0, 5)])]),                      # rows past the end
+    (10, [(4, 4, [(0, 5)])]),                       # empty group
+    (10, [(0, 5, [(0, 11)])]),                      # interval past the end
+    (10, [(0, 5, [(6, 3)])]),                       # reversed interval
+    (2000, [(0, 5, [(2 * i, 2 * i + 1) for i in range(300)])]),  # 300 disjoint intervals in one group
+])
+def test_create_ranges_rejects_bad_input(n, groups):
+    with pytest.raises(aj.AttnJvpError) as e:
+        aj.attn_jvp_create_ranges(n, groups, 1, 1, 128)
+    assert e.value.code == 1
+    assert aj.attn_jvp_last_error_detail()
+
+
+def test_range_plan_entry_points_refuse_the_wrong_plan_kind():
+    lib = aj._load()
+    pr, _ = _plan("gaps")
+    pd = aj.attn_jvp_create((4, 3, 1, 1), 1, 1, 64, aj.ATTN_JVP_BF16)
+    good = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(9)]  # table + 8 tensors
+    assert lib.attn_jvp_fwd(pr.handle, *good[1:], None, None) == 1
+    assert "attn_jvp_fwd_table" in aj.attn_jvp_last_error_detail()
+    assert lib.attn_jvp_fwd_table(pd.handle, *good, None, None) == 1
+    assert lib.attn_jvp_fwd_table(pr.handle, None, *good[1:], None, None) == 2
+    assert lib.attn_jvp_fwd_table(pr.handle, ctypes.c_void_p(0x100002), *good[1:], None, None) == 3
+    bwd = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(10)]
+    assert lib.attn_jvp_bwd(pr.handle, *bwd, None) == 1
+    assert aj.attn_jvp_plan_table_size(pd) == 0
