@@ -14,6 +14,11 @@ counted (partial tiles included), exp and other vector work not counted.
 With --clean-tangent-zero: 4 d per clean-row pair, 8 d per noisy-row /
 clean-key pair, 12 d per noisy-row / noisy-key pair (attn_jvp_plan_flops).
 
+--ranges runs the workload's mask as a range list (query groups x key
+intervals, attn_jvp_fwd_table); --config 6, the c1-4 teacher-forcing
+workload (a one-frame first chunk, then four-frame chunks), exists only as a
+range list.
+
 --backward measures the backward instead (attn_jvp_bwd: the dq kernel, then
 the dk/dv kernel, from q, k, v, o, lse and dO on the same plan); useful
 FLOPs = 10 d x (allowed pairs) x B x H (q.k, dO.v, dS k, dS q, P dO).
@@ -54,7 +59,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, help="workload id (2..5)")
+    ap.add_argument("--config", type=int, default=3, help="workload id (2..5; 6 = c1-4, range list)")
+    ap.add_argument("--ranges", action="store_true",
+                    help="run the mask as a range list through the schedule-table kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=1)
     ap.add_argument("--heads", type=int, default=0,
@@ -172,6 +179,30 @@ def cpu_baseline_bwd(w, heads):
     }
 
 
+def cpu_baseline_ranges(w, heads):
+    """The oracle on the range-list mask, untuned, on (b, h) slices."""
+    import oracle
+    import seeded_inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    rm = oracle.RangeMask(*w.mask_ranges())
+    flops, elapsed = 0, 0.0
+    for h in range(heads):
+        args = [si.slice_values(w, t, 0, h) for t in si.TENSORS]
+        t0 = time.perf_counter()
+        oracle.masked_attention_jvp_slice(*args, rm)
+        elapsed += time.perf_counter() - t0
+        flops += 12 * w.head_dim * oracle.pair_count(rm)
+    return {
+        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{heads} of {w.batch * w.heads} (b,h) slices of {w.name} (all rows, range-list mask), "
+                  f"fp64 NumPy, {elapsed:.1f} s",
+    }
+
+
 def cpu_baseline(w, heads, clean_tangent_zero=False):
     """The oracle, untuned, on (b, h) slices of the same workload."""
     import numpy as np
@@ -215,7 +246,16 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
-    w = si.WORKLOADS[args.config]
+    w = si.WORKLOADS.get(args.config) or si.RANGE_WORKLOADS.get(args.config)
+    if w is None:
+        print(json.dumps({"error": f"unknown workload {args.config}"}))
+        sys.exit(2)
+    use_ranges = args.ranges or args.config in si.RANGE_WORKLOADS
+    if use_ranges and (args.backward or args.clean_tangent_zero):
+        print(json.dumps({"error": "range-list plans run the forward + JVP only"}))
+        sys.exit(2)
+    if args.ranges and args.config not in si.RANGE_WORKLOADS:
+        w = w.with_(name=f"{w.name}_ranges")
     if args.heads > 0 and args.heads != w.heads:
         w = w.with_(heads=args.heads, name=f"{w.name}_h{args.heads}")
     flags = 0
@@ -235,11 +275,18 @@ def main():
         bits = si.full_tensor_bits(w, t)
         x[t] = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
         del bits
-    plan = aj.attn_jvp_create_ex(w.desc, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16, 0.0, flags)
+    if use_ranges:
+        n_tok, groups = w.mask_ranges()
+        plan = aj.attn_jvp_create_ranges(n_tok, groups, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16)
+        table = torch.from_numpy(aj.attn_jvp_plan_table(plan)).to(dev)
+    else:
+        plan = aj.attn_jvp_create_ex(w.desc, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16, 0.0, flags)
     o = torch.empty_like(x["q"])
     to = torch.empty_like(x["q"])
     lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
-    if not args.backward:
+    if use_ranges:
+        call = lambda: aj.attn_jvp_fwd_table(plan, table, *(x[t] for t in si.TENSORS), o, to, lse)
+    elif not args.backward:
         call = lambda: aj.attn_jvp_fwd(plan, *(x[t] for t in si.TENSORS), o, to, lse)
     else:
         # o and lse of these inputs, once, outside the timed region
@@ -283,7 +330,7 @@ def main():
     traffic = traffic_for(w.name, part)
     nw = info["block_q"] // 32
     kernel = (f"bwd_dq_bf16_kernel<{w.head_dim},{nw}> + bwd_dkdv_bf16_kernel<{w.head_dim},{nw}>" if args.backward
-              else f"fwd_bf16_kernel<{w.head_dim},{nw},{'true' if flags else 'false'}>")
+              else f"fwd_bf16_kernel<{w.head_dim},{nw},{'true' if flags else 'false'},{'true' if use_ranges else 'false'}>")
 
     out = {
         "metric": METRIC_BWD if args.backward else METRIC,
@@ -305,6 +352,8 @@ def main():
             "head_dim": w.head_dim, "tokens_per_frame": w.tokens_per_frame, "n_frames": w.n_frames,
             "frames_per_chunk": w.frames_per_chunk, "tf_layout": w.tf_layout,
             "clean_tangent_zero": bool(flags), "pass": "backward" if args.backward else "forward+jvp",
+            "mask": "range list" if use_ranges else "descriptor",
+            "chunk_frames": list(w.chunks),
         },
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "useful_tflop_per_step": round(useful / 1e12, 4),
@@ -328,6 +377,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_sample_heads) if args.backward
+                               else cpu_baseline_ranges(w, args.cpu_sample_heads) if use_ranges
                                else cpu_baseline(w, args.cpu_sample_heads, bool(flags)))
     print(json.dumps(out), flush=True)
 

@@ -92,12 +92,17 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 
   const MaskGeom g = p.g;
   const int N = g.seq_len;
-  const int bh = blockIdx.x / p.n_qblocks;
+  // Range-list plans: workgroups take the (heavy-first) table order in XCD
+  // groups of 16 (xcd_grouped): neighbouring blocks of that order, which
+  // stream nearly the same key tiles, share an XCD's L2.
+  int task = 0;
+  if constexpr (TABLE) task = xcd_grouped((int)blockIdx.x, (int)gridDim.x, 16);
+  const int bh = TABLE ? task / p.n_qblocks : (int)(blockIdx.x / p.n_qblocks);
   int qb, r0, r1, ntiles, e0 = 0;
   TileSpans sp{0, 0, 0, 0};
   if constexpr (TABLE) {
     // range-list plan: block, rows and tile list from the schedule table
-    qb = p.tb_order[blockIdx.x - bh * p.n_qblocks];
+    qb = p.tb_order[task - bh * p.n_qblocks];
     r0 = qb * BR;
     r1 = r0 + BR < N ? r0 + BR : N;
     e0 = p.tb_blk[qb];
@@ -222,8 +227,11 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   // branch-free: past the run's last tile that tile is loaded again into the
   // stage that just became free, which nothing reads, so the ring always has
   // the same number of loads in flight.
-  auto issue_part = [&](auto mode, uint16_t* dst, int t, int q, int t_end) {
-    const int tile = tile_at(t < t_end ? t : t_end - 1);
+  // (range-list plans pass the tile index, read once per step: tile_pre)
+  auto issue_part = [&](auto mode, uint16_t* dst, int t, int q, int t_end, int tile_pre) {
+    int tile;
+    if constexpr (TABLE) tile = tile_pre;
+    else tile = span_tile(sp, t < t_end ? t : t_end - 1);
     const int soff = tile * BC * D * 2;
     if constexpr (decltype(mode)::value == kFull) {
       const int i = q >> 2, tt = q & 3;
@@ -236,8 +244,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     }
   };
   auto issue = [&](auto mode, uint16_t* dst, int t, int t_end) {
+    int tile_pre = 0;
+    if constexpr (TABLE) tile_pre = tile_at(t < t_end ? t : t_end - 1);
 #pragma unroll
-    for (int q = 0; q < lpt(mode); ++q) issue_part(mode, dst, t, q, t_end);
+    for (int q = 0; q < lpt(mode); ++q) issue_part(mode, dst, t, q, t_end, tile_pre);
   };
 
   // accO = sum p~ v, accV = sum p~ tv, accS = sum (p~ ts') v with the
@@ -424,6 +434,15 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    // range-list plans: the tile of this step's DMA and whether tile j+1 is
+    // whole, each read once from the LDS entries here, far ahead of use
+    int dma_tile = 0;
+    bool next_whole = false;
+    if constexpr (TABLE) {
+      dma_tile = tile_at(j + 3 < t_end ? j + 3 : t_end - 1);
+      next_whole = tile_whole(j + 1);
+    }
+
     const uint16_t* nx = stage(NX{});  // on the last tile a stale stage; unused
     const uint16_t* cur = stage(st);
     float wv[16];
@@ -463,7 +482,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     };
     auto dma = [&](int s) {  // this k-step's share of tile j+3's DMA
 #pragma unroll
-      for (int q = s * LPTM / KS; q < (s + 1) * LPTM / KS; ++q) issue_part(mode, stage(AH{}), j + 3, q, t_end);
+      for (int q = s * LPTM / KS; q < (s + 1) * LPTM / KS; ++q)
+        issue_part(mode, stage(AH{}), j + 3, q, t_end, dma_tile);
     };
 
     // phase 1: scores of tile j+1 under the back half of tile j's softmax.
@@ -548,7 +568,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     auto slot_work = [&](int gidx, int sl) {
       const int u = gidx * NS2 + sl;
       // (after group 1's first MFMA: two MFMAs past the last score product in every mode)
-      if (gidx == 1 && sl == 0 && !tile_whole(j + 1)) mask_tile(j + 1, Sn, TSn);  // rare
+      if (gidx == 1 && sl == 0 && !(TABLE ? next_whole : tile_whole(j + 1))) mask_tile(j + 1, Sn, TSn);  // rare
       if (sl == 0 && gidx + 2 < NG) vread(gidx + 2);
       if (u == UB) {
         // every read of tile j's stage is done; tile j+2 has landed here
