@@ -19,6 +19,9 @@ intervals, attn_jvp_fwd_table); --config 6, the c1-4 teacher-forcing
 workload (a one-frame first chunk, then four-frame chunks), exists only as a
 range list.
 
+--primal measures the forward without tangents (attn_jvp_fwd_primal: o and
+lse only; useful FLOPs = 4 d x allowed pairs x B x H, for q.k and p.v).
+
 --backward measures the backward instead (attn_jvp_bwd: the dq kernel, then
 the dk/dv kernel, from q, k, v, o, lse and dO on the same plan); useful
 FLOPs = 10 d x (allowed pairs) x B x H (q.k, dO.v, dS k, dS q, P dO).
@@ -44,6 +47,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4 SIMD x 1024 bf16 flop/clk x 2.4 GHz (dense)
 METRIC = "useful TFLOP/s of masked attn fwd+JVP and % of bf16 MFMA peak, 1 GPU"
 METRIC_BWD = "useful TFLOP/s of masked attn backward (dq, dk, dv) and % of bf16 MFMA peak, 1 GPU"
+METRIC_PRIMAL = "useful TFLOP/s of masked attn forward without tangents and % of bf16 MFMA peak, 1 GPU"
 _CSRC = os.path.join(ROOT, "masked_attention_jvp_amd", "csrc")
 KERNEL_SRCS = {
     "fwd": [os.path.join(_CSRC, f) for f in ("attn_jvp_kernels.hip", "kernel_common.h", "attn_jvp_launch.h",
@@ -70,6 +74,8 @@ def parse():
     ap.add_argument("--clean-tangent-zero", action="store_true",
                     help="teacher-forcing plans whose clean tokens carry no tangent (useful FLOPs counted "
                          "for that case: about half the general work)")
+    ap.add_argument("--primal", action="store_true",
+                    help="time the forward without tangents (o and lse) instead of the forward + JVP")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (dq, dk, dv) on the same plan instead of the forward + JVP")
     ap.add_argument("--mode", choices=["attn", "copy"], default="attn",
@@ -179,6 +185,30 @@ def cpu_baseline_bwd(w, heads):
     }
 
 
+def cpu_baseline_primal(w, heads):
+    """The oracle (which forms o together with the tangent) on (b, h) slices;
+    only the primal's 4 d flops per pair are counted."""
+    import oracle
+    import seeded_inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    flops, elapsed = 0, 0.0
+    for h in range(heads):
+        args = [si.slice_values(w, t, 0, h) for t in si.TENSORS]
+        t0 = time.perf_counter()
+        oracle.masked_attention_jvp_slice(*args, w.desc)
+        elapsed += time.perf_counter() - t0
+        flops += 4 * w.head_dim * oracle.pair_count(w.desc)
+    return {
+        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{heads} of {w.batch * w.heads} (b,h) slices of {w.name} (all rows; the oracle forms o with "
+                  f"its tangent, 4 d flops per pair counted), fp64 NumPy, {elapsed:.1f} s",
+    }
+
+
 def cpu_baseline_ranges(w, heads):
     """The oracle on the range-list mask, untuned, on (b, h) slices."""
     import oracle
@@ -251,6 +281,9 @@ def main():
         print(json.dumps({"error": f"unknown workload {args.config}"}))
         sys.exit(2)
     use_ranges = args.ranges or args.config in si.RANGE_WORKLOADS
+    if args.primal and (args.backward or args.clean_tangent_zero or use_ranges):
+        print(json.dumps({"error": "--primal takes a descriptor workload without other modes"}))
+        sys.exit(2)
     if use_ranges and (args.backward or args.clean_tangent_zero):
         print(json.dumps({"error": "range-list plans run the forward + JVP only"}))
         sys.exit(2)
@@ -267,6 +300,8 @@ def main():
         w = w.with_(name=f"{w.name}_ctz")
     if args.backward:
         w = w.with_(name=f"{w.name}_bwd")
+    if args.primal:
+        w = w.with_(name=f"{w.name}_primal")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
@@ -286,6 +321,8 @@ def main():
     lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
     if use_ranges:
         call = lambda: aj.attn_jvp_fwd_table(plan, table, *(x[t] for t in si.TENSORS), o, to, lse)
+    elif args.primal:
+        call = lambda: aj.attn_jvp_fwd_primal(plan, x["q"], x["k"], x["v"], o, lse)
     elif not args.backward:
         call = lambda: aj.attn_jvp_fwd(plan, *(x[t] for t in si.TENSORS), o, to, lse)
     else:
@@ -323,17 +360,20 @@ def main():
     ms_per_step = total_ms / args.steps
 
     info = plan.info
-    useful = aj.attn_jvp_plan_bwd_flops(plan) if args.backward else aj.attn_jvp_plan_flops(plan)
+    useful = (aj.attn_jvp_plan_bwd_flops(plan) if args.backward
+              else 4 * w.head_dim * info["allowed_pairs_per_head"] * w.batch * w.heads if args.primal
+              else aj.attn_jvp_plan_flops(plan))
     value = useful / (ms_per_step * 1e-3) / 1e12
     achieved = useful / (avg_ms * 1e-3) / 1e12
     part = "bwd" if args.backward else "fwd"
     traffic = traffic_for(w.name, part)
     nw = info["block_q"] // 32
     kernel = (f"bwd_dq_bf16_kernel<{w.head_dim},{nw}> + bwd_dkdv_bf16_kernel<{w.head_dim},{nw}>" if args.backward
+              else f"fwd_bf16_kernel<{w.head_dim},{nw},true,false> (primal mode)" if args.primal
               else f"fwd_bf16_kernel<{w.head_dim},{nw},{'true' if flags else 'false'},{'true' if use_ranges else 'false'}>")
 
     out = {
-        "metric": METRIC_BWD if args.backward else METRIC,
+        "metric": METRIC_BWD if args.backward else METRIC_PRIMAL if args.primal else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -351,7 +391,8 @@ def main():
             "workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
             "head_dim": w.head_dim, "tokens_per_frame": w.tokens_per_frame, "n_frames": w.n_frames,
             "frames_per_chunk": w.frames_per_chunk, "tf_layout": w.tf_layout,
-            "clean_tangent_zero": bool(flags), "pass": "backward" if args.backward else "forward+jvp",
+            "clean_tangent_zero": bool(flags),
+            "pass": "backward" if args.backward else "forward" if args.primal else "forward+jvp",
             "mask": "range list" if use_ranges else "descriptor",
             "chunk_frames": list(w.chunks),
         },
@@ -377,6 +418,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_sample_heads) if args.backward
+                               else cpu_baseline_primal(w, args.cpu_sample_heads) if args.primal
                                else cpu_baseline_ranges(w, args.cpu_sample_heads) if use_ranges
                                else cpu_baseline(w, args.cpu_sample_heads, bool(flags)))
     print(json.dumps(out), flush=True)

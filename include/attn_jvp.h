@@ -170,6 +170,16 @@ int attn_jvp_fwd(const attn_jvp_plan* plan, const void* q, const void* k, const 
                  const void* tq, const void* tk, const void* tv, void* o, void* t_o,
                  float* lse, void* hip_stream);
 
+/* The masked attention alone, without tangents: o (and lse when non-NULL)
+ * of the plan's mask, as attn_jvp_fwd computes them (bit-identical), at
+ * 4 d useful flops per allowed pair instead of 12 d.  This is the forward
+ * that the backward (attn_jvp_bwd) pairs with: together they replace the
+ * plain FlashAttention-2 of a student's training step (Causal-rCM, section
+ * 3.2.1 and the TF-dCM comparison of section 6).  Descriptor plans; the
+ * plan's flags do not matter.  Same checks and error codes as attn_jvp_fwd. */
+int attn_jvp_fwd_primal(const attn_jvp_plan* plan, const void* q, const void* k, const void* v,
+                        void* o, float* lse, void* hip_stream);
+
 /* Backward of the masked attention (without tangents) on the same plan:
  * the gradients of a loss L with respect to q, k and v given dO = dL/do
  * (Causal-rCM, section 3.2.1: the student's FlashAttention-2 based masked

@@ -11,10 +11,10 @@ mirror the C ABI of ``include/attn_jvp.h`` one to one:
     attn_jvp_plan_bwd_flops, attn_jvp_plan_bwd_info, attn_jvp_launch_order,
     attn_jvp_bwd_launch_order, attn_jvp_row_ranges, attn_jvp_key_ranges,
     attn_jvp_tile_map, attn_jvp_create_ranges, attn_jvp_plan_table_size,
-    attn_jvp_plan_table, attn_jvp_fwd_table
+    attn_jvp_plan_table, attn_jvp_fwd_table, attn_jvp_fwd_primal
 
-plus ``masked_attention_jvp(...)``, ``masked_attention_jvp_ranges(...)`` and
-``masked_attention_bwd(...)``, which allocate the outputs (and the backward's
+plus ``masked_attention_jvp(...)``, ``masked_attention_jvp_ranges(...)``,
+``masked_attention_fwd(...)`` (no tangents) and ``masked_attention_bwd(...)``, which allocate the outputs (and the backward's
 workspace, or a range-list plan's device table) and call ``attn_jvp_fwd`` /
 ``attn_jvp_fwd_table`` / ``attn_jvp_bwd`` on the current stream.  If the library is not built the
 import of this module still works, but every call raises ``AttnJvpError``;
@@ -35,7 +35,8 @@ __all__ = [
     "attn_jvp_launch_order", "attn_jvp_row_ranges", "attn_jvp_tile_map", "masked_attention_jvp",
     "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops", "attn_jvp_key_ranges",
     "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order", "attn_jvp_create_ranges", "attn_jvp_plan_table_size",
-    "attn_jvp_plan_table", "attn_jvp_fwd_table", "masked_attention_jvp_ranges",
+    "attn_jvp_plan_table", "attn_jvp_fwd_table", "masked_attention_jvp_ranges", "attn_jvp_fwd_primal",
+    "masked_attention_fwd",
     "masked_attention_bwd",
 ]
 
@@ -104,11 +105,13 @@ def _load():
         lib.attn_jvp_plan_table_size.argtypes = [vp, P(ctypes.c_size_t)]
         lib.attn_jvp_plan_table.argtypes = [vp, vp, ctypes.c_size_t]
         lib.attn_jvp_fwd_table.argtypes = [vp] * 10 + [vp, vp]
+        lib.attn_jvp_fwd_primal.argtypes = [vp] * 7
         for name in ("attn_jvp_create", "attn_jvp_create_ex", "attn_jvp_fwd", "attn_jvp_destroy",
                      "attn_jvp_plan_info", "attn_jvp_plan_flops", "attn_jvp_launch_order", "attn_jvp_row_ranges",
                      "attn_jvp_tile_map", "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops",
                      "attn_jvp_key_ranges", "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order",
-                     "attn_jvp_create_ranges", "attn_jvp_plan_table_size", "attn_jvp_plan_table", "attn_jvp_fwd_table"):
+                     "attn_jvp_create_ranges", "attn_jvp_plan_table_size", "attn_jvp_plan_table", "attn_jvp_fwd_table",
+                     "attn_jvp_fwd_primal"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -342,6 +345,29 @@ def attn_jvp_fwd(plan: Plan, q, k, v, tq, tk, tv, o, t_o, lse=None, stream=None)
     _check(code, "attn_jvp_fwd")
 
 
+def attn_jvp_fwd_primal(plan: Plan, q, k, v, o, lse=None, stream=None) -> None:
+    """o (and lse) of the plan's masked attention, without tangents."""
+    import torch
+    ins = dict(q=q, k=k, v=v, o=o)
+    for name, t in ins.items():
+        _check_tensor(name, t, plan, plan.shape)
+    dev = q.device
+    for name, t in ins.items():
+        if t.device != dev:
+            raise AttnJvpError(f"{name} is on {t.device}, q is on {dev}")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != plan.shape[:3] or not lse.is_contiguous() \
+                or lse.device != dev:
+            raise AttnJvpError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        code = _load().attn_jvp_fwd_primal(plan.handle, *[ctypes.c_void_p(t.data_ptr()) for t in ins.values()],
+                                           ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
+                                           ctypes.c_void_p(stream.cuda_stream))
+    _check(code, "attn_jvp_fwd_primal")
+
+
 def attn_jvp_bwd(plan: Plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace, stream=None) -> None:
     """Enqueue the backward (dq, dk, dv) on `stream` (default: torch's current
     stream).  `workspace` is a float32 CUDA tensor of at least
@@ -425,6 +451,18 @@ def masked_attention_jvp(q, k, v, tq, tk, tv, desc, scale=None, return_lse=False
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
     attn_jvp_fwd(plan, q, k, v, tq, tk, tv, o, t_o, lse)
     return (o, t_o, lse) if return_lse else (o, t_o)
+
+
+def masked_attention_fwd(q, k, v, desc, scale=None, return_lse=False):
+    """(o[, lse]) of the masked attention alone (no tangents) for [B, H, N, d]
+    bf16 or fp32 CUDA tensors: the forward that pairs with the backward."""
+    import torch
+    dtype = ATTN_JVP_BF16 if q.dtype == torch.bfloat16 else ATTN_JVP_FP32
+    plan = _cached_plan(desc, q.shape, dtype, scale, 0)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    attn_jvp_fwd_primal(plan, q, k, v, o, lse)
+    return (o, lse) if return_lse else o
 
 
 def masked_attention_bwd(q, k, v, o, lse, d_o, desc, scale=None, return_workspace=False):

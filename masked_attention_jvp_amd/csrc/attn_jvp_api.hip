@@ -440,37 +440,40 @@ int attn_jvp_destroy(attn_jvp_plan* p) {
 
 namespace {
 
+// primal: o and lse only; tq, tk, tv and t_o are absent (NULL) and never touched.
 int fwd_common(const attn_jvp_plan* p, const void* table, const void* q, const void* k, const void* v,
-               const void* tq, const void* tk, const void* tv, void* o, void* t_o, float* lse, void* hip_stream) {
+               const void* tq, const void* tk, const void* tv, void* o, void* t_o, float* lse, void* hip_stream,
+               bool primal = false) {
   const void* ins[6] = {q, k, v, tq, tk, tv};
   static const char* names[8] = {"q", "k", "v", "tq", "tk", "tv", "o", "t_o"};
   void* outs[2] = {o, t_o};
-  for (int i = 0; i < 6; ++i)
+  const int n_in = primal ? 3 : 6, n_out = primal ? 1 : 2;
+  for (int i = 0; i < n_in; ++i)
     if (ins[i] == nullptr) return fail(ATTN_JVP_E_NULL, "%s is NULL", names[i]);
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < n_out; ++i)
     if (outs[i] == nullptr) return fail(ATTN_JVP_E_NULL, "%s is NULL", names[6 + i]);
-  for (int i = 0; i < 6; ++i)
+  for (int i = 0; i < n_in; ++i)
     if ((uintptr_t)ins[i] % 16) return fail(ATTN_JVP_E_ALIGN, "%s is not 16-byte aligned", names[i]);
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < n_out; ++i)
     if ((uintptr_t)outs[i] % 16) return fail(ATTN_JVP_E_ALIGN, "%s is not 16-byte aligned", names[6 + i]);
   if ((uintptr_t)lse % 4) return fail(ATTN_JVP_E_ALIGN, "lse is not 4-byte aligned");
 
   const size_t elt = p->dtype == ATTN_JVP_BF16 ? 2 : 4;
   const size_t rows = (size_t)p->batch * p->heads * (size_t)p->g.seq_len;
   const size_t bytes = rows * p->head_dim * elt;
-  for (int i = 0; i < 2; ++i) {
-    for (int j = 0; j < 6; ++j)
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
       if (overlaps(outs[i], bytes, ins[j], bytes))
         return fail(ATTN_JVP_E_INVALID, "%s overlaps input %s", names[6 + i], names[j]);
     if (lse && overlaps(lse, rows * 4, outs[i], bytes)) return fail(ATTN_JVP_E_INVALID, "lse overlaps %s", names[6 + i]);
   }
-  if (overlaps(o, bytes, t_o, bytes)) return fail(ATTN_JVP_E_INVALID, "o overlaps t_o");
+  if (!primal && overlaps(o, bytes, t_o, bytes)) return fail(ATTN_JVP_E_INVALID, "o overlaps t_o");
   if (lse)
-    for (int j = 0; j < 6; ++j)
+    for (int j = 0; j < n_in; ++j)
       if (overlaps(lse, rows * 4, ins[j], bytes)) return fail(ATTN_JVP_E_INVALID, "lse overlaps input %s", names[j]);
   if (table) {
     const size_t tbytes = p->rs->table.size() * sizeof(int32_t);
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < n_out; ++i)
       if (overlaps(outs[i], bytes, table, tbytes)) return fail(ATTN_JVP_E_INVALID, "%s overlaps the table", names[6 + i]);
     if (lse && overlaps(lse, rows * 4, table, tbytes)) return fail(ATTN_JVP_E_INVALID, "lse overlaps the table");
   }
@@ -494,6 +497,13 @@ int fwd_common(const attn_jvp_plan* p, const void* table, const void* q, const v
   fp.scale = p->scale;
   fp.score_log2 = p->scale * 1.4426950408889634f;
   fp.ctz = (p->flags & ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO) ? 1 : 0;
+  fp.primal = 0;
+  if (primal) {  // the clean-tangent-zero kernel with every block in its primal mode
+    fp.tq = fp.tk = fp.tv = q;  // never read
+    fp.to = nullptr;
+    fp.ctz = 1;
+    fp.primal = 1;
+  }
   fp.tb_blk = fp.tb_order = fp.tb_ent = fp.tb_rows = fp.tb_iv = nullptr;
   if (table) {
     const int32_t* t = (const int32_t*)table;
@@ -516,6 +526,13 @@ int attn_jvp_fwd(const attn_jvp_plan* p, const void* q, const void* k, const voi
   if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
   if (p->rs) return fail(ATTN_JVP_E_INVALID, "range-list plans run through attn_jvp_fwd_table");
   return fwd_common(p, nullptr, q, k, v, tq, tk, tv, o, t_o, lse, hip_stream);
+}
+
+int attn_jvp_fwd_primal(const attn_jvp_plan* p, const void* q, const void* k, const void* v, void* o, float* lse,
+                        void* hip_stream) {
+  if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
+  if (p->rs) return fail(ATTN_JVP_E_INVALID, "attn_jvp_fwd_primal takes descriptor plans");
+  return fwd_common(p, nullptr, q, k, v, nullptr, nullptr, nullptr, o, nullptr, lse, hip_stream, true);
 }
 
 int attn_jvp_fwd_table(const attn_jvp_plan* p, const void* device_table, const void* q, const void* k,

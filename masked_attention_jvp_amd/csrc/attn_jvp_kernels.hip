@@ -127,7 +127,9 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     if constexpr (TABLE) return __builtin_amdgcn_readfirstlane(ent[t] & 0xffffff);
     else return span_tile(sp, t);
   };
-  const bool primal_only = CTZ && !is_noisy(g, r0);  // a clean-side block
+  // clean-side blocks of a clean-tangent-zero plan, and every block of a
+  // primal call (o and lse only)
+  const bool primal_only = CTZ && (p.primal != 0 || !is_noisy(g, r0));
   // Clean-tangent-zero, noisy block: the leading tiles whose keys all lie on
   // the clean side (below N_h) need no key tangents.  A tile that reaches N_h
   // (for short sides the two key intervals can even share one) runs in the
@@ -708,7 +710,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
         u32x2 ov = {pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])};
         u32x2 tv = {pack_bf16(t4[0], t4[1]), pack_bf16(t4[2], t4[3])};
         *(u32x2*)(Og + d0) = ov;
-        *(u32x2*)(tOg + d0) = tv;
+        if (!CTZ || p.to != nullptr) *(u32x2*)(tOg + d0) = tv;
       }
     }
     // one explicit fma: every instantiation rounds lse the same way
@@ -754,7 +756,7 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(FwdParams p) {
   // clean-tangent-zero: clean rows and clean keys carry no tangent and their
   // tangent rows are never read
   const bool ctz = p.ctz != 0;
-  const bool row_tangent = !(ctz && !is_noisy(g, r0));  // the block's rows are on one side
+  const bool row_tangent = !(ctz && (p.primal != 0 || !is_noisy(g, r0)));  // the block's rows are on one side
   float q[E], tq[E], ao[E], at[E];
   const int qrow = row_ok ? row : r0;
 #pragma unroll
@@ -772,7 +774,7 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(FwdParams p) {
   auto key_step = [&](int j) {
       const float* kj = K + (size_t)j * D;
       const float* tkj = tK + (size_t)j * D;
-      const bool key_tangent = !(ctz && j < g.side_len);
+      const bool key_tangent = !(ctz && (p.primal != 0 || j < g.side_len));
       float s = 0.f, ts = 0.f;
       if (key_tangent) {
 #pragma unroll
@@ -842,7 +844,7 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(FwdParams p) {
   for (int e = 0; e < E; ++e) {
     const float o = ao[e] * inv;
     O[e] = o;
-    tO[e] = row_tangent ? at[e] * inv - rb * o : 0.f;
+    if (p.to != nullptr) tO[e] = row_tangent ? at[e] * inv - rb * o : 0.f;
   }
   if (slice == 0 && p.lse != nullptr) p.lse[(size_t)bh * N + row] = l > 0.f ? m + logf(l) : -INFINITY;
 }

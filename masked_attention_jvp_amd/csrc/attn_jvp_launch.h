@@ -33,6 +33,7 @@ struct FwdParams {
   float score_log2;   // scale * log2(e)
   float scale;
   int32_t ctz;        // clean-tangent-zero plan (teacher forcing only)
+  int32_t primal;     // with ctz: every block forms o and lse only (no tangents; to may be null)
   // range-list plans (all null otherwise): sections of the device table
   const int32_t* tb_blk;    // [n_qblocks + 1] first entry of each query block
   const int32_t* tb_order;  // [n_qblocks] launch order

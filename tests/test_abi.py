@@ -37,7 +37,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     lib = ctypes.CDLL(aj.library_path)
     for name in names:
         assert hasattr(lib, name), name
@@ -285,3 +285,22 @@ def test_bwd_launch_order_is_an_xcd_grouped_permutation(desc, b, h):
         # the direction alternates: XCD 0 takes the first group in even rounds, the last in odd ones
         assert int(seg[0::8].min()) == 128 * r + (0 if r % 2 == 0 else 112)
     assert np.array_equal(order[128 * (total // 128):], np.arange(128 * (total // 128), total))
+
+
+def test_primal_argument_errors_before_any_device_call():
+    lib = aj._load()
+    p = aj.attn_jvp_create((4, 3, 1, 1), 1, 1, 64, aj.ATTN_JVP_BF16)
+    good = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(4)]  # q k v o
+    assert lib.attn_jvp_fwd_primal(None, *good, None, None) == 2
+    for i in range(4):
+        bad = list(good)
+        bad[i] = ctypes.c_void_p(0)
+        assert lib.attn_jvp_fwd_primal(p.handle, *bad, None, None) == 2
+    bad = list(good)
+    bad[2] = ctypes.c_void_p(good[2].value + 8)
+    assert lib.attn_jvp_fwd_primal(p.handle, *bad, None, None) == 3
+    bad = list(good)
+    bad[3] = bad[1]  # o aliases k
+    assert lib.attn_jvp_fwd_primal(p.handle, *bad, None, None) == 1
+    pr = aj.attn_jvp_create_ranges(16, [(0, 16, [(0, 16)])], 1, 1, 64)
+    assert lib.attn_jvp_fwd_primal(pr.handle, *good, None, None) == 1
