@@ -521,6 +521,9 @@ def masked_attention_bwd_rows(q, k, v, do, desc, rows, scale=None, batch_rows=25
         sel = order[i:j]
         rr = rows[sel]
         keys = np.nonzero(mask)[0]
+        i = j
+        if keys.size == 0:  # a row that sees no key (range lists): P = 0, every term is 0
+            continue
         kk, vv = k[keys], v[keys]
         s = sc * (q[rr] @ kk.T)
         e = np.exp(s - s.max(axis=1, keepdims=True))
@@ -532,7 +535,6 @@ def masked_attention_bwd_rows(q, k, v, do, desc, rows, scale=None, batch_rows=25
         dk[keys] += sc * (ds.T @ q[rr])
         dv[keys] += p.T @ do[rr]
         delta[sel] = dl
-        i = j
     return dq, dk, dv, delta
 
 

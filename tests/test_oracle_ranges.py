@@ -124,6 +124,30 @@ def test_range_mask_backward_matches_autograd():
         assert np.max(np.abs(a - b.numpy())) < 1e-12
 
 
+def test_range_mask_rows_backward_matches_autograd_with_rows_in_no_group():
+    # rows 6-8 and 15-19 lie in no group; dO is confined to the chosen rows
+    n, groups = 24, ((0, 6, ((0, 3), (10, 14))), (9, 15, ((0, 24),)), (20, 24, ((5, 6), (18, 24))))
+    rm = RangeMask(n, groups)
+    rng = np.random.default_rng(7)
+    q, k, v, do = (rng.standard_normal((n, 8)) for _ in range(4))
+    rows = np.array([21, 0, 7, 16, 12, 5, 23])
+    mask = torch.tensor(mask_dense(rm))
+    covered = mask.any(dim=1)
+    t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v)]
+    s = ((t[0] @ t[1].T) / np.sqrt(8)).masked_fill(~mask, float("-inf"))
+    p = torch.where(covered[:, None], torch.softmax(s, dim=-1), torch.zeros(n, n, dtype=torch.float64))
+    do_rows = np.zeros_like(do)
+    do_rows[rows] = do[rows]
+    (p @ t[2]).backward(torch.tensor(do_rows))
+    dq, dk, dv, delta = oracle.masked_attention_bwd_rows(q, k, v, do, rm, rows)
+    assert np.max(np.abs(dq - t[0].grad.numpy()[rows])) < 1e-12
+    assert np.max(np.abs(dk - t[1].grad.numpy())) < 1e-12
+    assert np.max(np.abs(dv - t[2].grad.numpy())) < 1e-12
+    po = (p @ t[2]).detach().numpy()
+    assert np.max(np.abs(delta - (do[rows] * po[rows]).sum(axis=1))) < 1e-12
+    assert np.all(dq[[2, 3]] == 0) and np.all(delta[[2, 3]] == 0)  # rows 7 and 16: no key
+
+
 @pytest.mark.parametrize("bq, bk", [(4, 4), (8, 4), (3, 5)])
 def test_range_tile_classes_by_brute_force(bq, bk):
     n, groups = si.und_gen_ranges(5, 3, 4)
