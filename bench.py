@@ -161,7 +161,7 @@ def traffic_for(workload_name, part="fwd"):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline_bwd(w, heads):
+def cpu_baseline_bwd(w, heads, ranges=False):
     """The oracle's backward, untuned, on (b, h) slices of the same workload."""
     import oracle
     import seeded_inputs as si
@@ -170,17 +170,19 @@ def cpu_baseline_bwd(w, heads):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = 1
+    mask = oracle.RangeMask(*w.mask_ranges()) if ranges else w.desc
     flops = 0
     elapsed = 0.0
     for h in range(heads):
         args = [si.slice_values(w, t, 0, h) for t in ("q", "k", "v", "do")]
         t0 = time.perf_counter()
-        oracle.masked_attention_bwd_slice(*args, w.desc)
+        oracle.masked_attention_bwd_slice(*args, mask)
         elapsed += time.perf_counter() - t0
-        flops += oracle.backward_useful_flops(w.desc, w.head_dim)
+        flops += oracle.backward_useful_flops(mask, w.head_dim)
     return {
         "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": f"{heads} of {w.batch * w.heads} (b,h) slices of {w.name} (all rows, backward), fp64 NumPy, "
+        "sample": f"{heads} of {w.batch * w.heads} (b,h) slices of {w.name} (all rows, backward"
+                  f"{', range-list mask' if ranges else ''}), fp64 NumPy, "
                   f"{elapsed:.1f} s",
     }
 
@@ -284,8 +286,8 @@ def main():
     if args.primal and (args.backward or args.clean_tangent_zero or use_ranges):
         print(json.dumps({"error": "--primal takes a descriptor workload without other modes"}))
         sys.exit(2)
-    if use_ranges and (args.backward or args.clean_tangent_zero):
-        print(json.dumps({"error": "range-list plans run the forward + JVP only"}))
+    if use_ranges and args.clean_tangent_zero:
+        print(json.dumps({"error": "range-list plans have no clean-tangent-zero option"}))
         sys.exit(2)
     if args.ranges and args.config not in si.RANGE_WORKLOADS:
         w = w.with_(name=f"{w.name}_ranges")
@@ -319,7 +321,7 @@ def main():
     o = torch.empty_like(x["q"])
     to = torch.empty_like(x["q"])
     lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
-    if use_ranges:
+    if use_ranges and not args.backward:
         call = lambda: aj.attn_jvp_fwd_table(plan, table, *(x[t] for t in si.TENSORS), o, to, lse)
     elif args.primal:
         call = lambda: aj.attn_jvp_fwd_primal(plan, x["q"], x["k"], x["v"], o, lse)
@@ -327,11 +329,17 @@ def main():
         call = lambda: aj.attn_jvp_fwd(plan, *(x[t] for t in si.TENSORS), o, to, lse)
     else:
         # o and lse of these inputs, once, outside the timed region
-        aj.attn_jvp_fwd(plan, *(x[t] for t in si.TENSORS), o, to, lse)
+        if use_ranges:
+            aj.attn_jvp_fwd_table(plan, table, *(x[t] for t in si.TENSORS), o, to, lse)
+        else:
+            aj.attn_jvp_fwd(plan, *(x[t] for t in si.TENSORS), o, to, lse)
         del to, x["tq"], x["tk"], x["tv"]
         dq, dk, dv = (torch.empty_like(x["q"]) for _ in range(3))
         ws = torch.empty(aj.attn_jvp_bwd_workspace_size(plan) // 4, dtype=torch.float32, device=dev)
-        call = lambda: aj.attn_jvp_bwd(plan, x["q"], x["k"], x["v"], o, lse, x["do"], dq, dk, dv, ws)
+        if use_ranges:
+            call = lambda: aj.attn_jvp_bwd_table(plan, table, x["q"], x["k"], x["v"], o, lse, x["do"], dq, dk, dv, ws)
+        else:
+            call = lambda: aj.attn_jvp_bwd(plan, x["q"], x["k"], x["v"], o, lse, x["do"], dq, dk, dv, ws)
 
     for _ in range(args.warmup):
         call()
@@ -368,7 +376,9 @@ def main():
     part = "bwd" if args.backward else "fwd"
     traffic = traffic_for(w.name, part)
     nw = info["block_q"] // 32
-    kernel = (f"bwd_dq_bf16_kernel<{w.head_dim},{nw}> + bwd_dkdv_bf16_kernel<{w.head_dim},{nw}>" if args.backward
+    tb = "true" if use_ranges else "false"
+    kernel = (f"bwd_dq_bf16_kernel<{w.head_dim},{nw},{tb}> + bwd_dkdv_bf16_kernel<{w.head_dim},{nw},{tb}>"
+              if args.backward
               else f"fwd_bf16_kernel<{w.head_dim},{nw},true,false> (primal mode)" if args.primal
               else f"fwd_bf16_kernel<{w.head_dim},{nw},{'true' if flags else 'false'},{'true' if use_ranges else 'false'}>")
 
@@ -417,7 +427,7 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_sample_heads) if args.backward
+        out["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_sample_heads, use_ranges) if args.backward
                                else cpu_baseline_primal(w, args.cpu_sample_heads) if args.primal
                                else cpu_baseline_ranges(w, args.cpu_sample_heads) if use_ranges
                                else cpu_baseline(w, args.cpu_sample_heads, bool(flags)))

@@ -158,7 +158,8 @@ int attn_jvp_plan_table(const attn_jvp_plan* plan, void* host_out, size_t bytes)
  * the plan's schedule table in device memory (bytes from attn_jvp_plan_table
  * of this plan; its contents are not checked).  attn_jvp_fwd refuses range-
  * list plans and this call refuses descriptor plans (ATTN_JVP_E_INVALID).
- * Range-list plans have no backward and no clean-tangent-zero option. */
+ * Range-list plans have no clean-tangent-zero option and no primal-only
+ * forward; their backward is attn_jvp_bwd_table. */
 int attn_jvp_fwd_table(const attn_jvp_plan* plan, const void* device_table, const void* q,
                        const void* k, const void* v, const void* tq, const void* tk, const void* tv,
                        void* o, void* t_o, float* lse, void* hip_stream);
@@ -210,26 +211,42 @@ int attn_jvp_bwd(const attn_jvp_plan* plan, const void* q, const void* k, const 
                  const void* o, const float* lse, const void* d_o, void* dq, void* dk, void* dv,
                  float* workspace, void* hip_stream);
 
+/* attn_jvp_bwd for range-list plans: the same operation, arguments and
+ * workspace contents, with the plan's schedule table in device memory (the
+ * table of attn_jvp_fwd_table, whose column sections this call uses).  o and
+ * lse come from attn_jvp_fwd_table; a row in no group (lse = -inf) gets
+ * dq = 0, delta = 0 and contributes nothing to dk and dv, and its second
+ * workspace entry is the most negative finite float instead of +inf.
+ * Refuses descriptor plans, and range-list plans whose mask columns do not fit
+ * the kernels (ATTN_JVP_E_INVALID, detail says why: a key seen by more than
+ * 255 separate row intervals, or, in bf16, a key block that streams more than
+ * 7680 query tiles); attn_jvp_bwd refuses range-list plans. */
+int attn_jvp_bwd_table(const attn_jvp_plan* plan, const void* device_table, const void* q,
+                       const void* k, const void* v, const void* o, const float* lse, const void* d_o,
+                       void* dq, void* dk, void* dv, float* workspace, void* hip_stream);
+
 /* Workspace bytes attn_jvp_bwd needs for the plan: 8 B H N. */
 int attn_jvp_bwd_workspace_size(const attn_jvp_plan* plan, size_t* bytes);
 
 /* Geometry of the backward: rows per dq-kernel block and query blocks per
  * (b, h) (the dq kernel walks the forward's key tiles for each), keys per
  * dk/dv-kernel block and key blocks per (b, h).  Key blocks are cut per side
- * like query blocks (clean side from key 0, noisy side from key N_h); a key
- * block streams the 32-row query tiles of the rows that attend to any of its
- * keys (attn_jvp_key_ranges).  Any output pointer may be NULL. */
+ * like query blocks (clean side from key 0, noisy side from key N_h; range-
+ * list plans: from key 0 over the whole sequence); a key block streams the
+ * 32-row query tiles of the rows that attend to any of its keys
+ * (attn_jvp_key_ranges).  Any output pointer may be NULL. */
 int attn_jvp_plan_bwd_info(const attn_jvp_plan* plan, int32_t* block_q, int32_t* block_kv,
                            int32_t* n_query_blocks, int32_t* n_key_blocks);
 
 /* Launch order of the dk/dv kernel: workgroup b (0 <= b < B H n_key_blocks)
  * processes task host_out[b], i.e. (b, h) slice task / n_key_blocks and key
  * block task mod n_key_blocks.  Tasks are heavy first (the earliest keys of a
- * side are seen by the most rows); workgroups are handed to the 8 XCDs round
- * robin, and each round of 128 workgroups gives each XCD a group of 16
- * neighbouring key blocks, which stream nearly the same query tiles through
- * that XCD's L2, the group-to-XCD direction alternating from round to round.
- * n is the capacity of host_out in int32 elements. */
+ * side are seen by the most rows; range-list plans: the key blocks that
+ * stream more query tiles first, in the table's order); workgroups are
+ * handed to the 8 XCDs round robin, and each round of 128 workgroups gives
+ * each XCD a group of 16 consecutive tasks, which stream nearly the same
+ * query tiles through that XCD's L2, the group-to-XCD direction alternating
+ * from round to round.  n is the capacity of host_out in int32 elements. */
 int attn_jvp_bwd_launch_order(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
 /* Useful floating-point operations of one attn_jvp_bwd call (all B * H
@@ -281,7 +298,10 @@ int attn_jvp_row_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 /* Per-key allowed query ranges (the columns of the mask), as the backward's
  * dk/dv kernel uses them: host_out[4*j + 0..3] = lo1, hi1, lo2, hi2 for keys
  * j = 0..N-1: row i attends to key j iff lo1 <= i < hi1 or lo2 <= i < hi2.
- * n is the capacity of host_out in int32 elements (>= 4N). */
+ * Range-list plans: the first two row intervals of the key (zeros for a key
+ * no row sees); ATTN_JVP_E_INVALID if some key is seen by more than two, or
+ * if the plan has no backward.  n is the capacity of host_out in int32
+ * elements (>= 4N). */
 int attn_jvp_key_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
 /* Launch order: workgroup t (0 <= t < n_query_blocks) of every (b, h)

@@ -36,6 +36,7 @@ __all__ = [
     "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops", "attn_jvp_key_ranges",
     "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order", "attn_jvp_create_ranges", "attn_jvp_plan_table_size",
     "attn_jvp_plan_table", "attn_jvp_fwd_table", "masked_attention_jvp_ranges", "attn_jvp_fwd_primal",
+    "attn_jvp_bwd_table", "masked_attention_bwd_ranges",
     "masked_attention_fwd",
     "masked_attention_bwd",
 ]
@@ -106,12 +107,13 @@ def _load():
         lib.attn_jvp_plan_table.argtypes = [vp, vp, ctypes.c_size_t]
         lib.attn_jvp_fwd_table.argtypes = [vp] * 10 + [vp, vp]
         lib.attn_jvp_fwd_primal.argtypes = [vp] * 7
+        lib.attn_jvp_bwd_table.argtypes = [vp] * 13
         for name in ("attn_jvp_create", "attn_jvp_create_ex", "attn_jvp_fwd", "attn_jvp_destroy",
                      "attn_jvp_plan_info", "attn_jvp_plan_flops", "attn_jvp_launch_order", "attn_jvp_row_ranges",
                      "attn_jvp_tile_map", "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops",
                      "attn_jvp_key_ranges", "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order",
                      "attn_jvp_create_ranges", "attn_jvp_plan_table_size", "attn_jvp_plan_table", "attn_jvp_fwd_table",
-                     "attn_jvp_fwd_primal"):
+                     "attn_jvp_fwd_primal", "attn_jvp_bwd_table"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -368,11 +370,7 @@ def attn_jvp_fwd_primal(plan: Plan, q, k, v, o, lse=None, stream=None) -> None:
     _check(code, "attn_jvp_fwd_primal")
 
 
-def attn_jvp_bwd(plan: Plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace, stream=None) -> None:
-    """Enqueue the backward (dq, dk, dv) on `stream` (default: torch's current
-    stream).  `workspace` is a float32 CUDA tensor of at least
-    attn_jvp_bwd_workspace_size(plan) bytes; on return it holds -delta and
-    -lse log2(e) per row, [B, H, 2, N]."""
+def _bwd_args(plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace):
     import torch
     ts = dict(q=q, k=k, v=v, o=o, d_o=d_o, dq=dq, dk=dk, dv=dv)
     for name, t in ts.items():
@@ -387,13 +385,42 @@ def attn_jvp_bwd(plan: Plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace, stream
             or workspace.numel() * 4 < attn_jvp_bwd_workspace_size(plan):
         raise AttnJvpError(f"workspace must be a contiguous float32 tensor of at least "
                            f"{attn_jvp_bwd_workspace_size(plan)} bytes")
+    return [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o, lse, d_o, dq, dk, dv, workspace)]
+
+
+def attn_jvp_bwd(plan: Plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace, stream=None) -> None:
+    """Enqueue the backward (dq, dk, dv) on `stream` (default: torch's current
+    stream).  `workspace` is a float32 CUDA tensor of at least
+    attn_jvp_bwd_workspace_size(plan) bytes; on return it holds -delta and
+    -lse log2(e) per row, [B, H, 2, N]."""
+    import torch
+    ptrs = _bwd_args(plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace)
     if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    ptrs = [q, k, v, o, lse, d_o, dq, dk, dv, workspace]
-    with torch.cuda.device(dev):
-        code = _load().attn_jvp_bwd(plan.handle, *[ctypes.c_void_p(t.data_ptr()) for t in ptrs],
-                                    ctypes.c_void_p(stream.cuda_stream))
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        code = _load().attn_jvp_bwd(plan.handle, *ptrs, ctypes.c_void_p(stream.cuda_stream))
     _check(code, "attn_jvp_bwd")
+
+
+def attn_jvp_bwd_table(plan: Plan, table, q, k, v, o, lse, d_o, dq, dk, dv, workspace, stream=None) -> None:
+    """attn_jvp_bwd for a range-list plan; `table` is the plan's table as an
+    int32 CUDA tensor (attn_jvp_plan_table copied to the device)."""
+    import torch
+    ptrs = _bwd_args(plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace)
+    _check_table(plan, table, q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        code = _load().attn_jvp_bwd_table(plan.handle, ctypes.c_void_p(table.data_ptr()), *ptrs,
+                                          ctypes.c_void_p(stream.cuda_stream))
+    _check(code, "attn_jvp_bwd_table")
+
+
+def _check_table(plan, table, dev):
+    import torch
+    if not isinstance(table, torch.Tensor) or table.device != dev or table.dtype != torch.int32 \
+            or not table.is_contiguous() or table.numel() * 4 < attn_jvp_plan_table_size(plan):
+        raise AttnJvpError("table must be the plan's int32 table as a contiguous tensor on q's device")
 
 
 def attn_jvp_fwd_table(plan: Plan, table, q, k, v, tq, tk, tv, o, t_o, lse=None, stream=None) -> None:
@@ -404,9 +431,7 @@ def attn_jvp_fwd_table(plan: Plan, table, q, k, v, tq, tk, tv, o, t_o, lse=None,
     for name, t in ins.items():
         _check_tensor(name, t, plan, plan.shape)
     dev = q.device
-    if not isinstance(table, torch.Tensor) or table.device != dev or table.dtype != torch.int32 \
-            or not table.is_contiguous() or table.numel() * 4 < attn_jvp_plan_table_size(plan):
-        raise AttnJvpError("table must be the plan's int32 table as a contiguous tensor on q's device")
+    _check_table(plan, table, dev)
     if lse is not None:
         if lse.dtype != torch.float32 or tuple(lse.shape) != plan.shape[:3] or not lse.is_contiguous() \
                 or lse.device != dev:
@@ -481,10 +506,9 @@ def masked_attention_bwd(q, k, v, o, lse, d_o, desc, scale=None, return_workspac
 _range_cache = {}
 
 
-def masked_attention_jvp_ranges(q, k, v, tq, tk, tv, groups, scale=None, return_lse=False):
-    """(o, t_o[, lse]) for a range-list mask: groups = [(row_lo, row_hi,
-    [(key_lo, key_hi), ...]), ...].  The plan and its device table are
-    cached per (mask, shape, dtype, scale, device)."""
+def _cached_range_plan(q, groups, scale):
+    """The plan of a range-list mask and its device table, cached per (mask,
+    shape, dtype, scale, device)."""
     import torch
     dtype = ATTN_JVP_BF16 if q.dtype == torch.bfloat16 else ATTN_JVP_FP32
     b, h, n, d = q.shape
@@ -496,9 +520,27 @@ def masked_attention_jvp_ranges(q, k, v, tq, tk, tv, groups, scale=None, return_
             plan = attn_jvp_create_ranges(n, groups, b, h, d, dtype, scale or 0.0)
             table = torch.from_numpy(attn_jvp_plan_table(plan)).to(q.device)
             hit = _range_cache[key] = (plan, table)
-    plan, table = hit
+    return hit
+
+
+def masked_attention_jvp_ranges(q, k, v, tq, tk, tv, groups, scale=None, return_lse=False):
+    """(o, t_o[, lse]) for a range-list mask: groups = [(row_lo, row_hi,
+    [(key_lo, key_hi), ...]), ...]."""
+    import torch
+    plan, table = _cached_range_plan(q, groups, scale)
     o = torch.empty_like(q)
     t_o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
     attn_jvp_fwd_table(plan, table, q, k, v, tq, tk, tv, o, t_o, lse)
     return (o, t_o, lse) if return_lse else (o, t_o)
+
+
+def masked_attention_bwd_ranges(q, k, v, o, lse, d_o, groups, scale=None, return_workspace=False):
+    """(dq, dk, dv[, workspace]) for a range-list mask (groups as in
+    masked_attention_jvp_ranges), from that forward's o and lse."""
+    import torch
+    plan, table = _cached_range_plan(q, groups, scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(attn_jvp_bwd_workspace_size(plan) // 4, dtype=torch.float32, device=q.device)
+    attn_jvp_bwd_table(plan, table, q, k, v, o, lse, d_o, dq, dk, dv, ws)
+    return (dq, dk, dv, ws) if return_workspace else (dq, dk, dv)

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <map>
 #include <new>
 #include <string>
 #include <utility>
@@ -24,18 +25,29 @@ using namespace attn_jvp;
 
 // Schedule of a range-list plan (query groups x key intervals), serialised
 // into one int32 table that the caller places in device memory:
-//   [0..7]     header: magic, n_qblocks, n_entries, n_intervals, max entries per block
+//   [0..7]     header: magic, n_qblocks, n_entries, n_intervals, max entries per
+//              query block, n_kblocks, n_col_entries, n_col_intervals
 //   blk        [n_qblocks + 1]  first entry of each query block
 //   order      [n_qblocks]      launch order (workgroup t -> query block)
 //   entries    one per streamed key tile: tile | (whole bit of wave w) << (24 + w)
 //   rows       [N]              per query row: (first interval << 8) | interval count
 //   intervals  [2 n_intervals]  key intervals (lo, hi), merged and sorted per group
+// and the same for the columns of the mask, which the backward's dk/dv kernel
+// walks (key blocks of 32 x waves keys, 32-row query tiles; per key the
+// merged row intervals that see it):
+//   cblk [n_kblocks + 1], corder [n_kblocks], centries, cols [N], cintervals.
+// The column sections are empty (n_kblocks = 0) when the backward cannot take
+// the plan (bwd_error says why).
 struct RangeSchedule {
   std::vector<int32_t> table;
   int64_t off_blk = 0, off_order = 0, off_ent = 0, off_rows = 0, off_iv = 0;
+  int64_t off_cblk = 0, off_corder = 0, off_cent = 0, off_cols = 0, off_civ = 0;
   int32_t n_entries = 0, max_entries = 0;
+  int32_t n_kblocks = 0, n_col_entries = 0;
   std::vector<uint8_t> ent_class;  // per entry: 1 every row of the block sees the whole tile, 2 otherwise
   bool rows_over_two = false;      // some row has more than two key intervals
+  bool cols_over_two = false;      // some key is seen by more than two row intervals
+  std::string bwd_error;           // non-empty: the backward refuses this plan
 };
 
 struct attn_jvp_plan {
@@ -147,6 +159,141 @@ int check_device(int* dev_out) {
   }
   if (st == 2) return fail(ATTN_JVP_E_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
   return ATTN_JVP_OK;
+}
+
+// One axis of a range-list schedule.  Items (query rows; keys for the
+// columns) are cut into blocks of bq from 0, the other axis into tiles of bt.
+// grp[i] is the group of item i (-1: none); group g's intervals on the other
+// axis are (iv[2k], iv[2k+1]) for g_iv[g] <= k < g_iv[g+1], sorted, disjoint
+// and not touching.  Per block: the tiles that meet the intervals of its
+// items' groups, ascending, each with a whole bit per wave of 32 items (every
+// item of the wave sees the whole tile; waves without items never mask) and
+// its class (1: every item of the block sees the whole tile, 2: not); the
+// blocks' heavy-first order (more tiles first, stable).
+struct SideSchedule {
+  std::vector<int32_t> blk, order, ent;
+  std::vector<uint8_t> cls;
+  int32_t max_entries = 0;
+};
+
+void build_side(int32_t n, const std::vector<int32_t>& grp, const std::vector<int32_t>& g_iv,
+                const std::vector<int32_t>& iv, int32_t bq, int32_t bt, SideSchedule* s) {
+  const int32_t nb = cdiv(n, bq), nw = bq / 32;
+  // does group g (or "no group", g < 0) see all of [t0, t1)?
+  auto covers_g = [&](int32_t g, int32_t t0, int32_t t1) {
+    if (g < 0) return false;
+    for (int32_t k = g_iv[g]; k < g_iv[g + 1]; ++k)
+      if (iv[2 * k] <= t0 && t1 <= iv[2 * k + 1]) return true;
+    return false;
+  };
+  s->blk.assign(nb + 1, 0);
+  s->ent.clear();
+  s->cls.clear();
+  s->max_entries = 0;
+  std::vector<std::pair<int32_t, int32_t>> runs;
+  std::vector<int32_t> bgroups;
+  for (int32_t b = 0; b < nb; ++b) {
+    const int32_t r0 = b * bq, r1 = std::min(r0 + bq, n);
+    bgroups.clear();  // distinct groups of the block's items (-1: items in no group)
+    for (int32_t r = r0; r < r1; ++r)
+      if (bgroups.empty() || bgroups.back() != grp[r]) bgroups.push_back(grp[r]);
+    runs.clear();
+    for (int32_t g : bgroups) {
+      if (g < 0) continue;
+      for (int32_t k = g_iv[g]; k < g_iv[g + 1]; ++k) runs.emplace_back(iv[2 * k] / bt, cdiv(iv[2 * k + 1], bt));
+    }
+    std::sort(runs.begin(), runs.end());
+    int32_t at = -1;
+    for (const auto& run : runs) {
+      for (int32_t t = std::max(run.first, at); t < run.second; ++t) {
+        const int32_t t0 = t * bt, t1c = std::min(t0 + bt, n);
+        int32_t e = t;
+        for (int32_t w = 0; w < nw; ++w) {
+          const int32_t wa = r0 + 32 * w, wb = std::min(wa + 32, r1);
+          bool whole = true;
+          // every item of the wave sees the whole tile (past n: zeros, not whole)
+          for (int32_t r = wa; r < wb && whole; ++r) {
+            if (r > wa && grp[r] == grp[r - 1]) continue;
+            whole = t0 + bt <= n && covers_g(grp[r], t0, t0 + bt);
+          }
+          if (whole) e |= 1 << (24 + w);
+        }
+        bool all = true;
+        for (int32_t g : bgroups) all = all && covers_g(g, t0, t1c);
+        s->ent.push_back(e);
+        s->cls.push_back(all ? 1 : 2);
+      }
+      at = std::max(at, run.second);
+    }
+    s->blk[b + 1] = (int32_t)s->ent.size();
+    s->max_entries = std::max(s->max_entries, s->blk[b + 1] - s->blk[b]);
+  }
+  s->order.resize(nb);
+  for (int32_t b = 0; b < nb; ++b) s->order[b] = b;
+  std::stable_sort(s->order.begin(), s->order.end(), [&](int32_t a, int32_t b2) {
+    return s->blk[a + 1] - s->blk[a] > s->blk[b2 + 1] - s->blk[b2];
+  });
+}
+
+// The columns of a range-list mask: key j is seen by the rows of every group
+// one of whose intervals holds j.  Sweeping the interval ends from left to
+// right, the set of such groups is constant between consecutive ends; each
+// stretch gets the merged row intervals of its groups (touching ones joined),
+// and consecutive stretches with equal lists share one column group.
+// Returns false if the column intervals would exceed 2^23.
+bool build_columns(int32_t n, const std::vector<int32_t>& g_lo, const std::vector<int32_t>& g_hi,
+                   const std::vector<int32_t>& g_iv, const std::vector<int32_t>& ivs,
+                   std::vector<int32_t>* col_grp, std::vector<int32_t>* c_iv, std::vector<int32_t>* civs,
+                   int32_t* max_count) {
+  struct Ev { int32_t x, add, a, b; };
+  std::vector<Ev> ev;
+  for (size_t g = 0; g < g_lo.size(); ++g)
+    for (int32_t k = g_iv[g]; k < g_iv[g + 1]; ++k) {
+      ev.push_back({ivs[2 * k], 1, g_lo[g], g_hi[g]});
+      ev.push_back({ivs[2 * k + 1], 0, g_lo[g], g_hi[g]});
+    }
+  // at equal x, ends (add = 0) before starts
+  std::sort(ev.begin(), ev.end(), [](const Ev& u, const Ev& v) { return u.x != v.x ? u.x < v.x : u.add < v.add; });
+  col_grp->assign(n, -1);
+  c_iv->assign(1, 0);
+  civs->clear();
+  *max_count = 0;
+  std::map<int32_t, int32_t> active;  // row_lo -> row_hi of the groups that see the current keys
+  std::vector<int32_t> cur, prev;
+  int32_t prev_id = -1, prev_end = -1;
+  size_t e = 0;
+  while (e < ev.size()) {
+    const int32_t x = ev[e].x;
+    for (; e < ev.size() && ev[e].x == x; ++e) {
+      if (ev[e].add) active[ev[e].a] = ev[e].b;
+      else active.erase(ev[e].a);
+    }
+    const int32_t y = e < ev.size() ? ev[e].x : n;
+    if (y <= x || active.empty()) continue;
+    cur.clear();
+    for (const auto& r : active) {
+      if (!cur.empty() && r.first == cur.back()) cur.back() = r.second;
+      else {
+        cur.push_back(r.first);
+        cur.push_back(r.second);
+      }
+    }
+    int32_t id;
+    if (prev_id >= 0 && prev_end == x && cur == prev) {
+      id = prev_id;
+    } else {
+      civs->insert(civs->end(), cur.begin(), cur.end());
+      if (civs->size() / 2 >= (size_t(1) << 23)) return false;
+      id = (int32_t)c_iv->size() - 1;
+      c_iv->push_back((int32_t)(civs->size() / 2));
+      *max_count = std::max(*max_count, (int32_t)(cur.size() / 2));
+      prev = cur;
+    }
+    for (int32_t j = x; j < y; ++j) (*col_grp)[j] = id;
+    prev_id = id;
+    prev_end = y;
+  }
+  return true;
 }
 
 }  // namespace
@@ -300,7 +447,7 @@ int attn_jvp_create_ranges(attn_jvp_plan** out, int32_t n_tokens, int32_t n_grou
   p->flags = 0;
   p->scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   block_sizes(dtype, head_dim, &p->block_q, &p->block_k);
-  const int32_t bq = p->block_q, bk = p->block_k, nw = bq / 32;
+  const int32_t bq = p->block_q, bk = p->block_k;
   p->n_qblocks = cdiv(n_tokens, bq);
   p->n_ktiles = cdiv(n_tokens, bk);
   if ((int64_t)batch * heads * p->n_qblocks >= (int64_t(1) << 31)) {
@@ -318,54 +465,9 @@ int attn_jvp_create_ranges(attn_jvp_plan** out, int32_t n_tokens, int32_t n_grou
       pairs += keys * (g_hi[g] - g_lo[g]);
       for (int32_t r = g_lo[g]; r < g_hi[g]; ++r) row_group[r] = g;
     }
-    // Does group g (or "no group", g < 0) see all of keys [k0, k1)?
-    auto covers_g = [&](int32_t g, int32_t k0, int32_t k1) {
-      if (g < 0) return false;
-      for (int32_t k = g_iv[g]; k < g_iv[g + 1]; ++k)
-        if (ivs[2 * k] <= k0 && k1 <= ivs[2 * k + 1]) return true;
-      return false;
-    };
-    std::vector<int32_t> blk(p->n_qblocks + 1, 0), ent;
-    std::vector<uint8_t> cls;
-    std::vector<std::pair<int32_t, int32_t>> runs;
-    std::vector<int32_t> bgroups;
-    for (int32_t b = 0; b < p->n_qblocks; ++b) {
-      const int32_t r0 = b * bq, r1 = std::min(r0 + bq, n_tokens);
-      // distinct groups of the block's rows (-1: rows in no group)
-      bgroups.clear();
-      for (int32_t r = r0; r < r1; ++r)
-        if (bgroups.empty() || bgroups.back() != row_group[r]) bgroups.push_back(row_group[r]);
-      runs.clear();
-      for (int32_t g : bgroups) {
-        if (g < 0) continue;
-        for (int32_t k = g_iv[g]; k < g_iv[g + 1]; ++k) runs.emplace_back(ivs[2 * k] / bk, cdiv(ivs[2 * k + 1], bk));
-      }
-      std::sort(runs.begin(), runs.end());
-      int32_t at = -1;
-      for (const auto& run : runs) {
-        for (int32_t t = std::max(run.first, at); t < run.second; ++t) {
-          const int32_t k0 = t * bk, k1c = std::min(k0 + bk, n_tokens);
-          int32_t e = t;
-          for (int32_t w = 0; w < nw; ++w) {
-            const int32_t wa = r0 + 32 * w, wb = std::min(wa + 32, r1);
-            bool whole = true;  // waves without valid rows never mask
-            // every row of the wave sees all 32 keys of the tile (keys past N are zeros: not whole)
-            for (int32_t r = wa; r < wb && whole; ++r) {
-              if (r > wa && row_group[r] == row_group[r - 1]) continue;
-              whole = k0 + bk <= n_tokens && covers_g(row_group[r], k0, k0 + bk);
-            }
-            if (whole) e |= 1 << (24 + w);
-          }
-          bool all = true;
-          for (int32_t g : bgroups) all = all && covers_g(g, k0, k1c);
-          ent.push_back(e);
-          cls.push_back(all ? 1 : 2);
-        }
-        at = std::max(at, run.second);
-      }
-      blk[b + 1] = (int32_t)ent.size();
-      rs->max_entries = std::max(rs->max_entries, blk[b + 1] - blk[b]);
-    }
+    SideSchedule qs;
+    build_side(n_tokens, row_group, g_iv, ivs, bq, bk, &qs);
+    rs->max_entries = qs.max_entries;
     if (dtype == ATTN_JVP_BF16 && rs->max_entries > kMaxTableEntries) {
       const int32_t me = rs->max_entries;
       delete rs;
@@ -373,13 +475,33 @@ int attn_jvp_create_ranges(attn_jvp_plan** out, int32_t n_tokens, int32_t n_grou
       return fail(ATTN_JVP_E_OVERFLOW, "a query block streams %d key tiles; range-list plans allow at most %d", me,
                   kMaxTableEntries);
     }
-    // heavy first: blocks with more tiles first (stable)
-    std::vector<int32_t> order(p->n_qblocks);
-    for (int32_t b = 0; b < p->n_qblocks; ++b) order[b] = b;
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int32_t a, int32_t b2) { return blk[a + 1] - blk[a] > blk[b2 + 1] - blk[b2]; });
-    rs->n_entries = (int32_t)ent.size();
+    rs->n_entries = (int32_t)qs.ent.size();
     const int32_t n_iv = (int32_t)(ivs.size() / 2);
+
+    // the columns, for the backward's dk/dv kernel
+    bwd_block_sizes(dtype, head_dim, &p->bwd_block_q, &p->bwd_block_kv);
+    std::vector<int32_t> col_grp, c_iv, civs;
+    int32_t max_col = 0;
+    SideSchedule ks;
+    if (!build_columns(n_tokens, g_lo, g_hi, g_iv, ivs, &col_grp, &c_iv, &civs, &max_col)) {
+      rs->bwd_error = "the columns of the mask need more than 2^23 row intervals";
+    } else if (max_col > 255) {
+      rs->bwd_error = "some key is seen by " + std::to_string(max_col) + " separate row intervals; at most 255";
+    } else {
+      build_side(n_tokens, col_grp, c_iv, civs, p->bwd_block_kv, 32, &ks);
+      if (dtype == ATTN_JVP_BF16 && ks.max_entries > kMaxTableEntries)
+        rs->bwd_error = "a key block streams " + std::to_string(ks.max_entries) +
+                        " query tiles; the backward allows at most " + std::to_string(kMaxTableEntries);
+    }
+    if (!rs->bwd_error.empty()) {
+      ks = SideSchedule{};
+      ks.blk.assign(1, 0);
+      civs.clear();
+      col_grp.assign(n_tokens, -1);
+    }
+    rs->n_kblocks = (int32_t)ks.order.size();
+    rs->n_col_entries = (int32_t)ks.ent.size();
+
     std::vector<int32_t>& tb = rs->table;
     tb.assign(8, 0);
     tb[0] = kTableMagic;
@@ -387,12 +509,16 @@ int attn_jvp_create_ranges(attn_jvp_plan** out, int32_t n_tokens, int32_t n_grou
     tb[2] = rs->n_entries;
     tb[3] = n_iv;
     tb[4] = rs->max_entries;
-    rs->off_blk = (int64_t)tb.size();
-    tb.insert(tb.end(), blk.begin(), blk.end());
-    rs->off_order = (int64_t)tb.size();
-    tb.insert(tb.end(), order.begin(), order.end());
-    rs->off_ent = (int64_t)tb.size();
-    tb.insert(tb.end(), ent.begin(), ent.end());
+    tb[5] = rs->n_kblocks;
+    tb[6] = rs->n_col_entries;
+    tb[7] = (int32_t)(civs.size() / 2);
+    auto put = [&](int64_t* off, const std::vector<int32_t>& v) {
+      *off = (int64_t)tb.size();
+      tb.insert(tb.end(), v.begin(), v.end());
+    };
+    put(&rs->off_blk, qs.blk);
+    put(&rs->off_order, qs.order);
+    put(&rs->off_ent, qs.ent);
     rs->off_rows = (int64_t)tb.size();
     for (int32_t r = 0; r < n_tokens; ++r) {
       const int32_t g = row_group[r];
@@ -400,14 +526,30 @@ int attn_jvp_create_ranges(attn_jvp_plan** out, int32_t n_tokens, int32_t n_grou
       tb.push_back(g < 0 ? 0 : (g_iv[g] << 8) | cnt);
       rs->rows_over_two = rs->rows_over_two || cnt > 2;
     }
-    rs->off_iv = (int64_t)tb.size();
-    tb.insert(tb.end(), ivs.begin(), ivs.end());
-    rs->ent_class = std::move(cls);
+    put(&rs->off_iv, ivs);
+    put(&rs->off_cblk, ks.blk);
+    put(&rs->off_corder, ks.order);
+    put(&rs->off_cent, ks.ent);
+    rs->off_cols = (int64_t)tb.size();
+    for (int32_t j = 0; j < n_tokens; ++j) {
+      const int32_t c = col_grp[j];
+      const int32_t cnt = c < 0 ? 0 : c_iv[c + 1] - c_iv[c];
+      tb.push_back(c < 0 ? 0 : (c_iv[c] << 8) | cnt);
+      rs->cols_over_two = rs->cols_over_two || cnt > 2;
+    }
+    put(&rs->off_civ, civs);
+    rs->ent_class = std::move(qs.cls);
     p->allowed_pairs = pairs;
     p->visited_tiles = rs->n_entries;
     p->useful_flops = 12 * pairs * head_dim * batch * heads;
-    p->bwd_block_q = p->bwd_block_kv = p->bwd_n_qblocks = p->bwd_n_kblocks = 0;
+    p->bwd_n_qblocks = p->n_qblocks;  // the dq kernel walks the forward's blocks and tiles
+    p->bwd_n_kblocks = cdiv(n_tokens, p->bwd_block_kv);
     p->bwd_useful_flops = 10 * pairs * head_dim * batch * heads;
+    if ((int64_t)batch * heads * p->bwd_n_kblocks >= (int64_t(1) << 31)) {
+      delete rs;
+      delete p;
+      return fail(ATTN_JVP_E_OVERFLOW, "backward grid does not fit");
+    }
   } catch (const std::bad_alloc&) {
     delete rs;
     delete p;
@@ -551,11 +693,11 @@ int attn_jvp_bwd_workspace_size(const attn_jvp_plan* p, size_t* bytes) {
   return ok();
 }
 
-int attn_jvp_bwd(const attn_jvp_plan* p, const void* q, const void* k, const void* v, const void* o,
-                 const float* lse, const void* d_o, void* dq, void* dk, void* dv, float* workspace,
-                 void* hip_stream) {
-  if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
-  if (p->rs) return fail(ATTN_JVP_E_INVALID, "the backward takes descriptor plans; range-list plans are forward only");
+namespace {
+
+int bwd_common(const attn_jvp_plan* p, const void* table, const void* q, const void* k, const void* v,
+               const void* o, const float* lse, const void* d_o, void* dq, void* dk, void* dv, float* workspace,
+               void* hip_stream) {
   static const char* names[10] = {"q", "k", "v", "o", "d_o", "lse", "dq", "dk", "dv", "workspace"};
   const void* ins[6] = {q, k, v, o, d_o, lse};
   void* outs[4] = {dq, dk, dv, workspace};
@@ -580,6 +722,8 @@ int attn_jvp_bwd(const attn_jvp_plan* p, const void* q, const void* k, const voi
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j]))
         return fail(ATTN_JVP_E_INVALID, "%s overlaps %s", names[6 + i], names[6 + j]);
+    if (table && overlaps(outs[i], out_bytes[i], table, p->rs->table.size() * sizeof(int32_t)))
+      return fail(ATTN_JVP_E_INVALID, "%s overlaps the table", names[6 + i]);
   }
 
   int dev;
@@ -602,9 +746,46 @@ int attn_jvp_bwd(const attn_jvp_plan* p, const void* q, const void* k, const voi
   bp.n_kblocks = p->bwd_n_kblocks;
   bp.scale = p->scale;
   bp.score_log2 = p->scale * 1.4426950408889634f;
+  bp.tb_blk = bp.tb_order = bp.tb_ent = bp.tb_rows = bp.tb_iv = nullptr;
+  bp.cb_blk = bp.cb_order = bp.cb_ent = bp.cb_cols = bp.cb_iv = nullptr;
+  if (table) {
+    const int32_t* t = (const int32_t*)table;
+    const RangeSchedule& rs = *p->rs;
+    bp.tb_blk = t + rs.off_blk;
+    bp.tb_order = t + rs.off_order;
+    bp.tb_ent = t + rs.off_ent;
+    bp.tb_rows = t + rs.off_rows;
+    bp.tb_iv = t + rs.off_iv;
+    bp.cb_blk = t + rs.off_cblk;
+    bp.cb_order = t + rs.off_corder;
+    bp.cb_ent = t + rs.off_cent;
+    bp.cb_cols = t + rs.off_cols;
+    bp.cb_iv = t + rs.off_civ;
+  }
   hipError_t e = launch_bwd(p->dtype, p->head_dim, p->batch * p->heads, bp, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(ATTN_JVP_E_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+int attn_jvp_bwd(const attn_jvp_plan* p, const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* d_o, void* dq, void* dk, void* dv, float* workspace,
+                 void* hip_stream) {
+  if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
+  if (p->rs) return fail(ATTN_JVP_E_INVALID, "range-list plans run the backward through attn_jvp_bwd_table");
+  return bwd_common(p, nullptr, q, k, v, o, lse, d_o, dq, dk, dv, workspace, hip_stream);
+}
+
+int attn_jvp_bwd_table(const attn_jvp_plan* p, const void* device_table, const void* q, const void* k,
+                       const void* v, const void* o, const float* lse, const void* d_o, void* dq, void* dk,
+                       void* dv, float* workspace, void* hip_stream) {
+  if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
+  if (p->rs == nullptr) return fail(ATTN_JVP_E_INVALID, "descriptor plans have no table: use attn_jvp_bwd");
+  if (!p->rs->bwd_error.empty()) return fail(ATTN_JVP_E_INVALID, "no backward for this plan: %s", p->rs->bwd_error.c_str());
+  if (device_table == nullptr) return fail(ATTN_JVP_E_NULL, "device_table is NULL");
+  if ((uintptr_t)device_table % 4) return fail(ATTN_JVP_E_ALIGN, "device_table is not 4-byte aligned");
+  return bwd_common(p, device_table, q, k, v, o, lse, d_o, dq, dk, dv, workspace, hip_stream);
 }
 
 int attn_jvp_plan_bwd_info(const attn_jvp_plan* p, int32_t* block_q, int32_t* block_kv, int32_t* n_query_blocks,
@@ -625,9 +806,22 @@ int attn_jvp_plan_bwd_flops(const attn_jvp_plan* p, int64_t* useful_flops) {
 
 int attn_jvp_key_ranges(const attn_jvp_plan* p, int32_t* out, size_t n) {
   if (p == nullptr || out == nullptr) return fail(ATTN_JVP_E_NULL, "plan and host_out must be non-NULL");
-  if (p->rs) return fail(ATTN_JVP_E_INVALID, "range-list plans have no backward key ranges");
   if (n < (size_t)p->g.seq_len * 4)
     return fail(ATTN_JVP_E_INVALID, "host_out holds %zu int32, need %zu", n, (size_t)p->g.seq_len * 4);
+  if (p->rs) {
+    if (!p->rs->bwd_error.empty()) return fail(ATTN_JVP_E_INVALID, "no backward for this plan: %s", p->rs->bwd_error.c_str());
+    if (p->rs->cols_over_two) return fail(ATTN_JVP_E_INVALID, "some key is seen by more than two row intervals");
+    const int32_t* cols = p->rs->table.data() + p->rs->off_cols;
+    const int32_t* iv = p->rs->table.data() + p->rs->off_civ;
+    for (int32_t j = 0; j < p->g.seq_len; ++j) {
+      const int32_t off = cols[j] >> 8, cnt = cols[j] & 255;
+      out[4 * j + 0] = cnt >= 1 ? iv[2 * off] : 0;
+      out[4 * j + 1] = cnt >= 1 ? iv[2 * off + 1] : 0;
+      out[4 * j + 2] = cnt >= 2 ? iv[2 * off + 2] : 0;
+      out[4 * j + 3] = cnt >= 2 ? iv[2 * off + 3] : 0;
+    }
+    return ok();
+  }
   for (int32_t j = 0; j < p->g.seq_len; ++j) {
     const Ranges r = col_ranges(p->g, j);
     out[4 * j + 0] = r.lo1;
@@ -688,10 +882,20 @@ int attn_jvp_launch_order(const attn_jvp_plan* p, int32_t* out, size_t n) {
 
 int attn_jvp_bwd_launch_order(const attn_jvp_plan* p, int32_t* out, size_t n) {
   if (p == nullptr || out == nullptr) return fail(ATTN_JVP_E_NULL, "plan and host_out must be non-NULL");
-  if (p->rs) return fail(ATTN_JVP_E_INVALID, "range-list plans have no backward");
+  if (p->rs && !p->rs->bwd_error.empty())
+    return fail(ATTN_JVP_E_INVALID, "no backward for this plan: %s", p->rs->bwd_error.c_str());
   const int64_t total = (int64_t)p->batch * p->heads * p->bwd_n_kblocks;
   if (n < (size_t)total) return fail(ATTN_JVP_E_INVALID, "host_out holds %zu int32, need %lld", n, (long long)total);
-  for (int32_t b = 0; b < (int32_t)total; ++b) out[b] = xcd_grouped(b, (int32_t)total, kDkdvXcdGroup);
+  const int32_t nkb = p->bwd_n_kblocks;
+  for (int32_t b = 0; b < (int32_t)total; ++b) {
+    const int32_t task = xcd_grouped(b, (int32_t)total, kDkdvXcdGroup);
+    if (p->rs) {  // range-list plans: the table's heavy-first key-block order within each (b, h)
+      const int32_t bh = task / nkb;
+      out[b] = bh * nkb + p->rs->table[p->rs->off_corder + (task - bh * nkb)];
+    } else {
+      out[b] = task;
+    }
+  }
   return ok();
 }
 

@@ -32,6 +32,7 @@
 // scheduling slot; whole tiles outside the key (query) ranges are never
 // visited and the element mask runs only on partial tiles.
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -107,12 +108,76 @@ __device__ __forceinline__ void mask_scores(f32x16& S, int x0, int h, const Rang
   }
 }
 
+// Range-list plans: an item's (a query row's, or a key's) intervals on the
+// other axis, from the table's info word ((first interval << 8) | count) and
+// interval list.  The first two are held as Ranges; further ones are read in
+// the mask branch.  Items in no group, and items past the end, have none.
+struct ItemIntervals {
+  Ranges r;
+  int n_iv, off;
+};
+
+__device__ __forceinline__ ItemIntervals item_intervals(const int32_t* info, const int32_t* iv, int item, bool ok) {
+  ItemIntervals it{{0, 0, 0, 0}, 0, 0};
+  if (ok) {
+    const int w = info[item];
+    it.n_iv = w & 255;
+    it.off = w >> 8;
+    if (it.n_iv >= 1) {
+      it.r.lo1 = iv[2 * it.off];
+      it.r.hi1 = iv[2 * it.off + 1];
+    }
+    if (it.n_iv >= 2) {
+      it.r.lo2 = iv[2 * it.off + 2];
+      it.r.hi2 = iv[2 * it.off + 3];
+    }
+  }
+  return it;
+}
+
+// The most intervals any lane's item has (wave-uniform).
+__device__ __forceinline__ int wave_max_intervals(int n_iv) {
+  int m = n_iv;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o));
+  return __builtin_amdgcn_readfirstlane(m);
+}
+
+// mask_scores with all of the item's intervals (max_iv: wave maximum).
+__device__ __forceinline__ void mask_scores_iv(f32x16& S, int x0, int h, const ItemIntervals& it, int max_iv,
+                                               const int32_t* iv) {
+  const int len1 = it.r.hi1 - it.r.lo1, len2 = it.r.hi2 - it.r.lo2;
+  const int b1 = x0 + 4 * h - it.r.lo1, b2 = x0 + 4 * h - it.r.lo2;
+  uint32_t okm = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int off = 8 * (i >> 2) + (i & 3);
+    if ((unsigned)(b1 + off) < (unsigned)len1 || (unsigned)(b2 + off) < (unsigned)len2) okm |= 1u << i;
+  }
+  for (int k = 2; k < max_iv; ++k) {  // items with more than two intervals (rare)
+    int lo = 0, len = 0;
+    if (k < it.n_iv) {
+      lo = iv[2 * (it.off + k)];
+      len = iv[2 * (it.off + k) + 1] - lo;
+    }
+    const int b3 = x0 + 4 * h - lo;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int off = 8 * (i >> 2) + (i & 3);
+      if ((unsigned)(b3 + off) < (unsigned)len) okm |= 1u << i;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) S[i] = ((okm >> i) & 1) ? S[i] : -INFINITY;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // dq kernel (bf16).  One wave = 32 query rows; the K and V tiles of 32 keys
-// stream through the LDS ring.
-template <int D, int NW>
+// stream through the LDS ring.  TABLE: range-list plans, with the forward's
+// block order, tile lists and row intervals from the table.
+template <int D, int NW, bool TABLE>
 __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   using TG = TileGeom<D, NW>;
@@ -134,12 +199,35 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
 
   const MaskGeom g = p.g;
   const int N = g.seq_len;
-  const int bh = blockIdx.x / p.n_qblocks;
-  const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks);
-  int r0, r1;
-  qblock_rows(g, BR, qb, &r0, &r1);
-  const TileSpans sp = block_tiles(block_ranges(g, r0, r1), BC);
-  const int ntiles = span_count(sp);
+  // Range-list plans take the table's heavy-first order in XCD groups of 16,
+  // as the forward does.
+  int task = 0;
+  if constexpr (TABLE) task = xcd_grouped((int)blockIdx.x, (int)gridDim.x, 16);
+  const int bh = TABLE ? task / p.n_qblocks : (int)(blockIdx.x / p.n_qblocks);
+  int r0, r1, ntiles, e0 = 0;
+  TileSpans sp{0, 0, 0, 0};
+  if constexpr (TABLE) {
+    const int qb = p.tb_order[task - bh * p.n_qblocks];
+    r0 = qb * BR;
+    r1 = r0 + BR < N ? r0 + BR : N;
+    e0 = p.tb_blk[qb];
+    ntiles = p.tb_blk[qb + 1] - e0;
+  } else {
+    const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks);
+    qblock_rows(g, BR, qb, &r0, &r1);
+    sp = block_tiles(block_ranges(g, r0, r1), BC);
+    ntiles = span_count(sp);
+  }
+  // range-list plans: the block's tile entries (tile | whole bit of wave w
+  // << (24 + w)), staged in LDS for the whole task
+  int32_t* ent = nullptr;
+  if constexpr (TABLE) {
+    __shared__ int32_t ent_buf[kMaxTableEntries];
+    for (int i = tid; i < ntiles; i += NW * 64) ent_buf[i] = p.tb_ent[e0 + i];
+    __syncthreads();
+    ent = ent_buf;
+  }
+  auto entry = [&](int t) { return __builtin_amdgcn_readfirstlane(ent[t < ntiles ? t : ntiles - 1]); };
 
   const size_t base = (size_t)bh * (size_t)N * D;
   const int slice_bytes = N * D * 2;
@@ -148,7 +236,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
 
   const int row = r0 + wave * 32 + n;
   const bool row_ok = row < r1;
-  const Ranges rr = row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0};
+  ItemIntervals riv{{0, 0, 0, 0}, 0, 0};
+  int max_iv = 0;
+  if constexpr (TABLE) {
+    riv = item_intervals(p.tb_rows, p.tb_iv, row, row_ok);
+    max_iv = wave_max_intervals(riv.n_iv);
+  }
+  const Ranges rr = TABLE ? riv.r : (row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0});
 
   // Q and dO fragments (B operands) stay in accumulation registers; -delta
   // = -dO . O and -lse log2(e) of the row go to the workspace for the dk/dv
@@ -175,6 +269,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
     ndelta = -pair_sum(part);
     const float lse = row_ok ? p.lse[(size_t)bh * N + row] : 0.f;
     nl = -lse * kLog2e;
+    // range-list plans: a row in no group has lse = -inf and no allowed key.
+    // The most negative finite float keeps its (masked) P at 0, where +inf
+    // would give exp2(-inf + inf); finite, because the dk/dv kernel's delta
+    // lanes read this plane past the last row, where 0 * -inf would be NaN.
+    if constexpr (TABLE) nl = lse == -INFINITY ? -FLT_MAX : nl;
     if (row_ok) p.ws[(size_t)bh * 2 * N + (size_t)h * N + row] = h ? nl : ndelta;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -198,15 +297,20 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   for (int i = 0; i < LOADS; ++i) dma_voff[i] = TG::dma_voff(wave, lane, i);
   // The q-th DMA instruction of tile t (past the last tile: that tile again,
   // into a stage nothing reads, so every step issues the same number).
-  auto issue_part = [&](uint16_t* dst, int t, int q, int t_end) {
-    const int tile = span_tile(sp, t < t_end ? t : t_end - 1);
+  // (range-list plans pass the tile index, read once per step: tile_pre)
+  auto issue_part = [&](uint16_t* dst, int t, int q, int t_end, int tile_pre) {
+    int tile;
+    if constexpr (TABLE) tile = tile_pre;
+    else tile = span_tile(sp, t < t_end ? t : t_end - 1);
     const int soff = tile * BC * D * 2;
     const int i = q >> 1, tt = q & 1;
     load16_lds_asm(tt ? desc_v : desc_k, dst + tt * TILE + (wave * LOADS + i) * 512, dma_voff[i], soff);
   };
   auto issue = [&](uint16_t* dst, int t, int t_end) {
+    int tile_pre = 0;
+    if constexpr (TABLE) tile_pre = entry(t) & 0xffffff;
 #pragma unroll
-    for (int q = 0; q < LPT; ++q) issue_part(dst, t, q, t_end);
+    for (int q = 0; q < LPT; ++q) issue_part(dst, t, q, t_end, tile_pre);
   };
 
   f32x16 accQ[DC];
@@ -218,9 +322,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   const float sl2 = p.score_log2;
 
   // Key tiles that every valid row of the wave sees whole (scalar test);
-  // a wave without valid rows masks every tile.
+  // a wave without valid rows masks every tile.  Range-list plans: the
+  // entry's bit of this wave.
   Ranges wfirst{0, 0, 0, 0}, wlast{0, 0, 0, 0};
-  {
+  if constexpr (!TABLE) {
     const int wa = r0 + wave * 32;
     const int wb = wa + 32 < r1 ? wa + 32 : r1;
     if (wa < wb) {
@@ -231,6 +336,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   auto tile_whole = [&](int t) {
     const int k0 = span_tile(sp, t) * BC;
     return run_covers(wfirst, wlast, k0, k0 + BC);
+  };
+  // the partial-tile mask of scores of the tile at key k0
+  auto mask_tile = [&](f32x16& S, int k0) {
+    if constexpr (TABLE) mask_scores_iv(S, k0, h, riv, max_iv, p.tb_iv);
+    else mask_scores(S, k0, h, rr);
   };
   auto exp_elem = [&](float x) { return __builtin_amdgcn_exp2f(fmaf(x, sl2, nl)); };
 
@@ -267,9 +377,15 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
       DS[jj >> 3][(jj & 7) >> 1] = pack_bf16(P[jj] * DP[jj], P[jj + 1] * DP[jj + 1]);
       pin(DS[jj >> 3][(jj & 7) >> 1]);
     };
+    // range-list plans: this step's DMA tile and the next tile's entry, read once
+    int dma_tile = 0, next_e = 0;
+    if constexpr (TABLE) {
+      dma_tile = entry(j + 3) & 0xffffff;
+      next_e = entry(j + 1);
+    }
     auto dma = [&](int s) {
 #pragma unroll
-      for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q) issue_part(stage(AH{}), j + 3, q, t_end);
+      for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q) issue_part(stage(AH{}), j + 3, q, t_end, dma_tile);
     };
 
     constexpr int PAIRS = 8 / KS;  // dS element pairs per k-step
@@ -298,7 +414,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
       const int c2 = gidx / DC, c = gidx % DC;
       accQ[c] = mfma_bf16(ktf[gidx], DS[c2], accQ[c]);
       __builtin_amdgcn_sched_barrier(0);
-      if (gidx == 0 && !tile_whole(j + 1)) mask_scores(Sn, span_tile(sp, j + 1) * BC, h, rr);  // rare
+      if constexpr (TABLE) {
+        if (gidx == 0 && !((next_e >> (24 + wave)) & 1)) mask_tile(Sn, (next_e & 0xffffff) * BC);  // rare
+      } else {
+        if (gidx == 0 && !tile_whole(j + 1)) mask_tile(Sn, span_tile(sp, j + 1) * BC);  // rare
+      }
       if (gidx == 0) {
         // every read of tile j's stage is issued; tile j+2 has landed here
         wait_lgkmcnt<0>();
@@ -338,7 +458,12 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     acc_hazard_wait();
     __builtin_amdgcn_sched_barrier(0);
-    if (!tile_whole(t_begin)) mask_scores(SA, span_tile(sp, t_begin) * BC, h, rr);
+    if constexpr (TABLE) {
+      const int e = entry(t_begin);
+      if (!((e >> (24 + wave)) & 1)) mask_tile(SA, (e & 0xffffff) * BC);
+    } else {
+      if (!tile_whole(t_begin)) mask_tile(SA, span_tile(sp, t_begin) * BC);
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) SA[i] = exp_elem(SA[i]);
     kvread(ring1, 0);
@@ -383,8 +508,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dk/dv kernel (bf16).  One wave = 32 keys; the Q and dO tiles of 32 rows
-// and the rows' delta and -lse log2(e) stream through the LDS ring.
-template <int D, int NW>
+// and the rows' delta and -lse log2(e) stream through the LDS ring.  TABLE:
+// range-list plans, with key blocks cut from key 0, their order, query-tile
+// lists and per-key row intervals from the table's column sections.
+template <int D, int NW, bool TABLE>
 __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   using TG = TileGeom<D, NW>;
@@ -417,11 +544,30 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
   // on one XCD (a quarter of the fetches past L2 of plain round robin).
   const int task = xcd_grouped((int)blockIdx.x, (int)gridDim.x, kDkdvXcdGroup);
   const int bh = task / p.n_kblocks;
-  const int kb = task - bh * p.n_kblocks;
-  int k0, k1;
-  qblock_rows(g, BK, kb, &k0, &k1);
-  const TileSpans sp = block_tiles(block_col_ranges(g, k0, k1), BQ);
-  const int ntiles = span_count(sp);
+  int k0, k1, ntiles, e0 = 0;
+  TileSpans sp{0, 0, 0, 0};
+  if constexpr (TABLE) {
+    const int kb = p.cb_order[task - bh * p.n_kblocks];
+    k0 = kb * BK;
+    k1 = k0 + BK < N ? k0 + BK : N;
+    e0 = p.cb_blk[kb];
+    ntiles = p.cb_blk[kb + 1] - e0;
+  } else {
+    const int kb = task - bh * p.n_kblocks;
+    qblock_rows(g, BK, kb, &k0, &k1);
+    sp = block_tiles(block_col_ranges(g, k0, k1), BQ);
+    ntiles = span_count(sp);
+  }
+  // range-list plans: the block's query-tile entries (tile | whole bit of
+  // wave w << (24 + w)), staged in LDS for the whole task
+  int32_t* ent = nullptr;
+  if constexpr (TABLE) {
+    __shared__ int32_t ent_buf[kMaxTableEntries];
+    for (int i = tid; i < ntiles; i += NW * 64) ent_buf[i] = p.cb_ent[e0 + i];
+    __syncthreads();
+    ent = ent_buf;
+  }
+  auto entry = [&](int t) { return __builtin_amdgcn_readfirstlane(ent[t < ntiles ? t : ntiles - 1]); };
 
   const size_t base = (size_t)bh * (size_t)N * D;
   const int slice_bytes = N * D * 2;
@@ -435,7 +581,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
 
   const int key = k0 + wave * 32 + n;
   const bool key_ok = key < k1;
-  const Ranges cr = key_ok ? col_ranges(g, key) : Ranges{0, 0, 0, 0};
+  ItemIntervals civ{{0, 0, 0, 0}, 0, 0};
+  int max_iv = 0;
+  if constexpr (TABLE) {
+    civ = item_intervals(p.cb_cols, p.cb_iv, key, key_ok);
+    max_iv = wave_max_intervals(civ.n_iv);
+  }
+  const Ranges cr = TABLE ? civ.r : (key_ok ? col_ranges(g, key) : Ranges{0, 0, 0, 0});
 
   // K and V fragments (B operands) stay in accumulation registers for the
   // whole task (zeros for keys past the block).
@@ -474,8 +626,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
   int dma_voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) dma_voff[i] = TG::dma_voff(wave, lane, i);
-  auto issue_part = [&](uint16_t* dst, float* rdst, int t, int q, int t_end) {
-    const int tile = span_tile(sp, t < t_end ? t : t_end - 1);
+  // (range-list plans pass the tile index, read once per step: tile_pre)
+  auto issue_part = [&](uint16_t* dst, float* rdst, int t, int q, int t_end, int tile_pre) {
+    int tile;
+    if constexpr (TABLE) tile = tile_pre;
+    else tile = span_tile(sp, t < t_end ? t : t_end - 1);
     if (q < 2 * LOADS) {
       const int i = q >> 1, tt = q & 1;
       load16_lds_asm(tt ? desc_do : desc_q, dst + tt * TILE + (wave * LOADS + i) * 512, dma_voff[i],
@@ -485,8 +640,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
     }
   };
   auto issue = [&](auto st, int t, int t_end) {
+    int tile_pre = 0;
+    if constexpr (TABLE) tile_pre = entry(t) & 0xffffff;
 #pragma unroll
-    for (int q = 0; q < LPT; ++q) issue_part(stage(st), rstage(st), t, q, t_end);
+    for (int q = 0; q < LPT; ++q) issue_part(stage(st), rstage(st), t, q, t_end, tile_pre);
   };
 
   f32x16 accV[DC], accK[DC];
@@ -500,9 +657,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
   }
   const float sl2 = p.score_log2;
 
-  // Query tiles that every valid key of the wave sees whole.
+  // Query tiles that every valid key of the wave sees whole (range-list
+  // plans: the entry's bit of this wave).
   Ranges wfirst{0, 0, 0, 0}, wlast{0, 0, 0, 0};
-  {
+  if constexpr (!TABLE) {
     const int wa = k0 + wave * 32;
     const int wb = wa + 32 < k1 ? wa + 32 : k1;
     if (wa < wb) {
@@ -513,6 +671,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
   auto tile_whole = [&](int t) {
     const int q0 = span_tile(sp, t) * BQ;
     return run_covers(wfirst, wlast, q0, q0 + BQ);
+  };
+  // the partial-tile mask of scores of the query tile at row q0
+  auto mask_tile = [&](f32x16& X, int q0) {
+    if constexpr (TABLE) mask_scores_iv(X, q0, h, civ, max_iv, p.cb_iv);
+    else mask_scores(X, q0, h, cr);
   };
   // Row terms of the lane's elements 4 q4 .. 4 q4 + 3 (rows 8 q4 + 4h + 0..3):
   // plane 0 -delta, plane 1 -lse log2(e).  Read a quad at a time, shortly
@@ -563,10 +726,16 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
       doT[gidx] = TG::tr_frag(cur + TILE, lane, gidx);
       qT[gidx] = TG::tr_frag(cur, lane, gidx);
     };
+    // range-list plans: this step's DMA tile and the next tile's entry, read once
+    int dma_tile = 0, next_e = 0;
+    if constexpr (TABLE) {
+      dma_tile = entry(j + 3) & 0xffffff;
+      next_e = entry(j + 1);
+    }
     auto dma = [&](int s) {
 #pragma unroll
       for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q)
-        issue_part(stage(AH{}), rstage(AH{}), j + 3, q, t_end);
+        issue_part(stage(AH{}), rstage(AH{}), j + 3, q, t_end, dma_tile);
     };
 
     constexpr int PAIRS = 8 / KS;  // dS element pairs per k-step
@@ -606,7 +775,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
         else accK[c] = mfma_bf16(qT[gidx], DSK[c2], accK[c]);
         __builtin_amdgcn_sched_barrier(0);
         const int u = 2 * gidx + sl;
-        if (u == 0 && !tile_whole(j + 1)) mask_scores(Xn, span_tile(sp, j + 1) * BQ, h, cr);  // rare
+        if constexpr (TABLE) {
+          if (u == 0 && !((next_e >> (24 + wave)) & 1)) mask_tile(Xn, (next_e & 0xffffff) * BQ);  // rare
+        } else {
+          if (u == 0 && !tile_whole(j + 1)) mask_tile(Xn, span_tile(sp, j + 1) * BQ);  // rare
+        }
         if (sl == 0 && gidx + 3 < NG) trread(gidx + 3);
         if (u == UB) {
           wait_lgkmcnt<0>();
@@ -663,7 +836,12 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
     __builtin_amdgcn_sched_barrier(0);
     acc_hazard_wait();
     __builtin_amdgcn_sched_barrier(0);
-    if (!tile_whole(t_begin)) mask_scores(XA, span_tile(sp, t_begin) * BQ, h, cr);
+    if constexpr (TABLE) {
+      const int e = entry(t_begin);
+      if (!((e >> (24 + wave)) & 1)) mask_tile(XA, (e & 0xffffff) * BQ);
+    } else {
+      if (!tile_whole(t_begin)) mask_tile(XA, span_tile(sp, t_begin) * BQ);
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) XA[i] = __builtin_amdgcn_exp2f(fmaf(XA[i], sl2, nlv[i]));
     qdread(ring1, 0);
@@ -722,21 +900,29 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
-template <int D>
+// TABLE: range-list plans; each row (key) walks its own intervals from the
+// table in ascending order.
+template <int D, bool TABLE>
 __global__ void __launch_bounds__(256) bwd_dq_fp32_kernel(BwdParams p) {
   constexpr int BR = 32, BC = 32, E = D / 8;
   const MaskGeom g = p.g;
   const int N = g.seq_len;
   const int slice = threadIdx.x & 7, lr = threadIdx.x >> 3;
   const int bh = blockIdx.x / p.n_qblocks;
-  const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks);
-  int r0, r1;
-  qblock_rows(g, BR, qb, &r0, &r1);
-  const TileSpans sp = block_tiles(block_ranges(g, r0, r1), BC);
-  const int ntiles = span_count(sp);
+  int r0, r1, ntiles = 0;
+  TileSpans sp{0, 0, 0, 0};
+  if constexpr (TABLE) {
+    r0 = p.tb_order[blockIdx.x - bh * p.n_qblocks] * BR;
+    r1 = r0 + BR < N ? r0 + BR : N;
+  } else {
+    const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks);
+    qblock_rows(g, BR, qb, &r0, &r1);
+    sp = block_tiles(block_ranges(g, r0, r1), BC);
+    ntiles = span_count(sp);
+  }
   const int row = r0 + lr;
   const bool row_ok = row < r1;
-  const Ranges rr = row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0};
+  const Ranges rr = TABLE ? Ranges{0, 0, 0, 0} : (row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0});
   const size_t base = (size_t)bh * (size_t)N * D;
   const float* __restrict__ K = (const float*)p.k + base + slice * E;
   const float* __restrict__ V = (const float*)p.v + base + slice * E;
@@ -752,28 +938,43 @@ __global__ void __launch_bounds__(256) bwd_dq_fp32_kernel(BwdParams p) {
     acc[e] = 0.f;
   }
   const float delta = sum8(part);
-  const float nl = -p.lse[(size_t)bh * N + qrow] * kLog2e;
+  const float lse = p.lse[(size_t)bh * N + qrow];
+  // (range-list plans: the most negative finite float for a row in no group,
+  // which has no key; as in the bf16 kernel)
+  const float nl = TABLE && lse == -INFINITY ? -FLT_MAX : -lse * kLog2e;
   if (row_ok && slice < 2) p.ws[(size_t)bh * 2 * N + (size_t)slice * N + row] = slice ? nl : -delta;
   const float sl2 = p.score_log2;
-  for (int it = 0; it < ntiles; ++it) {
-    const int k0 = span_tile(sp, it) * BC;
-    const int k1 = k0 + BC < N ? k0 + BC : N;
-    for (int j = k0; j < k1; ++j) {
-      if (!in_ranges(rr, j)) continue;  // uniform across the row's 8 lanes
-      const float* kj = K + (size_t)j * D;
-      const float* vj = V + (size_t)j * D;
-      float s = 0.f, dp = 0.f;
+  auto key_step = [&](int j) {
+    const float* kj = K + (size_t)j * D;
+    const float* vj = V + (size_t)j * D;
+    float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        s = fmaf(q[e], kj[e], s);
-        dp = fmaf(dob[e], vj[e], dp);
+    for (int e = 0; e < E; ++e) {
+      s = fmaf(q[e], kj[e], s);
+      dp = fmaf(dob[e], vj[e], dp);
+    }
+    s = sum8(s);
+    dp = sum8(dp);
+    const float pj = exp2f(fmaf(s, sl2, nl));
+    const float ds = pj * (dp - delta);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(ds, kj[e], acc[e]);
+  };
+  if constexpr (TABLE) {
+    if (row_ok) {  // uniform across the row's 8 lanes
+      const int info = p.tb_rows[row];
+      const int n_iv = info & 255, iv_off = info >> 8;
+      for (int k = 0; k < n_iv; ++k)
+        for (int j = p.tb_iv[2 * (iv_off + k)], j1 = p.tb_iv[2 * (iv_off + k) + 1]; j < j1; ++j) key_step(j);
+    }
+  } else {
+    for (int it = 0; it < ntiles; ++it) {
+      const int k0 = span_tile(sp, it) * BC;
+      const int k1 = k0 + BC < N ? k0 + BC : N;
+      for (int j = k0; j < k1; ++j) {
+        if (!in_ranges(rr, j)) continue;  // uniform across the row's 8 lanes
+        key_step(j);
       }
-      s = sum8(s);
-      dp = sum8(dp);
-      const float pj = exp2f(fmaf(s, sl2, nl));
-      const float ds = pj * (dp - delta);
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(ds, kj[e], acc[e]);
     }
   }
   if (!row_ok) return;
@@ -782,20 +983,26 @@ __global__ void __launch_bounds__(256) bwd_dq_fp32_kernel(BwdParams p) {
   for (int e = 0; e < E; ++e) dQ[e] = acc[e] * p.scale;
 }
 
-template <int D>
+template <int D, bool TABLE>
 __global__ void __launch_bounds__(256) bwd_dkdv_fp32_kernel(BwdParams p) {
   constexpr int BK = 32, BQ = 32, E = D / 8;
   const MaskGeom g = p.g;
   const int N = g.seq_len;
   const int slice = threadIdx.x & 7, lk = threadIdx.x >> 3;
   const int bh = blockIdx.x / p.n_kblocks;
-  int k0, k1;
-  qblock_rows(g, BK, blockIdx.x - bh * p.n_kblocks, &k0, &k1);
-  const TileSpans sp = block_tiles(block_col_ranges(g, k0, k1), BQ);
-  const int ntiles = span_count(sp);
+  int k0, k1, ntiles = 0;
+  TileSpans sp{0, 0, 0, 0};
+  if constexpr (TABLE) {
+    k0 = p.cb_order[blockIdx.x - bh * p.n_kblocks] * BK;
+    k1 = k0 + BK < N ? k0 + BK : N;
+  } else {
+    qblock_rows(g, BK, blockIdx.x - bh * p.n_kblocks, &k0, &k1);
+    sp = block_tiles(block_col_ranges(g, k0, k1), BQ);
+    ntiles = span_count(sp);
+  }
   const int key = k0 + lk;
   const bool key_ok = key < k1;
-  const Ranges cr = key_ok ? col_ranges(g, key) : Ranges{0, 0, 0, 0};
+  const Ranges cr = TABLE ? Ranges{0, 0, 0, 0} : (key_ok ? col_ranges(g, key) : Ranges{0, 0, 0, 0});
   const size_t base = (size_t)bh * (size_t)N * D;
   const float* __restrict__ Q = (const float*)p.q + base + slice * E;
   const float* __restrict__ dO = (const float*)p.dout + base + slice * E;
@@ -811,27 +1018,39 @@ __global__ void __launch_bounds__(256) bwd_dkdv_fp32_kernel(BwdParams p) {
     av[e] = 0.f;
   }
   const float sl2 = p.score_log2;
-  for (int it = 0; it < ntiles; ++it) {
-    const int q0 = span_tile(sp, it) * BQ;
-    const int q1 = q0 + BQ < N ? q0 + BQ : N;
-    for (int i = q0; i < q1; ++i) {
-      if (!in_ranges(cr, i)) continue;  // uniform across the key's 8 lanes
-      const float* qi = Q + (size_t)i * D;
-      const float* doi = dO + (size_t)i * D;
-      float s = 0.f, dp = 0.f;
+  auto row_step = [&](int i) {
+    const float* qi = Q + (size_t)i * D;
+    const float* doi = dO + (size_t)i * D;
+    float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        s = fmaf(qi[e], kk[e], s);
-        dp = fmaf(doi[e], vv[e], dp);
-      }
-      s = sum8(s);
-      dp = sum8(dp);
-      const float pij = exp2f(fmaf(s, sl2, nlr[i]));
-      const float ds = pij * (dp + ndl[i]);
+    for (int e = 0; e < E; ++e) {
+      s = fmaf(qi[e], kk[e], s);
+      dp = fmaf(doi[e], vv[e], dp);
+    }
+    s = sum8(s);
+    dp = sum8(dp);
+    const float pij = exp2f(fmaf(s, sl2, nlr[i]));
+    const float ds = pij * (dp + ndl[i]);
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        av[e] = fmaf(pij, doi[e], av[e]);
-        ak[e] = fmaf(ds, qi[e], ak[e]);
+    for (int e = 0; e < E; ++e) {
+      av[e] = fmaf(pij, doi[e], av[e]);
+      ak[e] = fmaf(ds, qi[e], ak[e]);
+    }
+  };
+  if constexpr (TABLE) {
+    if (key_ok) {  // uniform across the key's 8 lanes
+      const int info = p.cb_cols[key];
+      const int n_iv = info & 255, iv_off = info >> 8;
+      for (int k = 0; k < n_iv; ++k)
+        for (int i = p.cb_iv[2 * (iv_off + k)], i1 = p.cb_iv[2 * (iv_off + k) + 1]; i < i1; ++i) row_step(i);
+    }
+  } else {
+    for (int it = 0; it < ntiles; ++it) {
+      const int q0 = span_tile(sp, it) * BQ;
+      const int q1 = q0 + BQ < N ? q0 + BQ : N;
+      for (int i = q0; i < q1; ++i) {
+        if (!in_ranges(cr, i)) continue;  // uniform across the key's 8 lanes
+        row_step(i);
       }
     }
   }
@@ -857,25 +1076,31 @@ void bwd_block_sizes(int dtype, int head_dim, int* block_q, int* block_kv) {
   }
 }
 
-hipError_t launch_bwd(int dtype, int head_dim, int bh, const BwdParams& p, hipStream_t stream) {
+namespace {
+
+template <int D, bool TABLE>
+void launch_bwd_kernels(int dtype, int bh, const BwdParams& p, hipStream_t stream) {
   const dim3 gq((unsigned)bh * (unsigned)p.n_qblocks), gk((unsigned)bh * (unsigned)p.n_kblocks);
   if (dtype == kBf16) {
     const dim3 block(kBf16Waves * 64);
-    if (head_dim == 128) {
-      hipLaunchKernelGGL((bwd_dq_bf16_kernel<128, kBf16Waves>), gq, block, 0, stream, p);
-      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<128, kBf16Waves>), gk, block, 0, stream, p);
-    } else {
-      hipLaunchKernelGGL((bwd_dq_bf16_kernel<64, kBf16Waves>), gq, block, 0, stream, p);
-      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<64, kBf16Waves>), gk, block, 0, stream, p);
-    }
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, kBf16Waves, TABLE>), gq, block, 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, kBf16Waves, TABLE>), gk, block, 0, stream, p);
   } else {
-    if (head_dim == 128) {
-      hipLaunchKernelGGL((bwd_dq_fp32_kernel<128>), gq, dim3(256), 0, stream, p);
-      hipLaunchKernelGGL((bwd_dkdv_fp32_kernel<128>), gk, dim3(256), 0, stream, p);
-    } else {
-      hipLaunchKernelGGL((bwd_dq_fp32_kernel<64>), gq, dim3(256), 0, stream, p);
-      hipLaunchKernelGGL((bwd_dkdv_fp32_kernel<64>), gk, dim3(256), 0, stream, p);
-    }
+    hipLaunchKernelGGL((bwd_dq_fp32_kernel<D, TABLE>), gq, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_fp32_kernel<D, TABLE>), gk, dim3(256), 0, stream, p);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd(int dtype, int head_dim, int bh, const BwdParams& p, hipStream_t stream) {
+  const bool table = p.cb_ent != nullptr;
+  if (head_dim == 128) {
+    if (table) launch_bwd_kernels<128, true>(dtype, bh, p, stream);
+    else launch_bwd_kernels<128, false>(dtype, bh, p, stream);
+  } else {
+    if (table) launch_bwd_kernels<64, true>(dtype, bh, p, stream);
+    else launch_bwd_kernels<64, false>(dtype, bh, p, stream);
   }
   return hipGetLastError();
 }

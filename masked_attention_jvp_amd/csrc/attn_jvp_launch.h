@@ -52,12 +52,26 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* ws;          // per (b, h): [2][N] floats, delta then -lse * log2(e)
+  float* ws;          // per (b, h): [2][N] floats, -delta then -lse * log2(e)
   MaskGeom g;
   int32_t n_qblocks;  // dq kernel: query blocks per (b, h)
   int32_t n_kblocks;  // dk/dv kernel: key blocks per (b, h)
   float score_log2;   // scale * log2(e)
   float scale;
+  // range-list plans (all null otherwise): sections of the device table.
+  // Query side, as in FwdParams (the dq kernel walks the forward's schedule):
+  const int32_t* tb_blk;
+  const int32_t* tb_order;
+  const int32_t* tb_ent;
+  const int32_t* tb_rows;
+  const int32_t* tb_iv;
+  // columns (the dk/dv kernel): per key block its 32-row query tiles, per key
+  // its row intervals
+  const int32_t* cb_blk;    // [n_kblocks + 1] first entry of each key block
+  const int32_t* cb_order;  // [n_kblocks] launch order
+  const int32_t* cb_ent;    // query tile | (whole bit of wave w) << (24 + w)
+  const int32_t* cb_cols;   // [N] (first interval << 8) | interval count
+  const int32_t* cb_iv;     // (lo, hi) row intervals
 };
 
 // Query rows per block and keys per tile of the kernel chosen for dtype/head_dim.

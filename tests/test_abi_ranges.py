@@ -7,7 +7,12 @@
   ragged sizes and at the full c1-4 workload;
 * per-row key intervals equal the oracle mask; pair counts and useful FLOPs;
 * the serialised table: header, heavy-first launch order, per-wave whole bits
-  against the oracle mask.
+  against the oracle mask;
+* the table's column sections, which the backward's dk/dv kernel walks: per
+  key block exactly the 32-row query tiles with an allowed pair, per-wave
+  whole bits, and per key the row intervals that see it, all against the
+  columns of the oracle mask; key ranges, launch order and argument errors
+  of the backward on range-list plans.
 """
 import ctypes
 import os
@@ -24,6 +29,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(aj.library_path), reason="lib
 
 GAPS = (40, ((0, 6, ((0, 3), (10, 14))), (9, 15, ((0, 40),)), (15, 33, ((5, 6), (20, 33))), (35, 40, ((1, 2),))))
 MULTI = (70, ((0, 30, ((0, 3), (7, 9), (12, 20), (33, 40))), (30, 70, ((0, 70),))))  # rows with four intervals
+# keys 0-19 are seen by three separate row intervals, keys 60-99 by two
+STRIPES = (100, ((0, 10, ((0, 20),)), (20, 30, ((0, 20), (60, 100))), (40, 50, ((0, 20),)), (70, 100, ((60, 100),))))
 
 MASKS = {
     "tf_c1_2": si.chunked_mask_ranges(16, (1, 2, 2), 1),
@@ -33,6 +40,7 @@ MASKS = {
     "dense": (150, ((0, 150, ((0, 150),)),)),
     "gaps": GAPS,
     "multi": MULTI,
+    "stripes": STRIPES,
     "tf_eq_as_ranges": si.chunked_mask_ranges(50, (1,) * 5, 1),
 }
 
@@ -161,3 +169,145 @@ def test_range_plan_entry_points_refuse_the_wrong_plan_kind():
     bwd = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(10)]
     assert lib.attn_jvp_bwd(pr.handle, *bwd, None) == 1
     assert aj.attn_jvp_plan_table_size(pd) == 0
+
+
+def _sections(p):
+    """The table's column sections: cblk, corder, centries, cols, cintervals."""
+    t = aj.attn_jvp_plan_table(p)
+    nq, ne, niv, nkb, nce, nciv = (int(t[i]) for i in (1, 2, 3, 5, 6, 7))
+    n = p.seq_len
+    o = 8 + (nq + 1) + nq + ne + n + 2 * niv
+    out = []
+    for size in (nkb + 1, nkb, nce, n, 2 * nciv):
+        out.append(t[o:o + size])
+        o += size
+    assert o == len(t)
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(MASKS))
+@pytest.mark.parametrize("dtype", [aj.ATTN_JVP_BF16, aj.ATTN_JVP_FP32])
+def test_column_tiles_and_whole_bits_match_the_mask_columns(name, dtype):
+    p, rm = _plan(name, dtype, 64)
+    cblk, corder, cent, _, _ = _sections(p)
+    info = aj.attn_jvp_plan_bwd_info(p)
+    bk = info["block_kv"]
+    assert bk == (128 if dtype == aj.ATTN_JVP_BF16 else 32)
+    m = oracle.mask_dense(rm)
+    n = p.seq_len
+    nkb = -(-n // bk)
+    assert info["n_key_blocks"] == nkb == len(corder)
+    assert info["n_query_blocks"] == p.info["n_query_blocks"]
+    assert sorted(corder.tolist()) == list(range(nkb))
+    counts = np.diff(cblk)[corder]
+    assert np.all(np.diff(counts) <= 0)  # heavy (more query tiles) first
+    for kb in range(nkb):
+        k0, k1 = kb * bk, min(kb * bk + bk, n)
+        tiles = cent[cblk[kb]:cblk[kb + 1]] & 0xffffff
+        want = [t for t in range(-(-n // 32)) if m[32 * t:32 * t + 32, k0:k1].any()]
+        assert tiles.tolist() == want  # ascending, exactly the tiles with an allowed pair
+        for e in cent[cblk[kb]:cblk[kb + 1]]:
+            q0 = 32 * (int(e) & 0xffffff)
+            for w in range(bk // 32):
+                a, z = k0 + 32 * w, min(k0 + 32 * w + 32, k1)
+                whole = bool((int(e) >> (24 + w)) & 1)
+                if a >= z:
+                    assert whole  # no valid keys in this wave
+                else:
+                    assert whole == bool(q0 + 32 <= n and m[q0:q0 + 32, a:z].all())
+
+
+@pytest.mark.parametrize("name", sorted(MASKS))
+def test_column_intervals_are_the_mask_columns(name):
+    p, rm = _plan(name)
+    _, _, _, cols, civ = _sections(p)
+    m = oracle.mask_dense(rm)
+    rows = np.arange(p.seq_len)
+    over_two = False
+    for j in range(p.seq_len):
+        off, cnt = int(cols[j]) >> 8, int(cols[j]) & 255
+        iv = civ[2 * off:2 * off + 2 * cnt].reshape(-1, 2)
+        assert np.all(iv[:, 0] < iv[:, 1]) and np.all(iv[1:, 0] > iv[:-1, 1])  # sorted, disjoint, not touching
+        got = np.zeros(p.seq_len, bool)
+        for lo, hi in iv:
+            got |= (rows >= lo) & (rows < hi)
+        assert np.array_equal(got, m[:, j])
+        over_two = over_two or cnt > 2
+    if over_two:
+        with pytest.raises(aj.AttnJvpError) as e:
+            aj.attn_jvp_key_ranges(p)
+        assert e.value.code == 1
+    else:  # the first two row intervals of each key, as the descriptor plans export them
+        kr = aj.attn_jvp_key_ranges(p)
+        lo1, hi1, lo2, hi2 = (kr[:, i:i + 1] for i in range(4))
+        got = ((rows >= lo1) & (rows < hi1)) | ((rows >= lo2) & (rows < hi2))
+        assert np.array_equal(got, m.T)
+
+
+def test_range_bwd_flops_and_workspace():
+    p, rm = _plan("und_gen", b=2, h=3)
+    assert aj.attn_jvp_plan_bwd_flops(p) == 10 * 128 * 6 * oracle.pair_count(rm)
+    assert aj.attn_jvp_bwd_workspace_size(p) == 8 * 6 * p.seq_len
+
+
+@pytest.mark.parametrize("name, b, h", [("tf_c1_4_t50", 3, 40), ("und_gen", 2, 7)])
+def test_range_bwd_launch_order_is_the_table_order_xcd_grouped(name, b, h):
+    p, _ = _plan(name, b=b, h=h)
+    _, corder, _, _, _ = _sections(p)
+    nk = len(corder)
+    order = aj.attn_jvp_bwd_launch_order(p)
+    total = b * h * nk
+    assert sorted(order.tolist()) == list(range(total))
+    # back to task numbers: (b, h) slice times n_key_blocks plus the block's rank in the table order
+    rank = np.empty(nk, np.int64)
+    rank[corder] = np.arange(nk)
+    tasks = (order // nk) * nk + rank[order % nk]
+    for r in range(total // 128):  # XCD groups of 16 consecutive tasks, direction alternating by round
+        seg = tasks[128 * r: 128 * (r + 1)]
+        for x in range(8):
+            t = np.sort(seg[x::8])
+            assert np.array_equal(t, np.arange(t[0], t[0] + 16))
+        assert int(seg[0::8].min()) == 128 * r + (0 if r % 2 == 0 else 112)
+    assert np.array_equal(tasks[128 * (total // 128):], np.arange(128 * (total // 128), total))
+
+
+def test_bwd_table_argument_errors_before_any_device_call():
+    lib = aj._load()
+    pr, _ = _plan("gaps")
+    pd = aj.attn_jvp_create((4, 3, 1, 1), 1, 1, 64, aj.ATTN_JVP_BF16)
+    bwd = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(10)]  # q k v o lse d_o dq dk dv ws
+    table = ctypes.c_void_p(0x2000000)
+    assert lib.attn_jvp_bwd(pr.handle, *bwd, None) == 1
+    assert "attn_jvp_bwd_table" in aj.attn_jvp_last_error_detail()
+    assert lib.attn_jvp_bwd_table(None, table, *bwd, None) == 2
+    assert lib.attn_jvp_bwd_table(pd.handle, table, *bwd, None) == 1
+    assert lib.attn_jvp_bwd_table(pr.handle, None, *bwd, None) == 2
+    assert lib.attn_jvp_bwd_table(pr.handle, ctypes.c_void_p(0x2000002), *bwd, None) == 3
+    for i in range(10):
+        bad = list(bwd)
+        bad[i] = ctypes.c_void_p(0)
+        assert lib.attn_jvp_bwd_table(pr.handle, table, *bad, None) == 2
+    bad = list(bwd)
+    bad[7] = bad[6]  # dk aliases dq
+    assert lib.attn_jvp_bwd_table(pr.handle, table, *bad, None) == 1
+    bad = list(bwd)
+    bad[0] = ctypes.c_void_p(0x100008)  # q misaligned
+    assert lib.attn_jvp_bwd_table(pr.handle, table, *bad, None) == 3
+
+
+def test_plan_whose_columns_do_not_fit_has_a_forward_but_no_backward():
+    # 300 one-row groups with gaps between them all see key 0: 300 separate row intervals
+    n = 600
+    groups = [(2 * i, 2 * i + 1, [(0, 1)]) for i in range(300)]
+    p = aj.attn_jvp_create_ranges(n, groups, 1, 1, 128)
+    t = aj.attn_jvp_plan_table(p)
+    assert t[5] == 0 and t[6] == 0 and t[7] == 0  # no column sections
+    assert p.info["allowed_pairs_per_head"] == 300
+    lib = aj._load()
+    bwd = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(10)]
+    assert lib.attn_jvp_bwd_table(p.handle, ctypes.c_void_p(0x2000000), *bwd, None) == 1
+    assert "255" in aj.attn_jvp_last_error_detail()
+    for call in (aj.attn_jvp_key_ranges, aj.attn_jvp_bwd_launch_order):
+        with pytest.raises(aj.AttnJvpError) as e:
+            call(p)
+        assert e.value.code == 1
