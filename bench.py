@@ -139,11 +139,15 @@ class SmiSampler(threading.Thread):
 def kernel_hash(part="fwd"):
     """Hash of the code the kernels of one part (fwd, bwd) are built from
     (comments and blank lines removed), so that counters stay attached to an
-    unchanged kernel."""
+    unchanged kernel.  The shared launch header enters without the other
+    part's parameter struct, which its kernels never see."""
+    other = {"fwd": "BwdParams", "bwd": "FwdParams"}[part]
     h = hashlib.sha256()
     for path in KERNEL_SRCS[part]:
         with open(path) as f:
             code = re.sub(r"//[^\n]*", "", f.read())
+        if path.endswith("attn_jvp_launch.h"):
+            code = re.sub(r"struct " + other + r" \{.*?\n\};", "", code, flags=re.S)
         h.update("\n".join(l.rstrip() for l in code.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
