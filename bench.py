@@ -383,7 +383,7 @@ def main():
     tb = "true" if use_ranges else "false"
     kernel = (f"bwd_dq_bf16_kernel<{w.head_dim},{nw},{tb}> + bwd_dkdv_bf16_kernel<{w.head_dim},{nw},{tb}>"
               if args.backward
-              else f"fwd_bf16_kernel<{w.head_dim},{nw},true,false> (primal mode)" if args.primal
+              else f"fwd_primal_bf16_kernel<{w.head_dim},{nw}>" if args.primal
               else f"fwd_bf16_kernel<{w.head_dim},{nw},{'true' if flags else 'false'},{'true' if use_ranges else 'false'}>")
 
     out = {

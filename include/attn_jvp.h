@@ -177,7 +177,9 @@ int attn_jvp_fwd(const attn_jvp_plan* plan, const void* q, const void* k, const 
  * that the backward (attn_jvp_bwd) pairs with: together they replace the
  * plain FlashAttention-2 of a student's training step (Causal-rCM, section
  * 3.2.1 and the TF-dCM comparison of section 6).  Descriptor plans; the
- * plan's flags do not matter.  Same checks and error codes as attn_jvp_fwd. */
+ * plan's flags do not matter.  In bf16 it runs its own kernel, with query
+ * blocks of 256 rows (64 per wave); the per-row arithmetic is the forward's.
+ * Same checks and error codes as attn_jvp_fwd. */
 int attn_jvp_fwd_primal(const attn_jvp_plan* plan, const void* q, const void* k, const void* v,
                         void* o, float* lse, void* hip_stream);
 

@@ -655,7 +655,9 @@ int fwd_common(const attn_jvp_plan* p, const void* table, const void* q, const v
     fp.tb_rows = t + p->rs->off_rows;
     fp.tb_iv = t + p->rs->off_iv;
   }
-  const int grid = p->batch * p->heads * p->n_qblocks;
+  // the bf16 primal kernel takes query blocks of 64 rows per wave
+  if (primal && p->dtype == ATTN_JVP_BF16) fp.n_qblocks = n_query_blocks(p->g, kBf16PrimalRows);
+  const int grid = p->batch * p->heads * fp.n_qblocks;
   hipError_t e = launch_fwd(p->dtype, p->head_dim, grid, fp, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(ATTN_JVP_E_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();

@@ -719,6 +719,427 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Primal bf16 kernel: o and lse of the masked attention alone (no tangents),
+// for descriptor plans.  One wave holds 64 query rows as two 32-row blocks
+// (rb) that share every K and V fragment it reads from LDS, and a workgroup
+// of NW waves takes a query block of 64 NW rows: per MFMA, the DMA and the
+// fragment reads are half those of fwd_bf16_kernel's primal tile mode, which
+// spreads that traffic over 16 MFMAs per wave and tile.  The ring holds K and
+// V of 32-key tiles in 4 stages.  For every row the arithmetic is that of
+// fwd_bf16_kernel, in the same order: the same score MFMA chain, row max,
+// lazy reference, exponentials, sums, packs and output MFMA chain.  Tiles a
+// row does not see (streamed for other rows of the larger block) are masked
+// to exact zeros and leave its reference unchanged, so o and lse are
+// bit-identical to the forward + JVP's.
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64, 1) fwd_primal_bf16_kernel(FwdParams p) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  constexpr int BC = kBf16BlockK;  // keys per tile
+  static_assert(BC == 32, "one 32-key subtile per tile");
+  constexpr int STAGES = 4;
+  constexpr int RB = 2;                 // 32-row blocks per wave
+  constexpr int BR = NW * 32 * RB;      // rows per workgroup
+  constexpr int KS = D / 16;            // k-steps of the score products
+  constexpr int DC = D / 32;            // 32-wide column blocks of o
+  constexpr int NG = 2 * DC;            // P.V groups per tile
+  constexpr int CPR = D / 8;            // 16-byte groups per row
+  constexpr int TILE = BC * D;          // elements per tensor per stage
+  constexpr int LOADS = TILE * 2 / 1024 / NW;  // 1 KB DMA loads per wave per tensor
+  static_assert(LOADS * NW * 1024 == TILE * 2, "DMA split");
+  constexpr int LPT = 2 * LOADS;        // DMA instructions per wave and tile: K, V
+  // LDS fragment reads run KA k-steps (K) and VA groups (V) ahead of their
+  // MFMAs: 2 KA and 2 VA scheduling slots.
+  constexpr int KA = 3, VA = 3;
+  static_assert(KA <= KS && VA <= KS && VA < NG, "read-ahead");
+  static_assert(LPT % KS == 0 || KS % LPT == 0, "DMA spread");
+
+  __shared__ __attribute__((aligned(1024))) uint16_t ring0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring2[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring3[2 * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+
+  const MaskGeom g = p.g;
+  const int N = g.seq_len;
+  const int bh = (int)(blockIdx.x / p.n_qblocks);
+  const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks);
+  int r0, r1;
+  qblock_rows(g, BR, qb, &r0, &r1);
+  const TileSpans sp = block_tiles(block_ranges(g, r0, r1), BC);
+  const int ntiles = span_count(sp);
+
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const int slice_bytes = N * D * 2;
+  const i32x4_t desc_k = make_desc((const uint16_t*)p.k + base, slice_bytes);
+  const i32x4_t desc_v = make_desc((const uint16_t*)p.v + base, slice_bytes);
+
+  int row[RB];
+  bool row_ok[RB];
+  Ranges rr[RB];
+  int f1[RB], g0[RB], g1[RB];  // whole-tile test per row block (scalars), as in fwd_bf16_kernel
+  u32x4 qf[RB][KS];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)p.q + base, slice_bytes);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      row[rb] = r0 + wave * 64 + rb * 32 + n;
+      row_ok[rb] = row[rb] < r1;
+      rr[rb] = row_ok[rb] ? row_ranges(g, row[rb]) : Ranges{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        qf[rb][s] = load16(rq, (row[rb] * D + 16 * s + 8 * h) * 2);
+        keep_in_acc(qf[rb][s]);  // B operands from accumulation registers, for the whole task
+      }
+      f1[rb] = 1 << 30;
+      g0[rb] = 0;
+      g1[rb] = 1 << 30;
+      const int wa = r0 + wave * 64 + rb * 32;
+      const int wb = wa + 32 < r1 ? wa + 32 : r1;
+      if (wa < wb) {
+        const Ranges first = row_ranges(g, wa), last = row_ranges(g, wb - 1);
+        f1[rb] = first.hi1;
+        g0[rb] = last.lo2;
+        g1[rb] = first.hi2;
+      }
+    }
+  }
+
+  auto stage = [&](auto st) -> uint16_t* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return ring0;
+    else if constexpr (S == 1) return ring1;
+    else if constexpr (S == 2) return ring2;
+    else return ring3;
+  };
+  int dma_voff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int blk = wave * LOADS + i;
+    const int rw = blk * (64 / CPR) + lane / CPR;
+    dma_voff[i] = (rw * D + (((lane % CPR) ^ row_swz<D>(rw)) << 3)) * 2;
+  }
+  // The q-th DMA instruction of tile t (K then V of each 1 KB block); past
+  // the run's last tile that tile again, into a stage nothing reads.
+  auto issue_part = [&](uint16_t* dst, int t, int q, int t_end) {
+    const int tile = span_tile(sp, t < t_end ? t : t_end - 1);
+    const int i = q >> 1, tt = q & 1;
+    load16_lds_asm(tt ? desc_v : desc_k, dst + tt * TILE + (wave * LOADS + i) * 512, dma_voff[i],
+                   tile * BC * D * 2);
+  };
+  auto issue = [&](uint16_t* dst, int t, int t_end) {
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) issue_part(dst, t, q, t_end);
+  };
+
+  f32x16 accO[RB][DC];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) accO[rb][c][i] = 0.f;
+    }
+  }
+  float m[RB], mn[RB], l[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = -INFINITY;
+    mn[rb] = -INFINITY;
+    l[rb] = 0.f;
+  }
+  const float sl2 = p.score_log2;
+  const int tr_key = 4 * h + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  auto tile_whole = [&](int rb, int t) {
+    const int k0 = span_tile(sp, t) * BC;
+    return k0 + BC <= f1[rb] || (k0 >= g0[rb] && k0 + BC <= g1[rb]);
+  };
+  auto mask_tile = [&](int rb, int t, f32x16& S) {
+    const int k0 = span_tile(sp, t) * BC;
+    const int len1 = rr[rb].hi1 - rr[rb].lo1, len2 = rr[rb].hi2 - rr[rb].lo2;
+    const int b1 = k0 + 4 * h - rr[rb].lo1, b2 = k0 + 4 * h - rr[rb].lo2;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int off = 8 * (i >> 2) + (i & 3);
+      const bool ok = (unsigned)(b1 + off) < (unsigned)len1 || (unsigned)(b2 + off) < (unsigned)len2;
+      S[i] = ok ? S[i] : -INFINITY;
+    }
+  };
+  auto next_ref = [&](float ref, float tmx) { return tmx > ref + kLazyRescaleLog2 ? fmaxf(ref, tmx) : ref; };
+  auto neg_ref = [](float ref) { return ref == -INFINITY ? 0.f : -ref; };
+  auto exp_elem = [&](float x, float nref) { return __builtin_amdgcn_exp2f(fmaf(x, sl2, nref)); };
+
+  u32x4 kf[KS];
+  auto kread = [&](const uint16_t* src, int s) {
+    kf[s] = *(const u32x4*)(src + n * D + (((2 * s + h) ^ row_swz<D>(n)) << 3));
+  };
+
+  // The current tile's p~ and the next tile's scores, per row block; the
+  // roles alternate from step to step.  A tile's elements 0-7 are
+  // exponentiated in the phase 2 that follows its score products, elements
+  // 8-15 early in the next step's phase 1 (before their packs), which splits
+  // the exponentials evenly between the two phases.
+  constexpr int EH = 8;  // first deferred element
+  f32x16 SA[RB], SB[RB];
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  // Step j (stage st holds tile j).  Top: rescale where a reference moved.
+  // Phase 1: scores of tile j+1 for both row blocks (one MFMA per slot; each
+  // K fragment serves the two MFMAs of its k-step) under the packs and sums
+  // of tile j.  Phase 2: P.V of tile j (each V fragment serves both row
+  // blocks) under tile j+1's mask, row max, reference and exponentials.
+  // Ring use as in fwd_bf16_kernel: step j reads K of tile j+1 and V of tile
+  // j and issues the DMA of tile j+3 into the stage of tile j-1; the barrier
+  // follows the last read of tile j's stage, after each wave's share of tile
+  // j+2 has landed, and the first K reads of tile j+2 follow it.
+  auto step = [&](auto st, int j, int t_end, f32x16 (&P)[RB], f32x16 (&Sn)[RB]) {
+    constexpr int ST = decltype(st)::value;
+    using NX = std::integral_constant<int, (ST + 1) % STAGES>;
+    using N2 = std::integral_constant<int, (ST + 2) % STAGES>;
+    using AH = std::integral_constant<int, (ST + 3) % STAGES>;
+
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int c = 0; c < DC; ++c) keep_in_acc(accO[rb][c]);
+    }
+    if (__builtin_expect(__any(mn[0] != m[0] || mn[1] != m[1]), 0)) {  // rare after the first tile
+      acc_hazard_wait();
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float alpha = (m[rb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[rb] - mn[rb]);
+        m[rb] = mn[rb];
+        l[rb] *= alpha;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) accO[rb][c][i] = acc_write(acc_read(accO[rb][c][i]) * alpha);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // reference of tile j's p~ (the one its elements 0-7 were taken against)
+    float nrefp[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) nrefp[rb] = neg_ref(mn[rb]);
+
+    const uint16_t* nx = stage(NX{});
+    const uint16_t* cur = stage(st);
+    u32x4 PK[RB][2];
+    u32x4 vfr[NG];
+    auto vread = [&](int gidx) {
+      const int c2 = gidx / DC, c = gidx % DC;
+      const int col = 32 * c + tr_col;
+      const int k1 = 16 * c2 + tr_key, k2 = k1 + 8;
+      const int o1 = k1 * D + (((col >> 3) ^ row_swz<D>(k1)) << 3) + (col & 7);
+      const int o2 = k2 * D + (((col >> 3) ^ row_swz<D>(k2)) << 3) + (col & 7);
+      const u32x2 va = read_tr16(cur + TILE + o1), vb = read_tr16(cur + TILE + o2);
+      vfr[gidx] = u32x4{va[0], va[1], vb[0], vb[1]};
+    };
+    auto pack_p = [&](int rb, int jj) {
+      PK[rb][jj >> 3][(jj & 7) >> 1] = pack_bf16(P[rb][jj], P[rb][jj + 1]);
+      l[rb] += P[rb][jj] + P[rb][jj + 1];
+      pin(PK[rb][jj >> 3][(jj & 7) >> 1]);
+      pin(l[rb]);
+    };
+    // tile j's deferred exponentials (elements 8-15) in the first KS/2 k-steps
+    auto exps_deferred = [&](int rb, int s) {
+#pragma unroll
+      for (int e = EH; e < 16; ++e) {
+        if ((e - EH) * (KS / 2) / (16 - EH) == s) {
+          P[rb][e] = exp_elem(P[rb][e], nrefp[rb]);
+          pin(P[rb][e]);
+        }
+      }
+    };
+    auto dma = [&](int s) {  // this k-step's share of tile j+3's DMA
+      if constexpr (LPT >= KS) {
+#pragma unroll
+        for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q) issue_part(stage(AH{}), j + 3, q, t_end);
+      } else {
+        if (s % (KS / LPT) == 0) issue_part(stage(AH{}), j + 3, s / (KS / LPT), t_end);
+      }
+    };
+
+    // phase 1: per k-step, S0 += k.q0 | K reads KA k-steps ahead, DMA, pack
+    // p~ of row block 0 ; S1 += k.q1 | pack p~ of row block 1
+    constexpr int PAIRS_PER_STEP = 8 / KS;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int jj0 = 2 * s * PAIRS_PER_STEP;
+      if (s == 0) mfma_v_first_ba(Sn[0], kf[s], qf[0][s]);
+      else mfma_v_acc_ba(Sn[0], kf[s], qf[0][s]);
+      __builtin_amdgcn_sched_barrier(0);
+      dma(s);
+      if (s < KS / 2) exps_deferred(0, s);
+#pragma unroll
+      for (int u = 0; u < PAIRS_PER_STEP; ++u) pack_p(0, jj0 + 2 * u);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s == 0) mfma_v_first_ba(Sn[1], kf[s], qf[1][s]);
+      else mfma_v_acc_ba(Sn[1], kf[s], qf[1][s]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + KA < KS) kread(nx, s + KA);
+      if (s < KS / 2) exps_deferred(1, s);
+#pragma unroll
+      for (int u = 0; u < PAIRS_PER_STEP; ++u) pack_p(1, jj0 + 2 * u);
+      if (s >= KS - VA) vread(s - (KS - VA));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // phase 2: 2 NG slots, u = 2 gidx + rb.  Group 0 carries no vector work
+    // on Sn (two MFMAs must pass after its last score product); group 1 the
+    // mask of a partial tile; groups 1 .. MAXG the row max of each row block
+    // (slot rb of each group), the reference at the last of them; the later
+    // groups the exponentials of elements 0-7 (row block rb in slot rb).
+    constexpr int MAXG = NG >= 8 ? 2 : 1;          // groups carrying the row max
+    constexpr int MAX_PER = 16 / MAXG;             // elements per max slot
+    constexpr int EXP_SLOTS = NG - 1 - MAXG;       // groups carrying exponentials, per row block
+    static_assert(EXP_SLOTS > 0, "phase-2 split");
+    constexpr int UB = 2 * (NG - VA);              // linear slot of the barrier (after the last V read)
+    float tmax[RB] = {-INFINITY, -INFINITY}, ref[RB] = {mn[0], mn[1]}, nref[RB] = {0.f, 0.f};
+#pragma unroll
+    for (int gidx = 0; gidx < NG; ++gidx) {
+      const int c2 = gidx / DC, c = gidx % DC;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        accO[rb][c] = mfma_bf16(vfr[gidx], PK[rb][c2], accO[rb][c]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int u = 2 * gidx + rb;
+        if (gidx == 1 && rb == 0) {
+          const bool w0 = tile_whole(0, j + 1), w1 = tile_whole(1, j + 1);
+          if (__builtin_expect(!(w0 && w1), 0)) {  // rare: one branch around both masks
+            if (!w0) mask_tile(0, j + 1, Sn[0]);
+            if (!w1) mask_tile(1, j + 1, Sn[1]);
+          }
+        }
+        if (rb == 0 && gidx + VA < NG) vread(gidx + VA);
+        if (u == UB) {
+          // every read of tile j's stage is issued; tile j+2 has landed here
+          wait_lgkmcnt<0>();
+          wait_vmcnt<LPT>();
+          barrier_nofence();
+        }
+        if (gidx >= 1 && gidx <= MAXG) {
+#pragma unroll
+          for (int e = 0; e < MAX_PER; ++e) tmax[rb] = fmaxf(tmax[rb], Sn[rb][(gidx - 1) * MAX_PER + e]);
+          pin(tmax[rb]);
+          if (gidx == MAXG) {
+            ref[rb] = next_ref(mn[rb], pair_max(tmax[rb]) * sl2);
+            nref[rb] = neg_ref(ref[rb]);
+            pin(nref[rb]);
+          }
+        }
+        if (gidx > MAXG) {
+          const int slot = gidx - 1 - MAXG;
+#pragma unroll
+          for (int k = 0; k < EH; ++k) {
+            if (k * EXP_SLOTS / EH == slot) {
+              Sn[rb][k] = exp_elem(Sn[rb][k], nref[rb]);
+              pin(Sn[rb][k]);
+            }
+          }
+        }
+        // first K reads of tile j+2, behind the barrier
+#pragma unroll
+        for (int q = 0; q < KA; ++q)
+          if (u == (UB + 1 + q < 2 * NG ? UB + 1 + q : 2 * NG - 1)) kread(stage(N2{}), q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) mn[rb] = ref[rb];
+  };
+
+  // First tile: DMA of three tiles, the first tile's scores, mask, row max,
+  // reference and exponentials, and the first K reads of the next tile.
+  auto first_tile = [&](int t_end) {
+    issue(ring0, 0, t_end);
+    issue(ring1, 1, t_end);
+    issue(ring2, 2, t_end);
+    wait_vmcnt<LPT>();  // first two tiles
+    barrier_nofence();
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kread(ring0, s);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (s == 0) mfma_v_first_ba(SA[rb], kf[s], qf[rb][s]);
+        else mfma_v_acc_ba(SA[rb], kf[s], qf[rb][s]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    acc_hazard_wait();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (!tile_whole(rb, 0)) mask_tile(rb, 0, SA[rb]);
+      float tm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tm = fmaxf(tm, SA[rb][i]);
+      mn[rb] = next_ref(mn[rb], pair_max(tm) * sl2);
+      const float nr = neg_ref(mn[rb]);
+#pragma unroll
+      for (int i = 0; i < EH; ++i) SA[rb][i] = exp_elem(SA[rb][i], nr);  // 8-15 in the first step
+    }
+#pragma unroll
+    for (int q = 0; q < KA; ++q) kread(ring1, q);
+  };
+
+  if (ntiles > 0) {
+    first_tile(ntiles);
+    for (int j = 0; j < ntiles; j += 4) {
+      step(I0{}, j, ntiles, SA, SB);
+      if (j + 1 >= ntiles) break;
+      step(I1{}, j + 1, ntiles, SB, SA);
+      if (j + 2 >= ntiles) break;
+      step(I2{}, j + 2, ntiles, SA, SB);
+      if (j + 3 >= ntiles) break;
+      step(I3{}, j + 3, ntiles, SB, SA);
+    }
+    // the last step exponentiated scores of no tile: drop that reference
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) mn[rb] = m[rb];
+    wait_vmcnt<0>();
+    wait_lgkmcnt<0>();
+    barrier_nofence();
+  }
+
+  // ---- epilogue: o = acc_o / l, lse = m ln 2 + ln l
+  acc_hazard_wait();
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float lt = pair_sum(l[rb]);
+    if (row_ok[rb]) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      uint16_t* Og = (uint16_t*)p.o + base + (size_t)row[rb] * D;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * c + 8 * g4 + 4 * h;
+          float o4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = acc_read(accO[rb][c][4 * g4 + e]) * inv;
+          *(u32x2*)(Og + d0) = u32x2{pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])};
+        }
+      }
+      // one explicit fma, as in fwd_bf16_kernel
+      if (h == 0 && p.lse != nullptr)
+        p.lse[(size_t)bh * N + row[rb]] = lt > 0.f ? fmaf(m[rb], kLn2, logf(lt)) : -INFINITY;
+    }
+  }
+}
+
 // fp32 kernel: 32 query rows per workgroup, 8 lanes per row, each lane owning
 // D/8 consecutive columns.  Keys are taken one at a time from the same tile
 // schedule as the bf16 kernel, with the exact per-row mask; the online
@@ -864,6 +1285,11 @@ void block_sizes(int dtype, int head_dim, int* block_q, int* block_k) {
 hipError_t launch_fwd(int dtype, int head_dim, int grid, const FwdParams& p, hipStream_t stream) {
   const dim3 block(kBf16Waves * 64);
   const bool table = p.tb_ent != nullptr;
+  if (dtype == kBf16 && p.primal && !table) {  // the primal kernel: 64 rows per wave
+    if (head_dim == 128) hipLaunchKernelGGL((fwd_primal_bf16_kernel<128, kBf16Waves>), dim3(grid), block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_primal_bf16_kernel<64, kBf16Waves>), dim3(grid), block, 0, stream, p);
+    return hipGetLastError();
+  }
   if (dtype == kBf16) {
     if (head_dim == 128) {
       if (table) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, false, true>), dim3(grid), block, 0, stream, p);

@@ -12,6 +12,7 @@ constexpr int kBf16 = 0;
 constexpr int kFp32 = 1;
 constexpr int kBf16Waves = 4;   // waves per bf16 workgroup; 32 query rows per wave
 constexpr int kBf16BlockK = 32;  // keys per bf16 tile
+constexpr int kBf16PrimalRows = kBf16Waves * 64;  // rows per block of the bf16 primal kernel (64 per wave)
 
 // Range-list plans: the bf16 kernel stages a query block's tile entries in
 // LDS next to the 128 KB ring, so a block may stream at most this many tiles.
