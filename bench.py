@@ -26,7 +26,7 @@ lse only; useful FLOPs = 4 d x allowed pairs x B x H, for q.k and p.v).
 the dk/dv kernel, from q, k, v, o, lse and dO on the same plan); useful
 FLOPs = 10 d x (allowed pairs) x B x H (q.k, dO.v, dS k, dS q, P dO).
 
-Prints one JSON line.  --gpus above 1 is refused: this build measures one GPU.
+Prints one JSON line.  --gpus above 1 is refused: the benchmark measures one GPU.
 """
 from __future__ import annotations
 
@@ -268,7 +268,7 @@ def cpu_baseline(w, heads, clean_tangent_zero=False):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "this benchmark measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
     if args.mode == "copy":
         copy_reference(args.steps)
