@@ -191,7 +191,7 @@ def cpu_baseline_bwd(w, heads, ranges=False):
     }
 
 
-def cpu_baseline_primal(w, heads):
+def cpu_baseline_primal(w, heads, ranges=False):
     """The oracle (which forms o together with the tangent) on (b, h) slices;
     only the primal's 4 d flops per pair are counted."""
     import oracle
@@ -201,13 +201,14 @@ def cpu_baseline_primal(w, heads):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = 1
+    mask = oracle.RangeMask(*w.mask_ranges()) if ranges else w.desc
     flops, elapsed = 0, 0.0
     for h in range(heads):
         args = [si.slice_values(w, t, 0, h) for t in si.TENSORS]
         t0 = time.perf_counter()
-        oracle.masked_attention_jvp_slice(*args, w.desc)
+        oracle.masked_attention_jvp_slice(*args, mask)
         elapsed += time.perf_counter() - t0
-        flops += 4 * w.head_dim * oracle.pair_count(w.desc)
+        flops += 4 * w.head_dim * oracle.pair_count(mask)
     return {
         "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"{heads} of {w.batch * w.heads} (b,h) slices of {w.name} (all rows; the oracle forms o with "
@@ -287,8 +288,8 @@ def main():
         print(json.dumps({"error": f"unknown workload {args.config}"}))
         sys.exit(2)
     use_ranges = args.ranges or args.config in si.RANGE_WORKLOADS
-    if args.primal and (args.backward or args.clean_tangent_zero or use_ranges):
-        print(json.dumps({"error": "--primal takes a descriptor workload without other modes"}))
+    if args.primal and (args.backward or args.clean_tangent_zero):
+        print(json.dumps({"error": "--primal is the forward alone: no --backward, no --clean-tangent-zero"}))
         sys.exit(2)
     if use_ranges and args.clean_tangent_zero:
         print(json.dumps({"error": "range-list plans have no clean-tangent-zero option"}))
@@ -325,7 +326,9 @@ def main():
     o = torch.empty_like(x["q"])
     to = torch.empty_like(x["q"])
     lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
-    if use_ranges and not args.backward:
+    if use_ranges and args.primal:
+        call = lambda: aj.attn_jvp_fwd_primal_table(plan, table, x["q"], x["k"], x["v"], o, lse)
+    elif use_ranges and not args.backward:
         call = lambda: aj.attn_jvp_fwd_table(plan, table, *(x[t] for t in si.TENSORS), o, to, lse)
     elif args.primal:
         call = lambda: aj.attn_jvp_fwd_primal(plan, x["q"], x["k"], x["v"], o, lse)
@@ -383,6 +386,7 @@ def main():
     tb = "true" if use_ranges else "false"
     kernel = (f"bwd_dq_bf16_kernel<{w.head_dim},{nw},{tb}> + bwd_dkdv_bf16_kernel<{w.head_dim},{nw},{tb}>"
               if args.backward
+              else f"fwd_bf16_kernel<{w.head_dim},{nw},true,true> (primal tile mode)" if args.primal and use_ranges
               else f"fwd_primal_bf16_kernel<{w.head_dim},{nw}>" if args.primal
               else f"fwd_bf16_kernel<{w.head_dim},{nw},{'true' if flags else 'false'},{'true' if use_ranges else 'false'}>")
 
@@ -432,7 +436,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_sample_heads, use_ranges) if args.backward
-                               else cpu_baseline_primal(w, args.cpu_sample_heads) if args.primal
+                               else cpu_baseline_primal(w, args.cpu_sample_heads, use_ranges) if args.primal
                                else cpu_baseline_ranges(w, args.cpu_sample_heads) if use_ranges
                                else cpu_baseline(w, args.cpu_sample_heads, bool(flags)))
     print(json.dumps(out), flush=True)

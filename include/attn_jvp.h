@@ -158,8 +158,9 @@ int attn_jvp_plan_table(const attn_jvp_plan* plan, void* host_out, size_t bytes)
  * the plan's schedule table in device memory (bytes from attn_jvp_plan_table
  * of this plan; its contents are not checked).  attn_jvp_fwd refuses range-
  * list plans and this call refuses descriptor plans (ATTN_JVP_E_INVALID).
- * Range-list plans have no clean-tangent-zero option and no primal-only
- * forward; their backward is attn_jvp_bwd_table. */
+ * Range-list plans have no clean-tangent-zero option; their forward without
+ * tangents is attn_jvp_fwd_primal_table and their backward
+ * attn_jvp_bwd_table. */
 int attn_jvp_fwd_table(const attn_jvp_plan* plan, const void* device_table, const void* q,
                        const void* k, const void* v, const void* tq, const void* tk, const void* tv,
                        void* o, void* t_o, float* lse, void* hip_stream);
@@ -182,6 +183,14 @@ int attn_jvp_fwd(const attn_jvp_plan* plan, const void* q, const void* k, const 
  * Same checks and error codes as attn_jvp_fwd. */
 int attn_jvp_fwd_primal(const attn_jvp_plan* plan, const void* q, const void* k, const void* v,
                         void* o, float* lse, void* hip_stream);
+
+/* attn_jvp_fwd_primal for range-list plans, with the plan's schedule table
+ * in device memory (as for attn_jvp_fwd_table): o and lse bit-identical to
+ * attn_jvp_fwd_table's, at 4 d useful flops per allowed pair.  Refuses
+ * descriptor plans, and attn_jvp_fwd_primal refuses range-list plans
+ * (ATTN_JVP_E_INVALID).  Same checks and error codes as attn_jvp_fwd_table. */
+int attn_jvp_fwd_primal_table(const attn_jvp_plan* plan, const void* device_table, const void* q,
+                              const void* k, const void* v, void* o, float* lse, void* hip_stream);
 
 /* Backward of the masked attention (without tangents) on the same plan:
  * the gradients of a loss L with respect to q, k and v given dO = dL/do

@@ -36,7 +36,7 @@ __all__ = [
     "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops", "attn_jvp_key_ranges",
     "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order", "attn_jvp_create_ranges", "attn_jvp_plan_table_size",
     "attn_jvp_plan_table", "attn_jvp_fwd_table", "masked_attention_jvp_ranges", "attn_jvp_fwd_primal",
-    "attn_jvp_bwd_table", "masked_attention_bwd_ranges",
+    "attn_jvp_bwd_table", "masked_attention_bwd_ranges", "attn_jvp_fwd_primal_table", "masked_attention_fwd_ranges",
     "masked_attention_fwd",
     "masked_attention_bwd",
 ]
@@ -108,12 +108,13 @@ def _load():
         lib.attn_jvp_fwd_table.argtypes = [vp] * 10 + [vp, vp]
         lib.attn_jvp_fwd_primal.argtypes = [vp] * 7
         lib.attn_jvp_bwd_table.argtypes = [vp] * 13
+        lib.attn_jvp_fwd_primal_table.argtypes = [vp] * 8
         for name in ("attn_jvp_create", "attn_jvp_create_ex", "attn_jvp_fwd", "attn_jvp_destroy",
                      "attn_jvp_plan_info", "attn_jvp_plan_flops", "attn_jvp_launch_order", "attn_jvp_row_ranges",
                      "attn_jvp_tile_map", "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops",
                      "attn_jvp_key_ranges", "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order",
                      "attn_jvp_create_ranges", "attn_jvp_plan_table_size", "attn_jvp_plan_table", "attn_jvp_fwd_table",
-                     "attn_jvp_fwd_primal", "attn_jvp_bwd_table"):
+                     "attn_jvp_fwd_primal", "attn_jvp_bwd_table", "attn_jvp_fwd_primal_table"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -370,6 +371,28 @@ def attn_jvp_fwd_primal(plan: Plan, q, k, v, o, lse=None, stream=None) -> None:
     _check(code, "attn_jvp_fwd_primal")
 
 
+def attn_jvp_fwd_primal_table(plan: Plan, table, q, k, v, o, lse=None, stream=None) -> None:
+    """attn_jvp_fwd_primal for a range-list plan, with its device table."""
+    import torch
+    ins = dict(q=q, k=k, v=v, o=o)
+    for name, t in ins.items():
+        _check_tensor(name, t, plan, plan.shape)
+    dev = q.device
+    _check_table(plan, table, dev)
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != plan.shape[:3] or not lse.is_contiguous() \
+                or lse.device != dev:
+            raise AttnJvpError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        code = _load().attn_jvp_fwd_primal_table(plan.handle, ctypes.c_void_p(table.data_ptr()),
+                                                 *[ctypes.c_void_p(t.data_ptr()) for t in ins.values()],
+                                                 ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
+                                                 ctypes.c_void_p(stream.cuda_stream))
+    _check(code, "attn_jvp_fwd_primal_table")
+
+
 def _bwd_args(plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace):
     import torch
     ts = dict(q=q, k=k, v=v, o=o, d_o=d_o, dq=dq, dk=dk, dv=dv)
@@ -544,3 +567,15 @@ def masked_attention_bwd_ranges(q, k, v, o, lse, d_o, groups, scale=None, return
     ws = torch.empty(attn_jvp_bwd_workspace_size(plan) // 4, dtype=torch.float32, device=q.device)
     attn_jvp_bwd_table(plan, table, q, k, v, o, lse, d_o, dq, dk, dv, ws)
     return (dq, dk, dv, ws) if return_workspace else (dq, dk, dv)
+
+
+def masked_attention_fwd_ranges(q, k, v, groups, scale=None, return_lse=False):
+    """(o[, lse]) of a range-list mask without tangents (groups as in
+    masked_attention_jvp_ranges): the forward that pairs with
+    masked_attention_bwd_ranges."""
+    import torch
+    plan, table = _cached_range_plan(q, groups, scale)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    attn_jvp_fwd_primal_table(plan, table, q, k, v, o, lse)
+    return (o, lse) if return_lse else o

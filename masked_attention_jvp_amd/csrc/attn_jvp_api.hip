@@ -655,8 +655,8 @@ int fwd_common(const attn_jvp_plan* p, const void* table, const void* q, const v
     fp.tb_rows = t + p->rs->off_rows;
     fp.tb_iv = t + p->rs->off_iv;
   }
-  // the bf16 primal kernel takes query blocks of 64 rows per wave
-  if (primal && p->dtype == ATTN_JVP_BF16) fp.n_qblocks = n_query_blocks(p->g, kBf16PrimalRows);
+  // the bf16 primal kernel (descriptor plans) takes query blocks of 64 rows per wave
+  if (primal && p->dtype == ATTN_JVP_BF16 && !table) fp.n_qblocks = n_query_blocks(p->g, kBf16PrimalRows);
   const int grid = p->batch * p->heads * fp.n_qblocks;
   hipError_t e = launch_fwd(p->dtype, p->head_dim, grid, fp, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(ATTN_JVP_E_HIP, "kernel launch: %s", hipGetErrorString(e));
@@ -675,8 +675,17 @@ int attn_jvp_fwd(const attn_jvp_plan* p, const void* q, const void* k, const voi
 int attn_jvp_fwd_primal(const attn_jvp_plan* p, const void* q, const void* k, const void* v, void* o, float* lse,
                         void* hip_stream) {
   if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
-  if (p->rs) return fail(ATTN_JVP_E_INVALID, "attn_jvp_fwd_primal takes descriptor plans");
+  if (p->rs) return fail(ATTN_JVP_E_INVALID, "range-list plans run the primal forward through attn_jvp_fwd_primal_table");
   return fwd_common(p, nullptr, q, k, v, nullptr, nullptr, nullptr, o, nullptr, lse, hip_stream, true);
+}
+
+int attn_jvp_fwd_primal_table(const attn_jvp_plan* p, const void* device_table, const void* q, const void* k,
+                              const void* v, void* o, float* lse, void* hip_stream) {
+  if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
+  if (p->rs == nullptr) return fail(ATTN_JVP_E_INVALID, "descriptor plans have no table: use attn_jvp_fwd_primal");
+  if (device_table == nullptr) return fail(ATTN_JVP_E_NULL, "device_table is NULL");
+  if ((uintptr_t)device_table % 4) return fail(ATTN_JVP_E_ALIGN, "device_table is not 4-byte aligned");
+  return fwd_common(p, device_table, q, k, v, nullptr, nullptr, nullptr, o, nullptr, lse, hip_stream, true);
 }
 
 int attn_jvp_fwd_table(const attn_jvp_plan* p, const void* device_table, const void* q, const void* k,

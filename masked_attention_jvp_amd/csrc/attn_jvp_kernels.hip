@@ -64,7 +64,8 @@ enum : int { kFull = 0, kCleanKeys = 1, kPrimal = 2 };
 template <int D, int NW, bool CTZ, bool TABLE>
 __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-  static_assert(!(CTZ && TABLE), "range-list plans have no clean-tangent-zero mode");
+  // Range-list plans have no clean-tangent-zero option: with a table, the
+  // CTZ instance is the primal-only kernel (o and lse, every tile in kPrimal).
   constexpr int BC = kBf16BlockK;            // keys per tile (= one MFMA subtile)
   static_assert(BC == 32, "one 32-key subtile per tile");
   constexpr int STAGES = 4;                  // LDS ring depth; tiles j..j+3 resident or in flight
@@ -129,7 +130,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   };
   // clean-side blocks of a clean-tangent-zero plan, and every block of a
   // primal call (o and lse only)
-  const bool primal_only = CTZ && (p.primal != 0 || !is_noisy(g, r0));
+  const bool primal_only = (CTZ && TABLE) || (CTZ && (p.primal != 0 || !is_noisy(g, r0)));
   // Clean-tangent-zero, noisy block: the leading tiles whose keys all lie on
   // the clean side (below N_h) need no key tangents.  A tile that reaches N_h
   // (for short sides the two key intervals can even share one) runs in the
@@ -674,7 +675,9 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     barrier_nofence();
   };
 
-  if constexpr (CTZ) {
+  if constexpr (CTZ && TABLE) {
+    run(MPrimal{}, 0, ntiles);
+  } else if constexpr (CTZ) {
     if (primal_only) {
       run(MPrimal{}, 0, ntiles);
     } else {
@@ -1288,6 +1291,11 @@ hipError_t launch_fwd(int dtype, int head_dim, int grid, const FwdParams& p, hip
   if (dtype == kBf16 && p.primal && !table) {  // the primal kernel: 64 rows per wave
     if (head_dim == 128) hipLaunchKernelGGL((fwd_primal_bf16_kernel<128, kBf16Waves>), dim3(grid), block, 0, stream, p);
     else hipLaunchKernelGGL((fwd_primal_bf16_kernel<64, kBf16Waves>), dim3(grid), block, 0, stream, p);
+    return hipGetLastError();
+  }
+  if (dtype == kBf16 && table && p.primal) {  // range-list plans without tangents
+    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, true, true>), dim3(grid), block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, true, true>), dim3(grid), block, 0, stream, p);
     return hipGetLastError();
   }
   if (dtype == kBf16) {

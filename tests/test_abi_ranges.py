@@ -169,6 +169,22 @@ def test_range_plan_entry_points_refuse_the_wrong_plan_kind():
     bwd = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(10)]
     assert lib.attn_jvp_bwd(pr.handle, *bwd, None) == 1
     assert aj.attn_jvp_plan_table_size(pd) == 0
+    # the forward without tangents: q k v o (+ lse), table first for range plans
+    prim = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(4)]
+    table = ctypes.c_void_p(0x2000000)
+    assert lib.attn_jvp_fwd_primal(pr.handle, *prim, None, None) == 1
+    assert "attn_jvp_fwd_primal_table" in aj.attn_jvp_last_error_detail()
+    assert lib.attn_jvp_fwd_primal_table(pd.handle, table, *prim, None, None) == 1
+    assert lib.attn_jvp_fwd_primal_table(None, table, *prim, None, None) == 2
+    assert lib.attn_jvp_fwd_primal_table(pr.handle, None, *prim, None, None) == 2
+    assert lib.attn_jvp_fwd_primal_table(pr.handle, ctypes.c_void_p(0x2000002), *prim, None, None) == 3
+    for i in range(4):
+        bad = list(prim)
+        bad[i] = ctypes.c_void_p(0)
+        assert lib.attn_jvp_fwd_primal_table(pr.handle, table, *bad, None, None) == 2
+    bad = list(prim)
+    bad[3] = bad[0]  # o aliases q
+    assert lib.attn_jvp_fwd_primal_table(pr.handle, table, *bad, None, None) == 1
 
 
 def _sections(p):

@@ -86,3 +86,51 @@ def test_primal_error_paths():
     with pytest.raises(aj.AttnJvpError) as e:
         aj.attn_jvp_fwd_primal(plan, x["q"], x["k"], x["v"], mis)
     assert e.value.code == 3
+
+
+RANGE_MASKS = {
+    "tf_c1_4_t50": si.chunked_mask_ranges(50, (1, 4, 4), 1),
+    "und_gen": si.und_gen_ranges(20, 5, 30),
+    "gaps": (40, ((0, 6, ((0, 3), (10, 14))), (9, 15, ((0, 40),)), (15, 33, ((5, 6), (20, 33))),
+                  (35, 40, ((1, 2),)))),
+    "multi": (170, ((0, 60, ((0, 3), (37, 39), (72, 100), (133, 140))), (60, 170, ((0, 170),)))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RANGE_MASKS))
+@pytest.mark.parametrize("d, dtype", [(128, "bf16"), (64, "bf16"), (64, "fp32")])
+def test_range_primal_is_bit_identical_to_the_range_jvp_forward(name, d, dtype):
+    n, groups = RANGE_MASKS[name]
+    w = small_workload(430, n, 1, 1, 0, heads=2, d=d, dtype=dtype)
+    x = device_inputs(w)
+    o_ref, _, lse_ref = aj.masked_attention_jvp_ranges(*(x[t] for t in TENSORS), groups, return_lse=True)
+    o, lse = aj.masked_attention_fwd_ranges(x["q"], x["k"], x["v"], groups, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o), _bits(o_ref)) and torch.equal(_bits(lse), _bits(lse_ref))
+
+
+def test_range_primal_c1_4_workload():
+    w = si.RANGE_WORKLOADS[6]
+    n, groups = w.mask_ranges()
+    log(f"[range primal] {w.name}")
+    x = device_inputs(w)
+    o_ref, _, lse_ref = aj.masked_attention_jvp_ranges(*(x[t] for t in TENSORS), groups, return_lse=True)
+    o, lse = aj.masked_attention_fwd_ranges(x["q"], x["k"], x["v"], groups, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o), _bits(o_ref)) and torch.equal(_bits(lse), _bits(lse_ref))
+
+
+def test_range_primal_error_paths():
+    n, groups = RANGE_MASKS["gaps"]
+    w = small_workload(440, n, 1, 1, 0)
+    x = device_inputs(w)
+    plan = aj.attn_jvp_create_ranges(n, groups, w.batch, w.heads, w.head_dim)
+    table = torch.from_numpy(aj.attn_jvp_plan_table(plan)).cuda()
+    o = torch.empty_like(x["q"])
+    with pytest.raises(aj.AttnJvpError):  # the descriptor entry point on a range plan
+        aj.attn_jvp_fwd_primal(plan, x["q"], x["k"], x["v"], o)
+    with pytest.raises(aj.AttnJvpError) as e:  # o aliasing v
+        aj.attn_jvp_fwd_primal_table(plan, table, x["q"], x["k"], x["v"], x["v"])
+    assert e.value.code == 1
+    with pytest.raises(aj.AttnJvpError):  # table too short
+        aj.attn_jvp_fwd_primal_table(plan, table[:4], x["q"], x["k"], x["v"], o)
