@@ -213,3 +213,27 @@ def test_range_bwd_gpu_error_paths():
     assert e.value.code == 1
     with pytest.raises(aj.AttnJvpError):  # table too short
         aj.attn_jvp_bwd_table(plan, table[:4], x["q"], x["k"], x["v"], o, lse, x["do"], dq, dk, dv, ws)
+
+
+@pytest.mark.parametrize("name, dtype, d", [("gaps", "bf16", 128), ("tf_c1_4_t50", "bf16", 64), ("stripes", "fp32", 64)])
+def test_range_batch_and_heads_are_independent(name, dtype, d):
+    # B = 2, H = 3: the table kernels map workgroups to (b, h) slices through
+    # the XCD-grouped order over the whole grid; every slice against the oracle
+    n, groups = MASKS[name]
+    w = small_workload(560, n, 1, 1, 0, heads=3, batch=2, d=d, dtype=dtype)
+    log(f"[range batch x heads] {name} N={n} d={d} {dtype}")
+    x = _inputs(w)
+    o, to, lse = (to_f64(t) for t in aj.masked_attention_jvp_ranges(*(x[t] for t in TENSORS), groups,
+                                                                       return_lse=True))
+    po = to_f64(aj.masked_attention_fwd_ranges(x["q"], x["k"], x["v"], groups))
+    dq, dk, dv, _, _ = (to_f64(t) for t in _run_ranges(x, groups))
+    rm = RangeMask(n, groups)
+    tol = TOL[dtype]
+    for b in range(w.batch):
+        for h in range(w.heads):
+            sl = host_values(w, b, h)
+            ro, rto, _ = oracle.masked_attention_jvp_slice(*sl, rm)
+            rq, rk, rv, _ = oracle.masked_attention_bwd_slice(*sl[:3], si.slice_values(w, "do", b, h), rm)
+            assert np.array_equal(po[b, h], o[b, h])  # the primal forward gives the same o
+            for got, ref in ((o, ro), (to, rto), (dq, rq), (dk, rk), (dv, rv)):
+                assert rel_err(got[b, h], ref) < tol, (b, h)
