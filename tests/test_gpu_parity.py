@@ -170,6 +170,38 @@ def test_value_direction_gives_output_exactly(cfg):
     assert torch.equal(o.view(torch.int16), to.view(torch.int16))
 
 
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_tangent_linearity_is_exact(cfg):
+    # every step of the tangent is linear in (tq, tk, tv), and scaling by 2
+    # commutes with each rounding (fp32 sums, the bf16 packs of p~ ts and the
+    # bf16 outputs), so doubling the tangents doubles t_o bit for bit and
+    # leaves o unchanged -- at the full workload sizes, without the oracle
+    w = WORKLOADS[cfg]
+    log(f"[linearity] {w.name}")
+    x = device_inputs(w)
+    o1, to1 = aj.masked_attention_jvp(*(x[t] for t in TENSORS), w.desc)
+    t2 = [x[t] * 2 for t in ("tq", "tk", "tv")]
+    o2, to2 = aj.masked_attention_jvp(x["q"], x["k"], x["v"], *t2, w.desc)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal((to1 * 2).view(torch.int16), to2.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_query_and_key_tangents_are_symmetric(cfg):
+    # the directions (q, 0, 0) and (0, k, 0) give the same score tangent
+    # sigma q.k for every pair, accumulated in the same order (the other
+    # product adds exact zeros), hence the same t_o bit for bit
+    w = WORKLOADS[cfg]
+    x = device_inputs(w)
+    z = torch.zeros_like(x["q"])
+    _, ta = aj.masked_attention_jvp(x["q"], x["k"], x["v"], x["q"], z, z, w.desc)
+    _, tb = aj.masked_attention_jvp(x["q"], x["k"], x["v"], z, x["k"], z, w.desc)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ta).item() > 0
+    assert torch.equal(ta.view(torch.int16), tb.view(torch.int16))
+
+
 def test_zero_tangent_gives_zero():
     w = small_workload(150, 50, 5, 1, 1)
     x = device_inputs(w)
