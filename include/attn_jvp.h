@@ -322,10 +322,11 @@ int attn_jvp_key_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
  * work, clean and noisy blocks of the same chunks come in groups of 8 and 8,
  * so that the round-robin hand-out of workgroups to the 8 XCDs gives each XCD
  * both sides.  Range-list plans: host_out holds the heavy-first order of
- * the query blocks (more streamed tiles first); over the whole B H grid,
- * workgroups take that order in XCD groups of 16 consecutive tasks, as in
- * attn_jvp_bwd_launch_order.  n is the capacity of host_out in int32
- * elements. */
+ * the query blocks (more streamed tiles first).  For range-list plans and
+ * for descriptor plans without flags, "workgroup t" is the logical task t:
+ * over the whole B H grid, workgroups take the tasks in XCD groups of 128
+ * consecutive tasks, as in attn_jvp_bwd_launch_order (there with groups of
+ * 16).  n is the capacity of host_out in int32 elements. */
 int attn_jvp_launch_order(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
 /* Tile map, row-major [n_query_blocks][n_key_tiles], query blocks in index

@@ -199,11 +199,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
 
   const MaskGeom g = p.g;
   const int N = g.seq_len;
-  // Range-list plans take the table's heavy-first order in XCD groups of 16,
-  // as the forward does.
-  int task = 0;
-  if constexpr (TABLE) task = xcd_grouped((int)blockIdx.x, (int)gridDim.x, 16);
-  const int bh = TABLE ? task / p.n_qblocks : (int)(blockIdx.x / p.n_qblocks);
+  // Workgroups take the heavy-first order (range-list plans: the table's) in
+  // XCD groups of kFwdXcdGroup, as the forward does.
+  const int task = xcd_grouped((int)blockIdx.x, (int)gridDim.x, kFwdXcdGroup);
+  const int bh = task / p.n_qblocks;
   int r0, r1, ntiles, e0 = 0;
   TileSpans sp{0, 0, 0, 0};
   if constexpr (TABLE) {
@@ -213,7 +212,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
     e0 = p.tb_blk[qb];
     ntiles = p.tb_blk[qb + 1] - e0;
   } else {
-    const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks);
+    const int qb = heavy_first_qblock(g, BR, task - bh * p.n_qblocks);
     qblock_rows(g, BR, qb, &r0, &r1);
     sp = block_tiles(block_ranges(g, r0, r1), BC);
     ntiles = span_count(sp);

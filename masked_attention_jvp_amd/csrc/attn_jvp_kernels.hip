@@ -93,12 +93,13 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 
   const MaskGeom g = p.g;
   const int N = g.seq_len;
-  // Range-list plans: workgroups take the (heavy-first) table order in XCD
-  // groups of 16 (xcd_grouped): neighbouring blocks of that order, which
-  // stream nearly the same key tiles, share an XCD's L2.
+  // Workgroups take the heavy-first order in XCD groups of kFwdXcdGroup
+  // (xcd_grouped): neighbouring blocks of that order, which stream nearly the
+  // same key tiles, share an XCD's L2.  Clean-tangent-zero plans keep their
+  // balanced order (clean and noisy blocks in turn on every XCD).
   int task = 0;
-  if constexpr (TABLE) task = xcd_grouped((int)blockIdx.x, (int)gridDim.x, 16);
-  const int bh = TABLE ? task / p.n_qblocks : (int)(blockIdx.x / p.n_qblocks);
+  if constexpr (TABLE || !CTZ) task = xcd_grouped((int)blockIdx.x, (int)gridDim.x, kFwdXcdGroup);
+  const int bh = (TABLE || !CTZ) ? task / p.n_qblocks : (int)(blockIdx.x / p.n_qblocks);
   int qb, r0, r1, ntiles, e0 = 0;
   TileSpans sp{0, 0, 0, 0};
   if constexpr (TABLE) {
@@ -109,7 +110,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     e0 = p.tb_blk[qb];
     ntiles = p.tb_blk[qb + 1] - e0;
   } else {
-    qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks, CTZ);
+    if constexpr (CTZ) qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks, true);
+    else qb = heavy_first_qblock(g, BR, task - bh * p.n_qblocks, false);
     qblock_rows(g, BR, qb, &r0, &r1);
     sp = block_tiles(block_ranges(g, r0, r1), BC);
     ntiles = span_count(sp);
@@ -769,8 +771,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_primal_bf16_kernel(FwdParams p
 
   const MaskGeom g = p.g;
   const int N = g.seq_len;
-  const int bh = (int)(blockIdx.x / p.n_qblocks);
-  const int qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks);
+  // heavy-first order in XCD groups of kPrimalXcdGroup (xcd_grouped)
+  const int task = xcd_grouped((int)blockIdx.x, (int)gridDim.x, kPrimalXcdGroup);
+  const int bh = task / p.n_qblocks;
+  const int qb = heavy_first_qblock(g, BR, task - bh * p.n_qblocks);
   int r0, r1;
   qblock_rows(g, BR, qb, &r0, &r1);
   const TileSpans sp = block_tiles(block_ranges(g, r0, r1), BC);

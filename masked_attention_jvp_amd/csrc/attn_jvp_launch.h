@@ -86,6 +86,10 @@ void bwd_block_sizes(int dtype, int head_dim, int* block_q, int* block_kv);
 
 // Key blocks per XCD group of the dk/dv kernel's launch order (xcd_grouped).
 constexpr int kDkdvXcdGroup = 16;
+// Query blocks per XCD group of the forward + JVP's launch order (general
+// descriptor plans and range-list plans) and of the bf16 primal kernel's.
+constexpr int kFwdXcdGroup = 128;
+constexpr int kPrimalXcdGroup = 64;
 
 // Launch the backward (dq kernel, then dk/dv kernel) for bh = B * H slices.
 hipError_t launch_bwd(int dtype, int head_dim, int bh, const BwdParams& p, hipStream_t stream);
