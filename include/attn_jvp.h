@@ -254,10 +254,13 @@ int attn_jvp_plan_bwd_info(const attn_jvp_plan* plan, int32_t* block_q, int32_t*
  * block task mod n_key_blocks.  Tasks are heavy first (the earliest keys of a
  * side are seen by the most rows; range-list plans: the key blocks that
  * stream more query tiles first, in the table's order); workgroups are
- * handed to the 8 XCDs round robin, and each round of 128 workgroups gives
- * each XCD a group of 16 consecutive tasks, which stream nearly the same
- * query tiles through that XCD's L2, the group-to-XCD direction alternating
- * from round to round.  n is the capacity of host_out in int32 elements. */
+ * handed to the 8 XCDs round robin.  Grids of at least 2048 workgroups and
+ * 2 rounds of 128: each round gives each XCD a group of 16 consecutive tasks,
+ * which stream nearly the same query tiles through that XCD's L2, the
+ * group-to-XCD direction alternating from round to round; only an even
+ * number of rounds is grouped, the rest keeps its index.  Smaller grids:
+ * workgroup b takes rank b / (B H) of slice b mod (B H), heavy first across
+ * all slices.  n is the capacity of host_out in int32 elements. */
 int attn_jvp_bwd_launch_order(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
 /* Useful floating-point operations of one attn_jvp_bwd call (all B * H
@@ -325,8 +328,9 @@ int attn_jvp_key_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
  * the query blocks (more streamed tiles first).  For range-list plans and
  * for descriptor plans without flags, "workgroup t" is the logical task t:
  * over the whole B H grid, workgroups take the tasks in XCD groups of 128
- * consecutive tasks, as in attn_jvp_bwd_launch_order (there with groups of
- * 16).  n is the capacity of host_out in int32 elements. */
+ * consecutive tasks under the rule of attn_jvp_bwd_launch_order (there with
+ * groups of 16); clean-tangent-zero plans keep the index order.  n is the
+ * capacity of host_out in int32 elements. */
 int attn_jvp_launch_order(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
 /* Tile map, row-major [n_query_blocks][n_key_tiles], query blocks in index

@@ -899,7 +899,7 @@ int attn_jvp_bwd_launch_order(const attn_jvp_plan* p, int32_t* out, size_t n) {
   if (n < (size_t)total) return fail(ATTN_JVP_E_INVALID, "host_out holds %zu int32, need %lld", n, (long long)total);
   const int32_t nkb = p->bwd_n_kblocks;
   for (int32_t b = 0; b < (int32_t)total; ++b) {
-    const int32_t task = xcd_grouped(b, (int32_t)total, kDkdvXcdGroup);
+    const int32_t task = launch_task(b, (int32_t)total, nkb, kDkdvXcdGroup);
     if (p->rs) {  // range-list plans: the table's heavy-first key-block order within each (b, h)
       const int32_t bh = task / nkb;
       out[b] = bh * nkb + p->rs->table[p->rs->off_corder + (task - bh * nkb)];

@@ -201,7 +201,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   const int N = g.seq_len;
   // Workgroups take the heavy-first order (range-list plans: the table's) in
   // XCD groups of kFwdXcdGroup, as the forward does.
-  const int task = xcd_grouped((int)blockIdx.x, (int)gridDim.x, kFwdXcdGroup);
+  const int task = launch_task((int)blockIdx.x, (int)gridDim.x, p.n_qblocks, kFwdXcdGroup);
   const int bh = task / p.n_qblocks;
   int r0, r1, ntiles, e0 = 0;
   TileSpans sp{0, 0, 0, 0};
@@ -541,7 +541,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
   // first (the earliest keys of a side are seen by the most rows).  Groups of
   // 16 neighbouring key blocks, which stream nearly the same query tiles, run
   // on one XCD (a quarter of the fetches past L2 of plain round robin).
-  const int task = xcd_grouped((int)blockIdx.x, (int)gridDim.x, kDkdvXcdGroup);
+  const int task = launch_task((int)blockIdx.x, (int)gridDim.x, p.n_kblocks, kDkdvXcdGroup);
   const int bh = task / p.n_kblocks;
   int k0, k1, ntiles, e0 = 0;
   TileSpans sp{0, 0, 0, 0};

@@ -94,12 +94,13 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   const MaskGeom g = p.g;
   const int N = g.seq_len;
   // Workgroups take the heavy-first order in XCD groups of kFwdXcdGroup
-  // (xcd_grouped): neighbouring blocks of that order, which stream nearly the
+  // (launch_task): neighbouring blocks of that order, which stream nearly the
   // same key tiles, share an XCD's L2.  Clean-tangent-zero plans keep their
-  // balanced order (clean and noisy blocks in turn on every XCD).
-  int task = 0;
-  if constexpr (TABLE || !CTZ) task = xcd_grouped((int)blockIdx.x, (int)gridDim.x, kFwdXcdGroup);
-  const int bh = (TABLE || !CTZ) ? task / p.n_qblocks : (int)(blockIdx.x / p.n_qblocks);
+  // balanced order (clean and noisy blocks in turn on every XCD) in index
+  // order: at 3 heads it was 3 % faster than heavy first across heads.
+  const int task = (TABLE || !CTZ) ? launch_task((int)blockIdx.x, (int)gridDim.x, p.n_qblocks, kFwdXcdGroup)
+                                   : (int)blockIdx.x;
+  const int bh = task / p.n_qblocks;
   int qb, r0, r1, ntiles, e0 = 0;
   TileSpans sp{0, 0, 0, 0};
   if constexpr (TABLE) {
@@ -110,7 +111,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     e0 = p.tb_blk[qb];
     ntiles = p.tb_blk[qb + 1] - e0;
   } else {
-    if constexpr (CTZ) qb = heavy_first_qblock(g, BR, blockIdx.x - bh * p.n_qblocks, true);
+    if constexpr (CTZ) qb = heavy_first_qblock(g, BR, task - bh * p.n_qblocks, true);
     else qb = heavy_first_qblock(g, BR, task - bh * p.n_qblocks, false);
     qblock_rows(g, BR, qb, &r0, &r1);
     sp = block_tiles(block_ranges(g, r0, r1), BC);
@@ -771,8 +772,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_primal_bf16_kernel(FwdParams p
 
   const MaskGeom g = p.g;
   const int N = g.seq_len;
-  // heavy-first order in XCD groups of kPrimalXcdGroup (xcd_grouped)
-  const int task = xcd_grouped((int)blockIdx.x, (int)gridDim.x, kPrimalXcdGroup);
+  // heavy-first order in XCD groups of kPrimalXcdGroup (launch_task)
+  const int task = launch_task((int)blockIdx.x, (int)gridDim.x, p.n_qblocks, kPrimalXcdGroup);
   const int bh = task / p.n_qblocks;
   const int qb = heavy_first_qblock(g, BR, task - bh * p.n_qblocks);
   int r0, r1;

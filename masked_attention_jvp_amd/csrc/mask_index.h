@@ -127,22 +127,39 @@ AJ_HD int32_t heavy_first_qblock(const MaskGeom& g, int32_t block_q, int32_t t, 
   return (u & 1) * nbs + (rem - 1 - (u >> 1));
 }
 
-// XCD-aware launch order: workgroup b of a grid of `total` runs logical task
-// xcd_grouped(b).  Workgroups are handed to the 8 XCDs round robin (b mod 8),
-// and each XCD has its own L2.  Within every round of 8 G workgroups the
-// XCDs take groups of G consecutive logical tasks, so tasks that stream the
-// same tiles (neighbouring blocks of one chunk) share an L2.  The rounds keep
-// the logical (heavy-first) order, and the group-to-XCD direction alternates
-// from round to round (XCD x takes group x, then group 7 - x), so that work
-// that falls along the logical order is spread evenly over the XCDs.  The
-// last total mod 8 G workgroups keep their index.
-AJ_HD int32_t xcd_grouped(int32_t b, int32_t total, int32_t G) {
+// XCD-aware launch order.  Workgroup b of a grid of total = n_slices *
+// per_slice workgroups runs logical task launch_task(b, ...): (b, h) slice
+// task / per_slice, heavy-first rank task mod per_slice.  Workgroups are
+// handed to the 8 XCDs round robin (b mod 8): each XCD gets a fixed eighth of
+// the grid, runs it in order of arrival on its 32 CUs, and has its own L2.
+// * Large grids (at least kMinGroupedTasks workgroups and kMinGroupedRounds
+//   rounds of 8 G): every round gives each XCD a group of G consecutive
+//   logical tasks, so that tasks streaming the same tiles (neighbouring
+//   blocks of one chunk) share an L2.  The direction alternates from round to
+//   round (XCD x takes group x, then group 7 - x), so the falling heavy-first
+//   weights even out over each pair of rounds; only an even number of rounds
+//   is grouped and the rest keeps its index.
+// * Smaller grids: heavy first across all slices (the heaviest block of every
+//   slice, then the next, ...).  A lone unpaired round would load some XCDs
+//   far more than others (in a single round of 8 groups of 128, the first
+//   group carries about 7 times the work of the fourth), and with few tasks
+//   per CU a slice-by-slice order would leave the last slice's heavy blocks
+//   to the end.
+constexpr int32_t kMinGroupedRounds = 2;
+constexpr int32_t kMinGroupedTasks = 2048;  // 8 per CU
+AJ_HD int32_t launch_task(int32_t b, int32_t total, int32_t per_slice, int32_t G) {
   const int32_t round = 8 * G;
-  const int32_t r = b / round;
-  if ((r + 1) * round > total) return b;
-  const int32_t u = b - r * round;
-  const int32_t x = (r & 1) ? 7 - (u & 7) : (u & 7);  // snake: the direction alternates by round
-  return r * round + x * G + (u >> 3);
+  const int32_t rounds = total / round;
+  if (total >= kMinGroupedTasks && rounds >= kMinGroupedRounds) {
+    const int32_t r = b / round;
+    if (r >= (rounds & ~1)) return b;
+    const int32_t u = b - r * round;
+    const int32_t x = (r & 1) ? 7 - (u & 7) : (u & 7);
+    return r * round + x * G + (u >> 3);
+  }
+  const int32_t n_slices = total / per_slice;
+  const int32_t k = b / n_slices;
+  return (b - k * n_slices) * per_slice + k;
 }
 
 // Union of the key sets of rows [r0, r1) (one side, consecutive chunks).

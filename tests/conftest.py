@@ -28,3 +28,32 @@ def read_golden(name):
             else:
                 rows.append([int(ch) for ch in line])
     return meta, rows
+
+
+def check_launch_rule(tasks, total, per_slice, G):
+    """Workgroup b of a grid of `total` runs logical task tasks[b] (slice
+    task // per_slice, heavy-first rank task % per_slice); workgroups go to the
+    8 XCDs round robin.  Grids of >= 2048 workgroups and >= 2 rounds of 8 G:
+    an even number of rounds in which XCD x holds G consecutive tasks (group x,
+    then group 7 - x in the next round), the rest in index order.  Smaller
+    grids: heavy first across slices (rank b // slices of slice b % slices)."""
+    import numpy as np
+    tasks = np.asarray(tasks)
+    assert sorted(tasks.tolist()) == list(range(total))
+    rounds = total // (8 * G)
+    b = np.arange(total)
+    if total >= 2048 and rounds >= 2:
+        even = rounds - rounds % 2
+        for r in range(even):
+            seg = tasks[8 * G * r: 8 * G * (r + 1)]
+            for x in range(8):
+                t = np.sort(seg[x::8])
+                assert np.array_equal(t, np.arange(t[0], t[0] + G))
+            first = [int(seg[x::8].min()) for x in range(8)]
+            expect = [8 * G * r + G * (x if r % 2 == 0 else 7 - x) for x in range(8)]
+            assert first == expect
+        assert np.array_equal(tasks[8 * G * even:], b[8 * G * even:])
+        return "grouped"
+    n = total // per_slice
+    assert np.array_equal(tasks, (b % n) * per_slice + b // n)
+    return "interleaved"

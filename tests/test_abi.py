@@ -18,6 +18,8 @@ import re
 import numpy as np
 import pytest
 
+from conftest import check_launch_rule
+
 import oracle
 from oracle import MaskDesc
 import masked_attention_jvp_amd as aj
@@ -264,27 +266,19 @@ def test_bwd_argument_errors_before_any_device_call():
         assert "overlaps" in aj.attn_jvp_last_error_detail()
 
 
-@pytest.mark.parametrize("desc, b, h", [((1560, 21, 1, 1), 1, 12), ((1560, 21, 3, 1), 2, 12), ((50, 5, 1, 1), 1, 3),
-                                        ((1560, 21, 1, 0), 1, 12), ((1560, 21, 1, 1), 1, 40)])
-def test_bwd_launch_order_is_an_xcd_grouped_permutation(desc, b, h):
+@pytest.mark.parametrize("desc, b, h, regime", [
+    ((1560, 21, 1, 1), 1, 12, "grouped"), ((1560, 21, 3, 1), 2, 12, "grouped"), ((1560, 21, 1, 0), 1, 12, "grouped"),
+    ((1560, 21, 1, 1), 1, 40, "grouped"),
+    ((100, 40, 1, 1), 1, 35, "grouped"),       # 17 full rounds: 16 grouped, the rest in index order
+    ((50, 5, 1, 1), 1, 3, "interleaved"),      # 12 workgroups
+    ((1560, 21, 1, 1), 1, 3, "interleaved")])  # 1536 workgroups, under 8 per CU
+def test_bwd_launch_order_follows_the_xcd_rule(desc, b, h, regime):
     p = aj.attn_jvp_create(desc, b, h, 128, aj.ATTN_JVP_BF16)
     info = aj.attn_jvp_plan_bwd_info(p)
     nk = info["n_key_blocks"]
     assert nk == p.info["n_query_blocks"]  # key blocks are cut like query blocks
     order = aj.attn_jvp_bwd_launch_order(p)
-    total = b * h * nk
-    assert sorted(order.tolist()) == list(range(total))
-    # each full round of 128 workgroups: XCD x (workgroups x, x + 8, ...) holds 16 consecutive tasks
-    for r in range(total // 128):
-        seg = order[128 * r: 128 * (r + 1)]
-        groups = sorted(int(seg[x::8].min()) for x in range(8))
-        for x in range(8):
-            t = np.sort(seg[x::8])
-            assert np.array_equal(t, np.arange(t[0], t[0] + 16))
-        assert groups == [128 * r + 16 * g for g in range(8)]
-        # the direction alternates: XCD 0 takes the first group in even rounds, the last in odd ones
-        assert int(seg[0::8].min()) == 128 * r + (0 if r % 2 == 0 else 112)
-    assert np.array_equal(order[128 * (total // 128):], np.arange(128 * (total // 128), total))
+    assert check_launch_rule(order, b * h * nk, nk, 16) == regime
 
 
 def test_primal_argument_errors_before_any_device_call():

@@ -22,6 +22,7 @@ import pytest
 
 import oracle
 import seeded_inputs as si
+from conftest import check_launch_rule
 from oracle import RangeMask
 import masked_attention_jvp_amd as aj
 
@@ -266,8 +267,9 @@ def test_range_bwd_flops_and_workspace():
     assert aj.attn_jvp_bwd_workspace_size(p) == 8 * 6 * p.seq_len
 
 
-@pytest.mark.parametrize("name, b, h", [("tf_c1_4_t50", 3, 40), ("und_gen", 2, 7)])
-def test_range_bwd_launch_order_is_the_table_order_xcd_grouped(name, b, h):
+@pytest.mark.parametrize("name, b, h, regime", [("tf_c1_4_t50", 3, 40, "interleaved"), ("und_gen", 2, 7, "interleaved"),
+                                                ("tf_c1_4_t50", 4, 66, "grouped")])
+def test_range_bwd_launch_order_is_the_table_order_under_the_xcd_rule(name, b, h, regime):
     p, _ = _plan(name, b=b, h=h)
     _, corder, _, _, _ = _sections(p)
     nk = len(corder)
@@ -278,13 +280,7 @@ def test_range_bwd_launch_order_is_the_table_order_xcd_grouped(name, b, h):
     rank = np.empty(nk, np.int64)
     rank[corder] = np.arange(nk)
     tasks = (order // nk) * nk + rank[order % nk]
-    for r in range(total // 128):  # XCD groups of 16 consecutive tasks, direction alternating by round
-        seg = tasks[128 * r: 128 * (r + 1)]
-        for x in range(8):
-            t = np.sort(seg[x::8])
-            assert np.array_equal(t, np.arange(t[0], t[0] + 16))
-        assert int(seg[0::8].min()) == 128 * r + (0 if r % 2 == 0 else 112)
-    assert np.array_equal(tasks[128 * (total // 128):], np.arange(128 * (total // 128), total))
+    assert check_launch_rule(tasks, total, nk, 16) == regime
 
 
 def test_bwd_table_argument_errors_before_any_device_call():
