@@ -78,6 +78,9 @@ def parse():
                     help="time the forward without tangents (o and lse) instead of the forward + JVP")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (dq, dk, dv) on the same plan instead of the forward + JVP")
+    ap.add_argument("--no-smi", action="store_true",
+                    help="skip the amd-smi power / clock samples (for runs under a profiler, whose "
+                         "preloaded library should not follow bench.py into the amd-smi child process)")
     ap.add_argument("--mode", choices=["attn", "copy"], default="attn",
                     help="copy: a plain 1 GiB device copy, the reference for HBM byte counters")
     return ap.parse_args()
@@ -100,8 +103,14 @@ def copy_reference(steps):
                       "ms_per_copy": round(dt * 1e3, 4), "GB_per_s": round(4 * n / dt / 1e9, 1)}), flush=True)
 
 
+SMI_ENABLED = True
+
+
 def smi_sample():
-    """(socket power W, GFX clock MHz) from amd-smi, or None where unavailable."""
+    """(socket power W, GFX clock MHz) from amd-smi, or None where unavailable
+    or switched off."""
+    if not SMI_ENABLED:
+        return None
     try:
         out = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True, timeout=10).stdout
     except (OSError, subprocess.SubprocessError):
@@ -267,7 +276,9 @@ def cpu_baseline(w, heads, clean_tangent_zero=False):
 
 
 def main():
+    global SMI_ENABLED
     args = parse()
+    SMI_ENABLED = not args.no_smi
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU only; run with --gpus 1"}))
         sys.exit(2)

@@ -67,3 +67,14 @@ def test_traffic_is_reported_only_for_the_recorded_kernel_code(tmp_path, monkeyp
     rec["kernel_code_sha256_16"] = "0" * 16
     (tmp_path / f"traffic_{name}.json").write_text(json.dumps(rec))
     assert bench.traffic_for(name, "fwd") is None          # stale record
+
+
+def test_no_smi_switches_the_power_samples_off(monkeypatch):
+    calls = []
+    monkeypatch.setattr(bench.subprocess, "run", lambda *a, **k: calls.append(a) or None)
+    monkeypatch.setattr(bench, "SMI_ENABLED", False)
+    assert bench.smi_sample() is None and calls == []
+    s = bench.SmiSampler()
+    s.start()
+    s.join(timeout=5)
+    assert not s.is_alive() and s.summary() is None and calls == []
