@@ -67,7 +67,9 @@ def parse():
     ap.add_argument("--ranges", action="store_true",
                     help="run the mask as a range list through the schedule-table kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-heads", type=int, default=1)
+    ap.add_argument("--cpu-sample-heads", type=int, default=1 << 30,
+                    help="at most this many (b, h) slices for the CPU baseline, which stops once "
+                         "10 s of oracle time are spent")
     ap.add_argument("--heads", type=int, default=0,
                     help="override the workload's head count, e.g. 3 = one GPU's share of the 12-head "
                          "workload under 4-way head (Ulysses) sharding")
@@ -174,105 +176,75 @@ def traffic_for(workload_name, part="fwd"):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline_bwd(w, heads, ranges=False):
-    """The oracle's backward, untuned, on (b, h) slices of the same workload."""
-    import oracle
-    import seeded_inputs as si
+# The CPU baseline times whole (b, h) slices of batch 0 until at least this
+# much oracle time is spent (or the slices run out).
+CPU_SAMPLE_MIN_S = 10.0
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = 1
-    mask = oracle.RangeMask(*w.mask_ranges()) if ranges else w.desc
-    flops = 0
-    elapsed = 0.0
-    for h in range(heads):
-        args = [si.slice_values(w, t, 0, h) for t in ("q", "k", "v", "do")]
+        return 1
+
+
+def _time_oracle(w, max_heads, tensors, run, flops_per_slice, what):
+    """run(args) is the oracle on one slice's host values; returns the
+    cpu_baseline record over the slices timed."""
+    import seeded_inputs as si
+    flops, elapsed, n = 0, 0.0, 0
+    for h in range(min(max_heads, w.heads)):
+        args = [si.slice_values(w, t, 0, h) for t in tensors]
         t0 = time.perf_counter()
-        oracle.masked_attention_bwd_slice(*args, mask)
+        run(args)
         elapsed += time.perf_counter() - t0
-        flops += oracle.backward_useful_flops(mask, w.head_dim)
+        flops += flops_per_slice
+        n += 1
+        if elapsed >= CPU_SAMPLE_MIN_S:
+            break
     return {
-        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": f"{heads} of {w.batch * w.heads} (b,h) slices of {w.name} (all rows, backward"
-                  f"{', range-list mask' if ranges else ''}), fp64 NumPy, "
-                  f"{elapsed:.1f} s",
+        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+        "sample": f"{n} of {w.batch * w.heads} (b,h) slices of {w.name} ({what}), fp64 NumPy, {elapsed:.1f} s",
     }
 
 
-def cpu_baseline_primal(w, heads, ranges=False):
+def cpu_baseline_bwd(w, max_heads, ranges=False):
+    """The oracle's backward, untuned, on (b, h) slices of the same workload."""
+    import oracle
+    mask = oracle.RangeMask(*w.mask_ranges()) if ranges else w.desc
+    return _time_oracle(w, max_heads, ("q", "k", "v", "do"), lambda a: oracle.masked_attention_bwd_slice(*a, mask),
+                        oracle.backward_useful_flops(mask, w.head_dim),
+                        "all rows, backward" + (", range-list mask" if ranges else ""))
+
+
+def cpu_baseline_primal(w, max_heads, ranges=False):
     """The oracle (which forms o together with the tangent) on (b, h) slices;
     only the primal's 4 d flops per pair are counted."""
     import oracle
     import seeded_inputs as si
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
     mask = oracle.RangeMask(*w.mask_ranges()) if ranges else w.desc
-    flops, elapsed = 0, 0.0
-    for h in range(heads):
-        args = [si.slice_values(w, t, 0, h) for t in si.TENSORS]
-        t0 = time.perf_counter()
-        oracle.masked_attention_jvp_slice(*args, mask)
-        elapsed += time.perf_counter() - t0
-        flops += 4 * w.head_dim * oracle.pair_count(mask)
-    return {
-        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": f"{heads} of {w.batch * w.heads} (b,h) slices of {w.name} (all rows; the oracle forms o with "
-                  f"its tangent, 4 d flops per pair counted), fp64 NumPy, {elapsed:.1f} s",
-    }
+    return _time_oracle(w, max_heads, si.TENSORS, lambda a: oracle.masked_attention_jvp_slice(*a, mask),
+                        4 * w.head_dim * oracle.pair_count(mask),
+                        "all rows; the oracle forms o with its tangent, 4 d flops per pair counted")
 
 
-def cpu_baseline_ranges(w, heads):
+def cpu_baseline_ranges(w, max_heads):
     """The oracle on the range-list mask, untuned, on (b, h) slices."""
     import oracle
     import seeded_inputs as si
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
     rm = oracle.RangeMask(*w.mask_ranges())
-    flops, elapsed = 0, 0.0
-    for h in range(heads):
-        args = [si.slice_values(w, t, 0, h) for t in si.TENSORS]
-        t0 = time.perf_counter()
-        oracle.masked_attention_jvp_slice(*args, rm)
-        elapsed += time.perf_counter() - t0
-        flops += 12 * w.head_dim * oracle.pair_count(rm)
-    return {
-        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": f"{heads} of {w.batch * w.heads} (b,h) slices of {w.name} (all rows, range-list mask), "
-                  f"fp64 NumPy, {elapsed:.1f} s",
-    }
+    return _time_oracle(w, max_heads, si.TENSORS, lambda a: oracle.masked_attention_jvp_slice(*a, rm),
+                        12 * w.head_dim * oracle.pair_count(rm), "all rows, range-list mask")
 
 
-def cpu_baseline(w, heads, clean_tangent_zero=False):
+def cpu_baseline(w, max_heads, clean_tangent_zero=False):
     """The oracle, untuned, on (b, h) slices of the same workload."""
-    import numpy as np
     import oracle
     import seeded_inputs as si
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
-    flops = 0
-    elapsed = 0.0
     fn = oracle.masked_attention_jvp_slice_ctz if clean_tangent_zero else oracle.masked_attention_jvp_slice
-    for h in range(heads):
-        args = [si.slice_values(w, t, 0, h) for t in si.TENSORS]
-        t0 = time.perf_counter()
-        fn(*args, w.desc)
-        elapsed += time.perf_counter() - t0
-        flops += oracle.useful_flops(w.desc, w.head_dim, clean_tangent_zero)
-    return {
-        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": f"{heads} of {w.batch * w.heads} (b,h) slices of {w.name} (all rows), fp64 NumPy, "
-                  f"{elapsed:.1f} s",
-    }
+    return _time_oracle(w, max_heads, si.TENSORS, lambda a: fn(*a, w.desc),
+                        oracle.useful_flops(w.desc, w.head_dim, clean_tangent_zero), "all rows")
 
 
 def main():

@@ -78,3 +78,14 @@ def test_no_smi_switches_the_power_samples_off(monkeypatch):
     s.start()
     s.join(timeout=5)
     assert not s.is_alive() and s.summary() is None and calls == []
+
+
+def test_cpu_baseline_times_slices_until_its_time_floor(monkeypatch):
+    import seeded_inputs as si
+    w = si.WORKLOADS[1]  # 2 heads
+    monkeypatch.setattr(bench, "CPU_SAMPLE_MIN_S", 0.0)  # the first slice already reaches it
+    rec = bench.cpu_baseline(w, 1 << 30)
+    assert rec["kind"] == "oracle" and rec["value"] > 0 and rec["sample"].startswith("1 of 2 ")
+    monkeypatch.setattr(bench, "CPU_SAMPLE_MIN_S", 1e9)  # never reached: every slice of batch 0
+    assert bench.cpu_baseline(w, 1 << 30)["sample"].startswith("2 of 2 ")
+    assert bench.cpu_baseline_bwd(w, 1)["sample"].startswith("1 of 2 ")  # the cap
