@@ -1,0 +1,126 @@
+"""Large scores, through the C ABI: the online softmax's rescaling.
+
+The kernels keep a per-row reference max and rescale l, r and the output
+accumulators only when a tile's max passes it by more than 2^8 (exp2 units),
+and the backward recomputes P from the forward's lse.  The seeded workloads
+(RMS-normalised q, k) hardly ever move the reference after the first tile,
+so these cases drive it on purpose:
+
+* scaled queries: q ~ N(0, 8^2) per element, so scores are N(0, 64) and the
+  row maxima jump by more than 2^8 between tiles now and then;
+* a ramp along the keys: q and every key share a direction e, with k_j . e
+  growing linearly in j, so that each 32-key tile's scores pass the previous
+  tile's by more than 2^8 (after the softmax scale and log2(e)): the
+  reference moves on every tile of every row, and p concentrates on the
+  last keys a row sees.  tq and tk have no component along e: otherwise
+  the score tangents would share a large part over those keys, and t_o,
+  the p-weighted spread of ts times v, would live on a cancellation that
+  the bf16 rounding of p~ ts (the MFMA operand of the pages' algorithm)
+  does not resolve, just as for dq below.
+
+Forward + JVP, the forward without tangents and the backward are compared
+with the fp64 oracle on the same rounded values (bf16 within 1e-2, fp32
+within 1e-4 normwise).  lse is held to atol + rtol |lse|: an fp32 score of
+magnitude |s| carries rounding of order 1e-7 |s| from each operation that
+forms it, so at |lse| near 265 (the ramp) an fp32 evaluation of the plain
+definition is already 8e-5 off; fp32: 1e-5 + 1e-6 |lse|, bf16: 2e-2 +
+1e-4 |lse|.
+
+One exception, bf16 dq on the ramp.  Each row of dS = P (dP - delta) sums
+to zero exactly, and dq_i = scale sum_j dS_ij k_j; with the ramp every key
+carries a large common component along e (up to about 740), so dq lives on
+that cancellation.  Rounding dS to bf16 for the dS k product (unit roundoff
+2^-9) breaks it and moves dq_i by up to 2^-9 scale sum_j |dS_ij| |k_j|,
+about a tenth of |dq| here, for any kernel that feeds dS to the matrix unit
+in bf16.  That dq is held to twice this rounding bound (Frobenius norms)
+instead, and the fp32 plan to the normwise 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import masked_attention_jvp_amd as aj
+from gpu_util import log, to_f64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    aj._load()
+
+
+DESC = (96, 7, 1, 1)  # teacher forcing, 7 frames of 96 tokens: N = 1344, partial tiles on both sides
+TOL = {"bf16": 1e-2, "fp32": 1e-4}
+LSE_TOL = {"bf16": (2e-2, 1e-4), "fp32": (1e-5, 1e-6)}  # (atol, rtol)
+
+
+def _dq_rounding_bound(q, k, v, do, lse, desc):
+    """Frobenius norm of 2^-9 scale |dS| |K| (the definition's dS, fp64)."""
+    d = q.shape[1]
+    scale = 1.0 / np.sqrt(d)
+    allowed = oracle.mask_dense(desc)
+    p = np.where(allowed, np.exp(scale * (q @ k.T) - lse[:, None]), 0.0)
+    dp = do @ v.T
+    ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+    return float(np.linalg.norm(2.0 ** -9 * scale * (np.abs(ds) @ np.abs(k))))
+
+
+def _inputs(kind, n, d, heads, dtype, seed):
+    rng = np.random.default_rng(seed)
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    q, k, v = f(heads, n, d), f(heads, n, d), f(heads, n, d)
+    tq, tk, tv = (0.1 * f(heads, n, d) for _ in range(3))
+    do = f(heads, n, d)
+    if kind == "scaled":
+        q *= 8.0
+    else:  # ramp: along e = first axis, q . e = 4 and k_j . e = slope * j
+        # per key the score grows by 4 slope / sqrt(d); 9 exp2 units per 32 keys
+        slope = 9.0 / 32 / np.log2(np.e) * np.sqrt(d) / 4.0
+        q[:, :, 0] = 4.0
+        k[:, :, 0] = slope * np.arange(n, dtype=np.float32)
+        tq[:, :, 0] = 0.0
+        tk[:, :, 0] = 0.0
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = {name: torch.from_numpy(a[None]).to(tdt) for name, a in
+           (("q", q), ("k", k), ("v", v), ("tq", tq), ("tk", tk), ("tv", tv), ("do", do))}
+    host = {name: t[0].double().numpy() for name, t in dev.items()}  # the rounded values
+    return {name: t.cuda() for name, t in dev.items()}, host
+
+
+@pytest.mark.parametrize("kind", ["scaled", "ramp"])
+@pytest.mark.parametrize("dtype, d", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
+def test_large_scores_forward_jvp_primal_backward(kind, dtype, d):
+    tpf, f, c, tf = DESC
+    n = tpf * f * (1 + tf)
+    heads = 2
+    x, hv = _inputs(kind, n, d, heads, dtype, seed=900 + d + (kind == "ramp"))
+    o, to, lse = aj.masked_attention_jvp(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], DESC, return_lse=True)
+    po, plse = aj.masked_attention_fwd(x["q"], x["k"], x["v"], DESC, return_lse=True)
+    dq, dk, dv = aj.masked_attention_bwd(x["q"], x["k"], x["v"], o, lse, x["do"], DESC)
+    torch.cuda.synchronize()
+    bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t.view(torch.int32))
+    assert torch.equal(bits(po), bits(o)) and torch.equal(plse, lse)
+    for h in range(heads):
+        sl = [hv[t][h] for t in ("q", "k", "v", "tq", "tk", "tv")]
+        ro, rto, rl = oracle.masked_attention_jvp_slice(*sl, DESC)
+        rq, rk, rv, _ = oracle.masked_attention_bwd_slice(*sl[:3], hv["do"][h], DESC)
+        errs = {"o": rel_err(to_f64(o[0, h]), ro), "to": rel_err(to_f64(to[0, h]), rto),
+                "dq": rel_err(to_f64(dq[0, h]), rq), "dk": rel_err(to_f64(dk[0, h]), rk),
+                "dv": rel_err(to_f64(dv[0, h]), rv)}
+        atol, rtol = LSE_TOL[dtype]
+        dl = float(np.max(np.abs(to_f64(lse[0, h]) - rl) / (atol + rtol * np.abs(rl))))
+        log(f"[{kind} {dtype} d={d} h={h}] max |lse| {np.max(np.abs(rl)):.1f}; "
+            + " ".join(f"{k} {e:.2e}" for k, e in errs.items()) + f" lse error / bound {dl:.2f}")
+        if dtype == "bf16" and kind == "ramp":
+            bound = _dq_rounding_bound(*sl[:3], hv["do"][h], rl, DESC)
+            adq = float(np.linalg.norm(to_f64(dq[0, h]) - rq))
+            log(f"    dq: |error| {adq:.3e} against the bf16 rounding bound {bound:.3e} (|dq| {np.linalg.norm(rq):.3e})")
+            assert adq < 2.0 * bound
+            del errs["dq"]
+        assert max(errs.values()) < TOL[dtype], errs
+        assert dl < 1.0
+        assert all(torch.isfinite(t).all().item() for t in (o, to, lse, dq, dk, dv))
