@@ -124,3 +124,35 @@ def test_large_scores_forward_jvp_primal_backward(kind, dtype, d):
         assert max(errs.values()) < TOL[dtype], errs
         assert dl < 1.0
         assert all(torch.isfinite(t).all().item() for t in (o, to, lse, dq, dk, dv))
+
+
+def test_large_scores_range_list_ramp():
+    """The ramp on a range-list mask (teacher forcing with a one-frame first
+    chunk, then chunks of 3 frames): the schedule-table kernels share the
+    rescaling but stage their tiles and masks from the table."""
+    import seeded_inputs as si
+    n, groups = si.chunked_mask_ranges(96, (1, 3, 3), 1)
+    rm = oracle.RangeMask(n, groups)
+    d, heads = 128, 2
+    x, hv = _inputs("ramp", n, d, heads, "bf16", seed=950)
+    o, to, lse = aj.masked_attention_jvp_ranges(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], groups,
+                                                return_lse=True)
+    po, plse = aj.masked_attention_fwd_ranges(x["q"], x["k"], x["v"], groups, return_lse=True)
+    dq, dk, dv = aj.masked_attention_bwd_ranges(x["q"], x["k"], x["v"], o, lse, x["do"], groups)
+    torch.cuda.synchronize()
+    assert torch.equal(po.view(torch.int16), o.view(torch.int16)) and torch.equal(plse, lse)
+    atol, rtol = LSE_TOL["bf16"]
+    for h in range(heads):
+        sl = [hv[t][h] for t in ("q", "k", "v", "tq", "tk", "tv")]
+        ro, rto, rl = oracle.masked_attention_jvp_slice(*sl, rm)
+        rq, rk, rv, _ = oracle.masked_attention_bwd_slice(*sl[:3], hv["do"][h], rm)
+        errs = {"o": rel_err(to_f64(o[0, h]), ro), "to": rel_err(to_f64(to[0, h]), rto),
+                "dk": rel_err(to_f64(dk[0, h]), rk), "dv": rel_err(to_f64(dv[0, h]), rv)}
+        adq = float(np.linalg.norm(to_f64(dq[0, h]) - rq))
+        bound = _dq_rounding_bound(*sl[:3], hv["do"][h], rl, rm)
+        dl = float(np.max(np.abs(to_f64(lse[0, h]) - rl) / (atol + rtol * np.abs(rl))))
+        log(f"[range ramp h={h}] max |lse| {np.max(np.abs(rl)):.1f}; "
+            + " ".join(f"{k} {e:.2e}" for k, e in errs.items())
+            + f" dq |error| {adq:.3e} (bound {bound:.3e}) lse error / bound {dl:.2f}")
+        assert max(errs.values()) < TOL["bf16"], errs
+        assert adq < 2.0 * bound and dl < 1.0
