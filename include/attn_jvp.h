@@ -325,12 +325,12 @@ int attn_jvp_key_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
  * work, clean and noisy blocks of the same chunks come in groups of 8 and 8,
  * so that the round-robin hand-out of workgroups to the 8 XCDs gives each XCD
  * both sides.  Range-list plans: host_out holds the heavy-first order of
- * the query blocks (more streamed tiles first).  For range-list plans and
- * for descriptor plans without flags, "workgroup t" is the logical task t:
- * over the whole B H grid, workgroups take the tasks in XCD groups of 128
- * consecutive tasks under the rule of attn_jvp_bwd_launch_order (there with
- * groups of 16); clean-tangent-zero plans keep the index order.  n is the
- * capacity of host_out in int32 elements. */
+ * the query blocks (more streamed tiles first).  "Workgroup t" is the
+ * logical task t: over the whole B H grid, workgroups take the tasks in XCD
+ * groups of 128 consecutive tasks under the rule of attn_jvp_bwd_launch_order
+ * (there with groups of 16), except that on the smaller grids
+ * clean-tangent-zero plans keep the index order.  n is the capacity of
+ * host_out in int32 elements. */
 int attn_jvp_launch_order(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
 /* Tile map, row-major [n_query_blocks][n_key_tiles], query blocks in index

@@ -95,11 +95,11 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   const int N = g.seq_len;
   // Workgroups take the heavy-first order in XCD groups of kFwdXcdGroup
   // (launch_task): neighbouring blocks of that order, which stream nearly the
-  // same key tiles, share an XCD's L2.  Clean-tangent-zero plans keep their
-  // balanced order (clean and noisy blocks in turn on every XCD) in index
-  // order: at 3 heads it was 3 % faster than heavy first across heads.
-  const int task = (TABLE || !CTZ) ? launch_task((int)blockIdx.x, (int)gridDim.x, p.n_qblocks, kFwdXcdGroup)
-                                   : (int)blockIdx.x;
+  // same key tiles, share an XCD's L2.  Clean-tangent-zero plans group their
+  // balanced order (8 clean and 8 noisy blocks in turn, so every group holds
+  // both sides) and keep it in index order on small grids, where that was
+  // 3 % faster than heavy first across heads.
+  const int task = launch_task((int)blockIdx.x, (int)gridDim.x, p.n_qblocks, kFwdXcdGroup, TABLE || !CTZ);
   const int bh = task / p.n_qblocks;
   int qb, r0, r1, ntiles, e0 = 0;
   TileSpans sp{0, 0, 0, 0};

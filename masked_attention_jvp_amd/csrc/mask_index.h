@@ -140,14 +140,15 @@ AJ_HD int32_t heavy_first_qblock(const MaskGeom& g, int32_t block_q, int32_t t, 
 //   weights even out over each pair of rounds; only an even number of rounds
 //   is grouped and the rest keeps its index.
 // * Smaller grids: heavy first across all slices (the heaviest block of every
-//   slice, then the next, ...).  A lone unpaired round would load some XCDs
+//   slice, then the next, ...), or with across_slices = false the index
+//   order.  A lone unpaired round would load some XCDs
 //   far more than others (in a single round of 8 groups of 128, the first
 //   group carries about 7 times the work of the fourth), and with few tasks
 //   per CU a slice-by-slice order would leave the last slice's heavy blocks
 //   to the end.
 constexpr int32_t kMinGroupedRounds = 2;
 constexpr int32_t kMinGroupedTasks = 2048;  // 8 per CU
-AJ_HD int32_t launch_task(int32_t b, int32_t total, int32_t per_slice, int32_t G) {
+AJ_HD int32_t launch_task(int32_t b, int32_t total, int32_t per_slice, int32_t G, bool across_slices = true) {
   const int32_t round = 8 * G;
   const int32_t rounds = total / round;
   if (total >= kMinGroupedTasks && rounds >= kMinGroupedRounds) {
@@ -157,6 +158,7 @@ AJ_HD int32_t launch_task(int32_t b, int32_t total, int32_t per_slice, int32_t G
     const int32_t x = (r & 1) ? 7 - (u & 7) : (u & 7);
     return r * round + x * G + (u >> 3);
   }
+  if (!across_slices) return b;
   const int32_t n_slices = total / per_slice;
   const int32_t k = b / n_slices;
   return (b - k * n_slices) * per_slice + k;
