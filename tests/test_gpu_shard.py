@@ -82,3 +82,18 @@ def test_shard_backward_equals_the_full_grid_bitwise():
     torch.cuda.synchronize()
     for name, a, b in zip(("dq", "dk", "dv"), sgrads, grads):
         assert torch.equal(_bits(a), _bits(sl(b))), name
+
+
+def test_shard_clean_tangent_zero_equals_the_full_grid_bitwise():
+    """The clean-tangent-zero plan: XCD-grouped at 12 heads, index order at 3."""
+    full = WORKLOADS[3]
+    shard = full.with_(heads=SHARD_HEADS)
+    x = device_inputs(full)
+    args = [x[t] for t in TENSORS]
+    o, to, lse = aj.masked_attention_jvp(*args, full.desc, return_lse=True, clean_tangent_zero=True)
+    torch.cuda.synchronize()
+    so, sto, slse = aj.masked_attention_jvp(*(a[:, :SHARD_HEADS].contiguous() for a in args), shard.desc,
+                                            return_lse=True, clean_tangent_zero=True)
+    torch.cuda.synchronize()
+    for a, b in ((so, o), (sto, to), (slse, lse)):
+        assert torch.equal(_bits(a), _bits(b[:, :SHARD_HEADS].contiguous()))
