@@ -328,9 +328,10 @@ int attn_jvp_key_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
  * the query blocks (more streamed tiles first).  "Workgroup t" is the
  * logical task t: over the whole B H grid, workgroups take the tasks in XCD
  * groups of 128 consecutive tasks under the rule of attn_jvp_bwd_launch_order
- * (there with groups of 16), except that on the smaller grids
- * clean-tangent-zero plans keep the index order.  n is the capacity of
- * host_out in int32 elements. */
+ * (there with groups of 16), except on the smaller grids: there
+ * clean-tangent-zero plans keep the index order, and general teacher-forcing
+ * plans go heavy first across the slices in groups of 32 consecutive tasks
+ * of one slice.  n is the capacity of host_out in int32 elements. */
 int attn_jvp_launch_order(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
 /* Tile map, row-major [n_query_blocks][n_key_tiles], query blocks in index

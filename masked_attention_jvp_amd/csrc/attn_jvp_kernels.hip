@@ -98,8 +98,12 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   // same key tiles, share an XCD's L2.  Clean-tangent-zero plans group their
   // balanced order (8 clean and 8 noisy blocks in turn, so every group holds
   // both sides) and keep it in index order on small grids, where that was
-  // 3 % faster than heavy first across heads.
-  const int task = launch_task((int)blockIdx.x, (int)gridDim.x, p.n_qblocks, kFwdXcdGroup, TABLE || !CTZ);
+  // 3 % faster than heavy first across heads.  On small grids general
+  // teacher-forcing plans take rank-major groups of 32 (3 % faster at 3 heads
+  // than heavy first across heads, which the other plans keep).
+  const int32_t small = (CTZ && !TABLE) ? kSmallIndex
+                        : (!TABLE && p.g.tf) ? kSmallRankGroups : kSmallAcross;
+  const int task = launch_task((int)blockIdx.x, (int)gridDim.x, p.n_qblocks, kFwdXcdGroup, small);
   const int bh = task / p.n_qblocks;
   int qb, r0, r1, ntiles, e0 = 0;
   TileSpans sp{0, 0, 0, 0};

@@ -139,16 +139,22 @@ AJ_HD int32_t heavy_first_qblock(const MaskGeom& g, int32_t block_q, int32_t t, 
 //   round (XCD x takes group x, then group 7 - x), so the falling heavy-first
 //   weights even out over each pair of rounds; only an even number of rounds
 //   is grouped and the rest keeps its index.
-// * Smaller grids: heavy first across all slices (the heaviest block of every
-//   slice, then the next, ...), or with across_slices = false the index
-//   order.  A lone unpaired round would load some XCDs
-//   far more than others (in a single round of 8 groups of 128, the first
-//   group carries about 7 times the work of the fourth), and with few tasks
-//   per CU a slice-by-slice order would leave the last slice's heavy blocks
-//   to the end.
+// * Smaller grids, by `small`: kSmallAcross, heavy first across all slices
+//   (the heaviest block of every slice, then the next, ...); kSmallRankGroups,
+//   the same across groups of kSmallGroup consecutive tasks of one slice
+//   (rank-major over the slices, then the round snake above), which keeps
+//   some L2 locality and balances as well where a slice's weights fall
+//   slowly along its order (teacher forcing, whose order alternates sides);
+//   kSmallIndex, the index order.  A lone unpaired round would load some
+//   XCDs far more than others (in a single round of 8 groups of 128, the
+//   first group carries about 7 times the work of the fourth), and with few
+//   tasks per CU a slice-by-slice order would leave the last slice's heavy
+//   blocks to the end.
 constexpr int32_t kMinGroupedRounds = 2;
 constexpr int32_t kMinGroupedTasks = 2048;  // 8 per CU
-AJ_HD int32_t launch_task(int32_t b, int32_t total, int32_t per_slice, int32_t G, bool across_slices = true) {
+constexpr int32_t kSmallIndex = 0, kSmallAcross = 1, kSmallRankGroups = 2;
+constexpr int32_t kSmallGroup = 32;
+AJ_HD int32_t launch_task(int32_t b, int32_t total, int32_t per_slice, int32_t G, int32_t small = kSmallAcross) {
   const int32_t round = 8 * G;
   const int32_t rounds = total / round;
   if (total >= kMinGroupedTasks && rounds >= kMinGroupedRounds) {
@@ -158,8 +164,33 @@ AJ_HD int32_t launch_task(int32_t b, int32_t total, int32_t per_slice, int32_t G
     const int32_t x = (r & 1) ? 7 - (u & 7) : (u & 7);
     return r * round + x * G + (u >> 3);
   }
-  if (!across_slices) return b;
+  if (small == kSmallIndex) return b;
   const int32_t n_slices = total / per_slice;
+  if (small == kSmallRankGroups) {
+    // groups of kSmallGroup tasks of one slice, group g = rank g / n_slices
+    // of slice g mod n_slices; full rounds of 8 groups snake over the XCDs,
+    // then the remaining groups and the tasks past the last whole group of
+    // each slice follow in that order
+    constexpr int32_t GS = kSmallGroup;
+    const int32_t per_groups = per_slice / GS;
+    const int32_t n_groups = n_slices * per_groups;
+    const int32_t full = n_groups / 8;
+    if (b < full * 8 * GS) {
+      const int32_t r = b / (8 * GS), u = b - r * 8 * GS;
+      const int32_t grp = r * 8 + ((r & 1) ? 7 - (u & 7) : (u & 7));
+      const int32_t rank = grp / n_slices;
+      return (grp - rank * n_slices) * per_slice + rank * GS + (u >> 3);
+    }
+    int32_t rest = b - full * 8 * GS;
+    if (rest < (n_groups - full * 8) * GS) {
+      const int32_t grp = full * 8 + rest / GS;
+      const int32_t rank = grp / n_slices;
+      return (grp - rank * n_slices) * per_slice + rank * GS + (rest - (rest / GS) * GS);
+    }
+    rest -= (n_groups - full * 8) * GS;
+    const int32_t k = rest / n_slices;
+    return (rest - k * n_slices) * per_slice + per_groups * GS + k;
+  }
   const int32_t k = b / n_slices;
   return (b - k * n_slices) * per_slice + k;
 }
