@@ -181,6 +181,24 @@ def traffic_for(workload_name, part="fwd"):
 CPU_SAMPLE_MIN_S = 10.0
 
 
+def host_info():
+    """CPU model (from /proc/cpuinfo) and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        cores = os.cpu_count()
+    return {"cpu_model": model, "cores_available": cores}
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -203,9 +221,12 @@ def _time_oracle(w, max_heads, tensors, run, flops_per_slice, what):
         n += 1
         if elapsed >= CPU_SAMPLE_MIN_S:
             break
+    hi = host_info()
     return {
         "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
         "sample": f"{n} of {w.batch * w.heads} (b,h) slices of {w.name} ({what}), fp64 NumPy, {elapsed:.1f} s",
+        "threads": "one process, NumPy fp64 with its BLAS on `cores` threads",
+        "cores_available": hi["cores_available"], "cpu_model": hi["cpu_model"],
     }
 
 
@@ -336,6 +357,9 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
+    # shader clock of every XCD over the timed launches: one clock sample
+    # right before the first and one right after the last, on the same stream
+    clk = torch.zeros(64, dtype=torch.int64, device=dev)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     smi_before = smi_sample()
@@ -343,10 +367,12 @@ def main():
     torch.cuda.synchronize()
     sampler.start()
     t0 = time.perf_counter()
+    aj.attn_jvp_clock_sample(clk[:32], stream)
     for i in range(args.steps):
         starts[i].record(stream)
         call()
         ends[i].record(stream)
+    aj.attn_jvp_clock_sample(clk[32:], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     sampler.stop.set()
@@ -356,6 +382,11 @@ def main():
     avg_ms = float(np.mean(per_launch_ms))
     total_ms = starts[0].elapsed_time(ends[-1])
     ms_per_step = total_ms / args.steps
+
+    c = clk.cpu().numpy()
+    sclk = aj.shader_clock_mhz(c[:32], c[32:])
+    sclk_mean = float(np.mean(list(sclk.values()))) if sclk else None
+    props = torch.cuda.get_device_properties(dev)
 
     info = plan.info
     useful = (aj.attn_jvp_plan_bwd_flops(plan) if args.backward
@@ -406,6 +437,13 @@ def main():
         "gpu_power_clock": {"before": smi_before, "after": smi_after,
                             "during": sampler.summary() if wall >= 2.0 else None},
         "wall_s_timed": round(wall, 3),
+        "gpu": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                "compute_units": props.multi_processor_count,
+                # average shader clock per XCD over the timed launches (s_memtime
+                # against the 100 MHz real-time counter)
+                "sclk_mhz_timed": {str(k): round(v, 1) for k, v in sorted(sclk.items())},
+                "sclk_mhz_timed_mean": round(sclk_mean, 1) if sclk_mean else None},
+        "host": host_info(),
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
@@ -415,6 +453,9 @@ def main():
             "traffic": traffic,
             "kernel": kernel,
             "avg_launch_ms": round(avg_ms, 4),
+            # the same peak at the clock measured over the timed launches
+            "peak_at_timed_sclk": round(PEAK_BF16_TFLOPS * sclk_mean / 2400.0, 1) if sclk_mean else None,
+            "frac_at_timed_sclk": round(achieved / (PEAK_BF16_TFLOPS * sclk_mean / 2400.0), 4) if sclk_mean else None,
         },
     }
     if not args.no_cpu_baseline:

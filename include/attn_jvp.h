@@ -342,6 +342,19 @@ int attn_jvp_launch_order(const attn_jvp_plan* plan, int32_t* host_out, size_t n
  * n is the capacity of host_out in bytes. */
 int attn_jvp_tile_map(const attn_jvp_plan* plan, uint8_t* host_out, size_t n);
 
+/* Measurement helper (not part of the operation): enqueues on `stream` a
+ * small kernel of 8 workgroups, one per XCD of an MI355X, and workgroup w
+ * stores into device_out[4w .. 4w+3] (uint64): its XCD number, the XCD's
+ * shader clock counter (s_memtime, which counts at the shader clock), the
+ * constant 100 MHz real-time counter (s_memrealtime), and 0.  Two samples
+ * taken on one stream around a run of launches give each XCD's average
+ * shader clock over that run: 100 MHz * (change of the shader counter) /
+ * (change of the real-time counter), pairing entries by XCD number.
+ * device_out: at least 32 uint64 of device memory, 8-byte aligned, owned by
+ * the caller.  Errors: ATTN_JVP_E_NULL, ATTN_JVP_E_ALIGN, a device that is
+ * not gfx950, or ATTN_JVP_E_HIP if the launch fails. */
+int attn_jvp_clock_sample(void* device_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -109,12 +109,14 @@ def _load():
         lib.attn_jvp_fwd_primal.argtypes = [vp] * 7
         lib.attn_jvp_bwd_table.argtypes = [vp] * 13
         lib.attn_jvp_fwd_primal_table.argtypes = [vp] * 8
+        lib.attn_jvp_clock_sample.argtypes = [vp, vp]
         for name in ("attn_jvp_create", "attn_jvp_create_ex", "attn_jvp_fwd", "attn_jvp_destroy",
                      "attn_jvp_plan_info", "attn_jvp_plan_flops", "attn_jvp_launch_order", "attn_jvp_row_ranges",
                      "attn_jvp_tile_map", "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops",
                      "attn_jvp_key_ranges", "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order",
                      "attn_jvp_create_ranges", "attn_jvp_plan_table_size", "attn_jvp_plan_table", "attn_jvp_fwd_table",
-                     "attn_jvp_fwd_primal", "attn_jvp_bwd_table", "attn_jvp_fwd_primal_table"):
+                     "attn_jvp_fwd_primal", "attn_jvp_bwd_table", "attn_jvp_fwd_primal_table",
+                     "attn_jvp_clock_sample"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -369,6 +371,35 @@ def attn_jvp_fwd_primal(plan: Plan, q, k, v, o, lse=None, stream=None) -> None:
                                            ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
                                            ctypes.c_void_p(stream.cuda_stream))
     _check(code, "attn_jvp_fwd_primal")
+
+
+def attn_jvp_clock_sample(out, stream=None) -> None:
+    """Enqueue one clock sample (attn_jvp_clock_sample) into ``out``, a
+    contiguous int64 device tensor of at least 32 elements: per XCD its
+    number, its shader clock counter and the 100 MHz real-time counter."""
+    import torch
+    if out.dtype != torch.int64 or not out.is_contiguous() or out.numel() < 32 or out.device.type != "cuda":
+        raise AttnJvpError("out must be a contiguous int64 CUDA tensor of at least 32 elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(out.device)
+    with torch.cuda.device(out.device):
+        code = _load().attn_jvp_clock_sample(ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+    _check(code, "attn_jvp_clock_sample")
+
+
+def shader_clock_mhz(before, after) -> dict:
+    """Average shader clock per XCD between two clock samples (host copies
+    of the 32 int64 of attn_jvp_clock_sample): 100 MHz times the change of
+    the XCD's shader counter over the change of the real-time counter."""
+    b = np.asarray(before, dtype=np.int64).reshape(-1, 4)
+    a = np.asarray(after, dtype=np.int64).reshape(-1, 4)
+    start = {int(x): (int(t), int(rt)) for x, t, rt, _ in b}
+    mhz = {}
+    for x, t, rt, _ in a:
+        x = int(x)
+        if x in start and int(rt) > start[x][1]:
+            mhz[x] = 100.0 * (int(t) - start[x][0]) / (int(rt) - start[x][1])
+    return mhz
 
 
 def attn_jvp_fwd_primal_table(plan: Plan, table, q, k, v, o, lse=None, stream=None) -> None:

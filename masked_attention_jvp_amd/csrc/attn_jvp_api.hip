@@ -298,6 +298,24 @@ bool build_columns(int32_t n, const std::vector<int32_t>& g_lo, const std::vecto
 
 }  // namespace
 
+// Measurement: workgroup w (of kClockSampleGroups, one per XCD when
+// workgroups go to the 8 XCDs round robin) stores its XCD number, the shader
+// clock counter (s_memtime, counting at the XCD's shader clock) and the
+// constant 100 MHz real-time counter (s_memrealtime).
+constexpr int kClockSampleGroups = 8;
+__global__ void clock_sample_kernel(uint64_t* out) {
+  if (threadIdx.x == 0) {
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    const uint64_t t = __builtin_amdgcn_s_memtime();
+    const uint64_t rt = __builtin_amdgcn_s_memrealtime();
+    out[4 * blockIdx.x + 0] = xcc & 0xf;
+    out[4 * blockIdx.x + 1] = t;
+    out[4 * blockIdx.x + 2] = rt;
+    out[4 * blockIdx.x + 3] = 0;
+  }
+}
+
 extern "C" {
 
 int attn_jvp_create(attn_jvp_plan** out, const attn_jvp_mask_desc* mask, int32_t batch, int32_t heads,
@@ -963,6 +981,19 @@ int attn_jvp_tile_map(const attn_jvp_plan* p, uint8_t* out, size_t n) {
       else row[kt] = cls == 0 ? 0 : 4;
     }
   }
+  return ok();
+}
+
+int attn_jvp_clock_sample(void* device_out, void* stream) {
+  if (device_out == nullptr) return fail(ATTN_JVP_E_NULL, "device_out must be non-NULL");
+  if ((uintptr_t)device_out % 8 != 0) return fail(ATTN_JVP_E_ALIGN, "device_out must be 8-byte aligned");
+  int dev = -1;
+  const int st = check_device(&dev);
+  if (st != ATTN_JVP_OK) return st;
+  hipLaunchKernelGGL(clock_sample_kernel, dim3(kClockSampleGroups), dim3(64), 0, (hipStream_t)stream,
+                     (uint64_t*)device_out);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ATTN_JVP_E_HIP, "clock sample launch: %s", hipGetErrorString(e));
   return ok();
 }
 

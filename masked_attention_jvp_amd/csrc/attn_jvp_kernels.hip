@@ -147,20 +147,20 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 
   const size_t base = (size_t)bh * (size_t)N * D;
   const int slice_bytes = N * D * 2;
-  const __amdgpu_buffer_rsrc_t rsrc[4] = {
-      make_rsrc((const uint16_t*)p.k + base, slice_bytes), make_rsrc((const uint16_t*)p.tk + base, slice_bytes),
-      make_rsrc((const uint16_t*)p.v + base, slice_bytes), make_rsrc((const uint16_t*)p.tv + base, slice_bytes)};
-  const i32x4_t desc_k = make_desc((const uint16_t*)p.k + base, slice_bytes);
-  const i32x4_t desc_v = make_desc((const uint16_t*)p.v + base, slice_bytes);
-  // Clean-tangent-zero: tk and tv are read only through resources over the
+  // DMA descriptors of k, tk, v, tv over this (b, h) slice.
+  const i32x4_t desc[4] = {make_desc((const uint16_t*)p.k + base, slice_bytes),
+                           make_desc((const uint16_t*)p.tk + base, slice_bytes),
+                           make_desc((const uint16_t*)p.v + base, slice_bytes),
+                           make_desc((const uint16_t*)p.tv + base, slice_bytes)};
+  // Clean-tangent-zero: tk and tv are read only through descriptors over the
   // noisy half, with per-lane offsets relative to its start; a clean key's
   // offset is negative, i.e. a huge unsigned offset, which the range check
   // turns into zeros.  So no clean-side tangent is ever read, and the one
   // tile that straddles the two halves gets zeros for its clean keys.
   const size_t half = (size_t)g.side_len * D;
   const int half_bytes = g.side_len * D * 2;
-  const __amdgpu_buffer_rsrc_t rsrc_tn[2] = {make_rsrc((const uint16_t*)p.tk + base + half, half_bytes),
-                                             make_rsrc((const uint16_t*)p.tv + base + half, half_bytes)};
+  const i32x4_t desc_tn[2] = {make_desc((const uint16_t*)p.tk + base + half, half_bytes),
+                              make_desc((const uint16_t*)p.tv + base + half, half_bytes)};
 
   const int row = r0 + wave * 32 + n;
   const bool row_ok = row < r1;
@@ -210,6 +210,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) tqf[s] = load16(rtq, (row * D + 16 * s + 8 * h) * 2);
     }
+    // tq stays in accumulation registers as a B operand, which leaves vector
+    // registers for the score-tangent start tile below
+#pragma unroll
+    for (int s = 0; s < KS; ++s) keep_in_acc(tqf[s]);
   }
 
   auto stage = [&](auto st) -> uint16_t* {
@@ -246,11 +250,11 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     if constexpr (decltype(mode)::value == kFull) {
       const int i = q >> 2, tt = q & 3;
       uint16_t* lds = dst + tt * TILE + (wave * LOADS + i) * 512;
-      if (CTZ && (tt & 1)) load16_lds(rsrc_tn[tt >> 1], lds, dma_voff[i] + (tile * BC - g.side_len) * D * 2, 0);
-      else load16_lds(rsrc[tt], lds, dma_voff[i], soff);
+      if (CTZ && (tt & 1)) load16_lds_asm(desc_tn[tt >> 1], lds, dma_voff[i] + (tile * BC - g.side_len) * D * 2, 0);
+      else load16_lds_asm(desc[tt], lds, dma_voff[i], soff);
     } else {
       const int i = q >> 1, tt = 2 * (q & 1);
-      load16_lds_asm(tt ? desc_v : desc_k, dst + tt * TILE + (wave * LOADS + i) * 512, dma_voff[i], soff);
+      load16_lds_asm(desc[tt], dst + tt * TILE + (wave * LOADS + i) * 512, dma_voff[i], soff);
     }
   };
   auto issue = [&](auto mode, uint16_t* dst, int t, int t_end) {
@@ -274,10 +278,31 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     }
   }
   // m: reference max of l, r and the accumulators; mn: reference of the
-  // latest exponentiated tile (exp2 units).  r = sum p~ ts' (unscaled).
+  // latest exponentiated tile (exp2 units).  r = sum p~ (ts' - c) (unscaled).
   float m = -INFINITY, mn = -INFINITY, l = 0.f, r = 0.f;
   const float sl2 = p.score_log2;
   const float scale = p.scale;
+  // Shift of the score tangent.  The accumulators take ts' - c for a per-row
+  // constant c, not ts': r holds sum p~ (ts' - c) and accS sum p~ (ts' - c) v.
+  // Eq. 45 is unchanged by it, since sum p~ (ts' - c) v / l - (sum p~ (ts' - c)
+  // / l) o = sum p~ ts' v / l - (r / l) o exactly (o = acc_o / l).  It keeps
+  // the bf16 rounding of p~ (ts' - c), the MFMA operand, relative to the
+  // spread of ts' around c rather than to ts' itself: when the score tangents
+  // of a row share a large part (a key component common to all keys, met by
+  // tq), t_o is a small difference of two large terms, and rounding p~ ts'
+  // would lose it.  c starts at 0 and moves to the p~-weighted mean of the
+  // current tile's ts' whenever the row's reference max moves: first when it
+  // becomes finite (the row's first tile with an allowed key), then whenever
+  // a tile's max passes it (the earlier tiles then weigh 2^-8 or less).
+  // Moving c by dc takes accS -= dc acc_o and r -= dc l.  Every score-tangent
+  // MFMA chain starts from -c (negc), so the hot loop does no extra work, and
+  // a row's arithmetic depends only on the tiles it sees, in their order (not
+  // on how blocks and runs are cut).
+  float c_ts = 0.f;
+  f32x16 negc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negc[i] = 0.f;
+  opaque(negc);
 
   // transposing-read addresses (element offsets inside a V tile): a lane
   // group of 16 covers 16 columns; its lane L names key 4h + L/4 (and +8),
@@ -428,6 +453,28 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     // Rare after the first tile.
     if (__builtin_expect(__any(mn != m), 0)) {
       const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+      // rows whose reference moved: the score-tangent shift moves by dc to the
+      // p~-weighted mean of this tile's ts' (TS holds ts' - c); others keep it
+      float dc = 0.f;
+      if constexpr (HAS_TS) {
+        float sp = 0.f, spt = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sp += P[i];
+          spt = fmaf(P[i], TS[i], spt);
+        }
+        sp = pair_sum(sp);
+        spt = pair_sum(spt);
+        dc = (mn != m && sp > 0.f) ? spt / sp : 0.f;
+        c_ts += dc;
+        r -= dc * l;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          TS[i] -= dc;
+          negc[i] = -c_ts;
+        }
+        opaque(negc);
+      }
       m = mn;
       l *= alpha;
       r *= alpha;
@@ -436,9 +483,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       for (int c = 0; c < DC; ++c) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          accO[c][i] = acc_write(acc_read(accO[c][i]) * alpha);
+          const float ao = acc_read(accO[c][i]);
+          accO[c][i] = acc_write(ao * alpha);
           if constexpr (HAS_TKV) accV[c][i] = acc_write(acc_read(accV[c][i]) * alpha);
-          if constexpr (HAS_TS) accS[c][i] = acc_write(acc_read(accS[c][i]) * alpha);
+          if constexpr (HAS_TS) accS[c][i] = acc_write(fmaf(-dc, ao, acc_read(accS[c][i])) * alpha);
         }
       }
     }
@@ -505,8 +553,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     for (int s = 0; s < KS; ++s) {
       const int jj0 = 2 * s * PAIRS_PER_STEP;
       if constexpr (HAS_TS) {
-        if (s == 0) mfma_v_first(TSn, kf[s], tqf[s]);
-        else mfma_v_acc(TSn, kf[s], tqf[s]);
+        if (s == 0) mfma_v_init_ba(TSn, kf[s], tqf[s], negc);
+        else mfma_v_acc_ba(TSn, kf[s], tqf[s]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < PAIRS_PER_STEP; ++u) w_mul(jj0 + 2 * u);
@@ -635,8 +683,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       if (s == 0) mfma_v_first(SA, kf[s], qf[s]);
       else mfma_v_acc(SA, kf[s], qf[s]);
       if constexpr (MODE != kPrimal) {
-        if (s == 0) mfma_v_first(TSA, kf[s], tqf[s]);
-        else mfma_v_acc(TSA, kf[s], tqf[s]);
+        if (s == 0) mfma_v_init_ba(TSA, kf[s], tqf[s], negc);
+        else mfma_v_acc_ba(TSA, kf[s], tqf[s]);
       }
       if constexpr (MODE == kFull) mfma_v_acc(TSA, tkf[s], qf[s]);
     }
@@ -1204,6 +1252,12 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(FwdParams p) {
     for (int e = 0; e < E; ++e) tq[e] = ((const float*)p.tq)[base + (size_t)qrow * D + slice * E + e];
   }
   float m = -INFINITY, l = 0.f, r = 0.f;
+  // Score-tangent shift, as in fwd_bf16_kernel: r and at take ts - c, with c
+  // the (scaled) ts of the row's first allowed key, which leaves eq. 45's
+  // t_o unchanged and keeps a part shared by all of the row's score tangents
+  // out of the sums (in fp32 a fixed c suffices).
+  float c_ts = 0.f;
+  bool c_set = false;  // uniform across the row's 8 lanes
   auto key_step = [&](int j) {
       const float* kj = K + (size_t)j * D;
       const float* tkj = tK + (size_t)j * D;
@@ -1229,6 +1283,11 @@ __global__ void __launch_bounds__(256) fwd_fp32_kernel(FwdParams p) {
       }
       s *= p.scale;
       ts *= p.scale;
+      if (!c_set) {
+        c_ts = ts;
+        c_set = true;
+      }
+      ts -= c_ts;
       const float mn = fmaxf(m, s);
       const float alpha = expf(m - mn);
       const float pj = expf(s - mn);

@@ -58,10 +58,19 @@ typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 // Buffer descriptor as four dwords (base, stride 0, byte size, the same
 // config word as make_rsrc): for the DMA below.  Loads at or past `bytes`
 // (vector + scalar offset, checked on the device) return zeros.
+// The empty asm keeps the four words together in one scalar register quad, as
+// the DMA instruction takes them (the compiler would otherwise share the
+// words two descriptors have in common and rebuild a quad before each DMA).
 __device__ __forceinline__ i32x4_t make_desc(const void* base, int bytes) {
   const uint64_t a = (uint64_t)base;
-  return i32x4_t{(int32_t)(uint32_t)a, (int32_t)(uint32_t)((a >> 32) & 0xffff), bytes, 0x00020000};
+  i32x4_t d{(int32_t)(uint32_t)a, (int32_t)(uint32_t)((a >> 32) & 0xffff), bytes, 0x00020000};
+  asm volatile("" : "+s"(d));
+  return d;
 }
+// LDS byte address of a pointer into LDS: the low 32 bits of its generic
+// address (a generic LDS address is the LDS aperture base plus the LDS
+// offset), with no null-pointer handling as in a cast to the LDS space.
+__device__ __forceinline__ int lds_addr(const void* p) { return (int)(uint32_t)(uintptr_t)p; }
 // The same DMA written out.  Where the compiler tracks its own LDS DMA
 // against later LDS reads, it may wait for every DMA in flight (vmcnt(0))
 // before a read of another ring stage, which exposes the whole DMA latency
@@ -69,22 +78,23 @@ __device__ __forceinline__ i32x4_t make_desc(const void* base, int bytes) {
 // barriers before a stage is read or refilled), so the DMA is hidden from the
 // compiler; the memory clobber keeps LDS accesses from moving across.
 // Vector-memory loads complete in order, so the compiler's own waits for its
-// loads stay correct (they only cover more).  One wait state between the M0
-// write and the DMA.
+// loads stay correct (they only cover more).  M0 (the LDS base of the DMA) is
+// an input operand, so the compiler sets it and knows its value afterwards;
+// the s_nop gives the one wait state an M0 write needs before the DMA.
 __device__ __forceinline__ void load16_lds_asm(i32x4_t r, uint16_t* lds, int voff, int soff) {
   // soff and the LDS address are wave-uniform; readfirstlane puts them in
   // scalar registers where the compiler computed them in vector ones
-  const int m0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(LDS_AS void*)lds);
+  const int m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
   const int so = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(r), "s"(so), "s"(m0) : "memory", "m0");
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(r), "s"(so), "{m0}"(m0) : "memory");
 }
 // 4 bytes per lane into LDS at lds + 4 * lane (same scheme as above).
 __device__ __forceinline__ void load4_lds_asm(i32x4_t r, float* lds, int voff, int soff) {
-  const int m0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(LDS_AS void*)lds);
+  const int m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
   const int so = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(r), "s"(so), "s"(m0) : "memory", "m0");
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(r), "s"(so), "{m0}"(m0) : "memory");
 }
 // The two bf16 halves of a packed word as floats (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
@@ -165,6 +175,11 @@ __device__ __forceinline__ void mfma_v_init_ba(f32x16& d, u32x4 a, u32x4 b, cons
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
 }
 
+// Hide a tile's value from the compiler (emits no instruction): a tile of
+// equal values otherwise becomes one register plus copies, which the register
+// allocator shuffles around a loop that rewrites the tile.
+__device__ __forceinline__ void opaque(f32x16& a) { asm volatile("" : "+v"(a)); }
+
 // Pin a value to this point of the instruction stream: it must be computed
 // before the (volatile, hence ordered) empty asm, so the compiler cannot sink
 // it into a later block.  Emits no instruction.
@@ -182,15 +197,26 @@ __device__ __forceinline__ void hold(const f32x16& c) { asm volatile("" ::"v"(c)
 // the compiler from moving LDS accesses across the barrier.
 __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 
+// Explicit waits, as the s_waitcnt builtin rather than inline asm: the
+// compiler then sees them and knows which of its own loads (and LDS DMAs) have
+// completed, so it adds no waits of its own for them later (an inline-asm wait
+// is opaque to it).  gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8; a field at its maximum does not wait.  The builtin
+// itself does not order memory accesses, so empty memory-clobbering asm on
+// both sides keeps loads and stores from moving across the wait.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_lgkmcnt() {
   static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace attn_jvp

@@ -39,10 +39,30 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     lib = ctypes.CDLL(aj.library_path)
     for name in names:
         assert hasattr(lib, name), name
+
+
+def test_clock_sample_argument_errors():
+    """attn_jvp_clock_sample rejects a null or misaligned buffer before any
+    device work (raw pointers through the C ABI)."""
+    lib = aj._load()
+    assert lib.attn_jvp_clock_sample(None, None) == 2  # ATTN_JVP_E_NULL
+    assert lib.attn_jvp_clock_sample(ctypes.c_void_p(0x1004), None) == 3  # ATTN_JVP_E_ALIGN
+
+
+def test_shader_clock_from_two_samples():
+    """Per XCD: 100 MHz x (shader counter change) / (real-time counter
+    change), pairing the two samples by XCD number in any order."""
+    before = np.array([[x, 1000 * x, 500, 0] for x in range(8)], dtype=np.int64)
+    after = np.array([[x, 1000 * x + 2000 * (10 + x), 500 + 100 * 10, 0] for x in reversed(range(8))],
+                     dtype=np.int64)
+    mhz = aj.shader_clock_mhz(before.ravel(), after.ravel())
+    assert sorted(mhz) == list(range(8))
+    for x in range(8):
+        assert mhz[x] == pytest.approx(100.0 * 2000 * (10 + x) / 1000)
 
 
 def test_error_strings():

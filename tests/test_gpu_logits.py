@@ -12,11 +12,19 @@ so these cases drive it on purpose:
   growing linearly in j, so that each 32-key tile's scores pass the previous
   tile's by more than 2^8 (after the softmax scale and log2(e)): the
   reference moves on every tile of every row, and p concentrates on the
-  last keys a row sees.  tq and tk have no component along e: otherwise
-  the score tangents would share a large part over those keys, and t_o,
-  the p-weighted spread of ts times v, would live on a cancellation that
-  the bf16 rounding of p~ ts (the MFMA operand of the pages' algorithm)
-  does not resolve, just as for dq below.
+  last keys a row sees.  tq and tk keep their components along e, so tq.k
+  carries a ramp too: over the few keys a row weighs most, the (scaled)
+  score tangents share a part of up to about 6.5 (d = 128, last rows) next
+  to a spread of about 0.1 among them.  t_o is the p-weighted spread of ts
+  times v (eq. 45: the shared part cancels between acc_tsv / l and (r / l) o),
+  so this is the case where rounding p~ ts to bf16 as an MFMA operand would
+  lose t_o; the kernels round p~ (ts - c) with a per-row centre c instead
+  (exact in eq. 45).
+
+A third case isolates that cancellation: every key's tangent shares one
+large component (tk_j = tk0_j + g u for a unit vector u, g = 64 and 1024), so
+the score tangents of row i share sigma g (q_i . u), of order 90 at g = 1024,
+a part that contributes exactly nothing to t_o.
 
 Forward + JVP, the forward without tangents and the backward are compared
 with the fp64 oracle on the same rounded values (bf16 within 1e-2, fp32
@@ -69,7 +77,7 @@ def _dq_rounding_bound(q, k, v, do, lse, desc):
     return float(np.linalg.norm(2.0 ** -9 * scale * (np.abs(ds) @ np.abs(k))))
 
 
-def _inputs(kind, n, d, heads, dtype, seed):
+def _inputs(kind, n, d, heads, dtype, seed, common=0.0):
     rng = np.random.default_rng(seed)
     f = lambda *s: rng.standard_normal(s).astype(np.float32)
     q, k, v = f(heads, n, d), f(heads, n, d), f(heads, n, d)
@@ -77,13 +85,15 @@ def _inputs(kind, n, d, heads, dtype, seed):
     do = f(heads, n, d)
     if kind == "scaled":
         q *= 8.0
-    else:  # ramp: along e = first axis, q . e = 4 and k_j . e = slope * j
+    elif kind == "ramp":  # along e = first axis, q . e = 4 and k_j . e = slope * j
         # per key the score grows by 4 slope / sqrt(d); 9 exp2 units per 32 keys
         slope = 9.0 / 32 / np.log2(np.e) * np.sqrt(d) / 4.0
         q[:, :, 0] = 4.0
         k[:, :, 0] = slope * np.arange(n, dtype=np.float32)
-        tq[:, :, 0] = 0.0
-        tk[:, :, 0] = 0.0
+    else:  # common: every key tangent shares common * u (per head, unit u)
+        u = f(heads, 1, d)
+        u /= np.linalg.norm(u, axis=2, keepdims=True)
+        tk += np.float32(common) * u
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     dev = {name: torch.from_numpy(a[None]).to(tdt) for name, a in
            (("q", q), ("k", k), ("v", v), ("tq", tq), ("tk", tk), ("tv", tv), ("do", do))}
@@ -156,3 +166,27 @@ def test_large_scores_range_list_ramp():
             + f" dq |error| {adq:.3e} (bound {bound:.3e}) lse error / bound {dl:.2f}")
         assert max(errs.values()) < TOL["bf16"], errs
         assert adq < 2.0 * bound and dl < 1.0
+
+
+@pytest.mark.parametrize("common", [64.0, 1024.0])
+@pytest.mark.parametrize("dtype, d", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
+def test_common_key_tangent_cancels(common, dtype, d):
+    """tk_j = tk0_j + g u: the score tangents of row i share sigma g (q_i . u),
+    which drops out of t_o (eq. 45); t_o must still match the oracle."""
+    tpf, f, c, tf = DESC
+    n = tpf * f * (1 + tf)
+    heads = 2
+    x, hv = _inputs("common", n, d, heads, dtype, seed=970 + d, common=common)
+    o, to, lse = aj.masked_attention_jvp(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], DESC, return_lse=True)
+    to_ctz = aj.masked_attention_jvp(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], DESC,
+                                     clean_tangent_zero=True)[1]
+    torch.cuda.synchronize()
+    for h in range(heads):
+        sl = [hv[t][h] for t in ("q", "k", "v", "tq", "tk", "tv")]
+        ro, rto, _ = oracle.masked_attention_jvp_slice(*sl, DESC)
+        _, rto_ctz, _ = oracle.masked_attention_jvp_slice_ctz(*sl, DESC)
+        eo, eto = rel_err(to_f64(o[0, h]), ro), rel_err(to_f64(to[0, h]), rto)
+        eto_ctz = rel_err(to_f64(to_ctz[0, h]), rto_ctz)
+        log(f"[common {common:g} {dtype} d={d} h={h}] rel err o {eo:.2e} to {eto:.2e} to (clean tangent zero) "
+            f"{eto_ctz:.2e}")
+        assert eo < TOL[dtype] and eto < TOL[dtype] and eto_ctz < TOL[dtype]
