@@ -236,6 +236,25 @@ int attn_jvp_bwd_table(const attn_jvp_plan* plan, const void* device_table, cons
                        const void* k, const void* v, const void* o, const float* lse, const void* d_o,
                        void* dq, void* dk, void* dv, float* workspace, void* hip_stream);
 
+/* attn_jvp_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and results (bit for
+ * bit), with the workspace in a fixed device array of the library, 32 MiB per
+ * GPU, which each GPU the library runs on holds until the process ends.  The
+ * call allocates nothing.  Plans with 8 B H N > 32 MiB (B H N > 4,194,304
+ * rows) get ATTN_JVP_E_OVERFLOW; range-list plans get ATTN_JVP_E_INVALID.
+ * All calls on one GPU share that array, which keeps the last call's
+ * contents (no call needs it cleared: the dq kernel writes every entry the
+ * dk/dv kernel reads), so calls whose work overlaps in time on one GPU (two
+ * streams, or two threads) race and give wrong results: order them on one
+ * stream, or use attn_jvp_bwd with separate workspaces.  The first call on a
+ * device looks up that device's array (hipGetSymbolAddress, with the device
+ * current); ATTN_JVP_E_HIP if that fails.  Other arguments and errors as for
+ * attn_jvp_bwd. */
+int attn_jvp_bwd_noalloc(const attn_jvp_plan* plan, const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                         void* hip_stream);
+
 /* Workspace bytes attn_jvp_bwd needs for the plan: 8 B H N. */
 int attn_jvp_bwd_workspace_size(const attn_jvp_plan* plan, size_t* bytes);
 

@@ -110,13 +110,14 @@ def _load():
         lib.attn_jvp_bwd_table.argtypes = [vp] * 13
         lib.attn_jvp_fwd_primal_table.argtypes = [vp] * 8
         lib.attn_jvp_clock_sample.argtypes = [vp, vp]
+        lib.attn_jvp_bwd_noalloc.argtypes = [vp] * 11
         for name in ("attn_jvp_create", "attn_jvp_create_ex", "attn_jvp_fwd", "attn_jvp_destroy",
                      "attn_jvp_plan_info", "attn_jvp_plan_flops", "attn_jvp_launch_order", "attn_jvp_row_ranges",
                      "attn_jvp_tile_map", "attn_jvp_bwd", "attn_jvp_bwd_workspace_size", "attn_jvp_plan_bwd_flops",
                      "attn_jvp_key_ranges", "attn_jvp_plan_bwd_info", "attn_jvp_bwd_launch_order",
                      "attn_jvp_create_ranges", "attn_jvp_plan_table_size", "attn_jvp_plan_table", "attn_jvp_fwd_table",
                      "attn_jvp_fwd_primal", "attn_jvp_bwd_table", "attn_jvp_fwd_primal_table",
-                     "attn_jvp_clock_sample"):
+                     "attn_jvp_clock_sample", "attn_jvp_bwd_noalloc"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -430,11 +431,14 @@ def _bwd_args(plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace):
     for name, t in ts.items():
         _check_tensor(name, t, plan, plan.shape)
     dev = q.device
-    for name, t in list(ts.items()) + [("lse", lse), ("workspace", workspace)]:
+    extra = [("lse", lse)] + ([("workspace", workspace)] if workspace is not None else [])
+    for name, t in list(ts.items()) + extra:
         if not isinstance(t, torch.Tensor) or t.device != dev:
             raise AttnJvpError(f"{name} must be a tensor on q's device ({dev})")
     if lse.dtype != torch.float32 or tuple(lse.shape) != plan.shape[:3] or not lse.is_contiguous():
         raise AttnJvpError("lse must be a contiguous float32 [B, H, N] tensor")
+    if workspace is None:  # attn_jvp_bwd_noalloc: the library's own workspace
+        return [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o, lse, d_o, dq, dk, dv)]
     if workspace.dtype != torch.float32 or not workspace.is_contiguous() \
             or workspace.numel() * 4 < attn_jvp_bwd_workspace_size(plan):
         raise AttnJvpError(f"workspace must be a contiguous float32 tensor of at least "
@@ -454,6 +458,18 @@ def attn_jvp_bwd(plan: Plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace, stream
     with torch.cuda.device(q.device):
         code = _load().attn_jvp_bwd(plan.handle, *ptrs, ctypes.c_void_p(stream.cuda_stream))
     _check(code, "attn_jvp_bwd")
+
+
+def attn_jvp_bwd_noalloc(plan: Plan, q, k, v, o, lse, d_o, dq, dk, dv, stream=None) -> None:
+    """attn_jvp_bwd with the library's fixed device workspace (allocates
+    nothing; calls on one GPU must not overlap in time)."""
+    import torch
+    ptrs = _bwd_args(plan, q, k, v, o, lse, d_o, dq, dk, dv, None)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        code = _load().attn_jvp_bwd_noalloc(plan.handle, *ptrs, ctypes.c_void_p(stream.cuda_stream))
+    _check(code, "attn_jvp_bwd_noalloc")
 
 
 def attn_jvp_bwd_table(plan: Plan, table, q, k, v, o, lse, d_o, dq, dk, dv, workspace, stream=None) -> None:

@@ -12,6 +12,7 @@
 #include <cstring>
 #include <algorithm>
 #include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <utility>
@@ -297,6 +298,31 @@ bool build_columns(int32_t n, const std::vector<int32_t>& g_lo, const std::vecto
 }
 
 }  // namespace
+
+// Workspace of attn_jvp_bwd_noalloc: a file-scope device array, so that
+// that entry point allocates nothing.  Each GPU the library runs on holds its
+// own copy until the process ends.  Host code never uses the array's name as
+// an address (on the host it is a stand-in, not device memory): the device
+// address of each GPU's copy comes from hipGetSymbolAddress, once per device,
+// and is kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t(32) << 20;  // 8 bytes per row: B H N <= 4,194,304
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+// Device address of this device's scratch array (dev is current).
+int scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(ATTN_JVP_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
 
 // Measurement: workgroup w (of kClockSampleGroups, one per XCD when
 // workgroups go to the 8 XCDs round robin) stores its XCD number, the shader
@@ -804,6 +830,28 @@ int attn_jvp_bwd(const attn_jvp_plan* p, const void* q, const void* k, const voi
   if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
   if (p->rs) return fail(ATTN_JVP_E_INVALID, "range-list plans run the backward through attn_jvp_bwd_table");
   return bwd_common(p, nullptr, q, k, v, o, lse, d_o, dq, dk, dv, workspace, hip_stream);
+}
+
+int attn_jvp_bwd_noalloc(const attn_jvp_plan* p, const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* d_o, void* dq, void* dk, void* dv, void* hip_stream) {
+  if (p == nullptr) return fail(ATTN_JVP_E_NULL, "plan is NULL");
+  if (p->rs) return fail(ATTN_JVP_E_INVALID, "range-list plans run the backward through attn_jvp_bwd_table");
+  static const char* names[9] = {"q", "k", "v", "o", "lse", "d_o", "dq", "dk", "dv"};
+  const void* args[9] = {q, k, v, o, lse, d_o, dq, dk, dv};
+  for (int i = 0; i < 9; ++i)
+    if (args[i] == nullptr) return fail(ATTN_JVP_E_NULL, "%s is NULL", names[i]);
+  const size_t need = (size_t)p->batch * p->heads * (size_t)p->g.seq_len * 2 * sizeof(float);
+  if (need > kScratchBytes)
+    return fail(ATTN_JVP_E_OVERFLOW, "attn_jvp_bwd_noalloc needs %zu workspace bytes (8 B H N), above its fixed %zu "
+                "(B H N <= %zu); use attn_jvp_bwd with a caller workspace", need, kScratchBytes,
+                kScratchBytes / 8);
+  int dev;
+  int st = check_device(&dev);
+  if (st != ATTN_JVP_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(dev, &ws);
+  if (st != ATTN_JVP_OK) return st;
+  return bwd_common(p, nullptr, q, k, v, o, lse, d_o, dq, dk, dv, (float*)ws, hip_stream);
 }
 
 int attn_jvp_bwd_table(const attn_jvp_plan* p, const void* device_table, const void* q, const void* k,

@@ -39,7 +39,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert len(names) == 25
+    assert len(names) == 26
     lib = ctypes.CDLL(aj.library_path)
     for name in names:
         assert hasattr(lib, name), name
@@ -51,6 +51,24 @@ def test_clock_sample_argument_errors():
     lib = aj._load()
     assert lib.attn_jvp_clock_sample(None, None) == 2  # ATTN_JVP_E_NULL
     assert lib.attn_jvp_clock_sample(ctypes.c_void_p(0x1004), None) == 3  # ATTN_JVP_E_ALIGN
+
+
+def test_bwd_noalloc_argument_errors():
+    """attn_jvp_bwd_noalloc refuses null pointers, range-list plans and plans
+    whose 8 B H N workspace exceeds its fixed 32 MiB, before any device work
+    (dummy, aligned pointers are never dereferenced)."""
+    lib = aj._load()
+    p = ctypes.c_void_p(1 << 20)
+    plan = aj.attn_jvp_create_ex((1560, 21, 1, 1), 1, 12, 128, aj.ATTN_JVP_BF16, 0.0, 0)
+    assert lib.attn_jvp_bwd_noalloc(None, p, p, p, p, p, p, p, p, p, None) == 2
+    assert lib.attn_jvp_bwd_noalloc(plan.handle, p, p, p, p, None, p, p, p, p, None) == 2
+    assert "lse" in aj.attn_jvp_last_error_detail()
+    big = aj.attn_jvp_create_ex((1560, 21, 1, 1), 1, 65, 128, aj.ATTN_JVP_BF16, 0.0, 0)  # 4,258,800 rows
+    assert lib.attn_jvp_bwd_noalloc(big.handle, p, p, p, p, p, p, p, p, p, None) == 7
+    assert "33554432" in aj.attn_jvp_last_error_detail()
+    n, groups = 64, [(0, 64, [(0, 64)])]
+    rp = aj.attn_jvp_create_ranges(n, groups, 1, 1, 128, aj.ATTN_JVP_BF16)
+    assert lib.attn_jvp_bwd_noalloc(rp.handle, p, p, p, p, p, p, p, p, p, None) == 1
 
 
 def test_shader_clock_from_two_samples():
