@@ -22,6 +22,7 @@ there is no fallback implementation.
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import os
 import threading
@@ -516,20 +517,41 @@ def attn_jvp_fwd_table(plan: Plan, table, q, k, v, tq, tk, tv, o, t_o, lse=None,
     _check(code, "attn_jvp_fwd_table")
 
 
-_plan_cache = {}
+# Plans and range-list tables are cached per mask and shape for the
+# convenience functions below, least recently used first out: a plan holds
+# host memory only; a range-list entry also holds its device table, which
+# each call marks as used on its stream, so that the allocator does not
+# reuse the memory of an evicted table before that stream's work is done.
+PLAN_CACHE_SIZE = 64
+RANGE_CACHE_SIZE = 16
+_plan_cache = collections.OrderedDict()
 _plan_lock = threading.Lock()
+
+
+def _cache_get(cache, key):
+    hit = cache.get(key)
+    if hit is not None:
+        cache.move_to_end(key)
+    return hit
+
+
+def _cache_put(cache, key, value, size):
+    cache[key] = value
+    cache.move_to_end(key)
+    while len(cache) > size:
+        cache.popitem(last=False)
 
 
 def _cached_plan(desc, shape, dtype, scale, flags=0):
     key = (tuple(int(x) for x in desc), tuple(shape), dtype, float(scale or 0.0), int(flags))
     with _plan_lock:
-        p = _plan_cache.get(key)
+        p = _cache_get(_plan_cache, key)
         if p is None:
             b, h, _, d = shape
             p = attn_jvp_create_ex(desc, b, h, d, dtype, scale or 0.0, flags)
             if tuple(p.shape) != tuple(shape):
                 raise AttnJvpError(f"mask {tuple(desc)} gives N={p.seq_len}, tensors have N={shape[2]}")
-            _plan_cache[key] = p
+            _cache_put(_plan_cache, key, p, PLAN_CACHE_SIZE)
         return p
 
 
@@ -573,7 +595,7 @@ def masked_attention_bwd(q, k, v, o, lse, d_o, desc, scale=None, return_workspac
     return (dq, dk, dv, ws) if return_workspace else (dq, dk, dv)
 
 
-_range_cache = {}
+_range_cache = collections.OrderedDict()
 
 
 def _cached_range_plan(q, groups, scale):
@@ -585,11 +607,14 @@ def _cached_range_plan(q, groups, scale):
     key = (tuple((int(lo), int(hi), tuple((int(a), int(z)) for a, z in ivs)) for lo, hi, ivs in groups),
            tuple(q.shape), dtype, float(scale or 0.0), str(q.device))
     with _plan_lock:
-        hit = _range_cache.get(key)
+        hit = _cache_get(_range_cache, key)
         if hit is None:
             plan = attn_jvp_create_ranges(n, groups, b, h, d, dtype, scale or 0.0)
             table = torch.from_numpy(attn_jvp_plan_table(plan)).to(q.device)
-            hit = _range_cache[key] = (plan, table)
+            hit = (plan, table)
+            _cache_put(_range_cache, key, hit, RANGE_CACHE_SIZE)
+    # the table is read by work enqueued on the current stream
+    hit[1].record_stream(torch.cuda.current_stream(q.device))
     return hit
 
 

@@ -336,3 +336,24 @@ def test_primal_argument_errors_before_any_device_call():
     assert lib.attn_jvp_fwd_primal(p.handle, *bad, None, None) == 1
     pr = aj.attn_jvp_create_ranges(16, [(0, 16, [(0, 16)])], 1, 1, 64)
     assert lib.attn_jvp_fwd_primal(pr.handle, *good, None, None) == 1
+
+
+def test_plan_cache_is_bounded_lru():
+    """The convenience functions' plan cache keeps at most PLAN_CACHE_SIZE
+    plans, evicting the least recently used."""
+    import torch
+    saved = dict(aj._plan_cache)
+    aj._plan_cache.clear()
+    try:
+        n = aj.PLAN_CACHE_SIZE
+        first = aj._cached_plan((4, 3, 1, 1), (1, 1, 24, 64), aj.ATTN_JVP_BF16, None)
+        for i in range(n + 5):
+            aj._cached_plan((4, 3, 1, 1), (1, 2 + i, 24, 64), aj.ATTN_JVP_BF16, None)
+            if i == 0:  # a hit moves the first plan to the back
+                assert aj._cached_plan((4, 3, 1, 1), (1, 1, 24, 64), aj.ATTN_JVP_BF16, None) is first
+        assert len(aj._plan_cache) == n
+        keys = list(aj._plan_cache)
+        assert all(k[1][1] >= 2 for k in keys), "the oldest plans are evicted"
+    finally:
+        aj._plan_cache.clear()
+        aj._plan_cache.update(saved)
