@@ -26,7 +26,7 @@
 //   the dP product) and -lse log2(e) of the tile's rows come from the
 //   workspace, staged in LDS with the tile.
 // Both follow the forward kernel's structure: 32-row tiles go HBM -> LDS by
-// DMA into a 4-stage ring (XOR-swizzled rows, zeros past the end), the score
+// DMA into a 6-stage ring (XOR-swizzled rows, zeros past the end), the score
 // products of tile j+1 run under the elementwise work of tile j and the
 // output products of tile j under the exponentials of tile j+1, one MFMA per
 // scheduling slot; whole tiles outside the key (query) ranges are never
@@ -47,10 +47,33 @@ namespace attn_jvp {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kBwdStages = 4;  // LDS ring depth: tiles j .. j+3 resident or in flight
+// The LDS ring.  Step j reads tiles j .. j+2 (tile j+2 only after its
+// mid-step barrier slot) and issues the DMA of tile j+A into the stage of
+// tile j+A-S.  Workgroup barriers sit in every P-th step; the one in step b
+// follows each wave's wait for its shares of tiles up to b+P+1, the tiles
+// read before the next barrier, and a wait for its own LDS reads, so every
+// read of tiles up to b is complete behind it.  Hence
+//   A >= P+2: tile b+P+1 was issued at least one step before barrier b;
+//   S >= A+P: a stage is refilled only after a barrier behind its last read;
+//   S % P == 0: the unrolled steps keep their barrier slots.
+// S = 6 stages of 16 KB (the dk/dv kernel's 1 KB more), A = 4, P = 2: one
+// barrier per two steps.
+constexpr int kBwdStages = 6;
+constexpr int kBwdAhead = 4;
+constexpr int kBwdBarrierEvery = 2;
+static_assert(kBwdAhead >= kBwdBarrierEvery + 2 && kBwdStages >= kBwdAhead + kBwdBarrierEvery &&
+                  kBwdStages % kBwdBarrierEvery == 0 && kBwdStages % 2 == 0,
+              "ring depth, prefetch distance and barrier period");
 
 template <int V>
 using IC = std::integral_constant<int, V>;
+
+// f(IC<S>{}) for S = 0, 1, .. N-1 while it returns true; false if one did.
+template <int S, int N, class F>
+__device__ __forceinline__ bool unrolled_while(F&& f) {
+  if constexpr (S == N) return true;
+  else return f(IC<S>{}) && unrolled_while<S + 1, N>(f);
+}
 
 // Per-lane addressing shared by the two bf16 kernels.
 template <int D, int NW>
@@ -185,12 +208,9 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   constexpr int BR = NW * 32;   // query rows per block
   constexpr int KS = TG::KS, DC = TG::DC, NG = TG::NG, TILE = TG::TILE, LOADS = TG::LOADS;
   constexpr int LPT = 2 * LOADS;  // DMA instructions per wave and tile: K, V
-  constexpr int STAGES = kBwdStages;
+  constexpr int STAGES = kBwdStages, AHEAD = kBwdAhead, BAR = kBwdBarrierEvery;
 
-  __shared__ __attribute__((aligned(1024))) uint16_t ring0[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t ring1[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t ring2[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t ring3[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[STAGES][2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -286,13 +306,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) negd[i] = ndelta;
 
-  auto stage = [&](auto st) -> uint16_t* {
-    constexpr int S = decltype(st)::value;
-    if constexpr (S == 0) return ring0;
-    else if constexpr (S == 1) return ring1;
-    else if constexpr (S == 2) return ring2;
-    else return ring3;
-  };
+  auto stage = [&](auto st) -> uint16_t* { return ring[decltype(st)::value]; };
   int dma_voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) dma_voff[i] = TG::dma_voff(wave, lane, i);
@@ -334,10 +348,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
       wlast = row_ranges(g, wb - 1);
     }
   }
-  auto tile_whole = [&](int t) {
-    const int k0 = span_tile(sp, t) * BC;
-    return run_covers(wfirst, wlast, k0, k0 + BC);
-  };
+  // as step ranges: tiles inside [wlast.lo1, wfirst.hi1) or [wlast.lo2,
+  // wfirst.hi2), the keys every valid row of the wave sees
+  const StepRange w1 = span_steps_in(sp, first_whole_tile(wlast.lo1, BC), end_whole_tile(wfirst.hi1, BC));
+  const StepRange w2 = span_steps_in(sp, first_whole_tile(wlast.lo2, BC), end_whole_tile(wfirst.hi2, BC));
+  auto tile_whole = [&](int t) { return in_steps(w1, t) || in_steps(w2, t); };
   // the partial-tile mask of scores of the tile at key k0
   auto mask_tile = [&](f32x16& S, int k0) {
     if constexpr (TABLE) mask_scores_iv(S, k0, h, riv, max_iv, p.tb_iv);
@@ -359,15 +374,14 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   // packs, and all transposed K reads of tile j.  Phase 2: dQ^T += K^T dS^T
   // of tile j under the mask (partial tiles) and exponentials of tile j+1.
   // Ring: step j reads K, V of tile j+1 and K^T of tile j, and issues the DMA
-  // of tile j+3 into the stage of tile j-1; the barrier opens phase 2 (every
-  // read of tile j's stage is then issued), after each wave's share of tile
-  // j+2 has landed; the first K, V reads of tile j+2 follow it, seven MFMAs
-  // ahead of their use.
+  // of tile j+AHEAD; phase 2 opens with the barrier slot (every read of tile
+  // j's stage is then issued), after which come the first K, V reads of tile
+  // j+2, seven MFMAs ahead of their use.
   auto step = [&](auto st, int j, int t_end, f32x16& P, f32x16& DP, f32x16& Sn, f32x16& DPn) {
     constexpr int ST = decltype(st)::value;
     using NX = IC<(ST + 1) % STAGES>;
     using N2 = IC<(ST + 2) % STAGES>;
-    using AH = IC<(ST + 3) % STAGES>;
+    using AH = IC<(ST + AHEAD) % STAGES>;
 #pragma unroll
     for (int c = 0; c < DC; ++c) keep_in_acc(accQ[c]);
     const uint16_t* nx = stage(NX{});
@@ -381,12 +395,12 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
     // range-list plans: this step's DMA tile and the next tile's entry, read once
     int dma_tile = 0, next_e = 0;
     if constexpr (TABLE) {
-      dma_tile = entry(j + 3) & 0xffffff;
+      dma_tile = entry(j + AHEAD) & 0xffffff;
       next_e = entry(j + 1);
     }
     auto dma = [&](int s) {
 #pragma unroll
-      for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q) issue_part(stage(AH{}), j + 3, q, t_end, dma_tile);
+      for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q) issue_part(stage(AH{}), j + AHEAD, q, t_end, dma_tile);
     };
 
     constexpr int PAIRS = 8 / KS;  // dS element pairs per k-step
@@ -420,10 +434,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
       } else {
         if (gidx == 0 && !tile_whole(j + 1)) mask_tile(Sn, span_tile(sp, j + 1) * BC);  // rare
       }
-      if (gidx == 0) {
-        // every read of tile j's stage is issued; tile j+2 has landed here
+      if (gidx == 0 && ST % BAR == 0) {
+        // tiles up to j+BAR+1 have landed; reads up to tile j are complete
         wait_lgkmcnt<0>();
-        wait_vmcnt<LPT>();
+        wait_vmcnt<(AHEAD - BAR - 1) * LPT>();
         barrier_nofence();
       }
 #pragma unroll
@@ -440,14 +454,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   };
 
   auto first_tile = [&](int t_begin, int t_end) {
-    issue(ring0, t_begin, t_end);
-    issue(ring1, t_begin + 1, t_end);
-    issue(ring2, t_begin + 2, t_end);
-    wait_vmcnt<LPT>();  // first two tiles
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) issue(ring[i], t_begin + i, t_end);
+    wait_vmcnt<(AHEAD - 2) * LPT>();  // first two tiles
     barrier_nofence();
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kvread(ring0, s);
+      kvread(ring[0], s);
       if (s == 0) {
         mfma_v_first_ba(SA, kf[s], qf[s]);
         mfma_v_init_ba(DA, vf[s], dof[s], negd);
@@ -467,20 +480,20 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) SA[i] = exp_elem(SA[i]);
-    kvread(ring1, 0);
-    kvread(ring1, 1);
+    kvread(ring[1], 0);
+    kvread(ring[1], 1);
   };
 
   if (ntiles > 0) {
     first_tile(0, ntiles);
-    for (int j = 0; j < ntiles; j += 4) {
-      step(IC<0>{}, j, ntiles, SA, DA, SB, DB);
-      if (j + 1 >= ntiles) break;
-      step(IC<1>{}, j + 1, ntiles, SB, DB, SA, DA);
-      if (j + 2 >= ntiles) break;
-      step(IC<2>{}, j + 2, ntiles, SA, DA, SB, DB);
-      if (j + 3 >= ntiles) break;
-      step(IC<3>{}, j + 3, ntiles, SB, DB, SA, DA);
+    for (int j = 0; j < ntiles; j += STAGES) {
+      const bool more = unrolled_while<0, STAGES>([&](auto st) {
+        constexpr int S = decltype(st)::value;
+        if constexpr (S % 2 == 0) step(st, j + S, ntiles, SA, DA, SB, DB);
+        else step(st, j + S, ntiles, SB, DB, SA, DA);
+        return j + S + 1 < ntiles;
+      });
+      if (!more) break;
     }
     // DMAs past the last tile and the last K, V reads may be in flight
     wait_vmcnt<0>();
@@ -520,17 +533,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
   constexpr int BK = NW * 32;   // keys per block
   constexpr int KS = TG::KS, DC = TG::DC, NG = TG::NG, TILE = TG::TILE, LOADS = TG::LOADS;
   constexpr int LPT = 2 * LOADS + 1;  // DMA instructions per wave and tile: Q, dO, row terms
-  constexpr int STAGES = kBwdStages;
+  constexpr int STAGES = kBwdStages, AHEAD = kBwdAhead, BAR = kBwdBarrierEvery;
 
-  __shared__ __attribute__((aligned(1024))) uint16_t ring0[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t ring1[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t ring2[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t ring3[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[STAGES][2 * TILE];
   // per stage and wave: -delta of the tile's 32 rows, then their -lse log2(e)
-  __shared__ __attribute__((aligned(256))) float rows0[NW * 64];
-  __shared__ __attribute__((aligned(256))) float rows1[NW * 64];
-  __shared__ __attribute__((aligned(256))) float rows2[NW * 64];
-  __shared__ __attribute__((aligned(256))) float rows3[NW * 64];
+  __shared__ __attribute__((aligned(256))) float rows[STAGES][NW * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -610,20 +617,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
     }
   }
 
-  auto stage = [&](auto st) -> uint16_t* {
-    constexpr int S = decltype(st)::value;
-    if constexpr (S == 0) return ring0;
-    else if constexpr (S == 1) return ring1;
-    else if constexpr (S == 2) return ring2;
-    else return ring3;
-  };
-  auto rstage = [&](auto st) -> float* {
-    constexpr int S = decltype(st)::value;
-    if constexpr (S == 0) return rows0 + wave * 64;
-    else if constexpr (S == 1) return rows1 + wave * 64;
-    else if constexpr (S == 2) return rows2 + wave * 64;
-    else return rows3 + wave * 64;
-  };
+  auto stage = [&](auto st) -> uint16_t* { return ring[decltype(st)::value]; };
+  auto rstage = [&](auto st) -> float* { return rows[decltype(st)::value] + wave * 64; };
   int dma_voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) dma_voff[i] = TG::dma_voff(wave, lane, i);
@@ -669,10 +664,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
       wlast = col_ranges(g, wb - 1);
     }
   }
-  auto tile_whole = [&](int t) {
-    const int q0 = span_tile(sp, t) * BQ;
-    return run_covers(wfirst, wlast, q0, q0 + BQ);
-  };
+  // as step ranges: query tiles inside [wlast.lo1, wfirst.hi1) or
+  // [wlast.lo2, wfirst.hi2), the rows that see every valid key of the wave
+  const StepRange w1 = span_steps_in(sp, first_whole_tile(wlast.lo1, BQ), end_whole_tile(wfirst.hi1, BQ));
+  const StepRange w2 = span_steps_in(sp, first_whole_tile(wlast.lo2, BQ), end_whole_tile(wfirst.hi2, BQ));
+  auto tile_whole = [&](int t) { return in_steps(w1, t) || in_steps(w2, t); };
   // the partial-tile mask of scores of the query tile at row q0
   auto mask_tile = [&](f32x16& X, int q0) {
     if constexpr (TABLE) mask_scores_iv(X, q0, h, civ, max_iv, p.cb_iv);
@@ -707,7 +703,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
     constexpr int ST = decltype(st)::value;
     using NX = IC<(ST + 1) % STAGES>;
     using N2 = IC<(ST + 2) % STAGES>;
-    using AH = IC<(ST + 3) % STAGES>;
+    using AH = IC<(ST + AHEAD) % STAGES>;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       keep_in_acc(accV[c]);
@@ -730,13 +726,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
     // range-list plans: this step's DMA tile and the next tile's entry, read once
     int dma_tile = 0, next_e = 0;
     if constexpr (TABLE) {
-      dma_tile = entry(j + 3) & 0xffffff;
+      dma_tile = entry(j + AHEAD) & 0xffffff;
       next_e = entry(j + 1);
     }
     auto dma = [&](int s) {
 #pragma unroll
       for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q)
-        issue_part(stage(AH{}), rstage(AH{}), j + 3, q, t_end, dma_tile);
+        issue_part(stage(AH{}), rstage(AH{}), j + AHEAD, q, t_end, dma_tile);
     };
 
     constexpr int PAIRS = 8 / KS;  // dS element pairs per k-step
@@ -782,9 +778,9 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
           if (u == 0 && !tile_whole(j + 1)) mask_tile(Xn, span_tile(sp, j + 1) * BQ);  // rare
         }
         if (sl == 0 && gidx + 3 < NG) trread(gidx + 3);
-        if (u == UB) {
+        if (u == UB && ST % BAR == 0) {
           wait_lgkmcnt<0>();
-          wait_vmcnt<LPT>();
+          wait_vmcnt<(AHEAD - BAR - 1) * LPT>();
           barrier_nofence();
         }
 #pragma unroll
@@ -812,10 +808,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
   };
 
   auto first_tile = [&](int t_begin, int t_end) {
-    issue(IC<0>{}, t_begin, t_end);
-    issue(IC<1>{}, t_begin + 1, t_end);
-    issue(IC<2>{}, t_begin + 2, t_end);
-    wait_vmcnt<LPT>();  // first two tiles
+    unrolled_while<0, AHEAD>([&](auto st) {
+      issue(st, t_begin + decltype(st)::value, t_end);
+      return true;
+    });
+    wait_vmcnt<(AHEAD - 2) * LPT>();  // first two tiles
     barrier_nofence();
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
@@ -824,7 +821,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      qdread(ring0, s);
+      qdread(ring[0], s);
       if (s == 0) {
         mfma_v_first_ba(XA, qf[s], kf[s]);
         mfma_v_init_ba(DA, dof[s], vf[s], *(const f32x16*)ndl);
@@ -845,22 +842,22 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) XA[i] = __builtin_amdgcn_exp2f(fmaf(XA[i], sl2, nlv[i]));
-    qdread(ring1, 0);
-    qdread(ring1, 1);
+    qdread(ring[1], 0);
+    qdread(ring[1], 1);
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) rows_read(rstage(IC<1>{}), 0, q4, ndl);
   };
 
   if (ntiles > 0) {
     first_tile(0, ntiles);
-    for (int j = 0; j < ntiles; j += 4) {
-      step(IC<0>{}, j, ntiles, XA, DA, XB, DB);
-      if (j + 1 >= ntiles) break;
-      step(IC<1>{}, j + 1, ntiles, XB, DB, XA, DA);
-      if (j + 2 >= ntiles) break;
-      step(IC<2>{}, j + 2, ntiles, XA, DA, XB, DB);
-      if (j + 3 >= ntiles) break;
-      step(IC<3>{}, j + 3, ntiles, XB, DB, XA, DA);
+    for (int j = 0; j < ntiles; j += STAGES) {
+      const bool more = unrolled_while<0, STAGES>([&](auto st) {
+        constexpr int S = decltype(st)::value;
+        if constexpr (S % 2 == 0) step(st, j + S, ntiles, XA, DA, XB, DB);
+        else step(st, j + S, ntiles, XB, DB, XA, DA);
+        return j + S + 1 < ntiles;
+      });
+      if (!more) break;
     }
     wait_vmcnt<0>();
     wait_lgkmcnt<0>();

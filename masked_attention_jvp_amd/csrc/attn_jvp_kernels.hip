@@ -327,15 +327,15 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   // grows with the row; range 2 slides with the row's chunk) a tile is whole
   // for all of them iff it lies in [0, f1) or in [g0, g1): f1 and g1 from the
   // wave's first valid row, g0 from its last.  Scalar values.
-  int f1 = 1 << 30, g0 = 0, g1 = 1 << 30;
+  // In step indices: the tiles lie in [0, f1) or [g0, g1) at steps w1, w2.
+  StepRange w1{0, 1 << 30}, w2{0, 0};
   if constexpr (!TABLE) {
     const int wa = r0 + wave * 32;
     const int wb = wa + 32 < r1 ? wa + 32 : r1;
     if (wa < wb) {
       const Ranges first = row_ranges(g, wa), last = row_ranges(g, wb - 1);
-      f1 = first.hi1;
-      g0 = last.lo2;
-      g1 = first.hi2;
+      w1 = span_steps_in(sp, 0, end_whole_tile(first.hi1, BC));
+      w2 = span_steps_in(sp, first_whole_tile(last.lo2, BC), end_whole_tile(first.hi2, BC));
     }
   }
 
@@ -349,8 +349,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       const int e = __builtin_amdgcn_readfirstlane(ent[t < ntiles ? t : ntiles - 1]);
       return ((e >> (24 + wave)) & 1) != 0;
     } else {
-      const int k0 = span_tile(sp, t) * BC;
-      return k0 + BC <= f1 || (k0 >= g0 && k0 + BC <= g1);
+      return in_steps(w1, t) || in_steps(w2, t);
     }
   };
   auto mask_tile = [&](int t, f32x16& S, f32x16& TS) {

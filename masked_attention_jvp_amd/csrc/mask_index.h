@@ -244,4 +244,30 @@ AJ_HD int32_t span_tile(const TileSpans& s, int32_t it) {
   return it < na ? s.a0 + it : s.b0 + (it - na);
 }
 
+// Streamed tiles with index below x (the span's tiles increase with the
+// step index, range a before range b).
+AJ_HD int32_t span_count_below(const TileSpans& s, int32_t x) {
+  const int32_t na = s.a1 - s.a0, nb = s.b1 - s.b0;
+  const int32_t ca = x - s.a0 < 0 ? 0 : (x - s.a0 > na ? na : x - s.a0);
+  const int32_t cb = x - s.b0 < 0 ? 0 : (x - s.b0 > nb ? nb : x - s.b0);
+  return ca + cb;
+}
+
+// Steps t of a span whose tile index lies in [lo, hi): t in the set iff
+// (unsigned)(t - first) < (unsigned)count (count 0: no step).  Since the
+// span's tiles increase with t, such steps are consecutive.
+struct StepRange {
+  int32_t first, count;
+};
+AJ_HD StepRange span_steps_in(const TileSpans& s, int32_t lo, int32_t hi) {
+  const int32_t a = span_count_below(s, lo), b = span_count_below(s, hi);
+  return StepRange{a, b > a ? b - a : 0};
+}
+AJ_HD bool in_steps(const StepRange& r, int32_t t) { return (uint32_t)(t - r.first) < (uint32_t)r.count; }
+
+// Tiles of `block` keys (or rows) that lie whole inside [x0, x1): indices
+// ceil(x0 / block) .. floor(x1 / block) - 1 (x0, x1 >= 0; empty if x1 <= x0).
+AJ_HD int32_t first_whole_tile(int32_t x0, int32_t block) { return cdiv(x0, block); }
+AJ_HD int32_t end_whole_tile(int32_t x1, int32_t block) { return x1 / block; }
+
 }  // namespace attn_jvp
