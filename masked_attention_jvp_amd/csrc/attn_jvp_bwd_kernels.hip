@@ -753,7 +753,11 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
       if (s == 1) hold(*(const f32x16*)ndl);  // two MFMAs past its read as the start of dP
 #pragma unroll
       for (int gq = s * NG / KS; gq < (s + 1) * NG / KS; ++gq) trread(gq);
-      if (s == KS - 1) rows_read(rstage(NX{}), 1, 0, nlv);
+      // -lse log2(e) of tile j+1's rows for phase 2's exponentials: read here,
+      // where the stage is resident and the reads have a phase to land
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        if (s == KS - 4 + q4) rows_read(rstage(NX{}), 1, q4, nlv);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -787,12 +791,6 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
             Xn[k] = __builtin_amdgcn_exp2f(fmaf(Xn[k], sl2, nlv[k]));
             pin(Xn[k]);
           }
-        }
-        // -lse log2(e) quads of tile j+1, three slots before their first use
-#pragma unroll
-        for (int q4 = 1; q4 < 4; ++q4) {
-          const int first = (4 * q4) * 2 * NG / 16;
-          if (u == (first >= 3 ? first - 3 : 0)) rows_read(rstage(NX{}), 1, q4, nlv);
         }
         if (u == UB + 1) {
           qdread(stage(N2{}), 0);
