@@ -11,6 +11,14 @@ eqs. 42-45), normwise relative error below 1e-2 on o and t_o, lse within
 same on both teacher-forcing layouts, against the oracle's definition with
 the clean tangents zeroed.
 
+The backward (dq, dk, dv; section 3.2.1: the student's FlashAttention-2
+based masked attention trains through it) gets the same treatment at the
+four workloads: o and lse from the forward, then the backward through the
+plan entry points bench.py --backward times, with dq, dk, dv and the
+workspace prefilled with NaN and required finite everywhere, and the first
+and last (b, h) slice against the oracle's backward over all rows and keys
+(normwise 1e-2 on dq, dk, dv and delta).
+
 The oracle takes about 8 s per slice of 65520 tokens on a 16-thread host.
 """
 import numpy as np
@@ -19,8 +27,9 @@ import torch
 
 import oracle
 import masked_attention_jvp_amd as aj
+import seeded_inputs as si
 from seeded_inputs import WORKLOADS, TENSORS
-from gpu_util import log, device_inputs, host_values, to_f64, rel_err
+from gpu_util import log, device_inputs, host_values, to_device, to_f64, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -68,3 +77,36 @@ def test_workload_whole_slices(cfg):
 @pytest.mark.parametrize("cfg", [3, 4])
 def test_workload_whole_slices_clean_tangent_zero(cfg):
     _whole_slices(WORKLOADS[cfg], aj.ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO, oracle.masked_attention_jvp_slice_ctz)
+
+
+def _whole_slices_bwd(w):
+    log(f"[whole slices, backward] {w.name} B={w.batch} H={w.heads}")
+    x = device_inputs(w)
+    x["do"] = to_device(w, si.full_tensor_bits(w, "do"))
+    plan = aj.attn_jvp_create_ex(w.desc, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16, 0.0, 0)
+    o = torch.empty_like(x["q"])
+    to = torch.empty_like(x["q"])
+    lse = torch.empty(w.shape[:3], dtype=torch.float32, device=x["q"].device)
+    aj.attn_jvp_fwd(plan, *(x[t] for t in TENSORS), o, to, lse)
+    del to, x["tq"], x["tk"], x["tv"]
+    nan = float("nan")
+    dq, dk, dv = (torch.full_like(x["q"], nan) for _ in range(3))
+    ws = torch.full((aj.attn_jvp_bwd_workspace_size(plan) // 4,), nan, dtype=torch.float32, device=x["q"].device)
+    aj.attn_jvp_bwd(plan, x["q"], x["k"], x["v"], o, lse, x["do"], dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv), ("workspace", ws)):
+        assert torch.isfinite(t).all().item(), f"{w.name}: {name} has elements not written (NaN) or not finite"
+    ws = ws.view(w.batch, w.heads, 2, w.seq_len)
+    for b, h in sorted({(0, 0), (w.batch - 1, w.heads - 1)}):
+        q, k, v = host_values(w, b, h)[:3]
+        rq, rk, rv, rd = oracle.masked_attention_bwd_slice(q, k, v, si.slice_values(w, "do", b, h), w.desc)
+        e = [rel_err(to_f64(t[b, h]), r) for t, r in ((dq, rq), (dk, rk), (dv, rv))]
+        ed = rel_err(-to_f64(ws[b, h, 0]), rd)
+        log(f"    (b={b}, h={h}) all {w.seq_len} rows and keys: rel err dq={e[0]:.3e} dk={e[1]:.3e} "
+            f"dv={e[2]:.3e} delta={ed:.3e}")
+        assert max(e) < TOL and ed < TOL
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_workload_whole_slices_backward(cfg):
+    _whole_slices_bwd(WORKLOADS[cfg])
