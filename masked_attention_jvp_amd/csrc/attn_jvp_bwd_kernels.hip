@@ -763,8 +763,9 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
 
     // phase 2: 2 NG slots; the last score product is two MFMAs back at the
     // first one.  The transposed reads were all issued in phase 1 (under
-    // the exponentials here they left too few issue slots); the barrier slot
-    // comes four slots before the end and the first reads of tile j+2 three.
+    // the exponentials here they left too few issue slots).  The barrier
+    // slot is 2 NG - 6; the first reads of tile j+2 follow it, in the next
+    // two slots.
     constexpr int UB = 2 * (NG - 3);  // slot of the barrier
 #pragma unroll
     for (int gidx = 0; gidx < NG; ++gidx) {
