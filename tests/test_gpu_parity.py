@@ -162,7 +162,7 @@ def test_run_to_run_bitwise_determinism(geom):
                                v.view(torch.int16) if v.dtype == torch.bfloat16 else v)
 
 
-@pytest.mark.parametrize("cfg", [3])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_value_direction_gives_output_exactly(cfg):
     # tangent (0, 0, v): the scores do not move, so t_o = o bit for bit
     w = WORKLOADS[cfg]
@@ -190,7 +190,7 @@ def test_tangent_linearity_is_exact(cfg):
     assert torch.equal((to1 * 2).view(torch.int16), to2.view(torch.int16))
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_query_and_key_tangents_are_symmetric(cfg):
     # the directions (q, 0, 0) and (0, k, 0) give the same score tangent
     # sigma q.k for every pair, accumulated in the same order (the other
