@@ -174,6 +174,21 @@ def test_value_direction_gives_output_exactly(cfg):
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_value_tangent_alone_gives_the_output_of_tv(cfg):
+    # tangent (0, 0, tv): the scores do not move, so t_o = sum_j p_ij tv_j,
+    # which is o with v replaced by tv -- the same bf16 packs of p~ meet tV
+    # in the same order as they meet V, so the two agree bit for bit
+    w = WORKLOADS[cfg]
+    x = device_inputs(w)
+    z = torch.zeros_like(x["q"])
+    _, to = aj.masked_attention_jvp(x["q"], x["k"], x["v"], z, z, x["tv"], w.desc)
+    o_tv, _ = aj.masked_attention_jvp(x["q"], x["k"], x["tv"], z, z, z, w.desc)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(to).item() > 0
+    assert torch.equal(to.view(torch.int16), o_tv.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_tangent_linearity_is_exact(cfg):
     # every step of the tangent is linear in (tq, tk, tv), and scaling by 2
     # commutes with each rounding (fp32 sums, the bf16 packs of p~ ts and the
