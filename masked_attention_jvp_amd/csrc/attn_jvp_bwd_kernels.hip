@@ -371,7 +371,9 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   f32x16 SA, DA, SB, DB;
 
   // Step j.  Phase 1: S^T, dP^T of tile j+1 under dS of tile j and its
-  // packs, and all transposed K reads of tile j.  Phase 2: dQ^T += K^T dS^T
+  // packs, and all transposed K reads of tile j; each k-step's DMA share
+  // follows its dP^T MFMA, next to the transposed reads, so that it does not
+  // pile onto the fragment reads and packs after the score MFMA.  Phase 2: dQ^T += K^T dS^T
   // of tile j under the mask (partial tiles) and exponentials of tile j+1.
   // (Half of the exponentials moved to the next phase 1 was 0.9 % slower.)
   // Ring: step j reads K, V of tile j+1 and K^T of tile j, and issues the DMA
@@ -411,13 +413,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
       else mfma_v_acc_ba(Sn, kf[s], qf[s]);
       __builtin_amdgcn_sched_barrier(0);
       if (s + 2 < KS) kvread(nx, s + 2);
-      dma(s);
 #pragma unroll
       for (int u = 0; u < PAIRS; ++u) ds_pair(2 * (s * PAIRS + u));
       __builtin_amdgcn_sched_barrier(0);
       if (s == 0) mfma_v_init_ba(DPn, vf[s], dof[s], negd);
       else mfma_v_acc_ba(DPn, vf[s], dof[s]);
       __builtin_amdgcn_sched_barrier(0);
+      dma(s);
 #pragma unroll
       for (int gq = 0; gq < NG; ++gq)
         if (gq * KS / NG == s) ktf[gq] = TG::tr_frag(cur, lane, gq);
@@ -698,8 +700,9 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
 
   // Step j.  Phase 1: X, dP of tile j+1 under dS of tile j and the packs of
   // P and dS.  Phase 2: dV^T += dO^T P and dK^T += Q^T dS of tile j under
-  // the mask (partial tiles) and exponentials of tile j+1.  Ring use as in
-  // the dq kernel, with the rows' terms in the same stage.
+  // the mask (partial tiles) and exponentials of tile j+1.  Ring use and
+  // the DMA's place after the dP MFMA as in the dq kernel, with the rows'
+  // terms in the same stage.
   auto step = [&](auto st, int j, int t_end, f32x16& P, f32x16& DP, f32x16& Xn, f32x16& DPn) {
     constexpr int ST = decltype(st)::value;
     using NX = IC<(ST + 1) % STAGES>;
@@ -743,13 +746,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
       else mfma_v_acc_ba(Xn, qf[s], kf[s]);
       __builtin_amdgcn_sched_barrier(0);
       if (s + 2 < KS) qdread(nx, s + 2);
-      dma(s);
 #pragma unroll
       for (int u = 0; u < PAIRS; ++u) ds_pair(2 * (s * PAIRS + u));
       __builtin_amdgcn_sched_barrier(0);
       if (s == 0) mfma_v_init_ba(DPn, dof[s], vf[s], *(const f32x16*)ndl);
       else mfma_v_acc_ba(DPn, dof[s], vf[s]);
       __builtin_amdgcn_sched_barrier(0);
+      dma(s);
       if (s == 1) hold(*(const f32x16*)ndl);  // two MFMAs past its read as the start of dP
 #pragma unroll
       for (int gq = s * NG / KS; gq < (s + 1) * NG / KS; ++gq) trread(gq);
