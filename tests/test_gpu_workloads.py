@@ -170,3 +170,35 @@ def test_range_workload_whole_slices_backward():
         log(f"    (b={b}, h={h}) all {w.seq_len} rows and keys: rel err dq={e[0]:.3e} dk={e[1]:.3e} "
             f"dv={e[2]:.3e} delta={ed:.3e}")
         assert max(e) < TOL and ed < TOL
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def test_full_workload_forward_and_backward_are_deterministic():
+    # No atomics and fixed schedules: repeated calls at the full size, where
+    # thousands of workgroups stream long tile runs through the DMA ring
+    # (the backward with one workgroup barrier per two steps), give the same
+    # bits every time.
+    w = WORKLOADS[3]
+    log(f"[full-size determinism] {w.name}")
+    x = device_inputs(w)
+    x["do"] = to_device(w, si.full_tensor_bits(w, "do"))
+    plan = aj.attn_jvp_create_ex(w.desc, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16, 0.0, 0)
+    dev = x["q"].device
+    fwd_ref = bwd_ref = None
+    for it in range(5):
+        o, to = torch.empty_like(x["q"]), torch.empty_like(x["q"])
+        lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+        aj.attn_jvp_fwd(plan, *(x[t] for t in TENSORS), o, to, lse)
+        dq, dk, dv = (torch.empty_like(x["q"]) for _ in range(3))
+        ws = torch.empty(aj.attn_jvp_bwd_workspace_size(plan) // 4, dtype=torch.float32, device=dev)
+        aj.attn_jvp_bwd(plan, x["q"], x["k"], x["v"], o, lse, x["do"], dq, dk, dv, ws)
+        torch.cuda.synchronize()
+        fwd, bwd = (o, to, lse), (dq, dk, dv, ws)
+        if fwd_ref is None:
+            fwd_ref, bwd_ref = fwd, bwd
+            continue
+        for a, b in zip(fwd_ref + bwd_ref, fwd + bwd):
+            assert torch.equal(_bits(a), _bits(b)), f"call {it} differs from call 0"
