@@ -249,6 +249,16 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
     ent = ent_buf;
   }
   auto entry = [&](int t) { return __builtin_amdgcn_readfirstlane(ent[t < ntiles ? t : ntiles - 1]); };
+  // Range-list plans: the raw entries a step needs (its DMA tile's and the
+  // next tile's) are read from LDS one step ahead, so that the step's top
+  // takes them without waiting for an LDS read.
+  int pf_dma = 0, pf_next = 0;
+  auto prefetch_entries = [&](int j) {
+    if constexpr (TABLE) {
+      pf_dma = ent[j + kBwdAhead < ntiles ? j + kBwdAhead : ntiles - 1];
+      pf_next = ent[j + 1 < ntiles ? j + 1 : ntiles - 1];
+    }
+  };
 
   const size_t base = (size_t)bh * (size_t)N * D;
   const int slice_bytes = N * D * 2;
@@ -395,11 +405,12 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
       DS[jj >> 3][(jj & 7) >> 1] = pack_bf16(P[jj] * DP[jj], P[jj + 1] * DP[jj + 1]);
       pin(DS[jj >> 3][(jj & 7) >> 1]);
     };
-    // range-list plans: this step's DMA tile and the next tile's entry, read once
+    // range-list plans: this step's DMA tile and the next tile's entry,
+    // prefetched by the previous step
     int dma_tile = 0, next_e = 0;
     if constexpr (TABLE) {
-      dma_tile = entry(j + AHEAD) & 0xffffff;
-      next_e = entry(j + 1);
+      dma_tile = __builtin_amdgcn_readfirstlane(pf_dma) & 0xffffff;
+      next_e = __builtin_amdgcn_readfirstlane(pf_next);
     }
     auto dma = [&](int s) {
 #pragma unroll
@@ -412,6 +423,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
       if (s == 0) mfma_v_first_ba(Sn, kf[s], qf[s]);
       else mfma_v_acc_ba(Sn, kf[s], qf[s]);
       __builtin_amdgcn_sched_barrier(0);
+      if (s == 0) prefetch_entries(j + 1);
       if (s + 2 < KS) kvread(nx, s + 2);
 #pragma unroll
       for (int u = 0; u < PAIRS; ++u) ds_pair(2 * (s * PAIRS + u));
@@ -489,6 +501,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
 
   if (ntiles > 0) {
     first_tile(0, ntiles);
+    prefetch_entries(0);
     for (int j = 0; j < ntiles; j += STAGES) {
       const bool more = unrolled_while<0, STAGES>([&](auto st) {
         constexpr int S = decltype(st)::value;
@@ -579,6 +592,16 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
     ent = ent_buf;
   }
   auto entry = [&](int t) { return __builtin_amdgcn_readfirstlane(ent[t < ntiles ? t : ntiles - 1]); };
+  // Range-list plans: the raw entries a step needs (its DMA tile's and the
+  // next tile's) are read from LDS one step ahead, so that the step's top
+  // takes them without waiting for an LDS read.
+  int pf_dma = 0, pf_next = 0;
+  auto prefetch_entries = [&](int j) {
+    if constexpr (TABLE) {
+      pf_dma = ent[j + kBwdAhead < ntiles ? j + kBwdAhead : ntiles - 1];
+      pf_next = ent[j + 1 < ntiles ? j + 1 : ntiles - 1];
+    }
+  };
 
   const size_t base = (size_t)bh * (size_t)N * D;
   const int slice_bytes = N * D * 2;
@@ -727,11 +750,12 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
       doT[gidx] = TG::tr_frag(cur + TILE, lane, gidx);
       qT[gidx] = TG::tr_frag(cur, lane, gidx);
     };
-    // range-list plans: this step's DMA tile and the next tile's entry, read once
+    // range-list plans: this step's DMA tile and the next tile's entry,
+    // prefetched by the previous step
     int dma_tile = 0, next_e = 0;
     if constexpr (TABLE) {
-      dma_tile = entry(j + AHEAD) & 0xffffff;
-      next_e = entry(j + 1);
+      dma_tile = __builtin_amdgcn_readfirstlane(pf_dma) & 0xffffff;
+      next_e = __builtin_amdgcn_readfirstlane(pf_next);
     }
     auto dma = [&](int s) {
 #pragma unroll
@@ -745,6 +769,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
       if (s == 0) mfma_v_first_ba(Xn, qf[s], kf[s]);
       else mfma_v_acc_ba(Xn, qf[s], kf[s]);
       __builtin_amdgcn_sched_barrier(0);
+      if (s == 0) prefetch_entries(j + 1);
       if (s + 2 < KS) qdread(nx, s + 2);
 #pragma unroll
       for (int u = 0; u < PAIRS; ++u) ds_pair(2 * (s * PAIRS + u));
@@ -850,6 +875,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
 
   if (ntiles > 0) {
     first_tile(0, ntiles);
+    prefetch_entries(0);
     for (int j = 0; j < ntiles; j += STAGES) {
       const bool more = unrolled_while<0, STAGES>([&](auto st) {
         constexpr int S = decltype(st)::value;

@@ -135,6 +135,16 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     if constexpr (TABLE) return __builtin_amdgcn_readfirstlane(ent[t] & 0xffffff);
     else return span_tile(sp, t);
   };
+  // Range-list plans: the raw entries a step needs (its DMA tile's and the
+  // next tile's) are read from LDS one step ahead, so that the step's top
+  // takes them without waiting for an LDS read.
+  int pf_dma = 0, pf_next = 0;
+  auto prefetch_entries = [&](int j, int t_end) {
+    if constexpr (TABLE) {
+      pf_dma = ent[j + 3 < t_end ? j + 3 : t_end - 1];
+      pf_next = ent[j + 1 < ntiles ? j + 1 : ntiles - 1];
+    }
+  };
   // clean-side blocks of a clean-tangent-zero plan, and every block of a
   // primal call (o and lse only)
   const bool primal_only = (CTZ && TABLE) || (CTZ && (p.primal != 0 || !is_noisy(g, r0)));
@@ -492,12 +502,12 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
 
     // range-list plans: the tile of this step's DMA and whether tile j+1 is
-    // whole, each read once from the LDS entries here, far ahead of use
+    // whole, from the entries the previous step read
     int dma_tile = 0;
     bool next_whole = false;
     if constexpr (TABLE) {
-      dma_tile = tile_at(j + 3 < t_end ? j + 3 : t_end - 1);
-      next_whole = tile_whole(j + 1);
+      dma_tile = __builtin_amdgcn_readfirstlane(pf_dma) & 0xffffff;
+      next_whole = ((__builtin_amdgcn_readfirstlane(pf_next) >> (24 + wave)) & 1) != 0;
     }
 
     const uint16_t* nx = stage(NX{});  // on the last tile a stale stage; unused
@@ -570,6 +580,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
       if (s == 0) mfma_v_first(Sn, kf[s], qf[s]);
       else mfma_v_acc(Sn, kf[s], qf[s]);
       __builtin_amdgcn_sched_barrier(0);
+      if (s == 0) prefetch_entries(j + 1, t_end);
       // (not in the first slot, so that the first MFMA of the k-step never
       // waits for it)
       if constexpr (HAS_TKV || !HAS_TS) {
@@ -725,6 +736,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   auto run = [&](auto mode, int t_begin, int t_end) {
     if (t_begin >= t_end) return;
     first_tile(mode, t_begin, t_end);
+    prefetch_entries(t_begin, t_end);
     for (int j = t_begin; j < t_end; j += 4) {
       step(mode, I0{}, j, t_end, SA, TSA, SB, TSB);
       if (j + 1 >= t_end) break;
