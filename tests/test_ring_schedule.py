@@ -1,4 +1,5 @@
-"""Host model of the backward kernels' LDS ring (no GPU).
+"""Host model of the LDS rings of the backward kernels and of the forward +
+JVP kernel (no GPU).
 
 Both backward kernels stream 32-row tiles through an S-stage LDS ring: step j
 reads tiles j, j+1 and (after its barrier slot) j+2, and issues the DMA of
@@ -113,3 +114,17 @@ def test_the_model_finds_planted_mistakes(S, A, P):
     # a refill of the stage still being read (A = S - P + 1, A = S), and a
     # read of a tile not yet waited for (A < P + 2 with barriers every P)
     assert _hazards(S, A, P) or not _lead_ok(A, P)
+
+
+def test_forward_ring_is_hazard_free():
+    # The forward + JVP kernel's ring has the same event order: K (and tK)
+    # fragments of tile j+1 in phase 1 with the DMA of tile j+3, the V reads
+    # of tile j, a barrier in every step after the wait for tile j+2, then
+    # the first K reads of tile j+2.
+    fwd = os.path.join(os.path.dirname(SRC), "attn_jvp_kernels.hip")
+    text = open(fwd).read()
+    kernel = text[text.index("fwd_bf16_kernel(FwdParams p)"):text.index("fwd_primal_bf16_kernel(FwdParams p)")]
+    S = int(re.search(r"constexpr int STAGES = (\d+);", kernel).group(1))
+    A = int(re.search(r"using AH = std::integral_constant<int, \(ST \+ (\d+)\) % STAGES>;", kernel).group(1))
+    assert (S, A) == (4, 3)
+    assert _hazards(S, A, 1) == [] and _lead_ok(A, 1)
