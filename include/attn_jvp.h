@@ -33,10 +33,17 @@
  * All device pointers must be 16-byte aligned (lse: 4-byte).
  *
  * Ownership: the caller owns every buffer.  A plan owns host memory only; the
- * library never allocates device memory and never synchronises.  attn_jvp_fwd
- * only enqueues work on the given stream; buffers must stay valid until the
- * stream reaches that point.  Outputs must not overlap inputs.  A plan is
- * immutable after creation and may be used from several threads and streams.
+ * library never allocates device memory and never synchronises.  It holds two
+ * fixed arrays per GPU for the process's lifetime: the workspace of
+ * attn_jvp_bwd_noalloc and the bf16 kernels' work queues, a ring of 256
+ * slots of 64 bytes that the calls on a GPU take in turn (each call's
+ * workgroups take their tasks from its slot, which is zero again when the
+ * call's kernels have run).  So at most 256 calls of this library may run at
+ * the same time on one GPU (on several streams); calls ordered on one stream
+ * are never limited.  attn_jvp_fwd only enqueues work on the given stream;
+ * buffers must stay valid until the stream reaches that point.  Outputs must
+ * not overlap inputs.  A plan is immutable after creation and may be used
+ * from several threads and streams.
  *
  * Errors: every function returns ATTN_JVP_OK or an error code and never
  * throws.  Argument errors are detected before any device work is enqueued.
@@ -215,8 +222,10 @@ int attn_jvp_fwd_primal_table(const attn_jvp_plan* plan, const void* device_tabl
  *                     N floats -delta_i followed by N floats -lse_i log2(e),
  *                     i.e. workspace[(b H + h) 2N + i] = -delta_i.
  * Enqueues two kernels on `hip_stream` (the dq kernel, which also fills the
- * workspace, then the dk/dv kernel); no atomics, so results do not depend on
- * scheduling.  No output may overlap an input or another output.  The plan's
+ * workspace, then the dk/dv kernel).  Their workgroups take tasks through
+ * integer atomics on the call's queue slot, but no result is accumulated by
+ * atomics and a task's arithmetic does not depend on the workgroup that runs
+ * it, so results do not depend on scheduling.  No output may overlap an input or another output.  The plan's
  * flags do not matter here.  Same checks and error codes as attn_jvp_fwd. */
 int attn_jvp_bwd(const attn_jvp_plan* plan, const void* q, const void* k, const void* v,
                  const void* o, const float* lse, const void* d_o, void* dq, void* dk, void* dv,
@@ -268,18 +277,24 @@ int attn_jvp_bwd_workspace_size(const attn_jvp_plan* plan, size_t* bytes);
 int attn_jvp_plan_bwd_info(const attn_jvp_plan* plan, int32_t* block_q, int32_t* block_kv,
                            int32_t* n_query_blocks, int32_t* n_key_blocks);
 
-/* Launch order of the dk/dv kernel: workgroup b (0 <= b < B H n_key_blocks)
- * processes task host_out[b], i.e. (b, h) slice task / n_key_blocks and key
- * block task mod n_key_blocks.  Tasks are heavy first (the earliest keys of a
- * side are seen by the most rows; range-list plans: the key blocks that
- * stream more query tiles first, in the table's order); workgroups are
- * handed to the 8 XCDs round robin.  Grids of at least 2048 workgroups and
- * 2 rounds of 128: each round gives each XCD a group of 16 consecutive tasks,
- * which stream nearly the same query tiles through that XCD's L2, the
- * group-to-XCD direction alternating from round to round; only an even
- * number of rounds is grouped, the rest keeps its index.  Smaller grids:
- * workgroup b takes rank b / (B H) of slice b mod (B H), heavy first across
- * all slices.  n is the capacity of host_out in int32 elements. */
+/* Launch order of the dk/dv kernel: position b (0 <= b < B H n_key_blocks)
+ * is task host_out[b], i.e. (b, h) slice task / n_key_blocks and key block
+ * task mod n_key_blocks, and is meant for XCD b mod 8 (workgroups go to the
+ * 8 XCDs round robin).  Ranks within a slice are heavy first (the earliest
+ * keys of a side are seen by the most rows; range-list plans: the key blocks
+ * that stream more query tiles first, in the table's order).  Orders of at
+ * least 2048 tasks and 2 rounds of 128: each round gives each XCD a group of
+ * 16 consecutive positions of a rank-major sequence (16 neighbouring key
+ * blocks of one slice, which stream nearly the same query tiles through that
+ * XCD's L2: the rank group 0 of every slice, then rank group 1, ...; where 16
+ * does not divide n_key_blocks, the task order itself), the group-to-XCD
+ * direction alternating from round to round; only an even number of rounds
+ * is grouped, the rest follows the sequence.  Smaller orders: rank b / (B H)
+ * of slice b mod (B H), heavy first across all slices.  The kernel's
+ * workgroups take these positions from 8 queues, one per XCD (queue x:
+ * positions x, x + 8, ...), and a workgroup whose XCD's queue is empty takes
+ * the next position of another's.  n is the capacity of host_out in int32
+ * elements. */
 int attn_jvp_bwd_launch_order(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
 /* Useful floating-point operations of one attn_jvp_bwd call (all B * H
@@ -345,12 +360,14 @@ int attn_jvp_key_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
  * so that the round-robin hand-out of workgroups to the 8 XCDs gives each XCD
  * both sides.  Range-list plans: host_out holds the heavy-first order of
  * the query blocks (more streamed tiles first).  "Workgroup t" is the
- * logical task t: over the whole B H grid, workgroups take the tasks in XCD
- * groups of 128 consecutive tasks under the rule of attn_jvp_bwd_launch_order
- * (there with groups of 16), except on the smaller grids: there
- * clean-tangent-zero plans keep the index order, and general teacher-forcing
- * plans go heavy first across the slices in groups of 32 consecutive tasks
- * of one slice.  n is the capacity of host_out in int32 elements. */
+ * logical task t: over the whole B H grid, the tasks are ordered in XCD
+ * groups of 128 under the rule of attn_jvp_bwd_launch_order (there with
+ * groups of 16) and taken from its per-XCD queues, except on the smaller
+ * grids: there clean-tangent-zero plans keep the index order, and general
+ * teacher-forcing plans go heavy first across the slices in groups of 32
+ * consecutive tasks of one slice.  (The bf16 kernel without tangents of
+ * descriptor plans, attn_jvp_fwd_primal, runs the same order with a fixed
+ * grid, workgroup b taking position b.)  n is the capacity of host_out in int32 elements. */
 int attn_jvp_launch_order(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
 /* Tile map, row-major [n_query_blocks][n_key_tiles], query blocks in index

@@ -324,6 +324,37 @@ int scratch_address(int dev, void** out) {
   return ok();
 }
 
+// Work queues of the bf16 kernels (take_task): a ring of kQueueSlots slots
+// of kQueueWords int32 in a file-scope device array, zero when the library
+// loads and zero again after every launch that used a slot, so no call
+// allocates for them (attn_jvp_bwd_noalloc included).  Calls on a device take
+// the slots in turn; a slot is used again kQueueSlots calls later, so calls
+// of this library that run at the same time on one GPU (on several streams)
+// must number at most kQueueSlots.  Host code takes each GPU's address of the
+// array from hipGetSymbolAddress, once per device.
+constexpr int kQueueSlots = 256;
+static __device__ __align__(256) int32_t task_queues[kQueueSlots * kQueueWords];
+std::mutex g_queue_mu;
+int32_t* g_queue_ptr[64];
+std::atomic<uint32_t> g_queue_next[64];
+
+// The next slot of this device's ring (dev is current).
+int queue_slot(int dev, int32_t** out) {
+  {
+    std::lock_guard<std::mutex> lock(g_queue_mu);
+    if (g_queue_ptr[dev] == nullptr) {
+      void* ptr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(task_queues));
+      if (e != hipSuccess || ptr == nullptr)
+        return fail(ATTN_JVP_E_HIP, "hipGetSymbolAddress(task_queues) on device %d: %s", dev, hipGetErrorString(e));
+      g_queue_ptr[dev] = (int32_t*)ptr;
+    }
+  }
+  const uint32_t slot = g_queue_next[dev].fetch_add(1, std::memory_order_relaxed) % kQueueSlots;
+  *out = g_queue_ptr[dev] + (size_t)slot * kQueueWords;
+  return ok();
+}
+
 // Measurement: workgroup w (of kClockSampleGroups, one per XCD when
 // workgroups go to the 8 XCDs round robin) stores its XCD number, the shader
 // clock counter (s_memtime, counting at the XCD's shader clock) and the
@@ -701,6 +732,8 @@ int fwd_common(const attn_jvp_plan* p, const void* table, const void* q, const v
   }
   // the bf16 primal kernel (descriptor plans) takes query blocks of 64 rows per wave
   if (primal && p->dtype == ATTN_JVP_BF16 && !table) fp.n_qblocks = n_query_blocks(p->g, kBf16PrimalRows);
+  st = queue_slot(dev, &fp.queues);
+  if (st != ATTN_JVP_OK) return st;
   const int grid = p->batch * p->heads * fp.n_qblocks;
   hipError_t e = launch_fwd(p->dtype, p->head_dim, grid, fp, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(ATTN_JVP_E_HIP, "kernel launch: %s", hipGetErrorString(e));
@@ -817,6 +850,9 @@ int bwd_common(const attn_jvp_plan* p, const void* table, const void* q, const v
     bp.cb_cols = t + rs.off_cols;
     bp.cb_iv = t + rs.off_civ;
   }
+  bp.n_slices = p->batch * p->heads;
+  st = queue_slot(dev, &bp.queues);
+  if (st != ATTN_JVP_OK) return st;
   hipError_t e = launch_bwd(p->dtype, p->head_dim, p->batch * p->heads, bp, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(ATTN_JVP_E_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();

@@ -9,8 +9,10 @@
 //   dS = P o (dP - delta),   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO,
 // where masked pairs have P = 0 and hence dS = 0.
 //
-// Two kernels per call, no atomics, so every result is a fixed function of
-// the inputs:
+// Two kernels per call, which accumulate no result through atomics (their
+// workgroups take tasks from work queues, but a task's arithmetic does not
+// depend on the workgroup that runs it), so every result is a fixed function
+// of the inputs:
 // * dq kernel: one workgroup per query block with the forward's key-tile
 //   schedule; lane = query.  It also writes -delta and -lse log2(e) of its
 //   rows to the workspace.  Per 32-key tile: S^T = K Q^T and dP^T - delta =
@@ -222,7 +224,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   // Workgroups take the heavy-first order (range-list plans: the table's) in
   // XCD groups of kFwdXcdGroup, as the forward does, small teacher-forcing
   // grids included (rank-major groups of 32: 1.4 % faster at 3 heads).
-  const int task = launch_task((int)blockIdx.x, (int)gridDim.x, p.n_qblocks, kFwdXcdGroup,
+  const int n_tasks = p.n_slices * p.n_qblocks;
+  const int pos = workgroup_task(p.queues, n_tasks);
+  if (pos < 0) return;  // the queues were empty: no task for this workgroup
+  const int task = launch_task(pos, n_tasks, p.n_qblocks, kFwdXcdGroup,
                                (!TABLE && g.tf) ? kSmallRankGroups : kSmallAcross);
   const int bh = task / p.n_qblocks;
   int r0, r1, ntiles, e0 = 0;
@@ -566,7 +571,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
   // first (the earliest keys of a side are seen by the most rows).  Groups of
   // 16 neighbouring key blocks, which stream nearly the same query tiles, run
   // on one XCD (a quarter of the fetches past L2 of plain round robin).
-  const int task = launch_task((int)blockIdx.x, (int)gridDim.x, p.n_kblocks, kDkdvXcdGroup);
+  const int n_tasks = p.n_slices * p.n_kblocks;
+  const int pos = workgroup_task(p.queues, n_tasks);
+  if (pos < 0) return;  // the queues were empty: no task for this workgroup
+  const int task = launch_task(pos, n_tasks, p.n_kblocks, kDkdvXcdGroup);
   const int bh = task / p.n_kblocks;
   int k0, k1, ntiles, e0 = 0;
   TileSpans sp{0, 0, 0, 0};
@@ -1106,9 +1114,12 @@ template <int D, bool TABLE>
 void launch_bwd_kernels(int dtype, int bh, const BwdParams& p, hipStream_t stream) {
   const dim3 gq((unsigned)bh * (unsigned)p.n_qblocks), gk((unsigned)bh * (unsigned)p.n_kblocks);
   if (dtype == kBf16) {
+    // both kernels take their tasks from the call's work queues, one after the other
     const dim3 block(kBf16Waves * 64);
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, kBf16Waves, TABLE>), gq, block, 0, stream, p);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, kBf16Waves, TABLE>), gk, block, 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, kBf16Waves, TABLE>), dim3((unsigned)queue_grid((int)gq.x)), block, 0,
+                       stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, kBf16Waves, TABLE>), dim3((unsigned)queue_grid((int)gk.x)), block, 0,
+                       stream, p);
   } else {
     hipLaunchKernelGGL((bwd_dq_fp32_kernel<D, TABLE>), gq, dim3(256), 0, stream, p);
     hipLaunchKernelGGL((bwd_dkdv_fp32_kernel<D, TABLE>), gk, dim3(256), 0, stream, p);

@@ -103,7 +103,9 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
   // than heavy first across heads, which the other plans keep).
   const int32_t small = (CTZ && !TABLE) ? kSmallIndex
                         : (!TABLE && p.g.tf) ? kSmallRankGroups : kSmallAcross;
-  const int task = launch_task((int)blockIdx.x, (int)gridDim.x, p.n_qblocks, kFwdXcdGroup, small);
+  const int pos = workgroup_task(p.queues, p.n_tasks);
+  if (pos < 0) return;  // the queues were empty: no task for this workgroup
+  const int task = launch_task(pos, p.n_tasks, p.n_qblocks, kFwdXcdGroup, small);
   const int bh = task / p.n_qblocks;
   int qb, r0, r1, ntiles, e0 = 0;
   TileSpans sp{0, 0, 0, 0};
@@ -1377,28 +1379,32 @@ void block_sizes(int dtype, int head_dim, int* block_q, int* block_k) {
   }
 }
 
-hipError_t launch_fwd(int dtype, int head_dim, int grid, const FwdParams& p, hipStream_t stream) {
+hipError_t launch_fwd(int dtype, int head_dim, int grid, const FwdParams& p0, hipStream_t stream) {
   const dim3 block(kBf16Waves * 64);
-  const bool table = p.tb_ent != nullptr;
+  const bool table = p0.tb_ent != nullptr;
+  FwdParams p = p0;
+  p.n_tasks = grid;
+  // grid of fwd_bf16_kernel, which takes its tasks from the work queues
+  const dim3 qgrid((unsigned)queue_grid(grid));
   if (dtype == kBf16 && p.primal && !table) {  // the primal kernel: 64 rows per wave
     if (head_dim == 128) hipLaunchKernelGGL((fwd_primal_bf16_kernel<128, kBf16Waves>), dim3(grid), block, 0, stream, p);
     else hipLaunchKernelGGL((fwd_primal_bf16_kernel<64, kBf16Waves>), dim3(grid), block, 0, stream, p);
     return hipGetLastError();
   }
   if (dtype == kBf16 && table && p.primal) {  // range-list plans without tangents
-    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, true, true>), dim3(grid), block, 0, stream, p);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, true, true>), dim3(grid), block, 0, stream, p);
+    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, true, true>), qgrid, block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, true, true>), qgrid, block, 0, stream, p);
     return hipGetLastError();
   }
   if (dtype == kBf16) {
     if (head_dim == 128) {
-      if (table) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, false, true>), dim3(grid), block, 0, stream, p);
-      else if (p.ctz) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, true, false>), dim3(grid), block, 0, stream, p);
-      else hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, false, false>), dim3(grid), block, 0, stream, p);
+      if (table) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, false, true>), qgrid, block, 0, stream, p);
+      else if (p.ctz) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, true, false>), qgrid, block, 0, stream, p);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, false, false>), qgrid, block, 0, stream, p);
     } else {
-      if (table) hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, false, true>), dim3(grid), block, 0, stream, p);
-      else if (p.ctz) hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, true, false>), dim3(grid), block, 0, stream, p);
-      else hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, false, false>), dim3(grid), block, 0, stream, p);
+      if (table) hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, false, true>), qgrid, block, 0, stream, p);
+      else if (p.ctz) hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, true, false>), qgrid, block, 0, stream, p);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, false, false>), qgrid, block, 0, stream, p);
     }
   } else {
     if (head_dim == 128) {

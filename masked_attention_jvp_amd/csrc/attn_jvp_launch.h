@@ -41,6 +41,10 @@ struct FwdParams {
   const int32_t* tb_ent;    // tile | (whole bit of wave w) << (24 + w)
   const int32_t* tb_rows;   // [N] (first interval << 8) | interval count
   const int32_t* tb_iv;     // (lo, hi) pairs
+  // bf16 kernels: the work queues of this call (kQueueWords words, take_task)
+  // and the number of tasks, (b, h) slices x n_qblocks
+  int32_t* queues;
+  int32_t n_tasks;
 };
 
 struct BwdParams {
@@ -73,7 +77,21 @@ struct BwdParams {
   const int32_t* cb_ent;    // query tile | (whole bit of wave w) << (24 + w)
   const int32_t* cb_cols;   // [N] (first interval << 8) | interval count
   const int32_t* cb_iv;     // (lo, hi) row intervals
+  // bf16 kernels: the work queues of this call (kQueueWords words, take_task),
+  // used by the dq kernel and then, zeroed again, by the dk/dv kernel; the
+  // number of (b, h) slices (tasks: n_slices x n_qblocks, n_slices x n_kblocks)
+  int32_t* queues;
+  int32_t n_slices;
 };
+
+// int32 words per call of the bf16 kernels' work queues (take_task uses 9).
+constexpr int kQueueWords = 16;
+
+// Workgroups of a grid that takes n tasks from work queues (take_task): an
+// eighth more (rounded to whole XCD rounds), which lets a faster XCD take up
+// to that many of the other XCDs' tasks; the spare workgroups of the slower
+// ones find the queues empty and exit.
+inline int queue_grid(int n) { return n + 8 * ((n + 63) / 64); }
 
 // Query rows per block and keys per tile of the kernel chosen for dtype/head_dim.
 void block_sizes(int dtype, int head_dim, int* block_q, int* block_k);

@@ -2,13 +2,56 @@
 // and the backward kernels: bf16 matrix-core products (register and
 // vector-register forms), lane-pair reductions, bf16 packing, buffer
 // resources and HBM -> LDS DMA, transposing LDS reads, the LDS row swizzle,
-// accumulation-register access, and explicit waits and barriers.
+// accumulation-register access, explicit waits and barriers, and the
+// workgroups' per-XCD work queues.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace attn_jvp {
+
+// Work queues.  A grid of more workgroups than tasks (queue_grid) takes the
+// n positions of a static order (launch_task) from 8 queues, queue y holding
+// positions y, y + 8, y + 16, .. in that order: the ones the static grid
+// would give XCD y, since workgroups go to the XCDs round robin.  A
+// workgroup takes the next position of its own XCD's queue, else of the next
+// queue that has any left, and gets -1 when all are empty; so every position
+// is taken exactly once, an XCD keeps its share (and its L2 locality) while
+// it lasts, and one that runs faster (the XCDs' clocks under the power cap
+// differ) takes the ends of the others'.  Which workgroup runs a task does
+// not change its results.  q: 9 int32, the 8 queue counters and the number
+// of workgroups that have taken (kQueueWords per call); zero before the launch.  The
+// last workgroup to take sets them back to zero (every taking is complete
+// by then: each workgroup counts itself only after its own atomics have
+// returned), so launches that use q one after another, on one stream or
+// joined by events, find it zeroed; launches that use it at the same time
+// would race.  Called by one lane.
+__device__ __forceinline__ int take_task(int32_t* q, int n) {
+  uint32_t xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  int pos = -1;
+  for (int k = 0; k < 8 && pos < 0; ++k) {
+    const int y = (int)((xcc + k) & 7);
+    const int ny = (n - y + 7) >> 3;  // positions y, y + 8, .. below n
+    if (__hip_atomic_load(&q[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= ny) continue;
+    const int i = __hip_atomic_fetch_add(&q[y], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (i < ny) pos = 8 * i + y;
+  }
+  const int taken = __hip_atomic_fetch_add(&q[8], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (taken == (int)(gridDim.x * gridDim.y * gridDim.z) - 1) {
+    for (int i = 0; i < 9; ++i) __hip_atomic_store(&q[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return pos;
+}
+// The workgroup's position (take_task by its first lane), the same in every
+// lane; -1: none is left and the workgroup has no task.  Once per kernel.
+__device__ __forceinline__ int workgroup_task(int32_t* q, int n) {
+  __shared__ int pos_shared;
+  if (threadIdx.x == 0) pos_shared = take_task(q, n);
+  __syncthreads();
+  return pos_shared;
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

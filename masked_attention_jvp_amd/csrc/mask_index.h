@@ -127,18 +127,28 @@ AJ_HD int32_t heavy_first_qblock(const MaskGeom& g, int32_t block_q, int32_t t, 
   return (u & 1) * nbs + (rem - 1 - (u >> 1));
 }
 
-// XCD-aware launch order.  Workgroup b of a grid of total = n_slices *
-// per_slice workgroups runs logical task launch_task(b, ...): (b, h) slice
-// task / per_slice, heavy-first rank task mod per_slice.  Workgroups are
-// handed to the 8 XCDs round robin (b mod 8): each XCD gets a fixed eighth of
-// the grid, runs it in order of arrival on its 32 CUs, and has its own L2.
+// XCD-aware launch order.  Position b of the order over total = n_slices *
+// per_slice tasks is logical task launch_task(b, ...): (b, h) slice task /
+// per_slice, heavy-first rank task mod per_slice.  Workgroups are handed to
+// the 8 XCDs round robin (workgroup b to XCD b mod 8), each XCD runs its
+// share in order of arrival on its 32 CUs and has its own L2, so position b
+// is meant for XCD b mod 8.  (Kernels with a static grid run position
+// blockIdx; the bf16 forward + JVP and backward kernels take positions from
+// per-XCD work queues, take_task, which keeps this split and lets an XCD that
+// has finished its share take the rest of another's.)
 // * Large grids (at least kMinGroupedTasks workgroups and kMinGroupedRounds
 //   rounds of 8 G): every round gives each XCD a group of G consecutive
-//   logical tasks, so that tasks streaming the same tiles (neighbouring
-//   blocks of one chunk) share an L2.  The direction alternates from round to
-//   round (XCD x takes group x, then group 7 - x), so the falling heavy-first
+//   positions, so that tasks streaming the same tiles (neighbouring blocks of
+//   one chunk) share an L2.  The direction alternates from round to round
+//   (XCD x takes group x, then group 7 - x), so the falling heavy-first
 //   weights even out over each pair of rounds; only an even number of rounds
-//   is grouped and the rest keeps its index.
+//   is grouped and the rest keeps its index.  Where G divides per_slice,
+//   positions are rank-major: group k of the sequence holds ranks
+//   (k / n_slices) G .. + G - 1 of slice k mod n_slices, so the whole grid
+//   runs heavy first across slices, with the lightest blocks of every slice
+//   at the end.  (Slice-major, the last round held one slice's heaviest
+//   blocks next to another's lightest, and the XCDs that took the heavy ones
+//   finished late.)
 // * Smaller grids, by `small`: kSmallAcross, heavy first across all slices
 //   (the heaviest block of every slice, then the next, ...); kSmallRankGroups,
 //   the same across groups of kSmallGroup consecutive tasks of one slice
@@ -159,10 +169,16 @@ AJ_HD int32_t launch_task(int32_t b, int32_t total, int32_t per_slice, int32_t G
   const int32_t rounds = total / round;
   if (total >= kMinGroupedTasks && rounds >= kMinGroupedRounds) {
     const int32_t r = b / round;
-    if (r >= (rounds & ~1)) return b;
-    const int32_t u = b - r * round;
-    const int32_t x = (r & 1) ? 7 - (u & 7) : (u & 7);
-    return r * round + x * G + (u >> 3);
+    int32_t t = b;
+    if (r < (rounds & ~1)) {
+      const int32_t u = b - r * round;
+      const int32_t x = (r & 1) ? 7 - (u & 7) : (u & 7);
+      t = r * round + x * G + (u >> 3);
+    }
+    if (per_slice % G != 0) return t;
+    const int32_t n_slices = total / per_slice;
+    const int32_t grp = t / G, rg = grp / n_slices, s = grp - rg * n_slices;
+    return s * per_slice + rg * G + (t - grp * G);
   }
   if (small == kSmallIndex) return b;
   const int32_t n_slices = total / per_slice;

@@ -31,28 +31,37 @@ def read_golden(name):
 
 
 def check_launch_rule(tasks, total, per_slice, G):
-    """Workgroup b of a grid of `total` runs logical task tasks[b] (slice
-    task // per_slice, heavy-first rank task % per_slice); workgroups go to the
-    8 XCDs round robin.  Grids of >= 2048 workgroups and >= 2 rounds of 8 G:
-    an even number of rounds in which XCD x holds G consecutive tasks (group x,
-    then group 7 - x in the next round), the rest in index order.  Smaller
-    grids: heavy first across slices (rank b // slices of slice b % slices)."""
+    """Position b of an order over `total` tasks is logical task tasks[b]
+    (slice task // per_slice, heavy-first rank task % per_slice); position b
+    is meant for XCD b mod 8.  Orders of >= 2048 tasks and >= 2 rounds of 8 G:
+    an even number of rounds in which XCD x holds G consecutive tasks (group
+    x of the round's 8 groups of the sequence, then group 7 - x in the next
+    round), the rest in sequence order.  The sequence is rank-major where G
+    divides per_slice (group k: ranks (k // slices) G .. + G - 1 of slice
+    k % slices), else the task order.  Smaller orders: heavy first across
+    slices (rank b // slices of slice b % slices)."""
     import numpy as np
     tasks = np.asarray(tasks)
     assert sorted(tasks.tolist()) == list(range(total))
     rounds = total // (8 * G)
     b = np.arange(total)
+    n = total // per_slice
+
+    def seq(t):
+        t = np.asarray(t)
+        if per_slice % G:
+            return t
+        k = t // G
+        return (k % n) * per_slice + (k // n) * G + t % G
+
     if total >= 2048 and rounds >= 2:
         even = rounds - rounds % 2
         for r in range(even):
             seg = tasks[8 * G * r: 8 * G * (r + 1)]
             for x in range(8):
-                t = np.sort(seg[x::8])
-                assert np.array_equal(t, np.arange(t[0], t[0] + G))
-            first = [int(seg[x::8].min()) for x in range(8)]
-            expect = [8 * G * r + G * (x if r % 2 == 0 else 7 - x) for x in range(8)]
-            assert first == expect
-        assert np.array_equal(tasks[8 * G * even:], b[8 * G * even:])
+                g = x if r % 2 == 0 else 7 - x
+                assert np.array_equal(seg[x::8], seq(8 * G * r + g * G + np.arange(G)))
+        assert np.array_equal(tasks[8 * G * even:], seq(b[8 * G * even:]))
         return "grouped"
     n = total // per_slice
     assert np.array_equal(tasks, (b % n) * per_slice + b // n)

@@ -139,7 +139,7 @@ def test_bwd_workload_sampled(cfg):
 
 @pytest.mark.parametrize("geom", [(160, 9, 3, 1, 128), (96, 7, 1, 0, 64)])
 def test_bwd_run_to_run_bitwise_determinism(geom):
-    # no atomics: the same call repeated gives the same bits
+    # no result accumulated by atomics: the same call repeated gives the same bits
     tpf, nf, fpc, tf, d = geom
     w = small_workload(240, tpf, nf, fpc, tf, heads=2, d=d)
     x = _inputs(w)

@@ -1,0 +1,108 @@
+"""The bf16 kernels' work queues (take_task in csrc/kernel_common.h; the ring
+of queue slots in csrc/attn_jvp_api.hip).
+
+Each call takes the next of 256 slots of per-XCD queue counters, its grid
+holds an eighth more workgroups than tasks, and the last workgroup to take a
+task zeroes the slot again.  If a slot were left non-zero, or a position were
+handed out twice or not at all, a later call would skip or repeat query or
+key blocks.  So: more calls than there are slots (every slot is used at least
+twice), alternating plans whose grids have fewer tasks than XCDs, one task
+per XCD and many, forward + JVP, the backward (whose two kernels use one slot
+one after the other) and range-list plans; every output prefilled with NaN
+and every call's bits equal to the first call's.
+"""
+import numpy as np
+import pytest
+import torch
+
+import masked_attention_jvp_amd as aj
+from seeded_inputs import TENSORS
+from gpu_util import log, small_workload, device_inputs
+
+pytestmark = pytest.mark.gpu
+
+N_SLOTS = 256  # kQueueSlots
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    aj._load()
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+class _Case:
+    """One plan and its inputs; fwd() and bwd() return fresh NaN-prefilled outputs."""
+
+    def __init__(self, w, ranges=False):
+        self.w = w
+        self.x = device_inputs(w)
+        if ranges:
+            n_tok, groups = w.mask_ranges()
+            self.plan = aj.attn_jvp_create_ranges(n_tok, groups, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16)
+            self.table = torch.from_numpy(aj.attn_jvp_plan_table(self.plan)).cuda()
+        else:
+            self.plan = aj.attn_jvp_create(w.desc, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16)
+            self.table = None
+        self.n_tasks = w.batch * w.heads * self.plan.info["n_query_blocks"]
+        self.d_o = torch.randn_like(self.x["q"], dtype=torch.float32).to(torch.bfloat16)
+        self.o, _, self.lse = self.fwd()
+        self.ws = torch.empty(aj.attn_jvp_bwd_workspace_size(self.plan) // 4, dtype=torch.float32, device="cuda")
+
+    def _nan(self, like, dtype=None):
+        return torch.full_like(like, float("nan"), dtype=dtype)
+
+    def fwd(self):
+        x = self.x
+        o, to = self._nan(x["q"]), self._nan(x["q"])
+        lse = torch.full(self.w.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+        if self.table is None:
+            aj.attn_jvp_fwd(self.plan, *(x[t] for t in TENSORS), o, to, lse)
+        else:
+            aj.attn_jvp_fwd_table(self.plan, self.table, *(x[t] for t in TENSORS), o, to, lse)
+        return o, to, lse
+
+    def bwd(self):
+        x = self.x
+        dq, dk, dv = (self._nan(x["q"]) for _ in range(3))
+        args = (x["q"], x["k"], x["v"], self.o, self.lse, self.d_o, dq, dk, dv, self.ws)
+        if self.table is None:
+            aj.attn_jvp_bwd(self.plan, *args)
+        else:
+            aj.attn_jvp_bwd_table(self.plan, self.table, *args)
+        return dq, dk, dv
+
+
+def test_queue_slots_are_reused_and_every_call_is_complete():
+    cases = [
+        _Case(small_workload(401, 50, 3, 1, 0, heads=1)),            # 2 tasks: six queues empty
+        _Case(small_workload(402, 50, 5, 1, 1, heads=2)),            # 8 tasks: one per XCD
+        _Case(small_workload(403, 37, 30, 2, 1, heads=3, batch=2)),  # 108 tasks
+        _Case(small_workload(404, 40, 6, 3, 1, heads=2), ranges=True),
+    ]
+    for c in cases:
+        log(f"[queues] {c.w.name} desc={c.w.desc} B={c.w.batch} H={c.w.heads} tasks={c.n_tasks} "
+            f"ranges={c.table is not None}")
+    ref = [(c.fwd(), c.bwd()) for c in cases]
+    torch.cuda.synchronize()
+    for (f, b) in ref:
+        for t in f + b:
+            assert not torch.isnan(t).any(), "a block was never computed"
+    calls = 0
+    it = 0
+    while calls < 2 * N_SLOTS + 16:
+        for c, (rf, rb) in zip(cases, ref):
+            f = c.fwd()
+            b = c.bwd()
+            calls += 2
+            for got, want in zip(f + b, rf + rb):
+                if not torch.equal(_bits(got), _bits(want)):
+                    torch.cuda.synchronize()
+                    raise AssertionError(f"call {calls} ({c.w.name}): outputs differ from the first call's")
+        it += 1
+    torch.cuda.synchronize()
+    log(f"    {calls} calls over {it} rounds, every one bit-identical to the first")

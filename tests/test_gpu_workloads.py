@@ -177,10 +177,12 @@ def _bits(t):
 
 
 def test_full_workload_forward_and_backward_are_deterministic():
-    # No atomics and fixed schedules: repeated calls at the full size, where
-    # thousands of workgroups stream long tile runs through the DMA ring
-    # (the backward with one workgroup barrier per two steps), give the same
-    # bits every time.
+    # No result is accumulated by atomics, and a task's arithmetic does not
+    # depend on which workgroup takes it from the work queues: repeated calls
+    # at the full size, where thousands of workgroups stream long tile runs
+    # through the DMA ring (the backward with one workgroup barrier per two
+    # steps) and take their tasks in a different interleaving every time,
+    # give the same bits every time.
     w = WORKLOADS[3]
     log(f"[full-size determinism] {w.name}")
     x = device_inputs(w)

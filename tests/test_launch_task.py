@@ -75,15 +75,26 @@ def test_launch_task_is_a_permutation(harness, slices, per_slice, G, small):
     assert np.array_equal(np.sort(tasks), np.arange(total)), "not a permutation"
 
 
+def _sequence_task(t, slices, per_slice, G):
+    """Task at position t of the grouped regime's sequence: rank-major where G
+    divides per_slice (group k = ranks (k // slices) G .. + G - 1 of slice
+    k % slices), else the index itself."""
+    t = np.asarray(t)
+    if per_slice % G:
+        return t
+    k = t // G
+    return (k % slices) * per_slice + (k // slices) * G + t % G
+
+
 @pytest.mark.parametrize("slices, per_slice, G", [g for g in GRIDS if _is_grouped(g[0] * g[1], g[2])])
 def test_grouped_regime_is_independent_of_the_small_rule(harness, slices, per_slice, G):
     total = slices * per_slice
     ref = harness(total, per_slice, G, SMALL_ACROSS)
     for small in (SMALL_INDEX, SMALL_RANK_GROUPS):
         assert np.array_equal(harness(total, per_slice, G, small), ref)
-    # XCD x (workgroups b = x mod 8) holds G consecutive tasks per round, the
-    # direction alternating from round to round; the odd last round and the
-    # rest keep the index
+    # XCD x (positions b = x mod 8) holds sequence group x of each round, then
+    # group 7 - x in the next; the odd last round and the rest keep their
+    # sequence positions
     rounds = total // (8 * G)
     even = rounds - rounds % 2
     for r in range(even):
@@ -91,8 +102,21 @@ def test_grouped_regime_is_independent_of_the_small_rule(harness, slices, per_sl
         for x in range(8):
             xs = seg[x::8]
             g = x if r % 2 == 0 else 7 - x
-            assert np.array_equal(xs, 8 * G * r + g * G + np.arange(G))
-    assert np.array_equal(ref[8 * G * even:], np.arange(8 * G * even, total))
+            assert np.array_equal(xs, _sequence_task(8 * G * r + g * G + np.arange(G), slices, per_slice, G))
+    assert np.array_equal(ref[8 * G * even:], _sequence_task(np.arange(8 * G * even, total), slices, per_slice, G))
+
+
+@pytest.mark.parametrize("slices, per_slice, G", [g for g in GRIDS if _is_grouped(g[0] * g[1], g[2]) and g[1] % g[2] == 0])
+def test_grouped_regime_is_heavy_first_across_slices(harness, slices, per_slice, G):
+    """Where G divides per_slice, the rounds take the slices' rank groups in
+    order: no position holds a rank group later than any position of a later
+    round, so the lightest blocks of every slice come last."""
+    total = slices * per_slice
+    tasks = harness(total, per_slice, G, SMALL_ACROSS)
+    rank_group = (tasks % per_slice) // G
+    rounds = total // (8 * G)
+    for r in range(rounds - 1):
+        assert rank_group[8 * G * r: 8 * G * (r + 1)].max() <= rank_group[8 * G * (r + 1):].min()
 
 
 @pytest.mark.parametrize("slices, per_slice", [(s, p) for s, p, G in GRIDS if not _is_grouped(s * p, 128)])
