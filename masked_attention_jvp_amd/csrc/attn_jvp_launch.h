@@ -87,11 +87,13 @@ struct BwdParams {
 // int32 words per call of the bf16 kernels' work queues (take_task uses 9).
 constexpr int kQueueWords = 16;
 
-// Workgroups of a grid that takes n tasks from work queues (take_task): an
-// eighth more (rounded to whole XCD rounds), which lets a faster XCD take up
-// to that many of the other XCDs' tasks; the spare workgroups of the slower
-// ones find the queues empty and exit.
-inline int queue_grid(int n) { return n + 8 * ((n + 63) / 64); }
+// Workgroups of a grid that takes n tasks from work queues (take_task): half
+// as many again (rounded to whole XCD rounds), which lets a faster XCD take up
+// to that many of the other XCDs' tasks (the last tasks are light, so it may
+// need many: with an eighth more, the fast XCDs ran out of workgroups before
+// the end of the dk/dv launch); the spare workgroups of the slower ones find
+// the queues empty and exit within microseconds.
+inline int queue_grid(int n) { return n + 8 * ((n + 15) / 16); }
 
 // Query rows per block and keys per tile of the kernel chosen for dtype/head_dim.
 void block_sizes(int dtype, int head_dim, int* block_q, int* block_k);
