@@ -11,22 +11,21 @@
 
 namespace attn_jvp {
 
-// Work queues.  A grid of more workgroups than tasks (queue_grid) takes the
-// n positions of a static order (launch_task) from 8 queues, queue y holding
-// positions y, y + 8, y + 16, .. in that order: the ones the static grid
-// would give XCD y, since workgroups go to the XCDs round robin.  A
-// workgroup takes the next position of its own XCD's queue, else of the next
-// queue that has any left, and gets -1 when all are empty; so every position
-// is taken exactly once, an XCD keeps its share (and its L2 locality) while
-// it lasts, and one that runs faster (the XCDs' clocks under the power cap
-// differ) takes the ends of the others'.  Which workgroup runs a task does
-// not change its results.  q: 9 int32, the 8 queue counters and the number
-// of workgroups that have taken (kQueueWords per call); zero before the launch.  The
-// last workgroup to take sets them back to zero (every taking is complete
-// by then: each workgroup counts itself only after its own atomics have
-// returned), so launches that use q one after another, on one stream or
-// joined by events, find it zeroed; launches that use it at the same time
-// would race.  Called by one lane.
+// Work queues.  A grid of more workgroups than tasks (queue_grid) takes the n
+// positions of a static order (launch_task) from 8 queues, queue y holding
+// positions y, y + 8, y + 16, .. in that order: the ones the static grid would
+// give XCD y, since workgroups go to the XCDs round robin.  A workgroup takes
+// the next position of its own XCD's queue, else of the next queue that has any
+// left, and gets -1 when all are empty; so every position is taken exactly
+// once, an XCD keeps its share (and its L2 locality) while it lasts, and one
+// that runs faster (the XCDs' clocks under the power cap differ) takes the ends
+// of the others'.  Which workgroup runs a task does not change its results.  q:
+// 9 int32, the 8 queue counters and the number of workgroups that have taken
+// (kQueueWords per call); zero before the launch.  The last workgroup to take
+// sets them back to zero (every taking is complete by then: each workgroup
+// counts itself only after its own atomics have returned), so launches that use
+// q one after another, on one stream or joined by events, find it zeroed;
+// launches that use it at the same time would race.  Called by one lane.
 __device__ __forceinline__ int take_task(int32_t* q, int n) {
   uint32_t xcc;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
