@@ -2,16 +2,17 @@
 of queue slots in csrc/attn_jvp_api.hip).
 
 Each call takes the next of 256 slots of per-XCD queue counters, its grid
-holds an eighth more workgroups than tasks, and the last workgroup to take a
-task zeroes the slot again.  If a slot were left non-zero, or a position were
+holds half again as many workgroups as tasks, and the last workgroup to take
+a task zeroes the slot again.  If a slot were left non-zero, or a position were
 handed out twice or not at all, a later call would skip or repeat query or
 key blocks.  So: more calls than there are slots (every slot is used at least
 twice), alternating plans whose grids have fewer tasks than XCDs, one task
 per XCD and many, forward + JVP, the backward (whose two kernels use one slot
 one after the other) and range-list plans; every output prefilled with NaN
-and every call's bits equal to the first call's.
+and every call's bits equal to the first call's.  Then calls that overlap on
+two streams, and replays of a captured HIP graph (whose launches keep the
+slot they took at capture) between eager calls.
 """
-import numpy as np
 import pytest
 import torch
 
@@ -106,3 +107,73 @@ def test_queue_slots_are_reused_and_every_call_is_complete():
         it += 1
     torch.cuda.synchronize()
     log(f"    {calls} calls over {it} rounds, every one bit-identical to the first")
+
+
+def test_calls_on_two_streams_at_once_take_different_slots():
+    """Calls issued alternately on two streams overlap on the GPU; consecutive
+    calls take consecutive slots, so each finds its own slot zeroed."""
+    a = _Case(small_workload(406, 50, 5, 1, 1, heads=2))
+    b = _Case(small_workload(407, 37, 30, 2, 1, heads=3, batch=2))
+    log(f"[queues] two streams: {a.n_tasks} and {b.n_tasks} tasks")
+    ref = {id(a): (a.fwd(), a.bwd()), id(b): (b.fwd(), b.bwd())}
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for i in range(60):
+        for c, s in ((a, s1), (b, s2)):
+            with torch.cuda.stream(s):
+                outs.append((c, c.fwd(), c.bwd()))
+    torch.cuda.synchronize()
+    for i, (c, f, bw) in enumerate(outs):
+        rf, rb = ref[id(c)]
+        for got, want in zip(f + bw, rf + rb):
+            assert torch.equal(_bits(got), _bits(want)), f"call {i} ({c.w.name}) differs"
+    log(f"    {2 * len(outs)} calls on two streams, every one bit-identical to the first")
+
+
+def test_graph_replays_find_their_queue_slot_zeroed():
+    """A captured call keeps the queue slot it took at capture time; every
+    replay finds it zeroed again (the last workgroup of the previous launch
+    zeroed it), with eager calls of another plan between the replays.  The
+    capture holds the forward and the no-allocation backward; outputs are
+    prefilled with NaN before each replay."""
+    c = _Case(small_workload(408, 40, 6, 3, 1, heads=2))
+    other = _Case(small_workload(409, 50, 5, 1, 1, heads=1))
+    x = c.x
+    o, to = torch.empty_like(x["q"]), torch.empty_like(x["q"])
+    lse = torch.empty(c.w.shape[:3], dtype=torch.float32, device="cuda")
+    dq, dk, dv = (torch.empty_like(x["q"]) for _ in range(3))
+
+    def call():
+        aj.attn_jvp_fwd(c.plan, *(x[t] for t in TENSORS), o, to, lse)
+        aj.attn_jvp_bwd_noalloc(c.plan, x["q"], x["k"], x["v"], o, lse, c.d_o, dq, dk, dv)
+
+    def nan_fill():
+        for t in (o, to, lse, dq, dk, dv):
+            t.fill_(float("nan"))
+
+    nan_fill()
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (o, to, lse, dq, dk, dv)]
+    for t in ref:
+        assert not torch.isnan(t).any()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one call on the capture stream before capturing
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for r in range(4):
+        nan_fill()
+        g.replay()
+        for _ in range(3):
+            other.fwd()
+            other.bwd()
+        torch.cuda.synchronize()
+        for got, want in zip((o, to, lse, dq, dk, dv), ref):
+            assert torch.equal(_bits(got), _bits(want)), f"replay {r} differs from the eager call"
+    log("    4 graph replays, each bit-identical to the eager call")
