@@ -222,8 +222,9 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   const MaskGeom g = p.g;
   const int N = g.seq_len;
   // Workgroups take the heavy-first order (range-list plans: the table's) in
-  // XCD groups of kFwdXcdGroup, as the forward does, small teacher-forcing
-  // grids included (rank-major groups of 32: 1.4 % faster at 3 heads).
+  // XCD groups of kFwdXcdGroup from the per-XCD work queues, as the forward
+  // does, small teacher-forcing grids included (rank-major groups of 32: 1.4 %
+  // faster at 3 heads).
   const int n_tasks = p.n_slices * p.n_qblocks;
   const int pos = workgroup_task(p.queues, n_tasks);
   if (pos < 0) return;  // the queues were empty: no task for this workgroup
@@ -570,7 +571,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
   // Key blocks are cut per side like query blocks; index order is heavy
   // first (the earliest keys of a side are seen by the most rows).  Groups of
   // 16 neighbouring key blocks, which stream nearly the same query tiles, run
-  // on one XCD (a quarter of the fetches past L2 of plain round robin).
+  // on one XCD (a quarter of the fetches past L2 of plain round robin); the
+  // workgroups take them from the per-XCD work queues.
   const int n_tasks = p.n_slices * p.n_kblocks;
   const int pos = workgroup_task(p.queues, n_tasks);
   if (pos < 0) return;  // the queues were empty: no task for this workgroup

@@ -93,9 +93,11 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdParams p) {
 
   const MaskGeom g = p.g;
   const int N = g.seq_len;
-  // Workgroups take the heavy-first order in XCD groups of kFwdXcdGroup
-  // (launch_task): neighbouring blocks of that order, which stream nearly the
-  // same key tiles, share an XCD's L2.  Clean-tangent-zero plans group their
+  // Workgroups take the positions of the heavy-first order, in XCD groups of
+  // kFwdXcdGroup (launch_task), from the per-XCD work queues (take_task):
+  // neighbouring blocks of that order, which stream nearly the same key tiles,
+  // share an XCD's L2, and an XCD that finishes its share early takes the
+  // rest of another's.  Clean-tangent-zero plans group their
   // balanced order (8 clean and 8 noisy blocks in turn, so every group holds
   // both sides) and keep it in index order on small grids, where that was
   // 3 % faster than heavy first across heads.  On small grids general
