@@ -283,10 +283,10 @@ int attn_jvp_plan_bwd_info(const attn_jvp_plan* plan, int32_t* block_q, int32_t*
  * 8 XCDs round robin).  Ranks within a slice are heavy first (the earliest
  * keys of a side are seen by the most rows; range-list plans: the key blocks
  * that stream more query tiles first, in the table's order).  Orders of at
- * least 2048 tasks and 2 rounds of 128: each round gives each XCD a group of
- * 16 consecutive positions of a rank-major sequence (16 neighbouring key
+ * least 2048 tasks and 2 rounds of 256: each round gives each XCD a group of
+ * 32 consecutive positions of a rank-major sequence (32 neighbouring key
  * blocks of one slice, which stream nearly the same query tiles through that
- * XCD's L2: the rank group 0 of every slice, then rank group 1, ...; where 16
+ * XCD's L2: the rank group 0 of every slice, then rank group 1, ...; where 32
  * does not divide n_key_blocks, the task order itself), the group-to-XCD
  * direction alternating from round to round; only an even number of rounds
  * is grouped, the rest follows the sequence.  Smaller orders: rank b / (B H)
@@ -362,7 +362,7 @@ int attn_jvp_key_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
  * the query blocks (more streamed tiles first).  "Workgroup t" is the
  * logical task t: over the whole B H grid, the tasks are ordered in XCD
  * groups of 128 under the rule of attn_jvp_bwd_launch_order (there with
- * groups of 16) and taken from its per-XCD queues, except on the smaller
+ * groups of 32) and taken from its per-XCD queues, except on the smaller
  * grids: there clean-tangent-zero plans keep the index order, and general
  * teacher-forcing plans go heavy first across the slices in groups of 32
  * consecutive tasks of one slice.  (The bf16 kernel without tangents of

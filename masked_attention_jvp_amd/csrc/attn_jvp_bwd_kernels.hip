@@ -570,7 +570,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dkdv_bf16_kernel(BwdParams p) 
   const int N = g.seq_len;
   // Key blocks are cut per side like query blocks; index order is heavy
   // first (the earliest keys of a side are seen by the most rows).  Groups of
-  // 16 neighbouring key blocks, which stream nearly the same query tiles, run
+  // 32 neighbouring key blocks, which stream nearly the same query tiles, run
   // on one XCD (a quarter of the fetches past L2 of plain round robin); the
   // workgroups take them from the per-XCD work queues.
   const int n_tasks = p.n_slices * p.n_kblocks;

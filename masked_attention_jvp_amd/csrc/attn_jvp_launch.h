@@ -105,7 +105,7 @@ hipError_t launch_fwd(int dtype, int head_dim, int grid, const FwdParams& p, hip
 void bwd_block_sizes(int dtype, int head_dim, int* block_q, int* block_kv);
 
 // Key blocks per XCD group of the dk/dv kernel's launch order (launch_task).
-constexpr int kDkdvXcdGroup = 16;
+constexpr int kDkdvXcdGroup = 32;
 // Query blocks per XCD group of the forward + JVP's launch order (general
 // descriptor plans and range-list plans) and of the bf16 primal kernel's.
 constexpr int kFwdXcdGroup = 128;

@@ -280,7 +280,7 @@ def test_range_bwd_launch_order_is_the_table_order_under_the_xcd_rule(name, b, h
     rank = np.empty(nk, np.int64)
     rank[corder] = np.arange(nk)
     tasks = (order // nk) * nk + rank[order % nk]
-    assert check_launch_rule(tasks, total, nk, 16) == regime
+    assert check_launch_rule(tasks, total, nk, 32) == regime  # kDkdvXcdGroup
 
 
 def test_bwd_table_argument_errors_before_any_device_call():
