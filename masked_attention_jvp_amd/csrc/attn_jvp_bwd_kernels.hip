@@ -19,7 +19,10 @@
 //   V dO^T - delta (score products in vector-register form, the second one
 //   started from -delta instead of 0), P^T = exp2(S^T scale log2(e) -
 //   lse log2(e)), dS^T = P^T o (dP^T - delta), then dQ^T += K^T dS^T with K^T
-//   from the transposing LDS read of the K tile.
+//   from the transposing LDS read of the K tile.  Two versions with the same
+//   arithmetic: descriptor plans run bwd_dq2_bf16_kernel, two workgroups per
+//   CU; range-list plans, whose tile entries take another 30 KB of LDS, run
+//   bwd_dq_bf16_kernel, one workgroup per CU with a cross-tile pipeline.
 // * dk/dv kernel: one workgroup per block of 32 NW keys, cut per side like
 //   the query blocks, over the 32-row query tiles of the rows that attend to
 //   any of its keys (at most two intervals); lane = key.  Per query tile:
@@ -518,6 +521,224 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
       if (!more) break;
     }
     // DMAs past the last tile and the last K, V reads may be in flight
+    wait_vmcnt<0>();
+    wait_lgkmcnt<0>();
+    barrier_nofence();
+  }
+
+  // ---- epilogue: dq = scale acc
+  acc_hazard_wait();
+  if (row_ok) {
+    const float scale = p.scale;
+    uint16_t* Qg = (uint16_t*)p.dq + base + (size_t)row * D;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * c + 8 * g4 + 4 * h;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc_read(accQ[c][4 * g4 + e]) * scale;
+        *(u32x2*)(Qg + d0) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq kernel (bf16) at two workgroups per CU.  The work, the tile order and
+// the order of every sum are those of bwd_dq_bf16_kernel above, so its dq is
+// bit-identical; the schedule differs.  With at most 256 registers per lane
+// and a 4-stage ring (64 KB), two workgroups share a CU and each SIMD holds
+// two waves, so the SIMD issues one wave's MFMAs while the other wave runs
+// its exponentials, waits or LDS reads: the hardware interleaving takes the
+// place of the cross-tile software pipeline above, which needs 328 registers.
+// Step j: barrier (tile j has landed, every read of tile j-1 is complete),
+// DMA of tile j+3 into tile j-1's stage under S^T and dP^T of tile j, then
+// the mask, exponentials and dS^T, then dQ^T += K^T dS^T.  A wave raises
+// its issue priority over its two MFMA phases, so that the SIMD keeps
+// feeding the matrix core from the wave that has products ready while the
+// other one runs its exponentials.
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64, 2) bwd_dq2_bf16_kernel(BwdParams p) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  using TG = TileGeom<D, NW>;
+  constexpr int BC = TG::ROWS;  // keys per tile
+  constexpr int BR = NW * 32;   // query rows per block
+  constexpr int KS = TG::KS, DC = TG::DC, NG = TG::NG, TILE = TG::TILE, LOADS = TG::LOADS;
+  constexpr int LPT = 2 * LOADS;  // DMA instructions per wave and tile: K, V
+  // Ring: tile t in stage t % STAGES, issued AHEAD steps before its use.  The
+  // barrier at the top of step j follows each wave's wait for its share of
+  // tile j and the MFMAs that consumed all its reads of tile j-1, whose
+  // stage the step then refills with tile j + AHEAD.
+  constexpr int STAGES = 4, AHEAD = 3;
+  static_assert(AHEAD == STAGES - 1, "the refilled stage is the previous tile's");
+
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[STAGES][2 * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+
+  const MaskGeom g = p.g;
+  const int N = g.seq_len;
+  const int n_tasks = p.n_slices * p.n_qblocks;
+  const int pos = workgroup_task(p.queues, n_tasks);
+  if (pos < 0) return;  // the queues were empty: no task for this workgroup
+  const int task = launch_task(pos, n_tasks, p.n_qblocks, kFwdXcdGroup, g.tf ? kSmallRankGroups : kSmallAcross);
+  const int bh = task / p.n_qblocks;
+  int r0, r1;
+  const int qb = heavy_first_qblock(g, BR, task - bh * p.n_qblocks);
+  qblock_rows(g, BR, qb, &r0, &r1);
+  const TileSpans sp = block_tiles(block_ranges(g, r0, r1), BC);
+  const int ntiles = span_count(sp);
+
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const int slice_bytes = N * D * 2;
+  const i32x4_t desc_k = make_desc((const uint16_t*)p.k + base, slice_bytes);
+  const i32x4_t desc_v = make_desc((const uint16_t*)p.v + base, slice_bytes);
+
+  const int row = r0 + wave * 32 + n;
+  const bool row_ok = row < r1;
+  const Ranges rr = row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0};
+
+  u32x4 qf[KS], dof[KS];
+  float ndelta, nl;
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)p.q + base, slice_bytes);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const uint16_t*)p.dout + base, slice_bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const uint16_t*)p.o + base, slice_bytes);
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int off = (row * D + 16 * s + 8 * h) * 2;
+      qf[s] = load16(rq, off);
+      dof[s] = load16(rdo, off);
+      const u32x4 of = load16(ro, off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part = fmaf(bf16_lo(dof[s][e]), bf16_lo(of[e]), part);
+        part = fmaf(bf16_hi(dof[s][e]), bf16_hi(of[e]), part);
+      }
+    }
+    ndelta = -pair_sum(part);
+    const float lse = row_ok ? p.lse[(size_t)bh * N + row] : 0.f;
+    nl = -lse * kLog2e;
+    if (row_ok) p.ws[(size_t)bh * 2 * N + (size_t)h * N + row] = h ? nl : ndelta;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      keep_in_acc(qf[s]);
+      keep_in_acc(dof[s]);
+    }
+  }
+  f32x16 negd;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negd[i] = ndelta;
+
+  auto stage = [&](auto st) -> uint16_t* { return ring[decltype(st)::value]; };
+  int dma_voff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) dma_voff[i] = TG::dma_voff(wave, lane, i);
+  // LDS byte address of this wave's first DMA block in stage 0 (scalar)
+  const int lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(&ring[0][0])) + wave * LOADS * 1024;
+  auto issue_part = [&](int stg, int t, int q, int t_end) {
+    const int tile = span_tile(sp, t < t_end ? t : t_end - 1);
+    const int soff = tile * BC * D * 2;
+    const int i = q >> 1, tt = q & 1;
+    load16_lds_at(tt ? desc_v : desc_k, lds_wave + stg * 4 * TILE + tt * 2 * TILE + i * 1024, dma_voff[i], soff);
+  };
+
+  f32x16 accQ[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) accQ[c][i] = 0.f;
+  }
+  const float sl2 = p.score_log2;
+
+  Ranges wfirst{0, 0, 0, 0}, wlast{0, 0, 0, 0};
+  {
+    const int wa = r0 + wave * 32;
+    const int wb = wa + 32 < r1 ? wa + 32 : r1;
+    if (wa < wb) {
+      wfirst = row_ranges(g, wa);
+      wlast = row_ranges(g, wb - 1);
+    }
+  }
+  const StepRange w1 = span_steps_in(sp, first_whole_tile(wlast.lo1, BC), end_whole_tile(wfirst.hi1, BC));
+  const StepRange w2 = span_steps_in(sp, first_whole_tile(wlast.lo2, BC), end_whole_tile(wfirst.hi2, BC));
+  auto tile_whole = [&](int t) { return in_steps(w1, t) || in_steps(w2, t); };
+
+  auto step = [&](auto st, int j) {
+    constexpr int ST = decltype(st)::value;
+    using AH = IC<(ST + AHEAD) % STAGES>;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) keep_in_acc(accQ[c]);
+    // this wave's share of tile j has landed (tiles j+1, j+2 may be in
+    // flight); behind the barrier every wave's share has, and every read of
+    // tile j-1, whose stage is refilled below, is complete
+    wait_vmcnt<(AHEAD - 1) * LPT>();
+    barrier_nofence();
+    const uint16_t* cur = stage(st);
+    u32x4 kf[KS], vf[KS];
+    auto kvread = [&](int s) {
+      kf[s] = TG::row_frag(cur, n, h, s);
+      vf[s] = TG::row_frag(cur + TILE, n, h, s);
+    };
+    f32x16 S, DP;
+    kvread(0);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s + 1 < KS) kvread(s + 1);
+      if (s == 0) mfma_v_first_ba(S, kf[s], qf[s]);
+      else mfma_v_acc_ba(S, kf[s], qf[s]);
+      if (s == 0) mfma_v_init_ba(DP, vf[s], dof[s], negd);
+      else mfma_v_acc_ba(DP, vf[s], dof[s]);
+#pragma unroll
+      for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q) issue_part(AH::value, j + AHEAD, q, ntiles);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    u32x4 ktf[NG];
+    ktf[0] = TG::tr_frag(cur, lane, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    acc_hazard_wait();
+    __builtin_amdgcn_sched_barrier(0);
+    if (!tile_whole(j)) mask_scores(S, span_tile(sp, j) * BC, h, rr);  // partial tiles only
+    u32x4 DS[2];
+#pragma unroll
+    for (int jj = 0; jj < 16; jj += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(S[jj], sl2, nl));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(S[jj + 1], sl2, nl));
+      DS[jj >> 3][(jj & 7) >> 1] = pack_bf16(p0 * DP[jj], p1 * DP[jj + 1]);
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int gidx = 0; gidx < NG; ++gidx) {
+      if (gidx + 1 < NG) ktf[gidx + 1] = TG::tr_frag(cur, lane, gidx + 1);
+      const int c2 = gidx / DC, c = gidx % DC;
+      accQ[c] = mfma_bf16(ktf[gidx], DS[c2], accQ[c]);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  if (ntiles > 0) {
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) {
+#pragma unroll
+      for (int q = 0; q < LPT; ++q) issue_part(i, i, q, ntiles);
+    }
+    for (int j = 0; j < ntiles; j += STAGES) {
+      const bool more = unrolled_while<0, STAGES>([&](auto st) {
+        constexpr int S = decltype(st)::value;
+        step(st, j + S);
+        return j + S + 1 < ntiles;
+      });
+      if (!more) break;
+    }
+    // DMAs past the last tile may be in flight
     wait_vmcnt<0>();
     wait_lgkmcnt<0>();
     barrier_nofence();
@@ -1118,8 +1339,12 @@ void launch_bwd_kernels(int dtype, int bh, const BwdParams& p, hipStream_t strea
   if (dtype == kBf16) {
     // both kernels take their tasks from the call's work queues, one after the other
     const dim3 block(kBf16Waves * 64);
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, kBf16Waves, TABLE>), dim3((unsigned)queue_grid((int)gq.x)), block, 0,
-                       stream, p);
+    if constexpr (TABLE)
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, kBf16Waves, true>), dim3((unsigned)queue_grid((int)gq.x)), block, 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dq2_bf16_kernel<D, kBf16Waves>), dim3((unsigned)queue_grid((int)gq.x)), block, 0,
+                         stream, p);
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, kBf16Waves, TABLE>), dim3((unsigned)queue_grid((int)gk.x)), block, 0,
                        stream, p);
   } else {

@@ -131,6 +131,13 @@ __device__ __forceinline__ void load16_lds_asm(i32x4_t r, uint16_t* lds, int vof
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voff), "s"(r), "s"(so), "{m0}"(m0) : "memory");
 }
+// The same with the LDS byte address given as a wave-uniform integer.
+__device__ __forceinline__ void load16_lds_at(i32x4_t r, int lds_byte, int voff, int soff) {
+  const int m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+  const int so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(r), "s"(so), "{m0}"(m0) : "memory");
+}
 // 4 bytes per lane into LDS at lds + 4 * lane (same scheme as above).
 __device__ __forceinline__ void load4_lds_asm(i32x4_t r, float* lds, int voff, int soff) {
   const int m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
