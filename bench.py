@@ -402,8 +402,10 @@ def main():
     kernel = (f"{dq_kernel} + bwd_dkdv_bf16_kernel<{w.head_dim},{nw},{tb}>"
               if args.backward
               else f"fwd_bf16_kernel<{w.head_dim},{nw},true,true> (primal tile mode)" if args.primal and use_ranges
-              else f"fwd_primal_bf16_kernel<{w.head_dim},{nw}>" if args.primal
-              else f"fwd_bf16_kernel<{w.head_dim},{nw},{'true' if flags else 'false'},{'true' if use_ranges else 'false'}>")
+              else f"fwd_bf16_kernel<{w.head_dim},{nw},true,false,true> (primal-only)" if args.primal
+              else (f"fwd_bf16_kernel<{w.head_dim},{nw},true,false,true> (clean side) + "
+                    f"fwd_bf16_kernel<{w.head_dim},{nw},true,false> (noisy side)") if flags
+              else f"fwd_bf16_kernel<{w.head_dim},{nw},false,{'true' if use_ranges else 'false'}>")
 
     out = {
         "metric": METRIC_BWD if args.backward else METRIC_PRIMAL if args.primal else METRIC,

@@ -715,6 +715,7 @@ int fwd_common(const attn_jvp_plan* p, const void* table, const void* q, const v
   fp.score_log2 = p->scale * 1.4426950408889634f;
   fp.ctz = (p->flags & ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO) ? 1 : 0;
   fp.primal = 0;
+  fp.side = -1;
   if (primal) {  // the clean-tangent-zero kernel with every block in its primal mode
     fp.tq = fp.tk = fp.tv = q;  // never read
     fp.to = nullptr;
@@ -730,8 +731,6 @@ int fwd_common(const attn_jvp_plan* p, const void* table, const void* q, const v
     fp.tb_rows = t + p->rs->off_rows;
     fp.tb_iv = t + p->rs->off_iv;
   }
-  // the bf16 primal kernel (descriptor plans) takes query blocks of 64 rows per wave
-  if (primal && p->dtype == ATTN_JVP_BF16 && !table) fp.n_qblocks = n_query_blocks(p->g, kBf16PrimalRows);
   st = queue_slot(dev, &fp.queues);
   if (st != ATTN_JVP_OK) return st;
   const int grid = p->batch * p->heads * fp.n_qblocks;

@@ -12,7 +12,6 @@ constexpr int kBf16 = 0;
 constexpr int kFp32 = 1;
 constexpr int kBf16Waves = 4;   // waves per bf16 workgroup; 32 query rows per wave
 constexpr int kBf16BlockK = 32;  // keys per bf16 tile
-constexpr int kBf16PrimalRows = kBf16Waves * 64;  // rows per block of the bf16 primal kernel (64 per wave)
 
 // Range-list plans: the bf16 kernel stages a query block's tile entries in
 // LDS next to the 128 KB ring, so a block may stream at most this many tiles.
@@ -35,6 +34,7 @@ struct FwdParams {
   float scale;
   int32_t ctz;        // clean-tangent-zero plan (teacher forcing only)
   int32_t primal;     // with ctz: every block forms o and lse only (no tangents; to may be null)
+  int32_t side;       // teacher forcing: -1 every query block, 0 the clean side's only, 1 the noisy side's
   // range-list plans (all null otherwise): sections of the device table
   const int32_t* tb_blk;    // [n_qblocks + 1] first entry of each query block
   const int32_t* tb_order;  // [n_qblocks] launch order
@@ -106,10 +106,8 @@ void bwd_block_sizes(int dtype, int head_dim, int* block_q, int* block_kv);
 
 // Key blocks per XCD group of the dk/dv kernel's launch order (launch_task).
 constexpr int kDkdvXcdGroup = 32;
-// Query blocks per XCD group of the forward + JVP's launch order (general
-// descriptor plans and range-list plans) and of the bf16 primal kernel's.
+// Query blocks per XCD group of the forward + JVP's launch order.
 constexpr int kFwdXcdGroup = 128;
-constexpr int kPrimalXcdGroup = 64;
 
 // Launch the backward (dq kernel, then dk/dv kernel) for bh = B * H slices.
 hipError_t launch_bwd(int dtype, int head_dim, int bh, const BwdParams& p, hipStream_t stream);

@@ -56,7 +56,7 @@ def test_shard_forward_equals_the_full_grid_bitwise(cfg):
     for a, b in ((so, o), (sto, to), (slse, lse)):
         assert torch.equal(_bits(a), _bits(b[:, :SHARD_HEADS].contiguous()))
     if cfg == 3:
-        # the primal kernel's own grid (256-row blocks, 768 of them) on the shard
+        # the primal-only kernel (two workgroups per CU) on the shard
         po, plse = aj.masked_attention_fwd(xs["q"], xs["k"], xs["v"], shard.desc, return_lse=True)
         torch.cuda.synchronize()
         assert torch.equal(_bits(po), _bits(so)) and torch.equal(_bits(plse), _bits(slse))

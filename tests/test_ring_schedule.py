@@ -123,7 +123,7 @@ def test_forward_ring_is_hazard_free():
     # the first K reads of tile j+2.
     fwd = os.path.join(os.path.dirname(SRC), "attn_jvp_kernels.hip")
     text = open(fwd).read()
-    kernel = text[text.index("fwd_bf16_kernel(FwdParams p)"):text.index("fwd_primal_bf16_kernel(FwdParams p)")]
+    kernel = text[text.index("fwd_bf16_kernel(FwdParams p)"):text.index("fwd_fp32_kernel(FwdParams p)")]
     S = int(re.search(r"constexpr int STAGES = (\d+);", kernel).group(1))
     A = int(re.search(r"using AH = std::integral_constant<int, \(ST \+ (\d+)\) % STAGES>;", kernel).group(1))
     assert (S, A) == (4, 3)
