@@ -7,11 +7,12 @@ a task zeroes the slot again.  If a slot were left non-zero, or a position were
 handed out twice or not at all, a later call would skip or repeat query or
 key blocks.  So: more calls than there are slots (every slot is used at least
 twice), alternating plans whose grids have fewer tasks than XCDs, one task
-per XCD and many, forward + JVP, the backward (whose two kernels use one slot
-one after the other) and range-list plans; every output prefilled with NaN
-and every call's bits equal to the first call's.  Then calls that overlap on
-two streams, and replays of a captured HIP graph (whose launches keep the
-slot they took at capture) between eager calls.
+per XCD and many, forward + JVP, the forward without tangents, the backward
+and the clean-tangent-zero forward (whose two kernels each use one slot one
+after the other) and range-list plans; every output prefilled with NaN and
+every call's bits equal to the first call's.  Then calls that overlap on two
+streams, and replays of a captured HIP graph (whose launches keep the slot
+they took at capture) between eager calls.
 """
 import pytest
 import torch
@@ -39,7 +40,7 @@ def _bits(t):
 class _Case:
     """One plan and its inputs; fwd() and bwd() return fresh NaN-prefilled outputs."""
 
-    def __init__(self, w, ranges=False):
+    def __init__(self, w, ranges=False, ctz=False):
         self.w = w
         self.x = device_inputs(w)
         if ranges:
@@ -47,7 +48,8 @@ class _Case:
             self.plan = aj.attn_jvp_create_ranges(n_tok, groups, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16)
             self.table = torch.from_numpy(aj.attn_jvp_plan_table(self.plan)).cuda()
         else:
-            self.plan = aj.attn_jvp_create(w.desc, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16)
+            flags = aj.ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO if ctz else 0
+            self.plan = aj.attn_jvp_create_ex(w.desc, w.batch, w.heads, w.head_dim, aj.ATTN_JVP_BF16, 0.0, flags)
             self.table = None
         self.n_tasks = w.batch * w.heads * self.plan.info["n_query_blocks"]
         self.d_o = torch.randn_like(self.x["q"], dtype=torch.float32).to(torch.bfloat16)
@@ -67,6 +69,16 @@ class _Case:
             aj.attn_jvp_fwd_table(self.plan, self.table, *(x[t] for t in TENSORS), o, to, lse)
         return o, to, lse
 
+    def prim(self):
+        x = self.x
+        o = self._nan(x["q"])
+        lse = torch.full(self.w.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+        if self.table is None:
+            aj.attn_jvp_fwd_primal(self.plan, x["q"], x["k"], x["v"], o, lse)
+        else:
+            aj.attn_jvp_fwd_primal_table(self.plan, self.table, x["q"], x["k"], x["v"], o, lse)
+        return o, lse
+
     def bwd(self):
         x = self.x
         dq, dk, dv = (self._nan(x["q"]) for _ in range(3))
@@ -84,23 +96,26 @@ def test_queue_slots_are_reused_and_every_call_is_complete():
         _Case(small_workload(402, 50, 5, 1, 1, heads=2)),            # 8 tasks: one per XCD
         _Case(small_workload(403, 37, 30, 2, 1, heads=3, batch=2)),  # 108 tasks
         _Case(small_workload(404, 40, 6, 3, 1, heads=2), ranges=True),
+        _Case(small_workload(405, 50, 5, 1, 1, heads=1), ctz=True),   # 2 + 2 tasks in two launches
+        _Case(small_workload(410, 37, 30, 2, 1, heads=3, batch=2), ctz=True),
     ]
     for c in cases:
         log(f"[queues] {c.w.name} desc={c.w.desc} B={c.w.batch} H={c.w.heads} tasks={c.n_tasks} "
             f"ranges={c.table is not None}")
-    ref = [(c.fwd(), c.bwd()) for c in cases]
+    ref = [(c.fwd(), c.prim(), c.bwd()) for c in cases]
     torch.cuda.synchronize()
-    for (f, b) in ref:
-        for t in f + b:
+    for (f, pr, b) in ref:
+        for t in f + pr + b:
             assert not torch.isnan(t).any(), "a block was never computed"
     calls = 0
     it = 0
     while calls < 2 * N_SLOTS + 16:
-        for c, (rf, rb) in zip(cases, ref):
+        for c, (rf, rp, rb) in zip(cases, ref):
             f = c.fwd()
+            pr = c.prim()
             b = c.bwd()
-            calls += 2
-            for got, want in zip(f + b, rf + rb):
+            calls += 3
+            for got, want in zip(f + pr + b, rf + rp + rb):
                 if not torch.equal(_bits(got), _bits(want)):
                     torch.cuda.synchronize()
                     raise AssertionError(f"call {calls} ({c.w.name}): outputs differ from the first call's")
@@ -177,3 +192,49 @@ def test_graph_replays_find_their_queue_slot_zeroed():
         for got, want in zip((o, to, lse, dq, dk, dv), ref):
             assert torch.equal(_bits(got), _bits(want)), f"replay {r} differs from the eager call"
     log("    4 graph replays, each bit-identical to the eager call")
+
+
+def test_graph_replays_of_the_two_launch_calls():
+    """A captured clean-tangent-zero forward (two launches, one slot) and a
+    forward without tangents, replayed between eager calls of other plans;
+    every replay bit-identical to the eager calls."""
+    c = _Case(small_workload(411, 40, 6, 3, 1, heads=2), ctz=True)
+    other = _Case(small_workload(412, 50, 5, 1, 1, heads=1))
+    x = c.x
+    o, to, po = torch.empty_like(x["q"]), torch.empty_like(x["q"]), torch.empty_like(x["q"])
+    lse, plse = (torch.empty(c.w.shape[:3], dtype=torch.float32, device="cuda") for _ in range(2))
+
+    def call():
+        aj.attn_jvp_fwd(c.plan, *(x[t] for t in TENSORS), o, to, lse)
+        aj.attn_jvp_fwd_primal(c.plan, x["q"], x["k"], x["v"], po, plse)
+
+    def nan_fill():
+        for t in (o, to, po, lse, plse):
+            t.fill_(float("nan"))
+
+    nan_fill()
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (o, to, po, lse, plse)]
+    for t in ref:
+        assert not torch.isnan(t).any()
+    assert torch.equal(_bits(ref[2]), _bits(ref[0])) and torch.equal(_bits(ref[4]), _bits(ref[3]))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for r in range(4):
+        nan_fill()
+        g.replay()
+        for _ in range(3):
+            other.fwd()
+            other.prim()
+        torch.cuda.synchronize()
+        for got, want in zip((o, to, po, lse, plse), ref):
+            assert torch.equal(_bits(got), _bits(want)), f"replay {r} differs from the eager call"
+    log("    4 graph replays of the clean-tangent-zero and primal calls, each bit-identical")
