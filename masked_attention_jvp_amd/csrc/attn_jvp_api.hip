@@ -723,6 +723,7 @@ int fwd_common(const attn_jvp_plan* p, const void* table, const void* q, const v
     fp.primal = 1;
   }
   fp.tb_blk = fp.tb_order = fp.tb_ent = fp.tb_rows = fp.tb_iv = nullptr;
+  fp.tb_max_entries = table ? p->rs->max_entries : 0;
   if (table) {
     const int32_t* t = (const int32_t*)table;
     fp.tb_blk = t + p->rs->off_blk;

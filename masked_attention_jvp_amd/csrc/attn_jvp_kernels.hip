@@ -69,12 +69,14 @@ __global__ void __launch_bounds__(NW * 64, PO ? 2 : 1) fwd_bf16_kernel(FwdParams
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   // Range-list plans have no clean-tangent-zero option: with a table, the
   // CTZ instance is the primal-only kernel (o and lse, every tile in kPrimal).
-  // PO: the primal-only kernel for descriptor plans (calls without tangents,
-  // and the clean side of a clean-tangent-zero plan).  Its ring holds K and V
-  // only (64 KB) and it fits 256 registers, so two workgroups share a CU and
-  // each SIMD holds two waves: the hardware issues one wave's MFMAs under the
-  // other's softmax.  Every row's arithmetic is the primal tile mode's.
-  static_assert(!PO || (CTZ && !TABLE), "PO is a clean-tangent-zero descriptor instance");
+  // PO: the primal-only kernel at two workgroups per CU (calls without
+  // tangents, and the clean side of a clean-tangent-zero plan; with a table,
+  // range-list blocks of at most kPoMaxTableEntries tiles).  Its ring holds K
+  // and V only (64 KB) and it fits 256 registers, so two workgroups share a
+  // CU and each SIMD holds two waves: the hardware issues one wave's MFMAs
+  // under the other's softmax.  Every row's arithmetic is the primal tile
+  // mode's.
+  static_assert(!PO || CTZ, "PO is a primal-only instance");
   constexpr int BC = kBf16BlockK;            // keys per tile (= one MFMA subtile)
   static_assert(BC == 32, "one 32-key subtile per tile");
   constexpr int STAGES = 4;                  // LDS ring depth; tiles j..j+3 resident or in flight
@@ -142,7 +144,7 @@ __global__ void __launch_bounds__(NW * 64, PO ? 2 : 1) fwd_bf16_kernel(FwdParams
   // << (24 + w)) staged in LDS for the whole task.
   int32_t* ent = nullptr;
   if constexpr (TABLE) {
-    __shared__ int32_t ent_buf[kMaxTableEntries];
+    __shared__ int32_t ent_buf[PO ? kPoMaxTableEntries : kMaxTableEntries];
     for (int i = tid; i < ntiles; i += NW * 64) ent_buf[i] = p.tb_ent[e0 + i];
     __syncthreads();
     ent = ent_buf;
@@ -984,8 +986,13 @@ hipError_t launch_fwd(int dtype, int head_dim, int grid, const FwdParams& p0, hi
     return hipGetLastError();
   }
   if (dtype == kBf16 && table && p.primal) {  // range-list plans without tangents
-    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, true, true>), qgrid, block, 0, stream, p);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, true, true>), qgrid, block, 0, stream, p);
+    if (p.tb_max_entries <= kPoMaxTableEntries) {
+      if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, true, true, true>), qgrid, block, 0, stream, p);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, true, true, true>), qgrid, block, 0, stream, p);
+    } else {
+      if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, true, true>), qgrid, block, 0, stream, p);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, true, true>), qgrid, block, 0, stream, p);
+    }
     return hipGetLastError();
   }
   if (dtype == kBf16 && p.ctz && !table) {

@@ -16,6 +16,11 @@ constexpr int kBf16BlockK = 32;  // keys per bf16 tile
 // Range-list plans: the bf16 kernel stages a query block's tile entries in
 // LDS next to the 128 KB ring, so a block may stream at most this many tiles.
 constexpr int kMaxTableEntries = 7680;
+// The primal-only instance (K and V in a 64 KB ring) fits two workgroups per
+// CU with at most this many entries staged (64 KB + 15.5 KB + the queue word
+// each); range-list plans whose blocks stream more take the one-workgroup
+// instance.
+constexpr int kPoMaxTableEntries = 3968;
 constexpr int32_t kTableMagic = 0x314a5441;  // "ATJ1"
 
 struct FwdParams {
@@ -41,6 +46,7 @@ struct FwdParams {
   const int32_t* tb_ent;    // tile | (whole bit of wave w) << (24 + w)
   const int32_t* tb_rows;   // [N] (first interval << 8) | interval count
   const int32_t* tb_iv;     // (lo, hi) pairs
+  int32_t tb_max_entries;   // the most entries any query block streams
   // bf16 kernels: the work queues of this call (kQueueWords words, take_task)
   // and the number of tasks, (b, h) slices x n_qblocks
   int32_t* queues;

@@ -134,3 +134,22 @@ def test_range_primal_error_paths():
     assert e.value.code == 1
     with pytest.raises(aj.AttnJvpError):  # table too short
         aj.attn_jvp_fwd_primal_table(plan, table[:4], x["q"], x["k"], x["v"], o)
+
+
+@pytest.mark.parametrize("n_tiles", [3968, 3969])
+def test_range_primal_at_the_two_workgroup_entry_limit(n_tiles):
+    """Range-list plans run the primal-only forward at two workgroups per CU
+    when no query block streams more than 3968 key tiles, and the
+    one-workgroup instance otherwise: one block of 128 rows sees all keys,
+    the others one tile.  Both sides of the limit give o and lse of the
+    forward + JVP bit for bit."""
+    n = 32 * n_tiles
+    groups = ((0, 128, ((0, n),)), (128, n, ((0, 32),)))
+    w = small_workload(431, n, 1, 1, 0, heads=1, d=64)
+    log(f"[range primal] entry limit: {n} tokens, {n_tiles} tiles in the first block")
+    x = device_inputs(w)
+    o_ref, _, lse_ref = aj.masked_attention_jvp_ranges(*(x[t] for t in TENSORS), groups, return_lse=True)
+    o, lse = aj.masked_attention_fwd_ranges(x["q"], x["k"], x["v"], groups, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o), _bits(o_ref)) and torch.equal(_bits(lse), _bits(lse_ref))
+    assert not torch.isnan(o.float()).any()
