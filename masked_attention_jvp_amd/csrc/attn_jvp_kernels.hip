@@ -1018,11 +1018,9 @@ hipError_t launch_fwd(int dtype, int head_dim, int grid, const FwdParams& p0, hi
   if (dtype == kBf16) {
     if (head_dim == 128) {
       if (table) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, false, true>), qgrid, block, 0, stream, p);
-      else if (p.ctz) hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, true, false>), qgrid, block, 0, stream, p);
       else hipLaunchKernelGGL((fwd_bf16_kernel<128, kBf16Waves, false, false>), qgrid, block, 0, stream, p);
     } else {
       if (table) hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, false, true>), qgrid, block, 0, stream, p);
-      else if (p.ctz) hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, true, false>), qgrid, block, 0, stream, p);
       else hipLaunchKernelGGL((fwd_bf16_kernel<64, kBf16Waves, false, false>), qgrid, block, 0, stream, p);
     }
   } else {
