@@ -398,7 +398,7 @@ def main():
     traffic = traffic_for(w.name, part)
     nw = info["block_q"] // 32
     tb = "true" if use_ranges else "false"
-    dq_kernel = f"bwd_dq_bf16_kernel<{w.head_dim},{nw},true>" if use_ranges else f"bwd_dq2_bf16_kernel<{w.head_dim},{nw}>"
+    dq_kernel = f"bwd_dq_bf16_kernel<{w.head_dim},{nw}>" if use_ranges else f"bwd_dq2_bf16_kernel<{w.head_dim},{nw}>"
     kernel = (f"{dq_kernel} + bwd_dkdv_bf16_kernel<{w.head_dim},{nw},{tb}>"
               if args.backward
               else f"fwd_bf16_kernel<{w.head_dim},{nw},true,true> (primal tile mode)" if args.primal and use_ranges

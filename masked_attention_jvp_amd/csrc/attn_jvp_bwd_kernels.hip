@@ -202,10 +202,13 @@ __device__ __forceinline__ void mask_scores_iv(f32x16& S, int x0, int h, const I
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// dq kernel (bf16).  One wave = 32 query rows; the K and V tiles of 32 keys
-// stream through the LDS ring.  TABLE: range-list plans, with the forward's
-// block order, tile lists and row intervals from the table.
-template <int D, int NW, bool TABLE>
+// dq kernel (bf16) of range-list plans, one workgroup per CU with a
+// cross-tile pipeline (the two-workgroup kernel below, given the tile
+// entries of a table, was not faster on these plans).  One wave = 32 query
+// rows; the K and V tiles of 32 keys stream through the LDS
+// ring; the forward's block order, tile lists and row intervals come from
+// the table.
+template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   using TG = TileGeom<D, NW>;
@@ -224,49 +227,31 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
 
   const MaskGeom g = p.g;
   const int N = g.seq_len;
-  // Workgroups take the heavy-first order (range-list plans: the table's) in
-  // XCD groups of kFwdXcdGroup from the per-XCD work queues, as the forward
-  // does, small teacher-forcing grids included (rank-major groups of 32: 1.4 %
-  // faster at 3 heads).
+  // Workgroups take the table's heavy-first order in XCD groups of
+  // kFwdXcdGroup from the per-XCD work queues, as the forward does.
   const int n_tasks = p.n_slices * p.n_qblocks;
   const int pos = workgroup_task(p.queues, n_tasks);
   if (pos < 0) return;  // the queues were empty: no task for this workgroup
-  const int task = launch_task(pos, n_tasks, p.n_qblocks, kFwdXcdGroup,
-                               (!TABLE && g.tf) ? kSmallRankGroups : kSmallAcross);
+  const int task = launch_task(pos, n_tasks, p.n_qblocks, kFwdXcdGroup, kSmallAcross);
   const int bh = task / p.n_qblocks;
-  int r0, r1, ntiles, e0 = 0;
-  TileSpans sp{0, 0, 0, 0};
-  if constexpr (TABLE) {
-    const int qb = p.tb_order[task - bh * p.n_qblocks];
-    r0 = qb * BR;
-    r1 = r0 + BR < N ? r0 + BR : N;
-    e0 = p.tb_blk[qb];
-    ntiles = p.tb_blk[qb + 1] - e0;
-  } else {
-    const int qb = heavy_first_qblock(g, BR, task - bh * p.n_qblocks);
-    qblock_rows(g, BR, qb, &r0, &r1);
-    sp = block_tiles(block_ranges(g, r0, r1), BC);
-    ntiles = span_count(sp);
-  }
-  // range-list plans: the block's tile entries (tile | whole bit of wave w
-  // << (24 + w)), staged in LDS for the whole task
-  int32_t* ent = nullptr;
-  if constexpr (TABLE) {
-    __shared__ int32_t ent_buf[kMaxTableEntries];
-    for (int i = tid; i < ntiles; i += NW * 64) ent_buf[i] = p.tb_ent[e0 + i];
-    __syncthreads();
-    ent = ent_buf;
-  }
+  const int qb = p.tb_order[task - bh * p.n_qblocks];
+  const int r0 = qb * BR;
+  const int r1 = r0 + BR < N ? r0 + BR : N;
+  const int e0 = p.tb_blk[qb];
+  const int ntiles = p.tb_blk[qb + 1] - e0;
+  // the block's tile entries (tile | whole bit of wave w << (24 + w)),
+  // staged in LDS for the whole task
+  __shared__ int32_t ent[kMaxTableEntries];
+  for (int i = tid; i < ntiles; i += NW * 64) ent[i] = p.tb_ent[e0 + i];
+  __syncthreads();
   auto entry = [&](int t) { return __builtin_amdgcn_readfirstlane(ent[t < ntiles ? t : ntiles - 1]); };
-  // Range-list plans: the raw entries a step needs (its DMA tile's and the
-  // next tile's) are read from LDS one step ahead, so that the step's top
-  // takes them without waiting for an LDS read.
+  // The raw entries a step needs (its DMA tile's and the next tile's) are
+  // read from LDS one step ahead, so that the step's top takes them without
+  // waiting for an LDS read.
   int pf_dma = 0, pf_next = 0;
   auto prefetch_entries = [&](int j) {
-    if constexpr (TABLE) {
-      pf_dma = ent[j + kBwdAhead < ntiles ? j + kBwdAhead : ntiles - 1];
-      pf_next = ent[j + 1 < ntiles ? j + 1 : ntiles - 1];
-    }
+    pf_dma = ent[j + kBwdAhead < ntiles ? j + kBwdAhead : ntiles - 1];
+    pf_next = ent[j + 1 < ntiles ? j + 1 : ntiles - 1];
   };
 
   const size_t base = (size_t)bh * (size_t)N * D;
@@ -276,13 +261,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
 
   const int row = r0 + wave * 32 + n;
   const bool row_ok = row < r1;
-  ItemIntervals riv{{0, 0, 0, 0}, 0, 0};
-  int max_iv = 0;
-  if constexpr (TABLE) {
-    riv = item_intervals(p.tb_rows, p.tb_iv, row, row_ok);
-    max_iv = wave_max_intervals(riv.n_iv);
-  }
-  const Ranges rr = TABLE ? riv.r : (row_ok ? row_ranges(g, row) : Ranges{0, 0, 0, 0});
+  const ItemIntervals riv = item_intervals(p.tb_rows, p.tb_iv, row, row_ok);
+  const int max_iv = wave_max_intervals(riv.n_iv);
 
   // Q and dO fragments (B operands) stay in accumulation registers; -delta
   // = -dO . O and -lse log2(e) of the row go to the workspace for the dk/dv
@@ -313,7 +293,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
     // The most negative finite float keeps its (masked) P at 0, where +inf
     // would give exp2(-inf + inf); finite, because the dk/dv kernel's delta
     // lanes read this plane past the last row, where 0 * -inf would be NaN.
-    if constexpr (TABLE) nl = lse == -INFINITY ? -FLT_MAX : nl;
+    nl = lse == -INFINITY ? -FLT_MAX : nl;
     if (row_ok) p.ws[(size_t)bh * 2 * N + (size_t)h * N + row] = h ? nl : ndelta;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -329,22 +309,18 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   int dma_voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) dma_voff[i] = TG::dma_voff(wave, lane, i);
-  // The q-th DMA instruction of tile t (past the last tile: that tile again,
-  // into a stage nothing reads, so every step issues the same number).
-  // (range-list plans pass the tile index, read once per step: tile_pre)
-  auto issue_part = [&](uint16_t* dst, int t, int q, int t_end, int tile_pre) {
-    int tile;
-    if constexpr (TABLE) tile = tile_pre;
-    else tile = span_tile(sp, t < t_end ? t : t_end - 1);
+  // The q-th DMA instruction of tile `tile` (the step's tile from the table,
+  // read once per step; past the last tile that tile again, into a stage
+  // nothing reads, so every step issues the same number).
+  auto issue_part = [&](uint16_t* dst, int q, int tile) {
     const int soff = tile * BC * D * 2;
     const int i = q >> 1, tt = q & 1;
     load16_lds_asm(tt ? desc_v : desc_k, dst + tt * TILE + (wave * LOADS + i) * 512, dma_voff[i], soff);
   };
-  auto issue = [&](uint16_t* dst, int t, int t_end) {
-    int tile_pre = 0;
-    if constexpr (TABLE) tile_pre = entry(t) & 0xffffff;
+  auto issue = [&](uint16_t* dst, int t) {
+    const int tile = entry(t) & 0xffffff;
 #pragma unroll
-    for (int q = 0; q < LPT; ++q) issue_part(dst, t, q, t_end, tile_pre);
+    for (int q = 0; q < LPT; ++q) issue_part(dst, q, tile);
   };
 
   f32x16 accQ[DC];
@@ -355,28 +331,10 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   }
   const float sl2 = p.score_log2;
 
-  // Key tiles that every valid row of the wave sees whole (scalar test);
-  // a wave without valid rows masks every tile.  Range-list plans: the
-  // entry's bit of this wave.
-  Ranges wfirst{0, 0, 0, 0}, wlast{0, 0, 0, 0};
-  if constexpr (!TABLE) {
-    const int wa = r0 + wave * 32;
-    const int wb = wa + 32 < r1 ? wa + 32 : r1;
-    if (wa < wb) {
-      wfirst = row_ranges(g, wa);
-      wlast = row_ranges(g, wb - 1);
-    }
-  }
-  // as step ranges: tiles inside [wlast.lo1, wfirst.hi1) or [wlast.lo2,
-  // wfirst.hi2), the keys every valid row of the wave sees
-  const StepRange w1 = span_steps_in(sp, first_whole_tile(wlast.lo1, BC), end_whole_tile(wfirst.hi1, BC));
-  const StepRange w2 = span_steps_in(sp, first_whole_tile(wlast.lo2, BC), end_whole_tile(wfirst.hi2, BC));
-  auto tile_whole = [&](int t) { return in_steps(w1, t) || in_steps(w2, t); };
-  // the partial-tile mask of scores of the tile at key k0
-  auto mask_tile = [&](f32x16& S, int k0) {
-    if constexpr (TABLE) mask_scores_iv(S, k0, h, riv, max_iv, p.tb_iv);
-    else mask_scores(S, k0, h, rr);
-  };
+  // A tile every valid row of the wave sees whole has this wave's bit set in
+  // its entry; the others take the partial-tile mask of scores of the tile
+  // at key k0.
+  auto mask_tile = [&](f32x16& S, int k0) { mask_scores_iv(S, k0, h, riv, max_iv, p.tb_iv); };
   auto exp_elem = [&](float x) { return __builtin_amdgcn_exp2f(fmaf(x, sl2, nl)); };
 
   u32x4 kf[KS], vf[KS];
@@ -399,7 +357,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   // of tile j+AHEAD; phase 2 opens with the barrier slot (every read of tile
   // j's stage is then issued), after which come the first K, V reads of tile
   // j+2, seven MFMAs ahead of their use.
-  auto step = [&](auto st, int j, int t_end, f32x16& P, f32x16& DP, f32x16& Sn, f32x16& DPn) {
+  auto step = [&](auto st, int j, f32x16& P, f32x16& DP, f32x16& Sn, f32x16& DPn) {
     constexpr int ST = decltype(st)::value;
     using NX = IC<(ST + 1) % STAGES>;
     using N2 = IC<(ST + 2) % STAGES>;
@@ -414,16 +372,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
       DS[jj >> 3][(jj & 7) >> 1] = pack_bf16(P[jj] * DP[jj], P[jj + 1] * DP[jj + 1]);
       pin(DS[jj >> 3][(jj & 7) >> 1]);
     };
-    // range-list plans: this step's DMA tile and the next tile's entry,
-    // prefetched by the previous step
-    int dma_tile = 0, next_e = 0;
-    if constexpr (TABLE) {
-      dma_tile = __builtin_amdgcn_readfirstlane(pf_dma) & 0xffffff;
-      next_e = __builtin_amdgcn_readfirstlane(pf_next);
-    }
+    // this step's DMA tile and the next tile's entry, prefetched by the
+    // previous step
+    const int dma_tile = __builtin_amdgcn_readfirstlane(pf_dma) & 0xffffff;
+    const int next_e = __builtin_amdgcn_readfirstlane(pf_next);
     auto dma = [&](int s) {
 #pragma unroll
-      for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q) issue_part(stage(AH{}), j + AHEAD, q, t_end, dma_tile);
+      for (int q = s * LPT / KS; q < (s + 1) * LPT / KS; ++q) issue_part(stage(AH{}), q, dma_tile);
     };
 
     constexpr int PAIRS = 8 / KS;  // dS element pairs per k-step
@@ -453,11 +408,7 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
       const int c2 = gidx / DC, c = gidx % DC;
       accQ[c] = mfma_bf16(ktf[gidx], DS[c2], accQ[c]);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (TABLE) {
-        if (gidx == 0 && !((next_e >> (24 + wave)) & 1)) mask_tile(Sn, (next_e & 0xffffff) * BC);  // rare
-      } else {
-        if (gidx == 0 && !tile_whole(j + 1)) mask_tile(Sn, span_tile(sp, j + 1) * BC);  // rare
-      }
+      if (gidx == 0 && !((next_e >> (24 + wave)) & 1)) mask_tile(Sn, (next_e & 0xffffff) * BC);  // rare
       if (gidx == 0 && ST % BAR == 0) {
         // tiles up to j+BAR+1 have landed; reads up to tile j are complete
         wait_lgkmcnt<0>();
@@ -477,9 +428,9 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
     }
   };
 
-  auto first_tile = [&](int t_begin, int t_end) {
+  auto first_tile = [&](int t_begin) {
 #pragma unroll
-    for (int i = 0; i < AHEAD; ++i) issue(ring[i], t_begin + i, t_end);
+    for (int i = 0; i < AHEAD; ++i) issue(ring[i], t_begin + i);
     wait_vmcnt<(AHEAD - 2) * LPT>();  // first two tiles
     barrier_nofence();
 #pragma unroll
@@ -496,12 +447,8 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     acc_hazard_wait();
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (TABLE) {
-      const int e = entry(t_begin);
-      if (!((e >> (24 + wave)) & 1)) mask_tile(SA, (e & 0xffffff) * BC);
-    } else {
-      if (!tile_whole(t_begin)) mask_tile(SA, span_tile(sp, t_begin) * BC);
-    }
+    const int e = entry(t_begin);
+    if (!((e >> (24 + wave)) & 1)) mask_tile(SA, (e & 0xffffff) * BC);
 #pragma unroll
     for (int i = 0; i < 16; ++i) SA[i] = exp_elem(SA[i]);
     kvread(ring[1], 0);
@@ -509,13 +456,13 @@ __global__ void __launch_bounds__(NW * 64, 1) bwd_dq_bf16_kernel(BwdParams p) {
   };
 
   if (ntiles > 0) {
-    first_tile(0, ntiles);
+    first_tile(0);
     prefetch_entries(0);
     for (int j = 0; j < ntiles; j += STAGES) {
       const bool more = unrolled_while<0, STAGES>([&](auto st) {
         constexpr int S = decltype(st)::value;
-        if constexpr (S % 2 == 0) step(st, j + S, ntiles, SA, DA, SB, DB);
-        else step(st, j + S, ntiles, SB, DB, SA, DA);
+        if constexpr (S % 2 == 0) step(st, j + S, SA, DA, SB, DB);
+        else step(st, j + S, SB, DB, SA, DA);
         return j + S + 1 < ntiles;
       });
       if (!more) break;
@@ -1340,7 +1287,7 @@ void launch_bwd_kernels(int dtype, int bh, const BwdParams& p, hipStream_t strea
     // both kernels take their tasks from the call's work queues, one after the other
     const dim3 block(kBf16Waves * 64);
     if constexpr (TABLE)
-      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, kBf16Waves, true>), dim3((unsigned)queue_grid((int)gq.x)), block, 0,
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, kBf16Waves>), dim3((unsigned)queue_grid((int)gq.x)), block, 0,
                          stream, p);
     else
       hipLaunchKernelGGL((bwd_dq2_bf16_kernel<D, kBf16Waves>), dim3((unsigned)queue_grid((int)gq.x)), block, 0,

@@ -90,11 +90,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
-// 16 bytes per lane from global (byte offset voff + soff, soff wave-uniform)
-// straight into LDS at lds + 16 * lane, through the compiler builtin.
-__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds, 16, voff, soff, 0, 0);
-}
 
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 // Buffer descriptor as four dwords (base, stride 0, byte size, the same
@@ -113,8 +108,10 @@ __device__ __forceinline__ i32x4_t make_desc(const void* base, int bytes) {
 // address (a generic LDS address is the LDS aperture base plus the LDS
 // offset), with no null-pointer handling as in a cast to the LDS space.
 __device__ __forceinline__ int lds_addr(const void* p) { return (int)(uint32_t)(uintptr_t)p; }
-// The same DMA written out.  Where the compiler tracks its own LDS DMA
-// against later LDS reads, it may wait for every DMA in flight (vmcnt(0))
+// 16 bytes per lane from global (byte offset voff + soff, soff wave-uniform)
+// straight into LDS at lds + 16 * lane, written out rather than through the
+// compiler builtin.  Where the compiler tracks its own LDS DMA against later
+// LDS reads, it may wait for every DMA in flight (vmcnt(0))
 // before a read of another ring stage, which exposes the whole DMA latency
 // once per tile.  A kernel using this DMA orders its ring itself (explicit vmcnt waits and
 // barriers before a stage is read or refilled), so the DMA is hidden from the
