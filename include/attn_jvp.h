@@ -354,20 +354,22 @@ int attn_jvp_key_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
 /* Launch order: workgroup t (0 <= t < n_query_blocks) of every (b, h)
  * handles query block host_out[t] (index order of attn_jvp_tile_map).
- * Heaviest (latest) blocks first.  With tf_layout = 1 the sides alternate
- * block by block; in clean-tangent-zero plans, whose clean blocks carry less
- * work, clean and noisy blocks of the same chunks come in groups of 8 and 8,
- * so that the round-robin hand-out of workgroups to the 8 XCDs gives each XCD
- * both sides.  Range-list plans: host_out holds the heavy-first order of
- * the query blocks (more streamed tiles first).  "Workgroup t" is the
- * logical task t: over the whole B H grid, the tasks are ordered in XCD
- * groups of 128 under the rule of attn_jvp_bwd_launch_order (there with
- * groups of 32) and taken from its per-XCD queues, except on the smaller
- * grids: there clean-tangent-zero plans keep the index order, and general
- * teacher-forcing plans go heavy first across the slices in groups of 32
- * consecutive tasks of one slice.  (The bf16 kernel without tangents of
- * descriptor plans, attn_jvp_fwd_primal, runs the same order with a fixed
- * grid, workgroup b taking position b.)  n is the capacity of host_out in int32 elements. */
+ * This is the order of attn_jvp_fwd.  Heaviest (latest) blocks first.  With
+ * tf_layout = 1 the sides alternate block by block; bf16 clean-tangent-zero
+ * plans make two launches, so their first n_query_blocks / 2 entries are the
+ * clean side's blocks and the rest the noisy side's, each heaviest first.
+ * Range-list plans: host_out holds the heavy-first order of the query blocks
+ * (more streamed tiles first).  "Workgroup t" is the logical task t: over
+ * the whole B H grid (of each launch), the tasks are ordered in XCD groups
+ * of 128 under the rule of attn_jvp_bwd_launch_order (there with groups of
+ * 32) and taken from its per-XCD queues, except on the smaller grids: there
+ * clean-tangent-zero plans keep the index order, and general teacher-forcing
+ * plans go heavy first across the slices in groups of 32 consecutive tasks
+ * of one slice.  (attn_jvp_fwd_primal of descriptor plans, whatever the
+ * plan's flags, takes the clean and noisy blocks of the same chunks in
+ * groups of 8 and 8, so that the round-robin hand-out of workgroups to the 8
+ * XCDs gives each XCD both sides, in the index order on small grids.)  n is
+ * the capacity of host_out in int32 elements. */
 int attn_jvp_launch_order(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
 
 /* Tile map, row-major [n_query_blocks][n_key_tiles], query blocks in index

@@ -988,6 +988,12 @@ int attn_jvp_launch_order(const attn_jvp_plan* p, int32_t* out, size_t n) {
     std::memcpy(out, p->rs->table.data() + p->rs->off_order, sizeof(int32_t) * p->n_qblocks);
     return ok();
   }
+  if ((p->flags & ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO) && p->dtype == ATTN_JVP_BF16) {
+    // two launches: the clean side's blocks, then the noisy side's, each heavy first
+    const int32_t nbs = p->n_qblocks / 2;
+    for (int32_t t = 0; t < p->n_qblocks; ++t) out[t] = (t < nbs ? 0 : nbs) + nbs - 1 - (t < nbs ? t : t - nbs);
+    return ok();
+  }
   const bool balanced = (p->flags & ATTN_JVP_FLAG_CLEAN_TANGENT_ZERO) != 0;
   for (int32_t t = 0; t < p->n_qblocks; ++t) out[t] = heavy_first_qblock(p->g, p->block_q, t, balanced);
   return ok();

@@ -160,15 +160,8 @@ def test_launch_order_is_a_heavy_first_permutation(desc, ctz):
             assert np.all(np.diff(order[side == sd]) < 0)
         if not ctz:  # sides alternate block by block
             assert np.all(side == np.arange(nq) % 2)
-        else:
-            # each aligned group of 16 slots holds 8 clean and 8 noisy blocks:
-            # with round-robin hand-out every XCD gets both sides
-            full = (nbs // 8) * 16
-            for g0 in range(0, full, 16):
-                assert side[g0:g0 + 8].sum() == 0 and side[g0 + 8:g0 + 16].sum() == 8
-            for x in range(8):
-                sl = side[:full][x::8]
-                assert int(sl.sum()) * 2 == len(sl)
+        else:  # two launches: the clean side's blocks, then the noisy side's
+            assert np.all(side[:nbs] == 0) and np.all(side[nbs:] == 1)
 
 
 def test_create_rejects_non_finite_scale():

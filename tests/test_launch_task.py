@@ -159,3 +159,49 @@ def test_small_rank_groups_structure(harness, slices, per_slice):
     k = np.arange(len(tail))
     assert np.array_equal(slice_of[pos:], k % slices)
     assert np.array_equal(rank[pos:], per_groups * GROUP + k // slices)
+
+
+BALANCED = r"""
+#include <cstdio>
+#include <cstdlib>
+#include "mask_index.h"
+int main(int argc, char** argv) {
+  attn_jvp::MaskGeom g{};
+  g.tf = 1;
+  g.chunk_len = atoi(argv[1]);
+  g.side_len = atoi(argv[2]);
+  g.seq_len = 2 * g.side_len;
+  const int bq = atoi(argv[3]);
+  const int nq = attn_jvp::n_query_blocks(g, bq);
+  for (int t = 0; t < nq; ++t) printf("%d\n", attn_jvp::heavy_first_qblock(g, bq, t, true));
+  return 0;
+}
+"""
+
+
+@pytest.mark.parametrize("chunk, side", [(1560, 32760), (4680, 32760), (50, 250), (16, 48), (100, 4000)])
+def test_balanced_order_of_the_forward_without_tangents(tmp_path, chunk, side):
+    """attn_jvp_fwd_primal (descriptor plans) takes heavy_first_qblock's
+    balanced order: every block once, each side heaviest first, and aligned
+    groups of 16 positions holding 8 clean then 8 noisy blocks, so that the
+    round-robin hand-out gives every XCD both sides."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not found")
+    src, exe = tmp_path / "bal.cpp", tmp_path / "bal"
+    src.write_text(BALANCED)
+    subprocess.run([gxx, "-O1", "-std=c++17", f"-I{CSRC}", str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe), str(chunk), str(side), "128"], capture_output=True, text=True, check=True).stdout
+    order = np.array([int(x) for x in out.split()])
+    nq = len(order)
+    nbs = nq // 2
+    assert sorted(order.tolist()) == list(range(nq))
+    sd = (order >= nbs).astype(int)
+    for s in (0, 1):
+        assert np.all(np.diff(order[sd == s]) < 0)
+    full = (nbs // 8) * 16
+    for g0 in range(0, full, 16):
+        assert sd[g0:g0 + 8].sum() == 0 and sd[g0 + 8:g0 + 16].sum() == 8
+    for x in range(8):
+        sl = sd[:full][x::8]
+        assert int(sl.sum()) * 2 == len(sl)
