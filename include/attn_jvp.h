@@ -361,8 +361,9 @@ int attn_jvp_key_ranges(const attn_jvp_plan* plan, int32_t* host_out, size_t n);
  * Range-list plans: host_out holds the heavy-first order of the query blocks
  * (more streamed tiles first).  "Workgroup t" is the logical task t: over
  * the whole B H grid (of each launch), the tasks are ordered in XCD groups
- * of 128 under the rule of attn_jvp_bwd_launch_order (there with groups of
- * 32) and taken from its per-XCD queues, except on the smaller grids: there
+ * of 128 (64 in the noisy-side launch of a clean-tangent-zero plan) under the
+ * rule of attn_jvp_bwd_launch_order (there with groups of 32) and taken from
+ * its per-XCD queues, except on the smaller grids: there
  * clean-tangent-zero plans keep the index order, and general teacher-forcing
  * plans go heavy first across the slices in groups of 32 consecutive tasks
  * of one slice.  (attn_jvp_fwd_primal of descriptor plans, whatever the

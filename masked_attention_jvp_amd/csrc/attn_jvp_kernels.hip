@@ -107,20 +107,22 @@ __global__ void __launch_bounds__(NW * 64, PO ? 2 : 1) fwd_bf16_kernel(FwdParams
   const MaskGeom g = p.g;
   const int N = g.seq_len;
   // Workgroups take the positions of the heavy-first order, in XCD groups of
-  // kFwdXcdGroup (launch_task), from the per-XCD work queues (take_task):
+  // kFwdXcdGroup (launch_task; the noisy-side launch of a clean-tangent-zero
+  // plan: kCtzNoisyXcdGroup), from the per-XCD work queues (take_task):
   // neighbouring blocks of that order, which stream nearly the same key tiles,
   // share an XCD's L2, and an XCD that finishes its share early takes the
-  // rest of another's.  Clean-tangent-zero plans group their
-  // balanced order (8 clean and 8 noisy blocks in turn, so every group holds
-  // both sides) and keep it in index order on small grids, where that was
-  // 3 % faster than heavy first across heads.  On small grids general
-  // teacher-forcing plans take rank-major groups of 32 (3 % faster at 3 heads
-  // than heavy first across heads, which the other plans keep).
+  // rest of another's.  The clean-tangent-zero instances (one side per
+  // launch; the primal call over both sides in the balanced order, 8 clean
+  // and 8 noisy blocks in turn) keep the index order on small grids, where
+  // that was 3 % faster than heavy first across heads.  On small grids
+  // general teacher-forcing plans take rank-major groups of 32 (3 % faster
+  // at 3 heads than heavy first across heads, which the other plans keep).
   const int32_t small = (CTZ && !TABLE) ? kSmallIndex
                         : (!TABLE && p.g.tf) ? kSmallRankGroups : kSmallAcross;
   const int pos = workgroup_task(p.queues, p.n_tasks);
   if (pos < 0) return;  // the queues were empty: no task for this workgroup
-  const int task = launch_task(pos, p.n_tasks, p.n_qblocks, kFwdXcdGroup, small);
+  constexpr int32_t kGroup = (CTZ && !PO && !TABLE) ? kCtzNoisyXcdGroup : kFwdXcdGroup;
+  const int task = launch_task(pos, p.n_tasks, p.n_qblocks, kGroup, small);
   const int bh = task / p.n_qblocks;
   int qb, r0, r1, ntiles, e0 = 0;
   TileSpans sp{0, 0, 0, 0};

@@ -114,6 +114,8 @@ void bwd_block_sizes(int dtype, int head_dim, int* block_q, int* block_kv);
 constexpr int kDkdvXcdGroup = 32;
 // Query blocks per XCD group of the forward + JVP's launch order.
 constexpr int kFwdXcdGroup = 128;
+// The same for the noisy-side launch of clean-tangent-zero plans.
+constexpr int kCtzNoisyXcdGroup = 64;
 
 // Launch the backward (dq kernel, then dk/dv kernel) for bh = B * H slices.
 hipError_t launch_bwd(int dtype, int head_dim, int bh, const BwdParams& p, hipStream_t stream);
