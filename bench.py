@@ -401,7 +401,8 @@ def main():
     dq_kernel = f"bwd_dq_bf16_kernel<{w.head_dim},{nw}>" if use_ranges else f"bwd_dq2_bf16_kernel<{w.head_dim},{nw}>"
     kernel = (f"{dq_kernel} + bwd_dkdv_bf16_kernel<{w.head_dim},{nw},{tb}>"
               if args.backward
-              else f"fwd_bf16_kernel<{w.head_dim},{nw},true,true> (primal tile mode)" if args.primal and use_ranges
+              else (f"fwd_bf16_kernel<{w.head_dim},{nw},true,true,true> (primal-only)" if int(table[4]) <= 3968  # entry limit
+                    else f"fwd_bf16_kernel<{w.head_dim},{nw},true,true> (primal tile mode)") if args.primal and use_ranges
               else f"fwd_bf16_kernel<{w.head_dim},{nw},true,false,true> (primal-only)" if args.primal
               else (f"fwd_bf16_kernel<{w.head_dim},{nw},true,false,true> (clean side) + "
                     f"fwd_bf16_kernel<{w.head_dim},{nw},true,false> (noisy side)") if flags
